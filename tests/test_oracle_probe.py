@@ -1,0 +1,156 @@
+"""Oracle pins for page 1's probe selection (probe max over sampled keys, importance
+budget (k+1)/2, probe fill, recency insurance).
+
+Pinned against: page 1's printed budget values, the probe positions the printed loop
+visits, numpy matmul block maxima, numpy argmax / lexsort / float32 cumsum, brute force
+on tiny inputs in a sort-based two-stage form, and config 3's needle and k=1 behaviour.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from top_kv_block_amd import workloads as W
+from tests.helpers import cdiv, check_selection_rows, f64, golden_rows
+
+
+def _run(oracle, wl, k, importance=True, n_probe=8, flags=W.RECENCY):
+    return oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, wl.N,
+                               importance=wl.importance if importance else None,
+                               n_probe=n_probe, flags=flags)
+
+
+def test_budget_table(oracle):
+    wl = W.random_case(31, 1, 4, 2, 32, [64 * 32], k=1, with_importance=True)
+    for k, budget, _printed in golden_rows("p1_importance_budget.txt"):
+        r = _run(oracle, wl, int(k))
+        assert np.all(r["n_imp"] == int(budget)), (k, r["n_imp"])
+        check_selection_rows(r["selected"], r["n_selected"], int(k))
+
+
+def test_k1_gives_only_slot_to_importance(oracle):
+    wl = W.random_case(32, 2, 4, 2, 32, [64 * 32, 1000], k=1, with_importance=True)
+    r = _run(oracle, wl, 1)
+    for b in range(2):
+        best = int(np.argmax(r["imp_sum"][b, :cdiv(int(wl.seq_lens[b]), 32)]))
+        assert np.all(r["selected"][b, :, 0] == best)
+        assert np.all(r["n_selected"][b] == 1)
+
+
+def test_probe_positions(oracle):
+    """probe = max of q.K over exactly the positions page 1's loop visits."""
+    for row in golden_rows("p1_probe_offsets.txt"):
+        ntok, npb, offs = int(row[0]), int(row[1]), [int(x) for x in row[2:]]
+        BS = 32
+        L = 2 * BS + ntok if ntok < BS else 3 * BS
+        wl = W.random_case(33, 1, 4, 2, BS, [L], k=2)
+        r = _run(oracle, wl, 2, importance=False, n_probe=npb)
+        i = cdiv(L, BS) - 1                                     # the last (maybe partial) block
+        phys = int(wl.block_tables[0, i])
+        keys = f64(wl.k_cache[phys])                            # [BS, N, D]
+        for h in range(wl.H):
+            dots = keys[offs, h // wl.G] @ f64(wl.query[0, h])
+            np.testing.assert_allclose(r["probe"][0, h, i], dots.max(), rtol=1e-12)
+
+
+def test_full_sampling_equals_block_max_and_lower_bound(oracle):
+    lens = [10 * 32 + 7, 96]
+    wl = W.random_case(34, 2, 8, 4, 32, lens, k=3)
+    full = _run(oracle, wl, 3, importance=False, n_probe=32)["probe"]
+    part = _run(oracle, wl, 3, importance=False, n_probe=8)["probe"]
+    for b, L in enumerate(lens):
+        for h in range(wl.H):
+            for i in range(cdiv(L, 32)):
+                phys = int(wl.block_tables[b, i])
+                keys = f64(wl.k_cache[phys, :min(32, L - 32 * i), h // wl.G])
+                bmax = (keys @ f64(wl.query[b, h])).max()
+                np.testing.assert_allclose(full[b, h, i], bmax, rtol=1e-12)
+                assert part[b, h, i] <= bmax + 1e-12
+
+
+def test_importance_sum_is_sequential_float32(oracle):
+    lens = [10 * 32 + 5]
+    wl = W.random_case(35, 1, 2, 1, 32, lens, k=2, with_importance=True)
+    r = _run(oracle, wl, 2)
+    imp = wl.importance.numpy()[0]
+    for i in range(cdiv(lens[0], 32)):
+        seg = imp[32 * i:min(32 * (i + 1), lens[0])]
+        want = np.cumsum(seg, dtype=np.float32)[-1]
+        assert r["imp_sum"][0, i].view(np.uint32) == np.float32(want).view(np.uint32)
+
+
+def test_no_importance_is_probe_lexsort_plus_recency(oracle):
+    wl = W.random_case(36, 1, 4, 2, 32, [40 * 32], k=6)
+    for flags in (0, W.RECENCY):
+        r = _run(oracle, wl, 6, importance=False, flags=flags)
+        for h in range(wl.H):
+            p = r["probe"][0, h, :40]
+            order = list(np.lexsort((np.arange(40), -p)))[:6]
+            if flags and 39 not in order:
+                order[-1] = 39
+            assert set(r["selected"][0, h].tolist()) == set(int(x) for x in order)
+
+
+def _two_stage(imp, probe, nb, k, has_imp, recency):
+    """Sort-based statement of the greedy stages (independent of the greedy loops)."""
+    chosen = []
+    if has_imp:
+        budget = min((k + 1) // 2, nb)
+        chosen = [int(x) for x in np.lexsort((np.arange(nb), -imp[:nb].astype(np.float64)))[:budget]]
+    rest = [i for i in range(nb) if i not in chosen]
+    rest_sorted = sorted(rest, key=lambda i: (-probe[i], i))
+    fill = rest_sorted[:max(0, min(k, nb) - len(chosen))]
+    if recency and nb > 0 and (nb - 1) not in chosen and (nb - 1) not in fill and fill:
+        fill[-1] = nb - 1
+    return set(chosen) | set(fill), len(chosen)
+
+
+def test_bruteforce_tiny(oracle):
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        BS = 16
+        nb = int(rng.integers(1, 9))
+        L = nb * BS - int(rng.integers(0, BS))
+        k = int(rng.integers(1, 10))
+        wl = W.random_case(100 + trial, 1, 2, 1, BS, [L], k=k, with_importance=True)
+        # coarse importance values -> exact ties in the importance stage
+        wl.importance = torch.round(wl.importance * 4) / 4
+        for has_imp in (True, False):
+            for rec in (0, W.RECENCY):
+                r = _run(oracle, wl, k, importance=has_imp, flags=rec)
+                for h in range(wl.H):
+                    want, n_imp = _two_stage(r["imp_sum"][0], r["probe"][0, h], nb, k, has_imp, rec)
+                    got = set(r["selected"][0, h, :r["n_selected"][0, h]].tolist())
+                    assert got == want, (trial, has_imp, rec, h, got, want)
+                    assert r["n_imp"][0, h] == n_imp
+
+
+def test_recency_never_evicts_importance(oracle):
+    wl = W.random_case(37, 1, 4, 2, 32, [64 * 32], k=4, with_importance=True)
+    imp = torch.zeros_like(wl.importance)
+    imp[0, :64] = 1.0                                     # importance on blocks 0 and 1
+    wl.importance = imp
+    r = _run(oracle, wl, 4)
+    for h in range(wl.H):
+        s = set(r["selected"][0, h].tolist())
+        assert {0, 1, 63} <= s
+
+
+def test_config3_k_sweep(oracle):
+    """k=1 takes the top importance block only; from k=4 on the needle block is in
+    every head's selection (k=2 shows page 1's small-k failure: recency evicts the
+    single probe pick); the most recent block is always kept when k > 1."""
+    base = W.config3()
+    needle_block = base.needles[0][1] // base.BS
+    nb = int(base.seq_lens[0]) // base.BS
+    for k in (1, 2, 4, 8, 16, 32):
+        r = _run(oracle, base, k)
+        sel, ns = r["selected"], r["n_selected"]
+        check_selection_rows(sel, ns, k)
+        assert np.all(r["n_imp"] == (k + 1) // 2)
+        if k == 1:
+            assert np.all(sel[0, :, 0] == int(np.argmax(r["imp_sum"][0, :nb])))
+        else:
+            assert np.all([nb - 1 in set(sel[0, h].tolist()) for h in range(base.H)])
+        if k >= 4:
+            assert all(needle_block in set(sel[0, h].tolist()) for h in range(base.H)), k
