@@ -1,0 +1,269 @@
+"""Decode-step benchmark of the sparse top-k KV-block attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload config5|config4]
+
+A step is one pass of the path over one batch: Quest block selection (grouped-query
+scoring, top-k, sink/window forcing) followed by exact attention over the selected
+blocks. The default workload is the large-batch serving decode: B=128, H=64, N=8, D=128,
+BS=128, seq_len=32768, k=16, bf16 K/V (8 GiB each) in a shuffled paged pool; step s uses
+query set s mod 4 and tokens_since_metadata_update = s mod 128. The metadata rebuild
+(every 128 steps in that workload) is timed on its own and reported beside the step.
+
+Prints one JSON line: steps/s, ms/step, achieved algorithmic HBM GB/s of the step and of
+the attention kernel (HIP events around each attention launch on the launch stream),
+and the CPU oracle's rate on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "sparse decode steps/s (select+attn) and achieved HBM GB/s vs MI355X peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def forced_count(L, BS, k, tsmu, flags):
+    """Blocks the sink/window rule forces in (their metadata is not read)."""
+    nb = cdiv(L, BS)
+    if nb == 0 or tsmu < 0:
+        return 0
+    cnt, lo = 0, nb
+    if flags & 2:
+        n_meta = min(max((L - tsmu) // BS, 0), nb - 1)
+        lo = max(n_meta, nb - k)
+        cnt = nb - lo
+    if (flags & 1) and cnt < k and lo > 0:
+        cnt += 1
+    return cnt
+
+
+def step_bytes(wl, sel_h, ns_h, tsmu_h):
+    """Algorithmic bytes of one step: what the method must read and write.
+
+    select: max+min metadata rows of every non-forced candidate block (2*D*esize per
+    (block, kv head)), the query, the indices written; attention: K and V rows of every
+    valid token of every selected block for its kv head, the query, the output."""
+    es = wl.k_cache.element_size()
+    sl = wl.seq_lens.cpu().tolist()
+    BS, N, D, H, B, k = wl.BS, wl.N, wl.D, wl.H, wl.B, wl.k
+    sel_b = 0
+    for b in range(B):
+        nb = cdiv(sl[b], BS)
+        cand = nb - forced_count(sl[b], BS, k, int(tsmu_h[b]), wl.flags)
+        sel_b += cand * N * 2 * D * es
+    sel_b += B * H * D * es + B * N * (k + 1) * 4
+    att_b = 0
+    for b in range(B):
+        for n in range(N):
+            for j in range(int(ns_h[b, n])):
+                blk = int(sel_h[b, n, j])
+                att_b += min(BS, sl[b] - blk * BS) * D * es * 2
+    att_b += 2 * B * H * D * es + B * N * (k + 1) * 4
+    return sel_b, att_b
+
+
+def gather_requests(wl, reqs):
+    """CPU copies of the sampled requests' blocks with remapped tables (marshalling)."""
+    BS = wl.BS
+    bt, mt = wl.block_tables.cpu(), wl.meta_tables.cpu()
+    sl, msl = wl.seq_lens.cpu(), wl.meta_seq_lens.cpu()
+    nbs = [cdiv(int(sl[b]), BS) for b in reqs]
+    phys = torch.cat([bt[b, :nb].long() for b, nb in zip(reqs, nbs)]).to(wl.k_cache.device)
+    kc, vc = wl.k_cache[phys].cpu(), wl.v_cache[phys].cpu()
+    nt = torch.zeros((len(reqs), bt.shape[1]), dtype=torch.int32)
+    nmt = torch.zeros((len(reqs), mt.shape[1]), dtype=torch.int32)
+    off = moff = 0
+    for j, nb in enumerate(nbs):
+        nt[j, :nb] = torch.arange(off, off + nb, dtype=torch.int32)
+        off += nb
+        m = cdiv(nb, BS)
+        nmt[j, :m] = torch.arange(moff, moff + m, dtype=torch.int32)
+        moff += m
+    return dict(kc=kc, vc=vc, bt=nt, mt=nmt, nmeta=max(1, moff), sl=sl[reqs].clone(), msl=msl[reqs].clone())
+
+
+def run_cpu_baseline(wl, qsets, tsmu_tab, n_req, min_seconds):
+    from oracle import oracle as O
+    reqs = list(range(min(n_req, wl.B)))
+    log(f"cpu baseline: gathering {len(reqs)} requests to the host")
+    g = gather_requests(wl, reqs)
+    mx, mn = O.build_metadata(g["kc"], g["bt"], g["msl"], g["mt"], g["nmeta"])   # untimed: not part of a step
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        q = qsets[steps % qsets.shape[0]].cpu()[reqs]
+        ts = tsmu_tab[steps % tsmu_tab.shape[0]].cpu()[reqs]
+        sel, ns, _ = O.block_select(q, mx, mn, g["mt"], g["sl"], wl.k, tsmu=ts, flags=wl.flags)
+        O.sparse_attn_decode(q, g["kc"], g["vc"], g["bt"], g["sl"], sel, ns, wl.N)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per_sample_step = el / steps
+    full_step = per_sample_step * wl.B / len(reqs)
+    return {"value": 1.0 / full_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(reqs)} of {wl.B} requests of the same workload, {steps} sample steps in {el:.1f} s, "
+                      f"scaled by {wl.B}/{len(reqs)}; single-threaded C oracle (fp64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="config5", choices=["config5", "config4"])
+    ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no cross-GPU step in this build (see the sharding "
+              "design); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from top_kv_block_amd import qsparse as qs
+    from top_kv_block_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {args.workload} on the GPU")
+    wl = W.config5(device=dev) if args.workload == "config5" else W.config4(device=dev)
+    qsets = wl.extra.get("query_sets", wl.query[None])
+    B, H, N, D, BS, k = wl.B, wl.H, wl.N, wl.D, wl.BS, wl.k
+    if args.workload == "config5":
+        tsmu_tab = (torch.arange(128, dtype=torch.int32, device=dev)[:, None] % 128).repeat(1, B).contiguous()
+    else:
+        tsmu_tab = wl.tsmu[None].contiguous()
+    mx = torch.zeros((wl.num_meta_blocks, BS, N, D), dtype=wl.k_cache.dtype, device=dev)
+    mn = torch.zeros_like(mx)
+    sel = torch.empty((B, N, k), dtype=torch.int32, device=dev)
+    ns = torch.empty((B, N), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, D), dtype=wl.query.dtype, device=dev)
+    ws_sel = torch.zeros(qs.block_select_workspace_bytes(B, N, BS, wl.mmbpr), dtype=torch.uint8, device=dev)
+    ws_att = torch.zeros(qs.sparse_attn_workspace_bytes(B, H, N, D, N, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def rebuild():
+        qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+
+    def select(s):
+        qs.qs_block_select(qsets[s % qsets.shape[0]], mx, mn, wl.meta_tables, wl.seq_lens, k,
+                           tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]], flags=wl.flags, selected=sel,
+                           n_selected=ns, workspace_buf=ws_sel)
+
+    def attend(s):
+        qs.qs_sparse_attn_decode(qsets[s % qsets.shape[0]], wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                 sel, ns, sel_heads=N, out=out, workspace_buf=ws_att)
+
+    log("metadata build")
+    rebuild()
+    torch.cuda.synchronize()
+    # metadata rebuild, timed on its own
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        rebuild()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rebuild_ms = e0.elapsed_time(e1) / 3
+    es = wl.k_cache.element_size()
+    mlens = [max(int(L), 0) for L in wl.meta_seq_lens.cpu().tolist()]
+    meta_bytes = sum(L * N * D * es for L in mlens) + \
+        sum(cdiv(cdiv(L, BS), BS) * BS * N * D * es * 2 for L in mlens)   # K read + max/min rows written
+
+    log(f"warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        select(s)
+        attend(s)
+    torch.cuda.synchronize()
+
+    # bytes of every step in the timed window (selection-dependent), computed afterwards
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    sels = []
+    log(f"timing {K} steps")
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(K):
+        select(s)
+        ev[s][0].record(stream)
+        attend(s)
+        ev[s][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # replay the selections of the timed steps to count their algorithmic bytes
+    log("counting algorithmic bytes of the timed steps")
+    sel_bytes = att_bytes = 0
+    sample_steps = sorted(set([0, 1, 2, 3] + list(range(0, K, max(1, K // 16)))))
+    for s in sample_steps:
+        select(s)
+        torch.cuda.synchronize()
+        sb, ab = step_bytes(wl, sel.cpu(), ns.cpu(), tsmu_tab[s % tsmu_tab.shape[0]].cpu())
+        sel_bytes += sb
+        att_bytes += ab
+    sel_bytes /= len(sample_steps)
+    att_bytes /= len(sample_steps)
+    ms_per_step = total_ms / K
+    step_gbps = (sel_bytes + att_bytes) / (ms_per_step * 1e-3) / 1e9
+    attn_avg_ms = float(attn_ms.mean())
+    attn_gbps = att_bytes / (attn_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "block_size": BS,
+                   "seq_len": int(wl.seq_lens.max()), "k": k, "flags": "sink+window",
+                   "query_sets": int(qsets.shape[0])},
+        "step_bytes": int(sel_bytes + att_bytes),
+        "step_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "select_bytes": int(sel_bytes),
+        "attention_bytes": int(att_bytes),
+        "metadata_rebuild_ms": round(rebuild_ms, 4),
+        "metadata_rebuild_gbps": round(meta_bytes / (rebuild_ms * 1e-3) / 1e9, 1),
+        "steps_per_s_with_rebuild_every_128": round(128.0 / (128 * ms_per_step + rebuild_ms) * 1000.0, 3),
+        "roofline": {"kernel": "attn_kernel (qs_sparse_attn_decode)", "bound": "hbm",
+                     "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(attn_avg_ms * 1000, 3), "bytes_per_launch": int(att_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_cpu_baseline(wl, qsets, tsmu_tab, args.cpu_sample, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * qsparse.h -- C ABI of the decode-time sparse top-k KV-block attention library
+ * (libqsparse.so, HIP kernels for CDNA4 / gfx950).
+ *
+ * Four operations, run in this order on each decode step:
+ *   qs_build_metadata      per-block, per-channel max/min of K (after prefill, and again
+ *                          whenever the metadata is refreshed);
+ *   qs_block_select        Quest top-k block selection on the grouped query, optional
+ *                          sink / local-window forcing;   (or)
+ *   qs_probe_select        probe + prefill-importance + recency block selection;
+ *   qs_sparse_attn_decode  exact softmax attention over the selected blocks only.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择"
+ *        (developer.aliyun.com/article/1767763).
+ *   [P3] "ops-transformer select_attention_operators: 基于 Quest 在 Ascend 910B 上实现
+ *        稀疏注意力块预测的加速内核" (bjdmk.com.cn/news/4805529).
+ *
+ * Conventions shared by every call
+ *   - Sizes: B requests, H query heads, N KV heads (H % N == 0, G = H / N query heads
+ *     per KV head, grouped contiguously: KV head n serves heads n*G .. n*G+G-1),
+ *     D = 128 head dimension, BS = block_size tokens per KV block (16, 32, 64 or 128).
+ *     A request with L tokens has nb = ceil(L / BS) blocks, numbered 0 .. nb-1 in
+ *     sequence order ("sequence-relative" indices).
+ *   - Pointers: every array argument is a device pointer to caller-owned, contiguous,
+ *     row-major memory in the layout stated next to it. The library never allocates,
+ *     frees or keeps a pointer after the call returns.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns without synchronising.
+ *   - Errors: arguments the host can see are checked before any HIP call; a failed
+ *     check returns QS_ERR_INVALID (inconsistent or null arguments) or
+ *     QS_ERR_UNSUPPORTED (valid but not implemented: D != 128, other block sizes or
+ *     dtypes) and enqueues nothing. A failed launch returns QS_ERR_HIP. qs_last_error()
+ *     gives a message for the calling thread's last failure. Nothing aborts or prints.
+ *   - Device-resident data (seq_lens, tables, selections) is read by the kernels. Table
+ *     entries out of range are never dereferenced: the block they name is skipped.
+ *     Negative seq_lens count as 0.
+ *   - Determinism: identical inputs give bit-identical outputs ([P1] section 1: same
+ *     query and same KV must select the same blocks; ties go to the lower index).
+ *   - Workspaces: calls that take `workspace` use its first 256 KiB for arrival
+ *     counters and the rest for scores and partial results. Zero-fill the first 256 KiB
+ *     once before the first use; every call returns the counters it used to zero, so one
+ *     workspace can serve calls of any size and either operation. It must be 256-byte
+ *     aligned, at least the size the matching *_workspace_bytes() returns, and not used
+ *     by calls that may run concurrently (calls on one stream are ordered).
+ */
+#ifndef QSPARSE_H
+#define QSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QS_OK = 0,
+    QS_ERR_INVALID = 1,
+    QS_ERR_UNSUPPORTED = 2,
+    QS_ERR_HIP = 3
+} qs_status;
+
+typedef enum {
+    QS_F32 = 0,  /* IEEE binary32 */
+    QS_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+    QS_I8 = 2    /* int8 codes with fp32 per-row scales (KV caches only) */
+} qs_dtype;
+
+/* flag bits of the selection calls */
+enum {
+    QS_FORCE_SINK = 1u,   /* qs_block_select: always include block 0 */
+    QS_FORCE_WINDOW = 2u, /* qs_block_select: always include the local-window blocks */
+    QS_RECENCY = 4u       /* qs_probe_select: recency insurance for the last block */
+};
+
+/*
+ * qs_build_metadata -- Quest block metadata.
+ * [P3] "quest_prefill_metadata: 元数据构建原理": for every KV block of every request and
+ * every KV head, the per-channel max and min of K over the block's tokens (the last
+ * block of a request over its valid tokens only). The BS vectors of BS consecutive
+ * blocks of a request fill one metadata block (same shape as a KV block), placed by
+ * metadata_block_tables; the unused rows of a request's last metadata block are set
+ * to +0.0 ([P3] "三个核心算子": absent blocks' metadata must be 0).
+ *
+ *   k_cache                [num_kv_blocks, BS, N, D], kv_dtype QS_F32 or QS_BF16
+ *   block_tables           [B, max_kv_blocks_per_req] int32, physical KV block of
+ *                          sequence block i of request b
+ *   seq_lens               [B] int32, tokens the metadata covers for each request
+ *   metadata_block_tables  [B, max_meta_blocks_per_req] int32, physical metadata block
+ *                          holding blocks j*BS .. j*BS+BS-1 of request b
+ *   maxblocks, minblocks   [num_meta_blocks, BS, N, D], same dtype as k_cache (outputs)
+ * Results are bit-exact: max/min use the IEEE total order (-0 < +0). Metadata blocks
+ * and rows beyond a request's last used metadata block are left untouched.
+ */
+qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size, qs_dtype kv_dtype,
+                            const void* k_cache, int32_t num_kv_blocks,
+                            const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                            const int32_t* seq_lens,
+                            const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                            void* maxblocks, void* minblocks, int32_t num_meta_blocks,
+                            void* stream);
+
+/* bytes of workspace qs_block_select needs for these sizes */
+size_t qs_block_select_workspace_bytes(int32_t B, int32_t N, int32_t block_size,
+                                       int32_t max_meta_blocks_per_req);
+
+/*
+ * qs_block_select -- Quest top-k block selection.
+ * [P3] "quest_block_select_paged: 解码期 top-k 预测算法": the grouped query of KV head n
+ * is the mean of its G query heads; the score of block i is
+ *     sum_d max(gq_d * kmax_d, gq_d * kmin_d),
+ * an upper bound of gq . k for every key k of the block; the k best blocks are returned
+ * as sequence-relative indices. [P3] "三个核心算子", variant _w: the sink block and the
+ * local-window blocks can be forced in; [P1] section 1: ties go to the lower index.
+ *
+ *   query                  [B, H, D], dtype QS_F32 or QS_BF16 (metadata has the same dtype)
+ *   maxblocks, minblocks   [num_meta_blocks, BS, N, D] (as written by qs_build_metadata)
+ *   metadata_block_tables  [B, max_meta_blocks_per_req] int32
+ *   seq_lens               [B] int32, tokens in each request (blocks 0..nb-1 are candidates)
+ *   tokens_since_update    [B] int32 or NULL (= all 0): tokens decoded since the metadata
+ *                          was built; blocks from floor((L - u) / BS) on have no metadata.
+ *                          A negative entry turns forcing off for that request.
+ *   flags                  QS_FORCE_SINK | QS_FORCE_WINDOW (other bits invalid)
+ *   k                      >= 1 blocks per (request, KV head)
+ *   selected               [B, N, k] int32 output: ascending block indices, then -1s
+ *   n_selected             [B, N] int32 output: min(k, nb)
+ *   block_scores           [B, N, max_meta_blocks_per_req * BS] fp32 output or NULL: the
+ *                          score of every non-forced block i < nb (NaN for forced blocks;
+ *                          entries i >= nb are not written)
+ * Forcing: with QS_FORCE_WINDOW the last block and every block without metadata are
+ * forced, the most recent first; with QS_FORCE_SINK block 0 is forced after them; at
+ * most k blocks are forced. The other min(k, nb) - forced picks are the best-scoring
+ * remaining blocks (higher score first, lower index on ties).
+ */
+qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
+                          const void* query, const void* maxblocks, const void* minblocks,
+                          int32_t num_meta_blocks,
+                          const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                          const int32_t* seq_lens, const int32_t* tokens_since_update,
+                          uint32_t flags, int32_t k,
+                          int32_t* selected, int32_t* n_selected, float* block_scores,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qs_probe_select -- page 1's probe + importance + recency selection, per query head.
+ * [P1] sections 1 and 2 (sparse_attn_head): for query head h (KV head h / G) the probe
+ * score of a block is the max of the unscaled q_h . K over the positions p0, p0+step, ...
+ * inside the block, step = max(1, block_tokens / n_probe); (k+1)/2 picks go first to the
+ * blocks with the largest summed prefill importance (fp32 sum in token order), the rest
+ * to the best probe scores (ties: lower index); with QS_RECENCY, if the last block is
+ * not picked it replaces the lowest-scoring probe pick (never an importance pick).
+ *
+ *   query          [B, H, D], q_dtype QS_F32 or QS_BF16
+ *   k_cache        [num_kv_blocks, BS, N, D], kv_dtype QS_F32 or QS_BF16
+ *   block_tables   [B, max_kv_blocks_per_req] int32 (max_kv_blocks_per_req <= 4096)
+ *   seq_lens       [B] int32
+ *   importance     [B, importance_stride] fp32 per-token prefill importance, or NULL
+ *                  (then every pick is a probe pick); tokens at or past importance_stride
+ *                  contribute nothing
+ *   n_probe        probes per block (values < 1 act as 1)
+ *   flags          0 or QS_RECENCY
+ *   selected       [B, H, k] int32 output (ascending, -1 padded); n_selected [B, H] int32
+ *   probe_scores   [B, H, max_kv_blocks_per_req] fp32 output or NULL (entries i >= nb
+ *                  are not written)
+ */
+qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                          qs_dtype q_dtype, qs_dtype kv_dtype,
+                          const void* query, const void* k_cache, int32_t num_kv_blocks,
+                          const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                          const int32_t* seq_lens,
+                          const float* importance, int32_t importance_stride,
+                          int32_t n_probe, int32_t k, uint32_t flags,
+                          int32_t* selected, int32_t* n_selected, float* probe_scores,
+                          void* stream);
+
+/* bytes of workspace qs_sparse_attn_decode needs for these sizes */
+size_t qs_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t sel_heads,
+                                      int32_t k);
+
+/*
+ * qs_sparse_attn_decode -- exact attention over the selected blocks.
+ * [P1] section 2: per-token scores only on the selected blocks (fp32 / bf16 K: float
+ * dot; int8 K: int8 x int8 dot times the scales), softmax renormalised over the
+ * selected tokens only, then the weighted sum of V. [P3] "quest_block_select_paged"
+ * notes: selected indices are sequence-relative and go through block_tables.
+ *
+ *   query          [B, H, D], q_dtype QS_F32 or QS_BF16; out [B, H, D] in q_dtype
+ *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_I8
+ *   k_scale/v_scale[num_kv_blocks, BS, N] fp32 per-row scales (QS_I8 only, else ignored)
+ *   block_tables   [B, max_kv_blocks_per_req] int32; seq_lens [B] int32
+ *   selected       [B, sel_heads, k] int32; n_selected [B, sel_heads] int32 (entries
+ *                  past n_selected, negative ones and ones >= nb are skipped; every other
+ *                  entry is attended once per occurrence)
+ *   sel_heads      selection rows per request: N (one per KV head, qs_block_select) or H
+ *                  (one per query head, qs_probe_select); any value with
+ *                  N | sel_heads | H. Query head h uses row h / (H / sel_heads).
+ *   softmax_scale  logit = softmax_scale * q . k; <= 0 selects 1/sqrt(D)
+ * int8: the query row of each head is quantised with s_q = absmax / 127 and codes
+ * clamp(rint(q / s_q), -127, 127) (fp32, half to even); logit =
+ * softmax_scale * float(int32 dot) * s_q * k_scale[t]; V[t] = v_code * v_scale[t].
+ * An empty selection writes zeros.
+ */
+qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                                qs_dtype q_dtype, qs_dtype kv_dtype,
+                                const void* query, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale, int32_t num_kv_blocks,
+                                const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                const int32_t* seq_lens,
+                                const int32_t* selected, const int32_t* n_selected,
+                                int32_t sel_heads, int32_t k, float softmax_scale,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* message for the calling thread's last failed call ("" if none) */
+const char* qs_last_error(void);
+
+/* library version string */
+const char* qs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSPARSE_H */

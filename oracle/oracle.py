@@ -46,7 +46,7 @@ def lib():
         L.qso_build_metadata.argtypes = [i, i, i, i, i, P, i, P, i, P, P, i, P, P, i]
         L.qso_block_select.argtypes = [i, i, i, i, i, i, P, P, P, P, i, i, P, P, ctypes.c_uint, i, P, P, P]
         L.qso_probe_select.argtypes = [i, i, i, i, i, i, i, P, P, i, P, i, P, P, i, i, i, ctypes.c_uint,
-                                       P, P, P, P, P]
+                                       P, P, P, P, P, P]
         L.qso_sparse_attn_decode.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, i, P, i, P, P, P, i, i,
                                              ctypes.c_double, P]
         L.qso_quantize_row_i8.argtypes = [P, i, P, P]
@@ -142,7 +142,8 @@ def block_select(query, maxb, minb, meta_tables, seq_lens, k, H=None, tsmu=None,
 def probe_select(query, k_cache, block_tables, seq_lens, k, N, importance=None, n_probe=8,
                  flags=RECENCY):
     """O3. Returns dict(selected [B,H,k], n_selected [B,H], probe [B,H,MKBPR] f64,
-    imp_sum [B,MKBPR] f32, n_imp [B,H])."""
+    imp_sum [B,MKBPR] f32, n_imp [B,H], kind [B,H,MKBPR] int8 (0 none, 1 importance,
+    2 probe, 3 recency-added, 4 evicted by recency))."""
     q = np.ascontiguousarray(_np(query))
     kc = np.ascontiguousarray(_np(k_cache))
     B, H, D = q.shape
@@ -157,11 +158,12 @@ def probe_select(query, k_cache, block_tables, seq_lens, k, N, importance=None, 
     probe = np.empty((B, H, mkbpr), np.float64)
     imps = np.zeros((B, mkbpr), np.float32)
     nimp = np.empty((B, H), np.int32)
+    kind = np.zeros((B, H, mkbpr), np.int8)
     rc = lib().qso_probe_select(B, H, N, D, BS, _dtype_code(q), _dtype_code(kc), _p(q), _p(kc), nkv,
                                 _p(bt), mkbpr, _p(sl), _p(imp), stride, n_probe, k, flags,
-                                _p(sel), _p(nsel), _p(probe), _p(imps), _p(nimp))
+                                _p(sel), _p(nsel), _p(probe), _p(imps), _p(nimp), _p(kind))
     _check(rc, "probe_select")
-    return dict(selected=sel, n_selected=nsel, probe=probe, imp_sum=imps, n_imp=nimp)
+    return dict(selected=sel, n_selected=nsel, probe=probe, imp_sum=imps, n_imp=nimp, kind=kind)
 
 
 def sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selected, n_selected,

@@ -303,9 +303,11 @@ int qso_block_select(int B, int H, int N, int D, int BS, int dtype,
  *     probe-chosen block; importance picks are never replaced.
  * readings: with no probe-chosen block recency does nothing; among equal lowest probe
  *   scores the later greedy pick (higher index) is replaced; importance is indexed
- *   importance[b * imp_stride + token]; output ascending, -1 padded.
+ *   importance[b * imp_stride + token] and tokens at or past imp_stride add nothing;
+ *   output ascending, -1 padded.
  * Outputs besides the selection (all optional): probe [B, H, mkbpr] (double),
- *   imp_sum [B, mkbpr] (float), n_imp [B, H].
+ *   imp_sum [B, mkbpr] (float), n_imp [B, H], kind [B, H, mkbpr] (int8: 0 not picked,
+ *   1 importance pick, 2 probe pick, 3 added by recency, 4 probe pick evicted by recency).
  */
 int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dtype,
                      const void* query, const void* k_cache, int num_kv_blocks,
@@ -314,7 +316,7 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
                      const float* importance, int imp_stride,
                      int n_probe, int k, unsigned flags,
                      int32_t* selected, int32_t* n_selected,
-                     double* probe_out, float* imp_out, int32_t* n_imp_out) {
+                     double* probe_out, float* imp_out, int32_t* n_imp_out, int8_t* kind_out) {
     if ((q_dtype != QSO_F32 && q_dtype != QSO_BF16) || (kv_dtype != QSO_F32 && kv_dtype != QSO_BF16))
         return QSO_BAD;
     if (N <= 0 || H % N != 0 || k < 1) return QSO_BAD;
@@ -343,7 +345,7 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
             if (pe > L) pe = L;
             float s = 0.0f;
             if (importance)
-                for (int32_t ps = p0; ps < pe; ++ps) s += importance[(size_t)b * imp_stride + ps];
+                for (int32_t ps = p0; ps < pe && ps < imp_stride; ++ps) s += importance[(size_t)b * imp_stride + ps];
             imp[i] = s;
             if (imp_out) imp_out[(size_t)b * mkbpr + i] = s;
         }
@@ -395,6 +397,11 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
                 sel[n_sel++] = best;
                 used[best] = 1;
             }
+            int8_t* kind = kind_out ? kind_out + ((size_t)b * H + h) * mkbpr : NULL;
+            if (kind) {
+                for (int32_t i = 0; i < mkbpr; ++i) kind[i] = 0;
+                for (int s = 0; s < n_sel; ++s) kind[sel[s]] = (int8_t)(s < n_imp ? 1 : 2);
+            }
             /* recency insurance */
             if ((flags & QSO_RECENCY) && nb > 0 && !used[nb - 1] && n_sel > n_imp) {
                 int victim = n_imp;
@@ -403,6 +410,7 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
                     if (probe[a] < probe[c] || (probe[a] == probe[c] && a > c)) victim = s;
                 }
                 used[sel[victim]] = 0;
+                if (kind) { kind[sel[victim]] = 4; kind[nb - 1] = 3; }
                 sel[victim] = nb - 1;
                 used[nb - 1] = 1;
             }

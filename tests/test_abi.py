@@ -1,0 +1,148 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the header
+declares, and rejects invalid arguments on the host before any HIP call.
+
+Every invalid call below also passes B = 0 where B is not under test: B = 0 returns
+before any launch, so a check that wrongly passed would still enqueue nothing.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qsparse.h")
+
+
+@pytest.fixture(scope="module")
+def qs():
+    from top_kv_block_amd import qsparse
+    return qsparse
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:qs_status|size_t|const char\s*\*)\s*(qs_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for n in ("qs_build_metadata", "qs_block_select", "qs_probe_select", "qs_sparse_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(qs):
+    names = _declared_functions()
+    assert set(names) == set(qs.EXPORTS)
+    for n in names:
+        assert hasattr(qs.lib, n), n
+    assert qs.lib.qs_version().decode().startswith("qsparse")
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: every call below fails validation
+WS = ctypes.c_void_p(1 << 20)          # 256-byte aligned fake workspace
+
+
+def _meta(qs, **kw):
+    a = dict(B=1, N=8, D=128, BS=128, dt=qs.QS_BF16, kc=FAKE, nkv=4, bt=FAKE, mkbpr=4, sl=FAKE, mt=FAKE,
+             mmbpr=1, mx=FAKE, mn=FAKE, nmeta=1)
+    a.update(kw)
+    return qs.lib.qs_build_metadata(a["B"], a["N"], a["D"], a["BS"], a["dt"], a["kc"], a["nkv"], a["bt"],
+                                    a["mkbpr"], a["sl"], a["mt"], a["mmbpr"], a["mx"], a["mn"], a["nmeta"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64, B=0), 2), (dict(BS=100, B=0), 2), (dict(BS=256, B=0), 2), (dict(dt=2, B=0), 2),
+    (dict(B=-1), 1), (dict(N=0, B=0), 1), (dict(kc=None, B=0), 1), (dict(mt=None, B=0), 1),
+    (dict(mx=ctypes.c_void_p((1 << 20) + 4), B=0), 1), (dict(nkv=0, B=0), 1), (dict(mmbpr=0, B=0), 1),
+])
+def test_build_metadata_rejects(qs, kw, status):
+    assert _meta(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_build_metadata")
+
+
+def test_build_metadata_b0_is_noop(qs):
+    assert _meta(qs, B=0) == 0
+    assert qs.lib.qs_last_error().decode() == ""
+
+
+def _select(qs, **kw):
+    a = dict(B=0, H=32, N=8, D=128, BS=128, dt=qs.QS_BF16, q=FAKE, mx=FAKE, mn=FAKE, nmeta=1, mt=FAKE, mmbpr=1,
+             sl=FAKE, ts=None, flags=0, k=8, sel=FAKE, nsel=FAKE, sc=None, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qs.lib.qs_block_select(a["B"], a["H"], a["N"], a["D"], a["BS"], a["dt"], a["q"], a["mx"], a["mn"],
+                                  a["nmeta"], a["mt"], a["mmbpr"], a["sl"], a["ts"], a["flags"], a["k"], a["sel"],
+                                  a["nsel"], a["sc"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=30), 1), (dict(k=0), 1), (dict(flags=4), 1), (dict(flags=8), 1), (dict(dt=2), 2), (dict(D=256), 2),
+    (dict(q=None), 1), (dict(ws=None), 1), (dict(ws=ctypes.c_void_p((1 << 20) + 16)), 1), (dict(wsb=16), 1),
+    (dict(nsel=None), 1), (dict(mmbpr=0), 1), (dict(B=-3), 1), (dict(BS=48), 2),
+])
+def test_block_select_rejects(qs, kw, status):
+    assert _select(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_block_select")
+
+
+def test_block_select_workspace_size(qs):
+    small = qs.block_select_workspace_bytes(20, 8, 128, 1)
+    big = qs.block_select_workspace_bytes(20, 8, 128, 8)
+    assert 0 < small < big and small % 256 == 0
+    assert _select(qs, wsb=small) == 0                  # exactly enough, B=0: no launch
+
+
+def _probe(qs, **kw):
+    a = dict(B=0, H=16, N=8, D=128, BS=32, qd=qs.QS_F32, kd=qs.QS_F32, q=FAKE, kc=FAKE, nkv=128, bt=FAKE,
+             mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32, flags=qs.QS_RECENCY, sel=FAKE, nsel=FAKE, ps=None)
+    a.update(kw)
+    return qs.lib.qs_probe_select(a["B"], a["H"], a["N"], a["D"], a["BS"], a["qd"], a["kd"], a["q"], a["kc"],
+                                  a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["imp"], a["stride"], a["npb"], a["k"],
+                                  a["flags"], a["sel"], a["nsel"], a["ps"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kd=2), 2), (dict(qd=2), 2), (dict(k=0), 1), (dict(flags=1), 1), (dict(mkbpr=5000), 2),
+    (dict(imp=FAKE, stride=0), 1), (dict(kc=None), 1), (dict(H=12), 1), (dict(BS=8), 2),
+])
+def test_probe_select_rejects(qs, kw, status):
+    assert _probe(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_probe_select")
+
+
+def _attn(qs, **kw):
+    a = dict(B=0, H=32, N=8, D=128, BS=128, qd=qs.QS_BF16, kd=qs.QS_BF16, q=FAKE, kc=FAKE, vc=FAKE, ks=None,
+             vs=None, nkv=64, bt=FAKE, mkbpr=64, sl=FAKE, sel=FAKE, nsel=FAKE, sh=8, k=16, scale=0.0, out=FAKE,
+             ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qs.lib.qs_sparse_attn_decode(a["B"], a["H"], a["N"], a["D"], a["BS"], a["qd"], a["kd"], a["q"], a["kc"],
+                                        a["vc"], a["ks"], a["vs"], a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["sel"],
+                                        a["nsel"], a["sh"], a["k"], a["scale"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sh=4), 1), (dict(sh=12), 1), (dict(sh=64), 1), (dict(k=0), 1), (dict(kd=2), 1),
+    (dict(qd=2), 2), (dict(kd=7), 2), (dict(out=None), 1), (dict(wsb=8), 1), (dict(scale=float("nan")), 1),
+    (dict(vc=ctypes.c_void_p((1 << 20) + 2)), 1), (dict(D=96), 2),
+])
+def test_sparse_attn_rejects(qs, kw, status):
+    assert _attn(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_sparse_attn_decode")
+
+
+def test_sparse_attn_workspace_size(qs):
+    b = qs.sparse_attn_workspace_bytes(128, 64, 8, 128, 8, 16)
+    assert b > 0 and b % 256 == 0
+    assert _attn(qs, wsb=qs.sparse_attn_workspace_bytes(0, 32, 8, 128, 8, 16)) == 0
+    assert qs.sparse_attn_workspace_bytes(1, 32, 8, 128, 5, 16) == 0     # H % sel_heads != 0
+
+
+def test_binding_refuses_cpu_tensors(qs):
+    import torch
+    x = torch.zeros((1, 4, 128))
+    with pytest.raises(ValueError):
+        qs.qs_sparse_attn_decode(x, torch.zeros((1, 32, 1, 128)), torch.zeros((1, 32, 1, 128)),
+                                 torch.zeros((1, 1), dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                                 torch.zeros((1, 1, 1), dtype=torch.int32), torch.zeros((1, 1), dtype=torch.int32))

@@ -1,0 +1,576 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Bars (the tolerance contract of the path):
+  * metadata max/min: bit-exact, including the +0.0 tail rows and untouched rows;
+  * block / probe scores: |gpu - oracle| <= 1e-3 * max(|oracle|, 1e-3 * max_row |oracle|);
+  * selections: forced and importance picks exact; the rest equal wherever the oracle's
+    k-th and (k+1)-th fill scores differ by more than 1e-3 relative, otherwise differing
+    only in blocks whose oracle score is within 1e-3 relative of the k-th;
+  * attention (on the oracle's selection): max abs error <= 1e-4 (fp32 out), <= 2e-2
+    (bf16 out); the int8 path (exact int32 dots) also within 2e-5 for fp32 queries.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import gpu_available
+from tests.helpers import as_sets, cdiv, check_selection_rows, near_tie_equal
+from top_kv_block_amd import workloads as W
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qs():
+    from top_kv_block_amd import qsparse
+    return qsparse
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8)
+
+
+def tnp(t):
+    """numpy copy of a device tensor; bf16 as uint16 bits."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# ------------------------------------------------------------------------------------------
+# comparison helpers
+# ------------------------------------------------------------------------------------------
+
+def check_scores(gpu, ref, valid_mask, rel=1e-3):
+    g = gpu[valid_mask].astype(np.float64)
+    o = ref[valid_mask]
+    if o.size == 0:
+        return
+    floor = 1e-3 * np.max(np.abs(o))
+    err = np.abs(g - o) / np.maximum(np.abs(o), floor)
+    assert np.all(err <= rel), f"score rel err {err.max():.3e}"
+
+
+def compare_quest(gsel, gns, osel, ons, osc, nbs, k):
+    check_selection_rows(gsel, gns, k)
+    B, N = gns.shape
+    np.testing.assert_array_equal(gns, ons)
+    near = 0
+    for b in range(B):
+        nb = nbs[b]
+        for n in range(N):
+            got = set(gsel[b, n, :gns[b, n]].tolist())
+            want = set(osel[b, n, :ons[b, n]].tolist())
+            sc = osc[b, n, :nb]
+            fixed = {i for i in range(nb) if np.isnan(sc[i])}
+            fill = {i: sc[i] for i in range(nb) if not np.isnan(sc[i])}
+            ok, why = near_tie_equal(got, want, fill, fixed)
+            assert ok, f"(b={b}, n={n}) {why}: gpu={sorted(got)} oracle={sorted(want)}"
+            near += why == "near tie"
+    return near
+
+
+def compare_probe(gsel, gns, o, nbs, k):
+    check_selection_rows(gsel, gns, k)
+    np.testing.assert_array_equal(gns, o["n_selected"])
+    B, H = gns.shape
+    for b in range(B):
+        nb = nbs[b]
+        for h in range(H):
+            got = set(gsel[b, h, :gns[b, h]].tolist())
+            want = set(o["selected"][b, h, :o["n_selected"][b, h]].tolist())
+            kind = o["kind"][b, h]
+            imp = {i for i in range(nb) if kind[i] == 1}
+            pr = o["probe"][b, h]
+            fill = {i: pr[i] for i in range(nb) if i not in imp}
+            pre = [i for i in range(nb) if kind[i] in (2, 4)]
+            if got != want:
+                assert imp <= got, f"(b={b}, h={h}) importance picks differ"
+                s_k = min(pr[i] for i in pre)
+                tol = 1e-3 * max(abs(s_k), 1e-30)
+                for i in got ^ want:
+                    assert i in fill and abs(fill[i] - s_k) <= tol, \
+                        f"(b={b}, h={h}) block {i}: gpu={sorted(got)} oracle={sorted(want)}"
+
+
+def attn_tol(q_dtype):
+    return 2e-2 if q_dtype == torch.bfloat16 else 1e-4
+
+
+# ------------------------------------------------------------------------------------------
+# runners
+# ------------------------------------------------------------------------------------------
+
+def run_meta(qs, wl, sentinel=7.0):
+    shape = (wl.num_meta_blocks, wl.BS, wl.N, wl.D)
+    mx = torch.full(shape, sentinel, dtype=wl.k_cache.dtype, device=DEV)
+    mn = torch.full(shape, sentinel, dtype=wl.k_cache.dtype, device=DEV)
+    qs.qs_build_metadata(wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.meta_seq_lens.to(DEV),
+                         wl.meta_tables.to(DEV), mx, mn)
+    return mx, mn
+
+
+def oracle_meta(oracle, wl, sentinel=7.0):
+    shape = (wl.num_meta_blocks, wl.BS, wl.N, wl.D)
+    s = torch.full(shape, sentinel, dtype=wl.k_cache.dtype)
+    return oracle.build_metadata(wl.k_cache.cpu(), wl.block_tables.cpu(), wl.meta_seq_lens.cpu(),
+                                 wl.meta_tables.cpu(), wl.num_meta_blocks, maxb=s, minb=s)
+
+
+def run_select(qs, wl, mx, mn, k=None, scores=True):
+    k = k or wl.k
+    B, N = wl.B, wl.N
+    sc = torch.full((B, N, wl.mmbpr * wl.BS), float("inf"), device=DEV) if scores else None
+    ts = None if wl.tsmu is None else wl.tsmu.to(DEV)
+    sel, ns = qs.qs_block_select(wl.query.to(DEV), mx, mn, wl.meta_tables.to(DEV), wl.seq_lens.to(DEV), k,
+                                 tokens_since_update=ts, flags=wl.flags, block_scores=sc)
+    return sel, ns, sc
+
+
+def nbs_of(wl):
+    return [cdiv(max(int(x), 0), wl.BS) for x in wl.seq_lens.cpu().tolist()]
+
+
+# ------------------------------------------------------------------------------------------
+# metadata
+# ------------------------------------------------------------------------------------------
+
+META_CASES = [
+    # seed, B, N, BS, lens, dtype
+    (1, 3, 8, 128, [128 * 5 + 3, 1, 128], torch.bfloat16),
+    (2, 4, 2, 32, [0, 31, 32 * 33 + 7, 32 * 64], torch.float32),
+    (3, 2, 1, 16, [16 * 16 * 2 + 1, 5], torch.bfloat16),
+    (4, 2, 4, 64, [64 * 70, 64 * 3 - 1], torch.float32),
+    (5, 1, 16, 128, [128 * 3 + 100], torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", META_CASES, ids=lambda c: f"seed{c[0]}")
+def test_metadata_random(qs, oracle, case):
+    seed, B, N, BS, lens, dtype = case
+    say(f"metadata random seed={seed} B={B} N={N} BS={BS} dtype={dtype}")
+    wl = W.random_case(seed, B, 2 * N, N, BS, lens, k=4, dtype=dtype, with_v=False)
+    mx, mn = run_meta(qs, wl)
+    torch.cuda.synchronize()
+    omx, omn = oracle_meta(oracle, wl)
+    assert np.array_equal(bits(tnp(mx)), bits(omx))
+    assert np.array_equal(bits(tnp(mn)), bits(omn))
+
+
+def test_metadata_signed_zeros(qs, oracle):
+    say("metadata signed zeros")
+    wl = W.random_case(6, 1, 2, 1, 32, [64], k=2, dtype=torch.bfloat16, with_v=False)
+    kc = wl.k_cache.clone()
+    kc[:, :, 0, :8] = 0.0
+    kc[:, 5, 0, :4] = -0.0
+    kc[:, :, 0, 8:16] = -0.0
+    kc[:, 9, 0, 8:12] = 0.0
+    wl.k_cache = kc
+    mx, mn = run_meta(qs, wl)
+    omx, omn = oracle_meta(oracle, wl)
+    assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
+
+
+def test_metadata_config1_and_config2(qs, oracle):
+    wl = W.config1()
+    say("metadata config1")
+    mx, mn = run_meta(qs, wl)
+    omx, omn = oracle_meta(oracle, wl)
+    assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
+    say("metadata config2 (full size, 640 MiB K cache)")
+    wl = W.config2(device=DEV)
+    mx, mn = run_meta(qs, wl)
+    omx, omn = oracle_meta(oracle, wl)
+    assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
+
+
+# ------------------------------------------------------------------------------------------
+# Quest select
+# ------------------------------------------------------------------------------------------
+
+SELECT_CASES = [
+    # seed, B, H, N, BS, lens, k, dtype, flags, tsmu
+    (11, 3, 8, 2, 32, [32 * 40 + 5, 32 * 7, 1], 5, torch.float32, 0, None),
+    (12, 4, 32, 8, 128, [128 * 300 + 17, 128 * 64, 0, 128 * 129], 8, torch.bfloat16, 0, None),
+    (13, 2, 16, 8, 128, [128 * 200, 128 * 3], 16, torch.bfloat16, 3, [0, 0]),
+    (14, 3, 16, 4, 64, [64 * 100 + 9, 64 * 20, 64 * 65], 12, torch.bfloat16, 3, [9, 200, -1]),
+    (15, 2, 4, 1, 16, [16 * 16 * 3 + 2, 16 * 5], 40, torch.float32, 1, None),
+    (16, 2, 8, 8, 32, [32 * 100, 32 * 2], 1, torch.float32, 2, [0, 64]),
+    (17, 1, 64, 8, 128, [128 * 1024], 64, torch.bfloat16, 3, [127]),
+    (18, 2, 24, 8, 64, [64 * 130 + 1, 64 * 66], 9, torch.bfloat16, 3, [1, 0]),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: f"seed{c[0]}")
+def test_block_select_random(qs, oracle, case):
+    seed, B, H, N, BS, lens, k, dtype, flags, tsmu = case
+    say(f"select random seed={seed} B={B} H={H} N={N} BS={BS} k={k} flags={flags}")
+    cover = None if tsmu is None else [max(0, L - max(t, 0)) for L, t in zip(lens, tsmu)]
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=dtype, with_v=False, meta_cover=cover,
+                       tsmu=tsmu, flags=flags)
+    mx, mn = run_meta(qs, wl, sentinel=0.0)
+    sel, ns, sc = run_select(qs, wl, mx, mn, k)
+    torch.cuda.synchronize()
+    omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k,
+                                         tsmu=wl.tsmu, flags=flags)
+    nbs = nbs_of(wl)
+    gsc = tnp(sc)
+    mask = np.zeros_like(osc, dtype=bool)
+    for b, nb in enumerate(nbs):
+        mask[b, :, :nb] = ~np.isnan(osc[b, :, :nb])
+        forced = np.isnan(osc[b, :, :nb])
+        assert np.all(np.isnan(gsc[b, :, :nb][forced])), "forced blocks must carry NaN scores"
+    check_scores(gsc, osc, mask)
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs, k)
+
+
+def test_block_select_exact_ties(qs, oracle):
+    """Metadata with few distinct values: many exactly equal scores; the lower index
+    must win every tie (the oracle and the GPU then agree exactly)."""
+    say("select exact ties")
+    B, H, N, BS, D = 2, 8, 2, 32, 128
+    g = torch.Generator().manual_seed(7)
+    nmeta = 4
+    mx = torch.randint(-1, 2, (nmeta, BS, N, D), generator=g).float()
+    mn = mx - torch.randint(0, 2, (nmeta, BS, N, D), generator=g).float()
+    q = torch.ones((B, H, D))
+    mt = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32)
+    sl = torch.tensor([BS * 60, BS * 33 + 1], dtype=torch.int32)
+    for k in (1, 7, 32):
+        sel, ns = qs.qs_block_select(q.to(DEV), mx.to(DEV), mn.to(DEV), mt.to(DEV), sl.to(DEV), k)
+        osel, ons, _ = oracle.block_select(q, mx, mn, mt, sl, k)
+        np.testing.assert_array_equal(tnp(sel), osel)
+        np.testing.assert_array_equal(tnp(ns), ons)
+
+
+def test_block_select_config1_needle(qs, oracle):
+    say("select config1")
+    wl = W.config1()
+    mx, mn = run_meta(qs, wl)
+    sel, ns, sc = run_select(qs, wl, mx, mn)
+    omx, omn = oracle_meta(oracle, wl)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k)
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs_of(wl), wl.k)
+    needle_block = wl.needles[0][1] // wl.BS
+    assert needle_block in set(tnp(sel)[0, 0].tolist())
+
+
+@pytest.mark.parametrize("flags", [0, W.FORCE_SINK | W.FORCE_WINDOW])
+def test_block_select_config2_full(qs, oracle, flags):
+    say(f"select config2 full flags={flags}")
+    wl = W.config2(device=DEV)
+    wl.flags = flags
+    if flags:
+        wl.tsmu = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
+    mx, mn = run_meta(qs, wl)
+    sel, ns, sc = run_select(qs, wl, mx, mn)
+    omx, omn = oracle_meta(oracle, wl)
+    osel, ons, osc = oracle.block_select(wl.query.cpu(), omx, omn, wl.meta_tables.cpu(), wl.seq_lens.cpu(),
+                                         wl.k, tsmu=None if wl.tsmu is None else wl.tsmu.cpu(), flags=flags)
+    nbs = nbs_of(wl)
+    check_scores(tnp(sc), osc, ~np.isnan(osc) & (np.arange(osc.shape[2]) < 128)[None, None, :])
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs, wl.k)
+
+
+def test_block_select_deterministic(qs):
+    say("select determinism")
+    wl = W.random_case(19, 4, 32, 8, 128, [128 * 500, 128 * 77 + 3, 128 * 1000, 128 * 2], k=16,
+                       dtype=torch.bfloat16, with_v=False)
+    mx, mn = run_meta(qs, wl)
+    outs = [run_select(qs, wl, mx, mn) for _ in range(3)]
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+# ------------------------------------------------------------------------------------------
+# probe select
+# ------------------------------------------------------------------------------------------
+
+PROBE_CASES = [
+    # seed, B, H, N, BS, lens, k, dtype, importance, flags, n_probe
+    (21, 2, 4, 2, 32, [32 * 40 + 20, 32 * 9], 6, torch.float32, True, 4, 8),
+    (22, 2, 16, 8, 32, [32 * 128, 32 * 3 + 1], 32, torch.float32, True, 4, 8),
+    (23, 1, 8, 8, 64, [64 * 50 + 3], 5, torch.bfloat16, False, 4, 8),
+    (24, 3, 4, 4, 16, [16 * 30, 0, 16 * 7 + 5], 9, torch.float32, True, 0, 3),
+    (25, 1, 4, 2, 32, [32 * 70], 4, torch.bfloat16, True, 4, 64),
+    (26, 1, 2, 1, 128, [128 * 40 + 77], 3, torch.float32, True, 4, 0),
+]
+
+
+@pytest.mark.parametrize("case", PROBE_CASES, ids=lambda c: f"seed{c[0]}")
+def test_probe_select_random(qs, oracle, case):
+    seed, B, H, N, BS, lens, k, dtype, use_imp, flags, n_probe = case
+    say(f"probe random seed={seed} B={B} H={H} N={N} BS={BS} k={k} imp={use_imp} flags={flags} n_probe={n_probe}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=dtype, with_v=False, with_importance=use_imp)
+    imp = wl.importance if use_imp else None
+    ps = torch.full((B, H, wl.mkbpr), float("inf"), device=DEV)
+    sel, ns = qs.qs_probe_select(wl.query.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV),
+                                 wl.seq_lens.to(DEV), k, importance=None if imp is None else imp.to(DEV),
+                                 n_probe=n_probe, flags=flags, probe_scores=ps)
+    o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, N, importance=imp,
+                            n_probe=n_probe, flags=flags)
+    nbs = nbs_of(wl)
+    mask = np.zeros(o["probe"].shape, dtype=bool)
+    for b, nb in enumerate(nbs):
+        mask[b, :, :nb] = True
+    check_scores(tnp(ps), o["probe"], mask)
+    compare_probe(tnp(sel), tnp(ns), o, nbs, k)
+
+
+def test_probe_select_config3_sweep(qs, oracle):
+    wl = W.config3()
+    for k in (1, 2, 4, 8, 16, 32):
+        say(f"probe config3 k={k}")
+        sel, ns = qs.qs_probe_select(wl.query.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV),
+                                     wl.seq_lens.to(DEV), k, importance=wl.importance.to(DEV), n_probe=8,
+                                     flags=W.RECENCY)
+        o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, wl.N,
+                                importance=wl.importance, n_probe=8, flags=W.RECENCY)
+        compare_probe(tnp(sel), tnp(ns), o, nbs_of(wl), k)
+        if k == 1:
+            best = int(np.argmax(o["imp_sum"][0, :128]))
+            assert np.all(tnp(sel)[0, :, 0] == best)
+
+
+# ------------------------------------------------------------------------------------------
+# sparse attention
+# ------------------------------------------------------------------------------------------
+
+def random_selection(seed, B, rows, k, nbs, extra_invalid=True):
+    g = torch.Generator().manual_seed(seed)
+    sel = torch.full((B, rows, k), -1, dtype=torch.int32)
+    ns = torch.zeros((B, rows), dtype=torch.int32)
+    for b in range(B):
+        nb = nbs[b]
+        for r in range(rows):
+            m = min(k, nb)
+            if m == 0:
+                continue
+            pick = torch.randperm(nb, generator=g)[:m].sort().values.to(torch.int32)
+            sel[b, r, :m] = pick
+            ns[b, r] = m
+            if extra_invalid and r % 3 == 1 and m < k:
+                sel[b, r, m] = nb + 5        # out of range: skipped
+                ns[b, r] = m + 1
+    return sel, ns
+
+
+ATTN_CASES = [
+    # seed, B, H, N, BS, lens, k, kv dtype, q dtype, sel_heads factor (1 -> N, 0 -> H)
+    (31, 2, 8, 2, 32, [32 * 20 + 7, 32 * 3], 6, torch.float32, torch.float32, 1),
+    (32, 3, 32, 8, 128, [128 * 70 + 1, 128 * 16, 0], 16, torch.bfloat16, torch.bfloat16, 1),
+    (33, 2, 64, 8, 128, [128 * 40, 128 * 33 + 64], 16, torch.bfloat16, torch.bfloat16, 1),
+    (34, 1, 16, 8, 32, [32 * 128], 32, torch.float32, torch.float32, 0),
+    (35, 2, 16, 8, 32, [32 * 100 + 3, 32 * 50], 12, torch.int8, torch.float32, 0),
+    (36, 2, 32, 8, 64, [64 * 30 + 11, 64 * 8], 7, torch.int8, torch.bfloat16, 1),
+    (37, 1, 24, 8, 64, [64 * 20], 5, torch.bfloat16, torch.bfloat16, 1),       # 3 heads per row
+    (38, 1, 40, 2, 16, [16 * 50 + 1], 9, torch.float32, torch.float32, 1),     # 20 heads per row
+    (39, 4, 4, 1, 128, [128 * 64, 1, 128 * 2, 0], 64, torch.bfloat16, torch.bfloat16, 1),
+    (40, 1, 8, 8, 16, [16 * 8], 1, torch.float32, torch.float32, 1),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: f"seed{c[0]}")
+def test_sparse_attn_random(qs, oracle, case):
+    seed, B, H, N, BS, lens, k, kvd, qd, shf = case
+    say(f"attn random seed={seed} B={B} H={H} N={N} BS={BS} k={k} kv={kvd} q={qd}")
+    int8 = kvd == torch.int8
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=torch.float32 if int8 else kvd, int8=int8)
+    q = wl.query.to(qd)
+    kc, vc = (wl.k_i8, wl.v_i8) if int8 else (wl.k_cache, wl.v_cache)
+    sel_heads = N if shf == 1 else H
+    sel, ns = random_selection(seed, B, sel_heads, k, nbs_of(wl))
+    out = qs.qs_sparse_attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), wl.block_tables.to(DEV),
+                                   wl.seq_lens.to(DEV), sel.to(DEV), ns.to(DEV), sel_heads=sel_heads,
+                                   k_scale=None if not int8 else wl.k_scale.to(DEV),
+                                   v_scale=None if not int8 else wl.v_scale.to(DEV))
+    ref = oracle.sparse_attn_decode(q, kc, vc, wl.block_tables, wl.seq_lens, sel, ns, sel_heads,
+                                    k_scale=wl.k_scale if int8 else None, v_scale=wl.v_scale if int8 else None)
+    got = out.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref).max()
+    tol = attn_tol(qd)
+    if int8 and qd == torch.float32:
+        tol = 2e-5
+    assert err <= tol, f"max abs err {err:.3e} > {tol}"
+
+
+def test_sparse_attn_empty_rows_write_zeros(qs):
+    say("attn empty selections")
+    wl = W.random_case(41, 2, 8, 2, 32, [0, 32 * 4], k=3)
+    sel = torch.full((2, 2, 3), -1, dtype=torch.int32)
+    ns = torch.tensor([[0, 3], [0, 2]], dtype=torch.int32)
+    out = torch.full((2, 8, 128), 5.0, device=DEV)
+    qs.qs_sparse_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV), wl.block_tables.to(DEV),
+                             wl.seq_lens.to(DEV), sel.to(DEV), ns.to(DEV), out=out)
+    assert torch.all(out == 0)
+
+
+def test_sparse_attn_config1(qs, oracle):
+    say("attn config1 (oracle selection)")
+    wl = W.config1()
+    omx, omn = oracle_meta(oracle, wl)
+    osel, ons, _ = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k)
+    out = qs.qs_sparse_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV),
+                                   wl.block_tables.to(DEV), wl.seq_lens.to(DEV), torch.from_numpy(osel).to(DEV),
+                                   torch.from_numpy(ons).to(DEV))
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, osel, ons, wl.N)
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_sparse_attn_config3(qs, oracle, int8):
+    wl = W.config3()
+    kc, vc = (wl.k_i8, wl.v_i8) if int8 else (wl.k_cache, wl.v_cache)
+    for k in (1, 2, 4, 8, 16, 32):
+        say(f"attn config3 k={k} int8={int8}")
+        o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, wl.N,
+                                importance=wl.importance, n_probe=8, flags=W.RECENCY)
+        sel, ns = torch.from_numpy(o["selected"]), torch.from_numpy(o["n_selected"])
+        out = qs.qs_sparse_attn_decode(wl.query.to(DEV), kc.to(DEV), vc.to(DEV), wl.block_tables.to(DEV),
+                                       wl.seq_lens.to(DEV), sel.to(DEV), ns.to(DEV), sel_heads=wl.H,
+                                       k_scale=wl.k_scale.to(DEV) if int8 else None,
+                                       v_scale=wl.v_scale.to(DEV) if int8 else None)
+        ref = oracle.sparse_attn_decode(wl.query, kc, vc, wl.block_tables, wl.seq_lens, sel, ns, wl.H,
+                                        k_scale=wl.k_scale if int8 else None, v_scale=wl.v_scale if int8 else None)
+        err = np.abs(out.cpu().numpy() - ref).max()
+        assert err <= (2e-5 if int8 else 1e-4), f"k={k} err {err:.3e}"
+
+
+# ------------------------------------------------------------------------------------------
+# large configurations: full-size launch, outputs checked on sampled requests
+# ------------------------------------------------------------------------------------------
+
+def sub_workload(wl, reqs):
+    """The sampled requests as a compact CPU workload (blocks gathered, tables remapped)."""
+    BS = wl.BS
+    bt = wl.block_tables.cpu()
+    mt = wl.meta_tables.cpu()
+    sl = wl.seq_lens.cpu()
+    msl = wl.meta_seq_lens.cpu()
+    nbs = [cdiv(int(sl[b]), BS) for b in reqs]
+    phys = torch.cat([bt[b, :nb].long() for b, nb in zip(reqs, nbs)])
+    kc = wl.k_cache[phys.to(wl.k_cache.device)].cpu()
+    vc = None if wl.v_cache is None else wl.v_cache[phys.to(wl.v_cache.device)].cpu()
+    nt = torch.zeros((len(reqs), bt.shape[1]), dtype=torch.int32)
+    off = 0
+    for j, nb in enumerate(nbs):
+        nt[j, :nb] = torch.arange(off, off + nb, dtype=torch.int32)
+        off += nb
+    mnb = [cdiv(nb, BS) for nb in nbs]
+    nmt = torch.zeros((len(reqs), mt.shape[1]), dtype=torch.int32)
+    off = 0
+    for j, m in enumerate(mnb):
+        nmt[j, :m] = torch.arange(off, off + m, dtype=torch.int32)
+        off += m
+    q = wl.query.cpu()[reqs]
+    sub = W.Workload(wl.name + "_sample", len(reqs), wl.H, wl.N, wl.D, BS, wl.k, q, kc, vc, nt, sl[reqs].clone(),
+                     nmt, max(1, off), msl[reqs].clone(),
+                     tsmu=None if wl.tsmu is None else wl.tsmu.cpu()[reqs].clone(), flags=wl.flags,
+                     sel_heads=wl.sel_heads)
+    return sub, nbs
+
+
+def check_large(qs, oracle, wl, reqs, label):
+    say(f"{label}: metadata + select + attention at full size")
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=wl.k_cache.dtype, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sc = torch.zeros((wl.B, wl.N, wl.mmbpr * wl.BS), device=DEV)
+    sel, ns = qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, tokens_since_update=wl.tsmu,
+                                 flags=wl.flags, block_scores=sc)
+    out = qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns)
+    torch.cuda.synchronize()
+    say(f"{label}: oracle on sampled requests {reqs}")
+    sub, nbs = sub_workload(wl, reqs)
+    omx, omn = oracle.build_metadata(sub.k_cache, sub.block_tables, sub.meta_seq_lens, sub.meta_tables,
+                                     sub.num_meta_blocks)
+    # metadata rows of the sampled requests, bit for bit
+    gmx, gmn = mx.cpu(), mn.cpu()
+    mt = wl.meta_tables.cpu()
+    for j, b in enumerate(reqs):
+        for m in range(cdiv(nbs[j], wl.BS)):
+            gm = int(mt[b, m])
+            assert np.array_equal(bits(tnp(gmx[gm])), bits(omx[int(sub.meta_tables[j, m])]))
+            assert np.array_equal(bits(tnp(gmn[gm])), bits(omn[int(sub.meta_tables[j, m])]))
+    osel, ons, osc = oracle.block_select(sub.query, omx, omn, sub.meta_tables, sub.seq_lens, wl.k,
+                                         tsmu=sub.tsmu, flags=sub.flags)
+    gsel, gns, gsc = tnp(sel)[reqs], tnp(ns)[reqs], tnp(sc)[reqs]
+    mask = np.zeros_like(osc, dtype=bool)
+    for j, nb in enumerate(nbs):
+        mask[j, :, :nb] = ~np.isnan(osc[j, :, :nb])
+    check_scores(gsc, osc, mask)
+    compare_quest(gsel, gns, osel, ons, osc, nbs, wl.k)
+    # attention on the oracle's selection for the sampled requests
+    sub_out = qs.qs_sparse_attn_decode(sub.query.to(DEV), sub.k_cache.to(DEV), sub.v_cache.to(DEV),
+                                       sub.block_tables.to(DEV), sub.seq_lens.to(DEV),
+                                       torch.from_numpy(osel).to(DEV), torch.from_numpy(ons).to(DEV))
+    ref = oracle.sparse_attn_decode(sub.query, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens, osel, ons,
+                                    wl.N)
+    err = np.abs(sub_out.float().cpu().numpy() - ref).max()
+    assert err <= 2e-2, f"attention err {err:.3e}"
+    # the full-size run's own outputs for these requests against the oracle on the GPU selection
+    ref_g = oracle.sparse_attn_decode(sub.query, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens, gsel,
+                                      gns, wl.N)
+    err_g = np.abs(out.float().cpu().numpy()[reqs] - ref_g).max()
+    assert err_g <= 2e-2, f"full-size attention err {err_g:.3e}"
+    return tnp(sel), tnp(ns)
+
+
+def test_config4_full_size_sampled(qs, oracle):
+    wl = W.config4(device=DEV)
+    sel, ns = check_large(qs, oracle, wl, [0, 3, 7], "config4")
+    # needle recall is reported, not gated
+    hits = sum(int((t // wl.BS) in set(sel[b, n, :ns[b, n]].tolist())) for b, t in wl.needles for n in range(wl.N))
+    say(f"config4 needle recall {hits}/{wl.B * wl.N}")
+
+
+def test_config5_full_size_sampled(qs, oracle):
+    wl = W.config5(device=DEV)
+    check_large(qs, oracle, wl, [0, 77, 127], "config5")
+
+
+def test_workspace_shared_across_shapes_and_operations(qs, oracle):
+    """One zeroed workspace serves select and attention calls of different sizes in turn
+    (no debug score output, so the select scores live in the workspace too)."""
+    say("shared workspace across shapes")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    cases = [(51, 4, 64, 8, 128, [128 * 300, 128 * 40, 128 * 999, 128 * 5], 16),
+             (52, 1, 16, 8, 32, [32 * 128], 32),
+             (53, 2, 32, 8, 64, [64 * 200 + 1, 64 * 90], 8),
+             (51, 4, 64, 8, 128, [128 * 300, 128 * 40, 128 * 999, 128 * 5], 16)]
+    for seed, B, H, N, BS, lens, k in cases:
+        say(f"  shared workspace case seed={seed} B={B} H={H} BS={BS} k={k}")
+        wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=torch.bfloat16)
+        mx, mn = run_meta(qs, wl, sentinel=0.0)
+        sel, ns = qs.qs_block_select(wl.query.to(DEV), mx, mn, wl.meta_tables.to(DEV), wl.seq_lens.to(DEV), k,
+                                     workspace_buf=ws)
+        omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
+        osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k)
+        compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs_of(wl), k)
+        for sh in (N, H):
+            rsel, rns = random_selection(seed, B, sh, k, nbs_of(wl))
+            out = qs.qs_sparse_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV),
+                                           wl.block_tables.to(DEV), wl.seq_lens.to(DEV), rsel.to(DEV), rns.to(DEV),
+                                           sel_heads=sh, workspace_buf=ws)
+            ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, rsel,
+                                            rns, sh)
+            assert np.abs(out.float().cpu().numpy() - ref).max() <= 2e-2
+    assert int(ws[:256 * 1024].count_nonzero()) == 0, "counters must return to zero"

@@ -154,3 +154,21 @@ def test_config3_k_sweep(oracle):
             assert np.all([nb - 1 in set(sel[0, h].tolist()) for h in range(base.H)])
         if k >= 4:
             assert all(needle_block in set(sel[0, h].tolist()) for h in range(base.H)), k
+
+
+def test_pick_kinds_partition_the_selection(oracle):
+    wl = W.random_case(38, 2, 4, 2, 32, [64 * 32, 20 * 32 + 3], k=7, with_importance=True)
+    r = _run(oracle, wl, 7)
+    for b in range(2):
+        nb = cdiv(int(wl.seq_lens[b]), 32)
+        for h in range(wl.H):
+            kind = r["kind"][b, h]
+            sel = set(r["selected"][b, h, :r["n_selected"][b, h]].tolist())
+            assert sel == set(np.nonzero((kind == 1) | (kind == 2) | (kind == 3))[0].tolist())
+            assert int((kind == 1).sum()) == r["n_imp"][b, h] == 4
+            assert int((kind == 3).sum()) == int((kind == 4).sum()) <= 1
+            if (kind == 3).any():
+                assert kind[nb - 1] == 3
+                victim = int(np.nonzero(kind == 4)[0][0])
+                probes = [i for i in range(nb) if kind[i] in (2, 4)]
+                assert min(probes, key=lambda i: (r["probe"][b, h, i], -i)) == victim

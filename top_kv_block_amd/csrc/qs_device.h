@@ -1,0 +1,139 @@
+// qs_device.h -- device helpers shared by the qsparse kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qs {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;            // every kernel runs 4 wave64s per workgroup
+constexpr int kWaves = kThreads / kWave;
+
+struct __attribute__((aligned(16))) u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// bf16 <-> f32 (bf16 is the upper half of a binary32)
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Monotone map from finite floats to uint32: a < b (IEEE total order, -0 < +0)
+// iff key(a) < key(b). Used for exact, deterministic top-k on scores.
+__device__ __forceinline__ uint32_t f2key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// sum over aligned groups of `width` lanes (width a power of two <= 64); every lane
+// of the group ends with the group's sum
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+template <int width>
+__device__ __forceinline__ int group_sum_i(int v) {
+#pragma unroll
+    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// exclusive prefix count of `flag` over the workgroup's threads in thread order;
+// `total` receives the workgroup total. Uses wsum[kWaves] of LDS; contains barriers.
+__device__ __forceinline__ int block_excl_count(bool flag, int* wsum, int& total) {
+    const uint64_t m = __ballot(flag);
+    const int lane = lane_id();
+    const int below = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    if (lane == 0) wsum[wave_id()] = __popcll(m);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = wsum[w];
+        off += (w < wave_id()) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return off + below;
+}
+
+// Block-wide radix select over a virtual array of n keys.
+// kf(i, &key) returns true if index i is a candidate and sets its key.
+// Finds the R-th largest candidate key T (1 <= R <= #candidates); on return `need_eq`
+// holds how many candidates equal to T belong to the top R (R minus those above T).
+// LDS: hist[256], sh[4]. Contains barriers: every thread of the workgroup must call it.
+template <class KeyFn>
+__device__ uint32_t block_radix_select(int n, int R, KeyFn kf, uint32_t* hist, int* sh, int& need_eq) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = R;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int j = threadIdx.x; j < 256; j += kThreads) hist[j] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            uint32_t key;
+            if (kf(i, key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave_id() == 0) {
+            // lane l owns bins 255-4l .. 252-4l (descending digit order across lanes)
+            const int l = lane_id();
+            uint32_t c[4];
+            uint32_t s = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * l - j]; s += c[j]; }
+            uint32_t incl = s;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t t = __shfl_up(incl, o, kWave);
+                if (l >= o) incl += t;
+            }
+            uint32_t run = incl - s;
+            if (run < uint32_t(need) && uint32_t(need) <= incl) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (run + c[j] >= uint32_t(need)) {
+                        sh[0] = 255 - 4 * l - j;
+                        sh[1] = int(run);
+                        break;
+                    }
+                    run += c[j];
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t d = uint32_t(sh[0]);
+        need -= sh[1];
+        prefix |= d << shift;
+        pmask |= 255u << shift;
+        __syncthreads();
+    }
+    need_eq = need;
+    return prefix;
+}
+
+}  // namespace qs

@@ -1,0 +1,117 @@
+// qs_internal.h -- launchers behind the C ABI (host side, already-validated arguments).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qs {
+
+// Every workspace starts with a counter area that only ever holds arrival counters
+// (zero at first use; every call returns the counters it used to zero), followed by
+// free-form data (scores, partial results). Keeping the two apart lets calls of any
+// size and either operation share one workspace.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr long long kMaxCounters = kCounterBytes / sizeof(uint32_t);
+
+// ---- metadata ----------------------------------------------------------------------
+struct MetaArgs {
+    int B, N, D, BS;
+    bool bf16;
+    const void* k_cache;
+    int num_kv_blocks;
+    const int32_t* block_tables;
+    int mkbpr;
+    const int32_t* seq_lens;
+    const int32_t* meta_tables;
+    int mmbpr;
+    void* maxb;
+    void* minb;
+    int num_meta;
+};
+hipError_t launch_build_metadata(const MetaArgs& a, hipStream_t s);
+
+// ---- Quest select ------------------------------------------------------------------
+struct SelectPlan {
+    int chunk;        // blocks scored per workgroup
+    int n_chunks;     // workgroups per (request, kv head)
+    size_t scores_off, counters_off, bytes;
+};
+SelectPlan plan_block_select(int B, int N, int BS, int mmbpr);
+
+struct SelectArgs {
+    int B, H, N, D, BS;
+    bool bf16;
+    const void* query;
+    const void* maxb;
+    const void* minb;
+    int num_meta;
+    const int32_t* meta_tables;
+    int mmbpr;
+    const int32_t* seq_lens;
+    const int32_t* tsmu;
+    uint32_t flags;
+    int k;
+    int32_t* selected;
+    int32_t* n_selected;
+    float* block_scores;
+    void* workspace;
+};
+hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& p, hipStream_t s);
+
+// ---- probe select ------------------------------------------------------------------
+constexpr int kProbeMaxBlocks = 4096;
+struct ProbeArgs {
+    int B, H, N, D, BS;
+    bool q_bf16, kv_bf16;
+    const void* query;
+    const void* k_cache;
+    int num_kv_blocks;
+    const int32_t* block_tables;
+    int mkbpr;
+    const int32_t* seq_lens;
+    const float* importance;
+    int imp_stride;
+    int n_probe;
+    int k;
+    uint32_t flags;
+    int32_t* selected;
+    int32_t* n_selected;
+    float* probe_scores;
+};
+hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s);
+
+// ---- sparse attention --------------------------------------------------------------
+struct AttnPlan {
+    int hpr;          // query heads per selection row
+    int hc;           // heads per workgroup (1, 2, 4 or 8)
+    int hchunks;      // workgroups across a row's heads
+    int splits;       // workgroups across a row's selection slots
+    int spb;          // selection slots per split
+    size_t part_off, counters_off, bytes;
+};
+AttnPlan plan_sparse_attn(int B, int H, int N, int D, int sel_heads, int k);
+
+struct AttnArgs {
+    int B, H, N, D, BS;
+    int q_dtype, kv_dtype;  // qs_dtype values
+    const void* query;
+    const void* k_cache;
+    const void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    int num_kv_blocks;
+    const int32_t* block_tables;
+    int mkbpr;
+    const int32_t* seq_lens;
+    const int32_t* selected;
+    const int32_t* n_selected;
+    int sel_heads;
+    int k;
+    float scale;
+    void* out;
+    void* workspace;
+};
+hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+
+}  // namespace qs

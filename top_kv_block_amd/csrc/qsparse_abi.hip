@@ -1,0 +1,200 @@
+// qsparse_abi.hip -- the C ABI: argument validation, workspace sizing, launches.
+//
+// Every check that the host can make happens before the first HIP call, so invalid
+// calls return QS_ERR_INVALID / QS_ERR_UNSUPPORTED without touching the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/qsparse.h"
+#include "qs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qs_status fail(qs_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qs_status ok() {
+    g_err[0] = '\0';
+    return QS_OK;
+}
+
+qs_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int kMaxGrid = 65535;
+
+bool block_size_ok(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+// shared size checks; returns QS_OK or an error with the message set
+qs_status check_dims(const char* fn, int32_t B, int32_t H, int32_t N, int32_t D, int32_t BS) {
+    if (B < 0 || B > kMaxGrid) return fail(QS_ERR_INVALID, "%s: B=%d out of range [0, %d]", fn, B, kMaxGrid);
+    if (N < 1 || N > kMaxGrid) return fail(QS_ERR_INVALID, "%s: N=%d must be in [1, %d]", fn, N, kMaxGrid);
+    if (H < N || H % N != 0) return fail(QS_ERR_INVALID, "%s: H=%d must be a positive multiple of N=%d", fn, H, N);
+    if (D != 128) return fail(QS_ERR_UNSUPPORTED, "%s: only D=128 is implemented (got %d)", fn, D);
+    if (!block_size_ok(BS)) return fail(QS_ERR_UNSUPPORTED, "%s: block_size must be 16, 32, 64 or 128 (got %d)", fn, BS);
+    return QS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qs_last_error(void) { return g_err; }
+
+const char* qs_version(void) { return "qsparse 0.1 (gfx950)"; }
+
+qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size, qs_dtype kv_dtype,
+                            const void* k_cache, int32_t num_kv_blocks, const int32_t* block_tables,
+                            int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
+                            const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req, void* maxblocks,
+                            void* minblocks, int32_t num_meta_blocks, void* stream) {
+    const char* fn = "qs_build_metadata";
+    qs_status st = check_dims(fn, B, N, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32 or QS_BF16", fn);
+    if (!k_cache || !block_tables || !seq_lens || !metadata_block_tables || !maxblocks || !minblocks)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(k_cache) || !aligned16(maxblocks) || !aligned16(minblocks))
+        return fail(QS_ERR_INVALID, "%s: k_cache, maxblocks and minblocks must be 16-byte aligned", fn);
+    if (num_kv_blocks < 1 || num_meta_blocks < 1 || max_kv_blocks_per_req < 1 || max_meta_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: block counts and table widths must be >= 1", fn);
+    if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
+        return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
+    if (B == 0) return ok();
+    qs::MetaArgs a{B, N, D, block_size, kv_dtype == QS_BF16, k_cache, num_kv_blocks, block_tables,
+                   max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
+                   maxblocks, minblocks, num_meta_blocks};
+    return hip_status(qs::launch_build_metadata(a, (hipStream_t)stream), fn);
+}
+
+size_t qs_block_select_workspace_bytes(int32_t B, int32_t N, int32_t block_size, int32_t max_meta_blocks_per_req) {
+    if (B < 0 || N < 1 || block_size < 1 || max_meta_blocks_per_req < 1) return 0;
+    return qs::plan_block_select(B, N, block_size, max_meta_blocks_per_req).bytes;
+}
+
+qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
+                          const void* query, const void* maxblocks, const void* minblocks, int32_t num_meta_blocks,
+                          const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                          const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags, int32_t k,
+                          int32_t* selected, int32_t* n_selected, float* block_scores, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    const char* fn = "qs_block_select";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (dtype != QS_F32 && dtype != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32 or QS_BF16", fn);
+    if (!query || !maxblocks || !minblocks || !metadata_block_tables || !seq_lens || !selected || !n_selected ||
+        !workspace)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(query) || !aligned16(maxblocks) || !aligned16(minblocks))
+        return fail(QS_ERR_INVALID, "%s: query, maxblocks and minblocks must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (flags & ~(uint32_t)(QS_FORCE_SINK | QS_FORCE_WINDOW))
+        return fail(QS_ERR_INVALID, "%s: flags may only hold QS_FORCE_SINK | QS_FORCE_WINDOW", fn);
+    if (k < 1) return fail(QS_ERR_INVALID, "%s: k=%d must be >= 1", fn, k);
+    if (num_meta_blocks < 1 || max_meta_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: num_meta_blocks and max_meta_blocks_per_req must be >= 1", fn);
+    if ((long long)max_meta_blocks_per_req * block_size > (1LL << 24))
+        return fail(QS_ERR_UNSUPPORTED, "%s: more than 2^24 blocks per request", fn);
+    const qs::SelectPlan plan = qs::plan_block_select(B, N, block_size, max_meta_blocks_per_req);
+    if (workspace_bytes < plan.bytes)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
+    if (B == 0) return ok();
+    qs::SelectArgs a{B, H, N, D, block_size, dtype == QS_BF16, query, maxblocks, minblocks, num_meta_blocks,
+                     metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
+                     selected, n_selected, block_scores, workspace};
+    return hip_status(qs::launch_block_select(a, plan, (hipStream_t)stream), fn);
+}
+
+qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
+                          qs_dtype kv_dtype, const void* query, const void* k_cache, int32_t num_kv_blocks,
+                          const int32_t* block_tables, int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
+                          const float* importance, int32_t importance_stride, int32_t n_probe, int32_t k,
+                          uint32_t flags, int32_t* selected, int32_t* n_selected, float* probe_scores,
+                          void* stream) {
+    const char* fn = "qs_probe_select";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
+    if ((q_dtype != QS_F32 && q_dtype != QS_BF16) || (kv_dtype != QS_F32 && kv_dtype != QS_BF16))
+        return fail(QS_ERR_UNSUPPORTED, "%s: query and K must be QS_F32 or QS_BF16", fn);
+    if (!query || !k_cache || !block_tables || !seq_lens || !selected || !n_selected)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(k_cache)) return fail(QS_ERR_INVALID, "%s: k_cache must be 16-byte aligned", fn);
+    if (flags & ~(uint32_t)QS_RECENCY) return fail(QS_ERR_INVALID, "%s: flags may only hold QS_RECENCY", fn);
+    if (k < 1) return fail(QS_ERR_INVALID, "%s: k=%d must be >= 1", fn, k);
+    if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
+    if (max_kv_blocks_per_req > qs::kProbeMaxBlocks)
+        return fail(QS_ERR_UNSUPPORTED, "%s: max_kv_blocks_per_req=%d exceeds %d", fn, max_kv_blocks_per_req,
+                    qs::kProbeMaxBlocks);
+    if (importance && importance_stride < 1)
+        return fail(QS_ERR_INVALID, "%s: importance_stride must be >= 1 when importance is given", fn);
+    if (B == 0) return ok();
+    qs::ProbeArgs a{B, H, N, D, block_size, q_dtype == QS_BF16, kv_dtype == QS_BF16, query, k_cache, num_kv_blocks,
+                    block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
+                    selected, n_selected, probe_scores};
+    return hip_status(qs::launch_probe_select(a, (hipStream_t)stream), fn);
+}
+
+size_t qs_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t sel_heads, int32_t k) {
+    if (B < 0 || N < 1 || H < N || sel_heads < 1 || H % sel_heads != 0 || k < 1 || D < 1) return 0;
+    return qs::plan_sparse_attn(B, H, N, D, sel_heads, k).bytes;
+}
+
+qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
+                                qs_dtype kv_dtype, const void* query, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale, int32_t num_kv_blocks,
+                                const int32_t* block_tables, int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
+                                const int32_t* selected, const int32_t* n_selected, int32_t sel_heads, int32_t k,
+                                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    const char* fn = "qs_sparse_attn_decode";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (q_dtype != QS_F32 && q_dtype != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: q_dtype must be QS_F32 or QS_BF16", fn);
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_I8)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32, QS_BF16 or QS_I8", fn);
+    if (!query || !k_cache || !v_cache || !block_tables || !seq_lens || !selected || !n_selected || !out ||
+        !workspace)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (kv_dtype == QS_I8 && (!k_scale || !v_scale))
+        return fail(QS_ERR_INVALID, "%s: int8 KV needs k_scale and v_scale", fn);
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(QS_ERR_INVALID, "%s: k_cache and v_cache must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (sel_heads < N || sel_heads > H || sel_heads % N != 0 || H % sel_heads != 0)
+        return fail(QS_ERR_INVALID, "%s: sel_heads=%d must satisfy N | sel_heads | H (N=%d, H=%d)", fn, sel_heads, N, H);
+    if (sel_heads > kMaxGrid) return fail(QS_ERR_INVALID, "%s: sel_heads exceeds %d", fn, kMaxGrid);
+    if (k < 1) return fail(QS_ERR_INVALID, "%s: k=%d must be >= 1", fn, k);
+    if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
+    if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
+    const qs::AttnPlan plan = qs::plan_sparse_attn(B, H, N, D, sel_heads, k);
+    if (workspace_bytes < plan.bytes)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
+    if ((long long)plan.splits * plan.hchunks > 0x7fffffffLL) return fail(QS_ERR_INVALID, "%s: grid too large", fn);
+    if (B == 0) return ok();
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
+    qs::AttnArgs a{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, v_cache, k_scale, v_scale,
+                   num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, selected, n_selected, sel_heads, k,
+                   scale, out, workspace};
+    return hip_status(qs::launch_sparse_attn(a, plan, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,267 @@
+"""Python binding of libqsparse.so (the C ABI in include/qsparse.h).
+
+Argument marshalling only: shape/dtype/device checks on torch tensors, output and
+workspace allocation, and the call on torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. Importing this
+module fails loudly if the library has not been built (python -m top_kv_block_amd.build).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsparse.so")
+
+QS_OK, QS_ERR_INVALID, QS_ERR_UNSUPPORTED, QS_ERR_HIP = 0, 1, 2, 3
+QS_F32, QS_BF16, QS_I8 = 0, 1, 2
+QS_FORCE_SINK, QS_FORCE_WINDOW, QS_RECENCY = 1, 2, 4
+
+# the C ABI's exported functions (also checked by the ABI tests)
+EXPORTS = (
+    "qs_build_metadata", "qs_block_select_workspace_bytes", "qs_block_select", "qs_probe_select",
+    "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_last_error", "qs_version",
+)
+
+
+class QsError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m top_kv_block_amd.build` "
+                          "(the HIP path has no fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    lib.qs_build_metadata.argtypes = [i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, P, i32, P, P, i32, P]
+    lib.qs_block_select_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.qs_block_select_workspace_bytes.restype = sz
+    lib.qs_block_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, u32, i32,
+                                    P, P, P, P, sz, P]
+    lib.qs_probe_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, i32, P, i32, P, P,
+                                    i32, i32, i32, u32, P, P, P, P]
+    lib.qs_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.qs_sparse_attn_workspace_bytes.restype = sz
+    lib.qs_sparse_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, P, P, i32,
+                                          P, i32, P, P, P, i32, i32, ctypes.c_float, P, P, sz, P]
+    for f in ("qs_build_metadata", "qs_block_select", "qs_probe_select", "qs_sparse_attn_decode"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.qs_last_error.restype = ctypes.c_char_p
+    lib.qs_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != QS_OK:
+        raise QsError(status, lib.qs_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return QS_F32
+    if t.dtype == torch.bfloat16:
+        return QS_BF16
+    if t.dtype == torch.int8:
+        return QS_I8
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    return dev
+
+
+def _i32(t, name):
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _rows(t, B, name, width=None):
+    """t must be a [>=B, width] (or [>=B]) table."""
+    if t is None:
+        return
+    _need(t.dim() >= 1 and t.shape[0] >= B, f"{name} needs at least {B} rows")
+    if width is not None:
+        _need(t.dim() == 2 and t.shape[1] == width, f"{name} must have {width} columns")
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+_workspaces = {}
+
+
+def workspace(nbytes, device, op):
+    """A zero-filled, 256-byte aligned workspace cached per (device, operation), grown on
+    demand. Calls that share one must be ordered on one stream."""
+    key = (torch.device(device).index or 0, op)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------------------------------------
+# the four operations (names and argument meaning as in include/qsparse.h)
+# ------------------------------------------------------------------------------------------
+
+def qs_build_metadata(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks):
+    """Per-block, per-channel max/min of K into the paged metadata blocks (in place)."""
+    dev = _dev(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks)
+    for n, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                 ("metadata_block_tables", metadata_block_tables)):
+        _i32(t, n)
+    nkv, BS, N, D = k_cache.shape
+    if maxblocks.shape != minblocks.shape or maxblocks.shape[1:] != k_cache.shape[1:]:
+        raise ValueError("maxblocks/minblocks must be [num_meta_blocks, BS, N, D]")
+    if maxblocks.dtype != k_cache.dtype or minblocks.dtype != k_cache.dtype:
+        raise TypeError("metadata dtype must match k_cache")
+    B = seq_lens.shape[0]
+    _rows(block_tables, B, "block_tables")
+    _rows(metadata_block_tables, B, "metadata_block_tables")
+    _check(lib.qs_build_metadata(B, N, D, BS, _dtype_code(k_cache), _ptr(k_cache), nkv, _ptr(block_tables),
+                                 block_tables.shape[1], _ptr(seq_lens), _ptr(metadata_block_tables),
+                                 metadata_block_tables.shape[1], _ptr(maxblocks), _ptr(minblocks),
+                                 maxblocks.shape[0], _stream(dev)))
+
+
+def block_select_workspace_bytes(B, N, block_size, mmbpr):
+    return lib.qs_block_select_workspace_bytes(B, N, block_size, mmbpr)
+
+
+def qs_block_select(query, maxblocks, minblocks, metadata_block_tables, seq_lens, k,
+                    tokens_since_update=None, flags=0, selected=None, n_selected=None,
+                    block_scores=None, workspace_buf=None):
+    """Quest top-k selection. Returns (selected [B, N, k] int32, n_selected [B, N] int32)."""
+    dev = _dev(query, maxblocks, minblocks, metadata_block_tables, seq_lens, tokens_since_update,
+               selected, n_selected, block_scores)
+    for n, t in (("metadata_block_tables", metadata_block_tables), ("seq_lens", seq_lens),
+                 ("tokens_since_update", tokens_since_update)):
+        _i32(t, n)
+    B, H, D = query.shape
+    nmeta, BS, N, D2 = maxblocks.shape
+    mmbpr = metadata_block_tables.shape[1]
+    _need(D2 == D and H % N == 0, "query and metadata shapes disagree")
+    _need(maxblocks.shape == minblocks.shape and maxblocks.dtype == minblocks.dtype == query.dtype,
+          "maxblocks/minblocks must match each other and the query dtype")
+    _rows(metadata_block_tables, B, "metadata_block_tables")
+    _rows(seq_lens, B, "seq_lens")
+    _rows(tokens_since_update, B, "tokens_since_update")
+    if selected is None:
+        selected = torch.empty((B, N, k), dtype=torch.int32, device=dev)
+    if n_selected is None:
+        n_selected = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _need(selected.numel() >= B * N * k and n_selected.numel() >= B * N, "selected must hold [B, N, k]")
+    if block_scores is not None and (block_scores.dtype != torch.float32 or
+                                     block_scores.numel() < B * N * mmbpr * BS):
+        raise ValueError("block_scores must be fp32 [B, N, MMBPR*BS]")
+    nbytes = block_select_workspace_bytes(B, N, BS, mmbpr)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select")
+    _check(lib.qs_block_select(B, H, N, D, BS, _dtype_code(query), _ptr(query), _ptr(maxblocks),
+                               _ptr(minblocks), nmeta, _ptr(metadata_block_tables), mmbpr, _ptr(seq_lens),
+                               _ptr(tokens_since_update), int(flags), int(k), _ptr(selected), _ptr(n_selected),
+                               _ptr(block_scores), _ptr(ws), ws.numel(), _stream(dev)))
+    return selected, n_selected
+
+
+def qs_probe_select(query, k_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
+                    flags=QS_RECENCY, selected=None, n_selected=None, probe_scores=None):
+    """Page 1's probe/importance/recency selection per query head.
+    Returns (selected [B, H, k] int32, n_selected [B, H] int32)."""
+    dev = _dev(query, k_cache, block_tables, seq_lens, importance, selected, n_selected, probe_scores)
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    if importance is not None and importance.dtype != torch.float32:
+        raise TypeError("importance must be fp32")
+    B, H, D = query.shape
+    nkv, BS, N, D2 = k_cache.shape
+    mkbpr = block_tables.shape[1]
+    if selected is None:
+        selected = torch.empty((B, H, k), dtype=torch.int32, device=dev)
+    if n_selected is None:
+        n_selected = torch.empty((B, H), dtype=torch.int32, device=dev)
+    _need(D2 == D and H % N == 0, "query and k_cache shapes disagree")
+    _rows(block_tables, B, "block_tables")
+    _rows(seq_lens, B, "seq_lens")
+    _rows(importance, B, "importance")
+    _need(selected.numel() >= B * H * k and n_selected.numel() >= B * H, "selected must hold [B, H, k]")
+    _need(probe_scores is None or (probe_scores.dtype == torch.float32 and probe_scores.numel() >= B * H * mkbpr),
+          "probe_scores must be fp32 [B, H, MKBPR]")
+    stride = 0 if importance is None else importance.shape[1]
+    _check(lib.qs_probe_select(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
+                               _ptr(k_cache), nkv, _ptr(block_tables), mkbpr, _ptr(seq_lens), _ptr(importance),
+                               stride, int(n_probe), int(k), int(flags), _ptr(selected), _ptr(n_selected),
+                               _ptr(probe_scores), _stream(dev)))
+    return selected, n_selected
+
+
+def sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k):
+    return lib.qs_sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k)
+
+
+def qs_sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selected, n_selected,
+                          sel_heads=None, k_scale=None, v_scale=None, softmax_scale=0.0, out=None,
+                          workspace_buf=None):
+    """Exact attention over the selected blocks. Returns out [B, H, D] in the query dtype."""
+    dev = _dev(query, k_cache, v_cache, block_tables, seq_lens, selected, n_selected, k_scale, v_scale, out)
+    for n, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("selected", selected),
+                 ("n_selected", n_selected)):
+        _i32(t, n)
+    B, H, D = query.shape
+    nkv, BS, N, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    if sel_heads is None:
+        sel_heads = selected.shape[1]
+    k = selected.shape[2]
+    _need(D2 == D and H % N == 0, "query and KV shapes disagree")
+    _need(selected.dim() == 3 and selected.shape[0] >= B and selected.shape[1] == sel_heads,
+          "selected must be [B, sel_heads, k]")
+    _need(n_selected.numel() >= B * sel_heads, "n_selected must be [B, sel_heads]")
+    _rows(block_tables, B, "block_tables")
+    _rows(seq_lens, B, "seq_lens")
+    if k_cache.dtype == torch.int8:
+        for nm, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _need(sc is not None and sc.dtype == torch.float32 and sc.numel() >= nkv * BS * N,
+                  f"{nm} must be fp32 [num_kv_blocks, BS, N]")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=query.dtype, device=dev)
+    _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
+    nbytes = sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "attn")
+    _check(lib.qs_sparse_attn_decode(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
+                                     _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nkv,
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(selected),
+                                     _ptr(n_selected), int(sel_heads), int(k), float(softmax_scale), _ptr(out),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return out
