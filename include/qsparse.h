@@ -37,12 +37,11 @@
  *     Negative seq_lens count as 0.
  *   - Determinism: identical inputs give bit-identical outputs ([P1] section 1: same
  *     query and same KV must select the same blocks; ties go to the lower index).
- *   - Workspaces: calls that take `workspace` use its first 256 KiB for arrival
- *     counters and the rest for scores and partial results. Zero-fill the first 256 KiB
- *     once before the first use; every call returns the counters it used to zero, so one
- *     workspace can serve calls of any size and either operation. It must be 256-byte
- *     aligned, at least the size the matching *_workspace_bytes() returns, and not used
- *     by calls that may run concurrently (calls on one stream are ordered).
+ *   - Workspaces: calls that take `workspace` use it as scratch for scores and partial
+ *     results; its contents on entry are ignored. It must be 256-byte aligned, at least
+ *     the size the matching *_workspace_bytes() returns, and not used by calls that may
+ *     run concurrently (calls on one stream are ordered). Kernels never synchronise
+ *     across workgroups; a call may run as two stream-ordered kernels.
  */
 #ifndef QSPARSE_H
 #define QSPARSE_H

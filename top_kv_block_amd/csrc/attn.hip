@@ -7,19 +7,29 @@
 // select_attention_operators" (page 3), section "quest_block_select_paged": selected
 // indices are sequence-relative and are mapped through block_tables.
 //
-// Design (CDNA4): single-query decode attention reads each selected K/V row once and
-// does O(G) flops per byte, so it is bound by the paged K/V gather. Workgroup
-// (split, row, request) takes a contiguous range of the row's selection slots; all
-// query heads that share the row (and the KV head) are processed together (up to 8 per
-// workgroup), so every K/V row is fetched once for all of them. A token row of one KV
-// head (128 channels) is read by LPR lanes with one 16-byte load each; the partial dot
-// is reduced with shuffles inside that lane group; each lane group is an independent
-// online-softmax worker (running max, sum and its slice of the output accumulator).
-// Groups merge through shuffles and LDS at the end; splits write (max, sum, acc)
-// partials and the workgroup that completes a row (device-scope arrival counter)
-// combines them in split order, so the result does not depend on scheduling.
-// int8 KV: the query row is quantised in fp32 (absmax / 127, half-to-even, clamp
-// +-127) and dots run on v_dot4_i32_i8 with exact int32 accumulation.
+// Design (CDNA4). Decode attention reads every selected K/V row once; the bytes are the
+// bound. A workgroup takes one selection row (all query heads sharing a KV head, so
+// each K/V row is fetched once for all of them) and a range of its selection slots.
+//
+// bf16 KV with a bf16 query (the serving path) runs on the matrix cores, because with
+// G query heads per KV head the work per token is a [G x 128] x [128 x T] product and on
+// the vector ALU (no packed fp32 here) it would cost about as many cycles as the HBM
+// stream: per 32-token chunk a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// (K rows load straight from HBM into the A operand, 16 B per lane; the heads are the
+// 16 columns), does the online softmax on the accumulator registers (each lane owns one
+// head, so the running max/sum and the output rescale need no lane exchange), rounds P
+// to bf16 and accumulates O^T = V^T P^T with 8 more MFMAs. V^T comes from a per-wave
+// LDS tile that the wave writes transposed (8x8 register transposes + 16-byte stores).
+// Four waves take interleaved 32-token chunks and merge (max, sum, acc) through LDS.
+//
+// fp32 and int8 KV (small, latency-bound workloads) run on the vector ALU: a token row
+// is read by LPR lanes with 16-byte loads, dots reduce by shuffles, each lane group is an
+// independent online-softmax worker. int8: the query row is quantised in fp32 (absmax /
+// 127, half-to-even, clamp +-127) and dots use v_dot4_i32_i8 with exact int32 sums.
+//
+// When there are too few rows to fill the chip the slots are split over workgroups,
+// each writing (max, sum, acc) partials, and a small second kernel merges them in split
+// order (no cross-workgroup synchronisation inside a kernel).
 #include <math.h>
 
 #include "qs_device.h"
@@ -29,7 +39,14 @@ namespace qs {
 namespace {
 
 constexpr int kTargetWorkgroups = 2048;
+constexpr int kNoSplitRows = 1024;   // rows at which each row gets one workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int D = 128;
+constexpr int PSTRIDE = D + 2;       // partial record: acc[D], max, sum
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void merge_state(float& m, float& l, float* a, int n, float m2, float l2,
                                             const float* a2) {
@@ -41,43 +58,253 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* a, int n,
     m = M;
 }
 
+struct AttnParams {
+    const uint8_t* query;
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const float* ksc;
+    const float* vsc;
+    int num_kv_blocks;
+    const int32_t* bt;
+    int mkbpr;
+    const int32_t* sl;
+    const int32_t* sel;
+    const int32_t* nsel;
+    int H, N, BS, sel_heads, k;
+    int hpr, hchunks, splits, spb;
+    float scale_log2;
+    uint8_t* out;
+    float* part;
+};
+
+// result of one workgroup for head g, channel d: either the output or a partial record
+__device__ __forceinline__ void emit(const AttnParams& p, int b, int row, int hcix, int split, int hc_cap, int h0,
+                                     int g, int d, float M, float Ls, float A, bool out_bf16) {
+    if (p.splits == 1) {
+        const float v = (Ls > 0.f) ? A / Ls : 0.f;
+        const size_t o = (size_t(b) * p.H + h0 + g) * D + d;
+        if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
+        else ((float*)p.out)[o] = v;
+    } else {
+        float* rec = p.part + (((size_t(row) * p.hchunks + hcix) * p.splits + split) * hc_cap + g) * PSTRIDE;
+        rec[d] = A;
+        if (d == 0) { rec[D] = M; rec[D + 1] = Ls; }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// bf16 matrix-core kernel
+// ------------------------------------------------------------------------------------
+constexpr int kVtPitch = 80;             // bytes per V^T row in LDS: 32 tokens (64 B) + pad
+constexpr int kVtBytes = D * kVtPitch;   // one wave's V^T tile
+
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) {
+    u32v4 t = {v.x, v.y, v.z, v.w};
+    return __builtin_bit_cast(bf16x8, t);
+}
+
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kVtBytes];  // 40 KiB
+
+    const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
+    const int s = blockIdx.y, b = blockIdx.z;
+    const int h0 = s * p.hpr + hcix * 16;
+    const int nh = min(16, p.hpr - hcix * 16);
+    const int G = p.H / p.N;
+    const int kh = (s * p.hpr) / G;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c16 = lane & 15, j = lane >> 4;
+
+    // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
+    bf16x8 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        u32x4 v{0u, 0u, 0u, 0u};
+        if (c16 < nh) v = ld16(p.query + ((size_t(b) * p.H + h0 + c16) * D + 32 * ks + 8 * j) * 2);
+        qb[ks] = as_bf8(v);
+    }
+
+    const int L = max(p.sl[b], 0);
+    const int nb = (L + p.BS - 1) / p.BS;
+    const int row = b * p.sel_heads + s;
+    const int ns = min(max(p.nsel[row], 0), p.k);
+    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
+    const int32_t* srow = p.sel + size_t(row) * p.k;
+    const int cpb = (p.BS + 31) / 32;                 // 32-token chunks per block
+    const int nq = max(0, slot1 - slot0) * cpb;
+    const size_t tstride = size_t(p.N) * D;           // elements between tokens of one KV head
+    uint8_t* vt = lds + w * kVtBytes;
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int q = w; q < nq; q += kWaves) {
+        const int slot = slot0 + q / cpb, cib = q % cpb;
+        const int blk = srow[slot];
+        if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
+        const int phys = p.bt[size_t(b) * p.mkbpr + blk];
+        if (phys < 0 || phys >= p.num_kv_blocks) continue;
+        const int nt = min(p.BS, L - blk * p.BS);
+        const int tb = cib * 32;
+        if (tb >= nt) continue;
+        const uint16_t* kb = (const uint16_t*)p.kc + (size_t(phys) * p.BS * p.N + kh) * D;
+        const uint16_t* vb = (const uint16_t*)p.vc + (size_t(phys) * p.BS * p.N + kh) * D;
+
+        // K: tile tau row r = c16 is token tb + 8*(r/4) + 4*tau + r%4 (so that lane group j
+        // ends up holding tokens tb + 8j .. 8j+7 in its accumulators)
+        u32x4 kr[2][4];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const int t = tb + 8 * (c16 >> 2) + 4 * tau + (c16 & 3);
+            const int tl = t < nt ? t : 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kr[tau][ks] = ld16(kb + size_t(tl) * tstride + 32 * ks + 8 * j);
+        }
+        // V: lane (c16, j) loads tokens tb + 8j + u, channels 8*c16 .. +7
+        u32x4 vr[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = tb + 8 * j + u;
+            const int tl = t < nt ? t : 0;
+            vr[u] = ld16(vb + size_t(tl) * tstride + 8 * c16);
+        }
+
+        // S^T (tokens x heads): lane holds tokens tb + 8j + 4*tau + i for head c16
+        f32x4 sacc[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[tau][ks]), qb[ks], sacc[tau], 0, 0, 0);
+        }
+        float sv[8];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tau = e >> 2, i = e & 3;
+            const float x = sacc[tau][i] * p.scale_log2;
+            sv[e] = (tb + 8 * j + e < nt) ? x : -INFINITY;
+            cmax = fmaxf(cmax, sv[e]);
+        }
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+        const float mn = fmaxf(m, cmax);
+        const float cf = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+        bf16x8 pv;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pe = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mn);
+            const __bf16 pb = (__bf16)pe;
+            pv[e] = pb;
+            psum += (float)pb;
+        }
+        lsum = lsum * cf + psum;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= cf;
+
+        // V^T tile: row d = 8*c16 + e holds tokens 8j .. 8j+7 at byte 16*j
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int wsel = e >> 1;
+            uint32_t x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const u32x4 r = vr[u];
+                x[u] = wsel == 0 ? r.x : wsel == 1 ? r.y : wsel == 2 ? r.z : r.w;
+            }
+            u32x4 t;
+            if (e & 1) {
+                t.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
+                t.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
+                t.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
+                t.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
+            } else {
+                t.x = (x[0] & 0xffffu) | (x[1] << 16);
+                t.y = (x[2] & 0xffffu) | (x[3] << 16);
+                t.z = (x[4] & 0xffffu) | (x[5] << 16);
+                t.w = (x[6] & 0xffffu) | (x[7] << 16);
+            }
+            st16(vt + (8 * c16 + e) * kVtPitch + 16 * j, t);
+        }
+        // this wave's V^T stores must land before its lanes read other lanes' rows
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // O^T (channels x heads) += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const u32x4 a = ld16(vt + (16 * dt + c16) * kVtPitch + 16 * j);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), pv, o[dt], 0, 0, 0);
+        }
+        // the next chunk overwrites the tile only after every lane has read it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // per-head sum over the four lane groups
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+
+    // merge the four waves through LDS: red_o[w][head][channel], red_m/red_l[w][head]
+    __syncthreads();
+    float* red_o = (float*)lds;                        // 4 * 16 * 128 floats = 32 KiB
+    float* red_m = red_o + kWaves * 16 * D;
+    float* red_l = red_m + kWaves * 16;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[(w * 16 + c16) * D + 16 * dt + 4 * j + i] = o[dt][i];
+    if (j == 0) { red_m[w * 16 + c16] = m; red_l[w * 16 + c16] = lsum; }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D; idx += kThreads) {
+        const int g = idx / D, d = idx % D;
+        if (g >= nh) continue;
+        float M = -INFINITY, Ls = 0.f, A = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww)
+            merge_state(M, Ls, &A, 1, red_m[ww * 16 + g], red_l[ww * 16 + g], &red_o[(ww * 16 + g) * D + d]);
+        emit(p, b, row, hcix, split, 16, h0, g, d, M, Ls, A, true);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// vector-ALU kernel (fp32 / bf16 with fp32 query / int8 KV)
+// ------------------------------------------------------------------------------------
 template <int KV, bool QBF16, int HC>
-__global__ __launch_bounds__(kThreads) void attn_kernel(
-    const uint8_t* __restrict__ query, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-    const float* __restrict__ ksc, const float* __restrict__ vsc, int num_kv_blocks,
-    const int32_t* __restrict__ bt, int mkbpr, const int32_t* __restrict__ sl,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ nsel, int H, int N, int BS, int sel_heads, int k,
-    int hpr, int hchunks, int splits, int spb, float scale_log2, uint8_t* __restrict__ out,
-    float* __restrict__ part, uint32_t* __restrict__ counters) {
-    constexpr int D = 128;
+__global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     constexpr int ke = KV == 0 ? 4 : (KV == 1 ? 2 : 1);
     constexpr int qe = QBF16 ? 2 : 4;
-    constexpr int LPR = D * ke / 16;  // lanes per K/V row
-    constexpr int EPL = 16 / ke;      // channels per lane
+    constexpr int LPR = D * ke / 16;    // lanes per K/V row
+    constexpr int EPL = 16 / ke;        // channels per lane
     constexpr int NG = kThreads / LPR;  // independent lane groups per workgroup
-    constexpr int U = 2;              // tokens in flight per group
+    constexpr int U = 2;                // tokens in flight per group
 
     __shared__ float red_m[kWaves][HC];
     __shared__ float red_l[kWaves][HC];
     __shared__ float red_a[kWaves][HC][D];
-    __shared__ int is_last;
 
-    const int split = blockIdx.x % splits, hcix = blockIdx.x / splits;
+    const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
     const int s = blockIdx.y, b = blockIdx.z;
-    const int h0 = s * hpr + hcix * HC;
-    const int nh = min(HC, hpr - hcix * HC);
-    const int G = H / N;
-    const int kh = (s * hpr) / G;
+    const int h0 = s * p.hpr + hcix * HC;
+    const int nh = min(HC, p.hpr - hcix * HC);
+    const int G = p.H / p.N;
+    const int kh = (s * p.hpr) / G;
     const int tid = threadIdx.x, lr = tid % LPR, grp = tid / LPR;
 
-    // ---- query: fp32 (pre-scaled by softmax_scale * log2 e) or int8 codes ----
+    // query: fp32 (pre-scaled by softmax_scale * log2 e) or int8 codes
     float qf[HC][EPL];
     int32_t q8[HC][EPL / 4 > 0 ? EPL / 4 : 1];
     float qscale[HC];
 #pragma unroll
     for (int g = 0; g < HC; ++g) {
         const int hh = h0 + (g < nh ? g : 0);
-        const uint8_t* qp = query + (size_t(b) * H + hh) * D * qe;
+        const uint8_t* qp = p.query + (size_t(b) * p.H + hh) * D * qe;
         float x[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -90,33 +317,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
             for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
             amax = group_max<LPR>(amax);
             const float sq = amax / 127.0f;
-            qscale[g] = sq * scale_log2;
+            qscale[g] = sq * p.scale_log2;
 #pragma unroll
-            for (int w = 0; w < EPL / 4; ++w) {
+            for (int wd = 0; wd < EPL / 4; ++wd) {
                 uint32_t packed = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int jj = 0; jj < 4; ++jj) {
                     float r = 0.f;
-                    if (sq != 0.f) r = fminf(fmaxf(rintf(x[4 * w + j] / sq), -127.f), 127.f);
-                    packed |= (uint32_t(int32_t(r)) & 0xffu) << (8 * j);
+                    if (sq != 0.f) r = fminf(fmaxf(rintf(x[4 * wd + jj] / sq), -127.f), 127.f);
+                    packed |= (uint32_t(int32_t(r)) & 0xffu) << (8 * jj);
                 }
-                q8[g][w] = int32_t(packed);
+                q8[g][wd] = int32_t(packed);
             }
         } else {
             qscale[g] = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) qf[g][e] = x[e] * scale_log2;
+            for (int e = 0; e < EPL; ++e) qf[g][e] = x[e] * p.scale_log2;
         }
     }
 
-    // ---- this split's selection slots ----
-    const int L = max(sl[b], 0);
-    const int nb = (L + BS - 1) / BS;
-    const int row = b * sel_heads + s;
-    const int ns = min(max(nsel[row], 0), k);
-    const int slot0 = split * spb, slot1 = min(ns, slot0 + spb);
-    const int32_t* srow = sel + size_t(row) * k;
-    const size_t tok_bytes = size_t(N) * D * ke;  // stride between tokens of one KV head
+    const int L = max(p.sl[b], 0);
+    const int nb = (L + p.BS - 1) / p.BS;
+    const int row = b * p.sel_heads + s;
+    const int ns = min(max(p.nsel[row], 0), p.k);
+    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
+    const int32_t* srow = p.sel + size_t(row) * p.k;
+    const size_t tok_bytes = size_t(p.N) * D * ke;
 
     float m[HC], l[HC], acc[HC][EPL];
 #pragma unroll
@@ -129,13 +355,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
     for (int slot = slot0; slot < slot1; ++slot) {
         const int blk = srow[slot];
-        if (blk < 0 || blk >= nb || blk >= mkbpr) continue;
-        const int phys = bt[size_t(b) * mkbpr + blk];
-        if (phys < 0 || phys >= num_kv_blocks) continue;
-        const int nt = min(BS, L - blk * BS);
-        const size_t tok0 = size_t(phys) * BS;
-        const uint8_t* kb = kc + (tok0 * N + kh) * D * ke + lr * 16;
-        const uint8_t* vb = vc + (tok0 * N + kh) * D * ke + lr * 16;
+        if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
+        const int phys = p.bt[size_t(b) * p.mkbpr + blk];
+        if (phys < 0 || phys >= p.num_kv_blocks) continue;
+        const int nt = min(p.BS, L - blk * p.BS);
+        const size_t tok0 = size_t(phys) * p.BS;
+        const uint8_t* kb = p.kc + (tok0 * p.N + kh) * D * ke + lr * 16;
+        const uint8_t* vb = p.vc + (tok0 * p.N + kh) * D * ke + lr * 16;
         for (int t0 = 0; t0 < nt; t0 += NG * U) {
             u32x4 kv[U], vv[U];
             float ks[U], vs[U];
@@ -148,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
                 kv[u] = ld16(kb + size_t(tt) * tok_bytes);
                 vv[u] = ld16(vb + size_t(tt) * tok_bytes);
                 if constexpr (KV == 2) {
-                    ks[u] = ksc[(tok0 + tt) * N + kh];
-                    vs[u] = vsc[(tok0 + tt) * N + kh];
+                    ks[u] = p.ksc[(tok0 + tt) * p.N + kh];
+                    vs[u] = p.vsc[(tok0 + tt) * p.N + kh];
                 } else {
                     ks[u] = vs[u] = 1.f;
                 }
@@ -161,13 +387,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
                 float vf[EPL];
                 if constexpr (KV == 0) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) vf[j] = __uint_as_float(vw[j]);
+                    for (int jj = 0; jj < 4; ++jj) vf[jj] = __uint_as_float(vw[jj]);
                 } else if constexpr (KV == 1) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) { vf[2 * j] = bf_lo(vw[j]); vf[2 * j + 1] = bf_hi(vw[j]); }
+                    for (int jj = 0; jj < 4; ++jj) { vf[2 * jj] = bf_lo(vw[jj]); vf[2 * jj + 1] = bf_hi(vw[jj]); }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) vf[j] = float(int8_t(vw[j / 4] >> (8 * (j % 4)))) * vs[u];
+                    for (int jj = 0; jj < 16; ++jj) vf[jj] = float(int8_t(vw[jj / 4] >> (8 * (jj % 4)))) * vs[u];
                 }
 #pragma unroll
                 for (int g = 0; g < HC; ++g) {
@@ -175,19 +401,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
                     if constexpr (KV == 2) {
                         int dot = 0;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) dot = __builtin_amdgcn_sdot4(q8[g][j], int32_t(kw[j]), dot, false);
+                        for (int jj = 0; jj < 4; ++jj) dot = __builtin_amdgcn_sdot4(q8[g][jj], int32_t(kw[jj]), dot, false);
                         dot = group_sum_i<LPR>(dot);
                         sc = float(dot) * (qscale[g] * ks[u]);
                     } else {
-                        float p = 0.f;
+                        float pp = 0.f;
                         if constexpr (KV == 0) {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) p += qf[g][j] * __uint_as_float(kw[j]);
+                            for (int jj = 0; jj < 4; ++jj) pp += qf[g][jj] * __uint_as_float(kw[jj]);
                         } else {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) p += qf[g][2 * j] * bf_lo(kw[j]) + qf[g][2 * j + 1] * bf_hi(kw[j]);
+                            for (int jj = 0; jj < 4; ++jj)
+                                pp += qf[g][2 * jj] * bf_lo(kw[jj]) + qf[g][2 * jj + 1] * bf_hi(kw[jj]);
                         }
-                        sc = group_sum<LPR>(p);
+                        sc = group_sum<LPR>(pp);
                     }
                     if (ok[u]) {
                         const float mn = fmaxf(m[g], sc);
@@ -203,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         }
     }
 
-    // ---- merge the lane groups of each wave (same lr = same channels) ----
+    // merge the lane groups of each wave (same lr = same channels)
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1) {
 #pragma unroll
@@ -226,128 +453,98 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         }
     }
     __syncthreads();
-
-    // ---- workgroup result per (head, channel) ----
-    const int qe_out = qe;
-    constexpr int PER = (HC * D + kThreads - 1) / kThreads;
-    float rm[PER], rl[PER], ra[PER];
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * kThreads;
-        rm[r] = -INFINITY; rl[r] = 0.f; ra[r] = 0.f;
-        if (idx < HC * D) {
-            const int g = idx / D, d = idx % D;
-            for (int ww = 0; ww < kWaves; ++ww) merge_state(rm[r], rl[r], &ra[r], 1, red_m[ww][g], red_l[ww][g], &red_a[ww][g][d]);
-        }
+    for (int idx = tid; idx < HC * D; idx += kThreads) {
+        const int g = idx / D, d = idx % D;
+        if (g >= nh) continue;
+        float M = -INFINITY, Ls = 0.f, A = 0.f;
+        for (int ww = 0; ww < kWaves; ++ww) merge_state(M, Ls, &A, 1, red_m[ww][g], red_l[ww][g], &red_a[ww][g][d]);
+        emit(p, b, row, hcix, split, HC, h0, g, d, M, Ls, A, QBF16);
     }
+}
 
-    auto emit = [&](int g, int d, float M, float Ls, float A) {
-        if (g >= nh) return;
+// ------------------------------------------------------------------------------------
+// combine pass for split rows: merges the splits' partials in split order
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, int hc_cap, bool out_bf16) {
+    const int hcix = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const int row = b * p.sel_heads + s;
+    const int h0 = s * p.hpr + hcix * hc_cap;
+    const int nh = min(hc_cap, p.hpr - hcix * hc_cap);
+    for (int idx = threadIdx.x; idx < nh * D; idx += kThreads) {
+        const int g = idx / D, d = idx % D;
+        float M = -INFINITY, Ls = 0.f, A = 0.f;
+        for (int sp = 0; sp < p.splits; ++sp) {
+            const float* rec = p.part + (((size_t(row) * p.hchunks + hcix) * p.splits + sp) * hc_cap + g) * PSTRIDE;
+            merge_state(M, Ls, &A, 1, rec[D], rec[D + 1], &rec[d]);
+        }
         const float v = (Ls > 0.f) ? A / Ls : 0.f;
-        const size_t o = (size_t(b) * H + h0 + g) * D + d;
-        if (QBF16) ((uint16_t*)out)[o] = f32_to_bf16_rne(v);
-        else ((float*)out)[o] = v;
-    };
-
-    if (splits == 1) {
-#pragma unroll
-        for (int r = 0; r < PER; ++r) {
-            const int idx = tid + r * kThreads;
-            if (idx < HC * D) emit(idx / D, idx % D, rm[r], rl[r], ra[r]);
-        }
-        return;
+        const size_t o = (size_t(b) * p.H + h0 + g) * D + d;
+        if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
+        else ((float*)p.out)[o] = v;
     }
-
-    // partials: [row][hchunk][split][HC][D + 2] = acc[0..D-1], max, sum
-    const size_t crow = size_t(row) * hchunks + hcix;
-    float* pbase = part + crow * size_t(splits) * HC * (D + 2);
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * kThreads;
-        if (idx < HC * D) {
-            const int g = idx / D, d = idx % D;
-            float* p = pbase + (size_t(split) * HC + g) * (D + 2);
-            p[d] = ra[r];
-            if (d == 0) { p[D] = rm[r]; p[D + 1] = rl[r]; }
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&counters[crow], 1u);
-        is_last = (prev == uint32_t(splits - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        const int idx = tid + r * kThreads;
-        if (idx < HC * D) {
-            const int g = idx / D, d = idx % D;
-            float M = -INFINITY, Ls = 0.f, A = 0.f;
-            for (int j = 0; j < splits; ++j) {
-                const float* p = pbase + (size_t(j) * HC + g) * (D + 2);
-                merge_state(M, Ls, &A, 1, p[D], p[D + 1], &p[d]);
-            }
-            emit(g, d, M, Ls, A);
-        }
-    }
-    if (tid == 0) counters[crow] = 0u;
-    (void)qe_out;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int KV, bool QB, int HC>
-void launch_t(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-    float* part = (float*)((uint8_t*)a.workspace + p.part_off);
-    uint32_t* counters = (uint32_t*)((uint8_t*)a.workspace + p.counters_off);
-    dim3 grid(unsigned(p.splits * p.hchunks), unsigned(a.sel_heads), unsigned(a.B));
-    hipLaunchKernelGGL((attn_kernel<KV, QB, HC>), grid, dim3(kThreads), 0, s, (const uint8_t*)a.query,
-                       (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale, a.v_scale, a.num_kv_blocks,
-                       a.block_tables, a.mkbpr, a.seq_lens, a.selected, a.n_selected, a.H, a.N, a.BS, a.sel_heads,
-                       a.k, p.hpr, p.hchunks, p.splits, p.spb, a.scale * kLog2e, (uint8_t*)a.out, part, counters);
-}
-
 template <int KV, bool QB>
-void launch_hc(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-    switch (p.hc) {
-        case 1: launch_t<KV, QB, 1>(a, p, s); break;
-        case 2: launch_t<KV, QB, 2>(a, p, s); break;
-        case 4: launch_t<KV, QB, 4>(a, p, s); break;
-        default: launch_t<KV, QB, 8>(a, p, s); break;
+void launch_vec(const AttnParams& prm, const AttnPlan& pl, dim3 grid, hipStream_t s) {
+    switch (pl.hc) {
+        case 1: hipLaunchKernelGGL((attn_vec_kernel<KV, QB, 1>), grid, dim3(kThreads), 0, s, prm); break;
+        case 2: hipLaunchKernelGGL((attn_vec_kernel<KV, QB, 2>), grid, dim3(kThreads), 0, s, prm); break;
+        case 4: hipLaunchKernelGGL((attn_vec_kernel<KV, QB, 4>), grid, dim3(kThreads), 0, s, prm); break;
+        default: hipLaunchKernelGGL((attn_vec_kernel<KV, QB, 8>), grid, dim3(kThreads), 0, s, prm); break;
     }
 }
 
 }  // namespace
 
-AttnPlan plan_sparse_attn(int B, int H, int N, int D, int sel_heads, int k) {
+AttnPlan plan_sparse_attn(int B, int H, int N, int D_, int sel_heads, int k, int q_dtype, int kv_dtype) {
+    (void)N;
+    (void)D_;
     AttnPlan p;
+    p.mfma = (q_dtype == 1 && kv_dtype == 1);
     p.hpr = H / sel_heads;
-    p.hc = p.hpr >= 8 ? 8 : (p.hpr >= 4 ? (p.hpr == 4 ? 4 : 8) : (p.hpr == 1 ? 1 : (p.hpr == 2 ? 2 : 4)));
+    if (p.mfma)
+        p.hc = 16;
+    else
+        p.hc = p.hpr >= 8 ? 8 : (p.hpr >= 4 ? (p.hpr == 4 ? 4 : 8) : (p.hpr == 1 ? 1 : (p.hpr == 2 ? 2 : 4)));
     p.hchunks = (p.hpr + p.hc - 1) / p.hc;
     const long long rows = (long long)B * sel_heads * p.hchunks;
-    const long long rows1 = rows > 0 ? rows : 1;
-    long long splits = (kTargetWorkgroups + rows1 - 1) / rows1;
-    if (splits < 1) splits = 1;
-    if (splits > k) splits = k;
-    if (rows > kMaxCounters) splits = 1;  // rows beyond the counter area: no split, no counters
+    long long splits = 1;
+    if (rows < kNoSplitRows) {
+        const long long rows1 = rows > 0 ? rows : 1;
+        splits = (kTargetWorkgroups + rows1 - 1) / rows1;
+        if (splits > k) splits = k;
+        if (splits < 1) splits = 1;
+    }
     p.spb = int((k + splits - 1) / splits);
     p.splits = (k + p.spb - 1) / p.spb;
-    const size_t part_bytes =
-        p.splits > 1 ? size_t(rows) * p.splits * p.hc * (size_t(D) + 2) * sizeof(float) : 0;
-    p.counters_off = 0;
-    p.part_off = kCounterBytes;
-    p.bytes = p.part_off + align256(part_bytes);
+    const size_t part_bytes = p.splits > 1 ? size_t(rows) * p.splits * p.hc * PSTRIDE * sizeof(float) : 0;
+    p.part_off = 0;
+    p.bytes = align256(part_bytes);
+    if (p.bytes < 256) p.bytes = 256;
     return p;
 }
 
-hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
+hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t s) {
+    AttnParams prm{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, a.k_scale,
+                   a.v_scale, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens, a.selected, a.n_selected,
+                   a.H, a.N, a.BS, a.sel_heads, a.k, pl.hpr, pl.hchunks, pl.splits, pl.spb, a.scale * kLog2e,
+                   (uint8_t*)a.out, (float*)((uint8_t*)a.workspace + pl.part_off)};
+    dim3 grid(unsigned(pl.splits * pl.hchunks), unsigned(a.sel_heads), unsigned(a.B));
     const bool qb = a.q_dtype == 1;
-    if (a.kv_dtype == 0) { if (qb) launch_hc<0, true>(a, p, s); else launch_hc<0, false>(a, p, s); }
-    else if (a.kv_dtype == 1) { if (qb) launch_hc<1, true>(a, p, s); else launch_hc<1, false>(a, p, s); }
-    else { if (qb) launch_hc<2, true>(a, p, s); else launch_hc<2, false>(a, p, s); }
+    if (pl.mfma) {
+        hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kThreads), 0, s, prm);
+    } else if (a.kv_dtype == 0) {
+        if (qb) launch_vec<0, true>(prm, pl, grid, s); else launch_vec<0, false>(prm, pl, grid, s);
+    } else if (a.kv_dtype == 1) {
+        if (qb) launch_vec<1, true>(prm, pl, grid, s); else launch_vec<1, false>(prm, pl, grid, s);
+    } else {
+        if (qb) launch_vec<2, true>(prm, pl, grid, s); else launch_vec<2, false>(prm, pl, grid, s);
+    }
+    if (pl.splits > 1)
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(pl.hchunks), unsigned(a.sel_heads), unsigned(a.B)),
+                           dim3(kThreads), 0, s, prm, pl.hc, qb);
     return hipGetLastError();
 }
 

@@ -7,13 +7,6 @@
 
 namespace qs {
 
-// Every workspace starts with a counter area that only ever holds arrival counters
-// (zero at first use; every call returns the counters it used to zero), followed by
-// free-form data (scores, partial results). Keeping the two apart lets calls of any
-// size and either operation share one workspace.
-constexpr size_t kCounterBytes = 256 * 1024;
-constexpr long long kMaxCounters = kCounterBytes / sizeof(uint32_t);
-
 // ---- metadata ----------------------------------------------------------------------
 struct MetaArgs {
     int B, N, D, BS;
@@ -33,9 +26,11 @@ hipError_t launch_build_metadata(const MetaArgs& a, hipStream_t s);
 
 // ---- Quest select ------------------------------------------------------------------
 struct SelectPlan {
-    int chunk;        // blocks scored per workgroup
-    int n_chunks;     // workgroups per (request, kv head)
-    size_t scores_off, counters_off, bytes;
+    bool row_mode;     // one workgroup per (request, KV head); else score grid + top-k kernel
+    int chunk;         // blocks per scoring workgroup (split mode)
+    int n_chunks;      // scoring workgroups per row (split mode)
+    size_t lds_bytes;  // dynamic LDS of the row-mode kernel (scores kept on chip)
+    size_t scores_off, bytes;
 };
 SelectPlan plan_block_select(int B, int N, int BS, int mmbpr);
 
@@ -83,14 +78,15 @@ hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s);
 
 // ---- sparse attention --------------------------------------------------------------
 struct AttnPlan {
+    bool mfma;        // bf16 matrix-core kernel (bf16 query and KV)
     int hpr;          // query heads per selection row
-    int hc;           // heads per workgroup (1, 2, 4 or 8)
+    int hc;           // head capacity of one workgroup (1, 2, 4, 8; 16 for the MFMA kernel)
     int hchunks;      // workgroups across a row's heads
-    int splits;       // workgroups across a row's selection slots
+    int splits;       // workgroups across a row's selection slots (1 = no combine pass)
     int spb;          // selection slots per split
-    size_t part_off, counters_off, bytes;
+    size_t part_off, bytes;
 };
-AttnPlan plan_sparse_attn(int B, int H, int N, int D, int sel_heads, int k);
+AttnPlan plan_sparse_attn(int B, int H, int N, int D, int sel_heads, int k, int q_dtype, int kv_dtype);
 
 struct AttnArgs {
     int B, H, N, D, BS;

@@ -152,7 +152,10 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
 
 size_t qs_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t sel_heads, int32_t k) {
     if (B < 0 || N < 1 || H < N || sel_heads < 1 || H % sel_heads != 0 || k < 1 || D < 1) return 0;
-    return qs::plan_sparse_attn(B, H, N, D, sel_heads, k).bytes;
+    // enough for either kernel family (matrix-core bf16 and vector-ALU)
+    const size_t a = qs::plan_sparse_attn(B, H, N, D, sel_heads, k, QS_BF16, QS_BF16).bytes;
+    const size_t b = qs::plan_sparse_attn(B, H, N, D, sel_heads, k, QS_F32, QS_F32).bytes;
+    return a > b ? a : b;
 }
 
 qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
@@ -185,7 +188,7 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
         return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
     if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
-    const qs::AttnPlan plan = qs::plan_sparse_attn(B, H, N, D, sel_heads, k);
+    const qs::AttnPlan plan = qs::plan_sparse_attn(B, H, N, D, sel_heads, k, int(q_dtype), int(kv_dtype));
     if (workspace_bytes < plan.bytes)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if ((long long)plan.splits * plan.hchunks > 0x7fffffffLL) return fail(QS_ERR_INVALID, "%s: grid too large", fn);

@@ -6,17 +6,20 @@
 // indices) and section "三个核心算子" (the _w variant forces the sink block and the local
 // window). Ties go to the lower block index ("0.8MB 跑通 Qwen 10-2" (page 1), section 1).
 //
-// Design (CDNA4): the score stream is HBM-bound (about 1 flop per metadata byte), so the
-// grid spreads it wide: workgroup (chunk, n, b) scores up to `chunk` blocks of one
-// (request, KV head). A block's max row and min row are 256 B each in bf16; 16 lanes
-// take 16 B apiece (one global_load_dwordx4), multiply by the grouped query held in
-// registers, and a 16-lane shuffle reduction yields the score. Scores go to a per-row
-// fp32 array; the workgroup that finishes a row last (device-scope arrival counter,
-// release/acquire fences) runs the exact top-k: a 4-pass, 8-bit radix select on an
-// order-preserving integer image of the scores finds the k-th best value T, then one
-// ordered pass keeps every block above T and the lowest-index blocks equal to T. That
-// reproduces "higher score first, lower index on ties" exactly, independent of the
-// order in which workgroups finish. Output is written in ascending block order.
+// Design (CDNA4): the score stream is HBM-bound (about 1 flop per metadata byte). A
+// block's max row and min row are 256 B each in bf16; 16 lanes take 16 B apiece (one
+// global_load_dwordx4), multiply by the grouped query held in registers, and a 16-lane
+// shuffle reduction yields the score; four passes of 16 rows are in flight per
+// workgroup. Two launch shapes, neither with any cross-workgroup synchronisation
+// inside a kernel (a device-scope fence costs an L2 write-back on this chip):
+//   row mode   one workgroup per (request, KV head) scores the whole row into LDS and
+//              selects from there -- used when there are enough rows to fill the GPU;
+//   split mode a scoring grid (chunk, KV head, request) writes the scores to the
+//              workspace, then a second kernel selects per row -- used for few, long rows.
+// The top-k is exact: a 4-pass, 8-bit radix select on an order-preserving integer image
+// of the scores finds the k-th best value T, then one ordered pass keeps every block
+// above T and the lowest-index blocks equal to T ("higher score first, lower index on
+// ties"). Output is written in ascending block order.
 #include <math.h>
 
 #include "qs_device.h"
@@ -25,10 +28,13 @@
 namespace qs {
 namespace {
 
-constexpr int kChunk = 64;
+constexpr int kChunk = 64;             // blocks per scoring workgroup in split mode
+constexpr int kRowModeRows = 512;      // rows at which one workgroup per row fills the chip
+constexpr int kRowModeMaxCap = 256;    // rows this short always use row mode
+constexpr int kLdsScoreCap = 8192;     // row mode keeps up to this many scores in LDS
 
 struct Forced {
-    int w_lo;   // blocks >= w_lo are forced (window), nb when none
+    int w_lo;   // blocks >= w_lo are forced (window); nb when none
     bool sink;  // block 0 forced
     int count;
     __device__ bool has(int i) const { return i >= w_lo || (sink && i == 0); }
@@ -41,7 +47,7 @@ __device__ __forceinline__ Forced forced_set(int L, int nb, int BS, int k, const
     if (!active || nb <= 0) return f;
     if (flags & 2u) {  // window: the last block and every block without metadata
         const long long u = tsmu ? tsmu[b] : 0;
-        long long num = (long long)L - u;
+        const long long num = (long long)L - u;
         long long n_meta = (num >= 0) ? num / BS : -((-num + BS - 1) / BS);
         if (n_meta < 0) n_meta = 0;
         if (n_meta > nb - 1) n_meta = nb - 1;
@@ -57,37 +63,36 @@ __device__ __forceinline__ Forced forced_set(int L, int nb, int BS, int k, const
     return f;
 }
 
+struct RowInfo {
+    int L, nb;
+    Forced F;
+};
+
+__device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* tsmu, uint32_t flags, int k, int b,
+                                            int BS, int cap) {
+    RowInfo r;
+    r.L = max(sl[b], 0);
+    r.nb = min((r.L + BS - 1) / BS, cap);
+    r.F = forced_set(r.L, r.nb, BS, k, tsmu, b, flags);
+    return r;
+}
+
+// Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
+// skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void select_kernel(
-    const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb, const uint8_t* __restrict__ minb,
-    int num_meta, const int32_t* __restrict__ mt, int mmbpr, const int32_t* __restrict__ sl,
-    const int32_t* __restrict__ tsmu, uint32_t flags, int k, int H, int N, int BS, int chunk,
-    int32_t* __restrict__ selected, int32_t* __restrict__ n_selected, float* __restrict__ dbg_scores,
-    float* __restrict__ ws_scores, uint32_t* __restrict__ counters) {
+__device__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
+                            const uint8_t* __restrict__ minb, int num_meta, const int32_t* __restrict__ mt, int mmbpr,
+                            int H, int N, int BS, int b, int n, const Forced& F, int i0, int i_end, float* dst,
+                            bool nan_forced) {
     constexpr int esize = BF16 ? 2 : 4;
     constexpr int D = 128;
     constexpr int LPR = D * esize / 16;  // lanes per metadata row
     constexpr int EPL = 16 / esize;      // channels per lane
     constexpr int RPP = kThreads / LPR;  // rows per pass
     constexpr int U = 4;                 // passes in flight
-
-    __shared__ uint32_t hist[256];
-    __shared__ int sh[4];
-    __shared__ int wsum[kWaves];
-    __shared__ int is_last;
-
-    const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
-    const int cap = mmbpr * BS;
-    const int L = max(sl[b], 0);
-    const int nb = min((L + BS - 1) / BS, cap);
-    const int n_chunks_b = max(1, (nb + chunk - 1) / chunk);
-    if (c >= n_chunks_b) return;
-    const Forced F = forced_set(L, nb, BS, k, tsmu, b, flags);
     const int tid = threadIdx.x;
-    const int lr = tid % LPR;    // lane within the row
-    const int slot = tid / LPR;  // row slot within a pass
+    const int lr = tid % LPR, slot = tid / LPR;
     const int G = H / N;
-    float* scores = (dbg_scores ? dbg_scores : ws_scores) + (size_t(b) * N + n) * cap;
 
     // grouped query for this lane's channels: mean over the group's G heads
     float gq[EPL];
@@ -107,9 +112,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) gq[e] = gq[e] / float(G);
 
-    // ---- scores of this chunk ----
-    const int i0 = c * chunk;
-    const int i_end = min(nb, i0 + chunk);
     const size_t row_bytes = size_t(N) * D * esize;
     for (int base = i0; base < i_end; base += RPP * U) {
         u32x4 vmx[U], vmn[U];
@@ -150,30 +152,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
             const int i = base + u * RPP + slot;
             if (lr == 0 && i < i_end) {
                 if (ok[u])
-                    scores[i] = s;
+                    dst[i] = s;
                 else if (!F.has(i))
-                    scores[i] = -INFINITY;  // metadata table entry out of range
-                else if (dbg_scores)
-                    scores[i] = __builtin_nanf("");
+                    dst[i] = -INFINITY;
+                else if (nan_forced)
+                    dst[i] = __builtin_nanf("");
             }
         }
     }
+}
 
-    // ---- the workgroup that completes the row selects ----
-    if (n_chunks_b > 1) {
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t prev = atomicAdd(&counters[size_t(b) * N + n], 1u);
-            is_last = (prev == uint32_t(n_chunks_b - 1));
-        }
-        __syncthreads();
-        if (!is_last) return;
-        __threadfence();
-    } else {
-        __syncthreads();
-    }
-
+// Exact top-k of a row from its scores (LDS or global); writes selected / n_selected.
+__device__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out, int32_t* n_out,
+                          uint32_t* hist, int* sh, int* wsum) {
+    const int tid = threadIdx.x;
     const int R = max(0, min(k, nb) - F.count);  // fill picks
     const int nc = nb - F.count;                   // fill candidates
     const bool take_all = R >= nc;
@@ -187,7 +179,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         };
         T = block_radix_select(nb, R, kf, hist, sh, need_eq);
     }
-    int32_t* out = selected + (size_t(b) * N + n) * k;
     int pos0 = 0, eq_seen = 0;
     for (int ib = 0; ib < nb; ib += kThreads) {
         const int i = ib + tid;
@@ -206,10 +197,73 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         eq_seen += eq_tot;
     }
     for (int j = pos0 + tid; j < k; j += kThreads) out[j] = -1;
-    if (tid == 0) {
-        n_selected[size_t(b) * N + n] = min(pos0, k);
-        if (n_chunks_b > 1) counters[size_t(b) * N + n] = 0u;
+    if (tid == 0) *n_out = min(pos0, k);
+}
+
+struct SelParams {
+    const uint8_t* query;
+    const uint8_t* maxb;
+    const uint8_t* minb;
+    int num_meta;
+    const int32_t* mt;
+    int mmbpr;
+    const int32_t* sl;
+    const int32_t* tsmu;
+    uint32_t flags;
+    int k, H, N, BS;
+    int32_t* selected;
+    int32_t* n_selected;
+    float* dbg_scores;
+    float* ws_scores;
+};
+
+// row mode: one workgroup per (KV head, request)
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
+    extern __shared__ float lds_scores[];
+    __shared__ uint32_t hist[256];
+    __shared__ int sh[4];
+    __shared__ int wsum[kWaves];
+    const int n = blockIdx.x, b = blockIdx.y;
+    const int cap = p.mmbpr * p.BS;
+    const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
+    float* gscores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
+    float* scores = (cap <= kLdsScoreCap) ? lds_scores : gscores;
+    score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb, scores,
+                      false);
+    __syncthreads();
+    if (p.dbg_scores) {
+        for (int i = threadIdx.x; i < r.nb; i += kThreads)
+            gscores[i] = r.F.has(i) ? __builtin_nanf("") : scores[i];
     }
+    topk_emit(scores, r.nb, r.F, p.k, p.selected + (size_t(b) * p.N + n) * p.k, p.n_selected + size_t(b) * p.N + n,
+              hist, sh, wsum);
+}
+
+// split mode, step 1: scoring grid (chunk, KV head, request)
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int chunk) {
+    const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+    const int cap = p.mmbpr * p.BS;
+    const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
+    const int i0 = c * chunk;
+    if (i0 >= r.nb) return;
+    float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
+    score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
+                      min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr);
+}
+
+// split mode, step 2: top-k per (KV head, request)
+__global__ __launch_bounds__(kThreads) void select_topk_kernel(SelParams p) {
+    __shared__ uint32_t hist[256];
+    __shared__ int sh[4];
+    __shared__ int wsum[kWaves];
+    const int n = blockIdx.x, b = blockIdx.y;
+    const int cap = p.mmbpr * p.BS;
+    const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
+    const float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
+    topk_emit(scores, r.nb, r.F, p.k, p.selected + (size_t(b) * p.N + n) * p.k, p.n_selected + size_t(b) * p.N + n,
+              hist, sh, wsum);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -219,29 +273,35 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 SelectPlan plan_block_select(int B, int N, int BS, int mmbpr) {
     SelectPlan p;
     const size_t cap = size_t(mmbpr) * BS;
-    // rows beyond the counter area are scored by one workgroup each (no counters)
-    p.chunk = ((long long)B * N <= kMaxCounters) ? kChunk : int(cap);
-    p.n_chunks = int((cap + p.chunk - 1) / p.chunk);
-    p.counters_off = 0;
-    p.scores_off = kCounterBytes;
-    p.bytes = p.scores_off + align256(size_t(B) * N * cap * sizeof(float));
+    const long long rows = (long long)B * N;
+    p.row_mode = rows >= kRowModeRows || cap <= size_t(kRowModeMaxCap);
+    p.chunk = kChunk;
+    p.n_chunks = int((cap + kChunk - 1) / kChunk);
+    p.lds_bytes = (p.row_mode && cap <= size_t(kLdsScoreCap)) ? cap * sizeof(float) : 0;
+    p.scores_off = 0;
+    p.bytes = align256(size_t(B) * N * cap * sizeof(float));
+    if (p.bytes < 256) p.bytes = 256;
     return p;
 }
 
-hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& p, hipStream_t s) {
-    dim3 grid(unsigned(p.n_chunks), unsigned(a.N), unsigned(a.B));
-    float* ws_scores = (float*)((uint8_t*)a.workspace + p.scores_off);
-    uint32_t* counters = (uint32_t*)((uint8_t*)a.workspace + p.counters_off);
-    if (a.bf16)
-        hipLaunchKernelGGL(select_kernel<true>, grid, dim3(kThreads), 0, s, (const uint8_t*)a.query,
-                           (const uint8_t*)a.maxb, (const uint8_t*)a.minb, a.num_meta, a.meta_tables, a.mmbpr,
-                           a.seq_lens, a.tsmu, a.flags, a.k, a.H, a.N, a.BS, p.chunk, a.selected, a.n_selected,
-                           a.block_scores, ws_scores, counters);
-    else
-        hipLaunchKernelGGL(select_kernel<false>, grid, dim3(kThreads), 0, s, (const uint8_t*)a.query,
-                           (const uint8_t*)a.maxb, (const uint8_t*)a.minb, a.num_meta, a.meta_tables, a.mmbpr,
-                           a.seq_lens, a.tsmu, a.flags, a.k, a.H, a.N, a.BS, p.chunk, a.selected, a.n_selected,
-                           a.block_scores, ws_scores, counters);
+hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& pl, hipStream_t s) {
+    SelParams p{(const uint8_t*)a.query, (const uint8_t*)a.maxb, (const uint8_t*)a.minb, a.num_meta, a.meta_tables,
+                a.mmbpr, a.seq_lens, a.tsmu, a.flags, a.k, a.H, a.N, a.BS, a.selected, a.n_selected,
+                a.block_scores, (float*)((uint8_t*)a.workspace + pl.scores_off)};
+    if (pl.row_mode) {
+        dim3 grid(unsigned(a.N), unsigned(a.B));
+        if (a.bf16)
+            hipLaunchKernelGGL(select_row_kernel<true>, grid, dim3(kThreads), pl.lds_bytes, s, p);
+        else
+            hipLaunchKernelGGL(select_row_kernel<false>, grid, dim3(kThreads), pl.lds_bytes, s, p);
+    } else {
+        dim3 g1(unsigned(pl.n_chunks), unsigned(a.N), unsigned(a.B));
+        if (a.bf16)
+            hipLaunchKernelGGL(select_score_kernel<true>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+        else
+            hipLaunchKernelGGL(select_score_kernel<false>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+        hipLaunchKernelGGL(select_topk_kernel, dim3(unsigned(a.N), unsigned(a.B)), dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -126,7 +126,7 @@ def workspace(nbytes, device, op):
     key = (torch.device(device).index or 0, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
