@@ -81,6 +81,20 @@ def step_bytes(wl, sel_h, ns_h, tsmu_h):
     return sel_b, att_b
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it was taken
+    on the current kernel source (else None: the counters are stale)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_attn_mfma_config5.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    h = hashlib.sha256()
+    for f in t["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return t["traffic_bytes"] if h.hexdigest() == t["source_sha256"] else None
+
+
 def gather_requests(wl, reqs):
     """CPU copies of the sampled requests' blocks with remapped tables (marshalling)."""
     BS = wl.BS
@@ -134,6 +148,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=1024,
+                    help="size of the plain device copy timed beside the step (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no cross-GPU step in this build (see the sharding "
@@ -190,6 +206,23 @@ def main():
     meta_bytes = sum(L * N * D * es for L in mlens) + \
         sum(cdiv(cdiv(L, BS), BS) * BS * N * D * es * 2 for L in mlens)   # K read + max/min rows written
 
+    copy_gbps = None
+    if args.copy_calibration_mib > 0:
+        # a plain device-to-device copy of known size: the bandwidth a simple streaming
+        # kernel reaches on this machine, and the reference the HBM byte counters are scaled by
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
         select(s)
@@ -204,15 +237,19 @@ def main():
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for s in range(K):
+        evs[s][0].record(stream)
         select(s)
         ev[s][0].record(stream)
         attend(s)
         ev[s][1].record(stream)
+        evs[s][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    select_ms = np.array([a.elapsed_time(b) for a, b in zip([e[0] for e in evs], [e[0] for e in ev])])
 
     # replay the selections of the timed steps to count their algorithmic bytes
     log("counting algorithmic bytes of the timed steps")
@@ -252,12 +289,16 @@ def main():
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "select_bytes": int(sel_bytes),
         "attention_bytes": int(att_bytes),
+        "select_avg_us": round(float(select_ms.mean()) * 1000, 3),
+        "select_gbps": round(sel_bytes / (float(select_ms.mean()) * 1e-3) / 1e9, 1),
+        "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
         "metadata_rebuild_ms": round(rebuild_ms, 4),
         "metadata_rebuild_gbps": round(meta_bytes / (rebuild_ms * 1e-3) / 1e9, 1),
         "steps_per_s_with_rebuild_every_128": round(128.0 / (128 * ms_per_step + rebuild_ms) * 1000.0, 3),
-        "roofline": {"kernel": "attn_kernel (qs_sparse_attn_decode)", "bound": "hbm",
+        "roofline": {"kernel": "attn_mfma_kernel (qs_sparse_attn_decode)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic() if args.workload == "config5" else None,
                      "avg_launch_us": round(attn_avg_ms * 1000, 3), "bytes_per_launch": int(att_bytes)},
     }
     if not args.no_cpu_baseline:

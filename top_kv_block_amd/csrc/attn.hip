@@ -103,7 +103,10 @@ __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, t);
 }
 
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p) {
+// 128 VGPRs: four workgroups (16 waves) per CU, which the 1024-row serving batch fills
+// in one round; LDS is 40 KiB per workgroup, 160 KiB per CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void attn_mfma_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kVtBytes];  // 40 KiB
 
     const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
