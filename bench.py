@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-steps", type=int, default=128,
+                    help="steps captured in one HIP graph for the replay figure (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="size of the plain device copy timed beside the step (0 = skip)")
     args = ap.parse_args()
@@ -229,27 +231,61 @@ def main():
         attend(s)
     torch.cuda.synchronize()
 
-    # bytes of every step in the timed window (selection-dependent), computed afterwards
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    sels = []
+    # (1) the step rate: K steps back to back, events only around the whole region
     log(f"timing {K} steps")
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for s in range(K):
-        evs[s][0].record(stream)
         select(s)
-        ev[s][0].record(stream)
         attend(s)
-        ev[s][1].record(stream)
-        evs[s][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+
+    # (2) per-kernel durations: the same K steps with HIP events around every launch, on
+    # the stream the kernels run on (the events themselves add a little time between
+    # launches, so the step rate above is taken without them)
+    log(f"timing {K} steps with per-launch events")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        evs[s][0].record(stream)
+        select(s)
+        evs[s][1].record(stream)
+        ev[s][0].record(stream)
+        attend(s)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    select_ms = np.array([a.elapsed_time(b) for a, b in zip([e[0] for e in evs], [e[0] for e in ev])])
+    select_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # (3) the same steps replayed from one captured HIP graph (no host launch overhead)
+    graph_ms = None
+    if args.graph_steps > 0:
+        log(f"capturing {args.graph_steps} steps in a HIP graph")
+        gs = args.graph_steps
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for s in range(gs):
+                    select(s)
+                    attend(s)
+        stream.wait_stream(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, K // gs)
+        g0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * gs)
 
     # replay the selections of the timed steps to count their algorithmic bytes
     log("counting algorithmic bytes of the timed steps")
@@ -289,6 +325,7 @@ def main():
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "select_bytes": int(sel_bytes),
         "attention_bytes": int(att_bytes),
+        "graph_replay_steps_per_s": None if graph_ms is None else round(1000.0 / graph_ms, 3),
         "select_avg_us": round(float(select_ms.mean()) * 1000, 3),
         "select_gbps": round(sel_bytes / (float(select_ms.mean()) * 1e-3) / 1e9, 1),
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),

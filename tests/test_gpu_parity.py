@@ -574,3 +574,50 @@ def test_workspace_shared_across_shapes_and_operations(qs, oracle):
             ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, rsel,
                                             rns, sh)
             assert np.abs(out.float().cpu().numpy() - ref).max() <= 2e-2
+
+
+def test_graph_replay_matches_eager(qs):
+    """The select + attention step captured in a HIP graph and replayed several times,
+    with eager work in between, gives bitwise the eager results every time (the path
+    records no memset nodes; the kernels are deterministic)."""
+    say("graph replay")
+    wl = W.random_case(61, 8, 64, 8, 128, [128 * 100 + 5] * 4 + [128 * 40] * 4, k=16, dtype=torch.bfloat16,
+                       flags=W.FORCE_SINK | W.FORCE_WINDOW, tsmu=[3] * 8)
+    wl = wl.to(DEV)
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=DEV)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)
+    out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.bfloat16, device=DEV)
+    ws1 = torch.empty(qs.block_select_workspace_bytes(wl.B, wl.N, wl.BS, wl.mmbpr), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(qs.sparse_attn_workspace_bytes(wl.B, wl.H, wl.N, wl.D, wl.N, wl.k), dtype=torch.uint8,
+                      device=DEV)
+
+    def step():
+        qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, tokens_since_update=wl.tsmu,
+                           flags=wl.flags, selected=sel, n_selected=ns, workspace_buf=ws1)
+        qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns,
+                                 out=out, workspace_buf=ws2)
+
+    step()
+    torch.cuda.synchronize()
+    want = (sel.clone(), ns.clone(), out.clone())
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    for rep in range(3):
+        sel.fill_(-7)
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, want[0]) and torch.equal(ns, want[1]), rep
+        assert torch.equal(out.view(torch.int16), want[2].view(torch.int16)), rep
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))

@@ -133,26 +133,36 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(
     const int items = nb * smax;
     const size_t row_bytes = size_t(N) * D * ke;
     for (int base = 0; base < items; base += GRP * U) {
-        u32x4 v[U];
-        int blk[U];
+        // table lookups of all items first, then the key loads back to back
+        int blk[U], row[U], phys[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int it = base + u * GRP + grp;
             blk[u] = -1;
-            v[u] = u32x4{0u, 0u, 0u, 0u};
+            row[u] = 0;
+            phys[u] = 0;
             if (it < items) {
                 const int i = it / smax, j = it % smax;
                 const int p0 = i * BS, len = min(BS, L - p0);
                 const int step = max(1, len / np);
                 const int ps = p0 + j * step;
                 if (ps < p0 + len) {
-                    const int phys = bt[size_t(b) * mkbpr + i];
-                    if (phys >= 0 && phys < num_kv_blocks) {
-                        v[u] = ld16(kc + (size_t(phys) * BS + (ps - p0)) * row_bytes + size_t(kh) * D * ke + lr * 16);
-                        blk[u] = i;
-                    }
+                    blk[u] = i;
+                    row[u] = ps - p0;
+                    phys[u] = bt[size_t(b) * mkbpr + i];
                 }
             }
+        }
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (phys[u] < 0 || phys[u] >= num_kv_blocks) {
+                blk[u] = -1;
+                phys[u] = 0;
+            }
+            // items without a sample read row 0 of block 0 (always valid) and are masked
+            const size_t off = blk[u] >= 0 ? (size_t(phys[u]) * BS + row[u]) * row_bytes + size_t(kh) * D * ke : 0;
+            v[u] = ld16(kc + off + lr * 16);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

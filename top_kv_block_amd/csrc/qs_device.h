@@ -41,24 +41,53 @@ __device__ __forceinline__ float key2f(uint32_t k) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-// sum over aligned groups of `width` lanes (width a power of two <= 64); every lane
-// of the group ends with the group's sum
+// DPP lane moves inside a row of 16 lanes (all patterns stay within the row)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// Sum over aligned groups of `width` lanes (a power of two <= 64); every lane of the
+// group ends with the same, bitwise identical sum. Groups of up to 16 lanes reduce with
+// DPP row operations (quad swaps, then half-row and row mirrors: after each step all
+// lanes of the merged span hold equal values, so a mirror pairs whole spans); wider
+// groups finish with cross-row shuffles.
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
+    if constexpr (width >= 2) v += dpp_f<kDppXor1>(v);
+    if constexpr (width >= 4) v += dpp_f<kDppXor2>(v);
+    if constexpr (width >= 8) v += dpp_f<kDppHalfMirror>(v);
+    if constexpr (width >= 16) v += dpp_f<kDppMirror>(v);
 #pragma unroll
-    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    for (int o = 16; o < width; o <<= 1) v += __shfl_xor(v, o, kWave);
     return v;
 }
 template <int width>
 __device__ __forceinline__ int group_sum_i(int v) {
+    if constexpr (width >= 2) v += dpp_i<kDppXor1>(v);
+    if constexpr (width >= 4) v += dpp_i<kDppXor2>(v);
+    if constexpr (width >= 8) v += dpp_i<kDppHalfMirror>(v);
+    if constexpr (width >= 16) v += dpp_i<kDppMirror>(v);
 #pragma unroll
-    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    for (int o = 16; o < width; o <<= 1) v += __shfl_xor(v, o, kWave);
     return v;
 }
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
+    if constexpr (width >= 2) v = fmaxf(v, dpp_f<kDppXor1>(v));
+    if constexpr (width >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
+    if constexpr (width >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    if constexpr (width >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
 #pragma unroll
-    for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    for (int o = 16; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     return v;
 }
 

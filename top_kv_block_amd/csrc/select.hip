@@ -80,7 +80,7 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 // Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
 // skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
 template <bool BF16>
-__device__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
+__device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
                             const uint8_t* __restrict__ minb, int num_meta, const int32_t* __restrict__ mt, int mmbpr,
                             int H, int N, int BS, int b, int n, const Forced& F, int i0, int i_end, float* dst,
                             bool nan_forced) {
@@ -114,23 +114,26 @@ __device__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __
 
     const size_t row_bytes = size_t(N) * D * esize;
     for (int base = i0; base < i_end; base += RPP * U) {
-        u32x4 vmx[U], vmn[U];
+        // table lookups for all passes first, so that the metadata loads below are issued
+        // back to back (a lookup between them would wait for every load in flight)
+        int mrow[U];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = base + u * RPP + slot;
-            ok[u] = false;
-            vmx[u] = u32x4{0u, 0u, 0u, 0u};
-            vmn[u] = vmx[u];
-            if (i < i_end && !F.has(i)) {
-                const int m = mt[size_t(b) * mmbpr + i / BS];
-                if (m >= 0 && m < num_meta) {
-                    const size_t off = (size_t(m) * BS + (i % BS)) * row_bytes + size_t(n) * D * esize + lr * 16;
-                    vmx[u] = ld16(maxb + off);
-                    vmn[u] = ld16(minb + off);
-                    ok[u] = true;
-                }
-            }
+            ok[u] = i < i_end && !F.has(i);
+            mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
+        }
+        u32x4 vmx[U], vmn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * RPP + slot;
+            ok[u] = ok[u] && mrow[u] >= 0 && mrow[u] < num_meta;
+            // rows that are not scored read the first row (always valid) and are masked
+            const size_t off = ok[u] ? (size_t(mrow[u]) * BS + (i % BS)) * row_bytes + size_t(n) * D * esize + lr * 16
+                                     : size_t(lr) * 16;
+            vmx[u] = ld16(maxb + off);
+            vmn[u] = ld16(minb + off);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -163,7 +166,7 @@ __device__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __
 }
 
 // Exact top-k of a row from its scores (LDS or global); writes selected / n_selected.
-__device__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out, int32_t* n_out,
+__device__ __forceinline__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out, int32_t* n_out,
                           uint32_t* hist, int* sh, int* wsum) {
     const int tid = threadIdx.x;
     const int R = max(0, min(k, nb) - F.count);  // fill picks
@@ -228,16 +231,22 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
     float* gscores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
-    float* scores = (cap <= kLdsScoreCap) ? lds_scores : gscores;
-    score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb, scores,
-                      false);
-    __syncthreads();
-    if (p.dbg_scores) {
-        for (int i = threadIdx.x; i < r.nb; i += kThreads)
-            gscores[i] = r.F.has(i) ? __builtin_nanf("") : scores[i];
+    int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
+    int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
+    if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
+        score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
+                          lds_scores, false);
+        __syncthreads();
+        if (p.dbg_scores)
+            for (int i = threadIdx.x; i < r.nb; i += kThreads)
+                gscores[i] = r.F.has(i) ? __builtin_nanf("") : lds_scores[i];
+        topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
+    } else {
+        score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
+                          gscores, p.dbg_scores != nullptr);
+        __syncthreads();
+        topk_emit(gscores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     }
-    topk_emit(scores, r.nb, r.F, p.k, p.selected + (size_t(b) * p.N + n) * p.k, p.n_selected + size_t(b) * p.N + n,
-              hist, sh, wsum);
 }
 
 // split mode, step 1: scoring grid (chunk, KV head, request)
