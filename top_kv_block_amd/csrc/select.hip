@@ -79,52 +79,36 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 
 // Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
 // skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
+// qstage: kThreads 16-byte LDS slots used to stage the group's query rows. Contains a
+// barrier: every thread of the workgroup must call it.
 template <bool BF16>
 __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
-                            const uint8_t* __restrict__ minb, int num_meta, const int32_t* __restrict__ mt, int mmbpr,
-                            int H, int N, int BS, int b, int n, const Forced& F, int i0, int i_end, float* dst,
-                            bool nan_forced) {
+                                            const uint8_t* __restrict__ minb, int num_meta,
+                                            const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
+                                            int n, const Forced& F, int i0, int i_end, float* dst, bool nan_forced,
+                                            u32x4* qstage) {
     constexpr int esize = BF16 ? 2 : 4;
     constexpr int D = 128;
     constexpr int LPR = D * esize / 16;  // lanes per metadata row
     constexpr int EPL = 16 / esize;      // channels per lane
     constexpr int RPP = kThreads / LPR;  // rows per pass
-    constexpr int U = 4;                 // passes in flight
+    constexpr int U = 4;                 // passes per batch
     const int tid = threadIdx.x;
     const int lr = tid % LPR, slot = tid / LPR;
     const int G = H / N;
-
-    // grouped query for this lane's channels: mean over the group's G heads
-    float gq[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) gq[e] = 0.f;
-    for (int g = 0; g < G; ++g) {
-        const u32x4 v = ld16(query + ((size_t(b) * H + size_t(n) * G + g) * D + lr * EPL) * esize);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (BF16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { gq[2 * j] += bf_lo(w[j]); gq[2 * j + 1] += bf_hi(w[j]); }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gq[j] += __uint_as_float(w[j]);
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) gq[e] = gq[e] / float(G);
-
     const size_t row_bytes = size_t(N) * D * esize;
-    for (int base = i0; base < i_end; base += RPP * U) {
-        // table lookups for all passes first, so that the metadata loads below are issued
-        // back to back (a lookup between them would wait for every load in flight)
+
+    // One batch = U passes of RPP rows. The table lookups of a batch come first, then its
+    // metadata loads back to back (a lookup between them would wait for every load in
+    // flight); the next batch's loads are issued before the current batch is consumed.
+    auto issue = [&](int base, u32x4 (&vmx)[U], u32x4 (&vmn)[U], bool (&ok)[U]) {
         int mrow[U];
-        bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = base + u * RPP + slot;
             ok[u] = i < i_end && !F.has(i);
             mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
         }
-        u32x4 vmx[U], vmn[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = base + u * RPP + slot;
@@ -135,6 +119,48 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
             vmx[u] = ld16(maxb + off);
             vmn[u] = ld16(minb + off);
         }
+    };
+
+    // the group's query rows: one 16-byte piece per thread, loaded ahead of batch 0
+    const int npieces = G * LPR;
+    const bool staged = npieces <= kThreads;
+    u32x4 qpiece{0u, 0u, 0u, 0u};
+    if (staged && tid < npieces)
+        qpiece = ld16(query + ((size_t(b) * H + size_t(n) * G + tid / LPR) * D + (tid % LPR) * EPL) * esize);
+    u32x4 vmx[U], vmn[U];
+    bool ok[U];
+    if (i0 < i_end) issue(i0, vmx, vmn, ok);
+
+    // grouped query for this lane's channels: mean over the group's G heads
+    float gq[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) gq[e] = 0.f;
+    auto add_piece = [&](const u32x4& v) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { gq[2 * j] += bf_lo(w[j]); gq[2 * j + 1] += bf_hi(w[j]); }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gq[j] += __uint_as_float(w[j]);
+        }
+    };
+    if (staged) {
+        if (tid < npieces) qstage[tid] = qpiece;
+        __syncthreads();
+        for (int g = 0; g < G; ++g) add_piece(qstage[g * LPR + lr]);
+    } else {
+        for (int g = 0; g < G; ++g)
+            add_piece(ld16(query + ((size_t(b) * H + size_t(n) * G + g) * D + lr * EPL) * esize));
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) gq[e] = gq[e] / float(G);
+
+    for (int base = i0; base < i_end; base += RPP * U) {
+        u32x4 nmx[U], nmn[U];
+        bool nok[U];
+        const bool more = base + RPP * U < i_end;
+        if (more) issue(base + RPP * U, nmx, nmn, nok);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t a[4] = {vmx[u].x, vmx[u].y, vmx[u].z, vmx[u].w};
@@ -161,6 +187,10 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
                 else if (nan_forced)
                     dst[i] = __builtin_nanf("");
             }
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) { vmx[u] = nmx[u]; vmn[u] = nmn[u]; ok[u] = nok[u]; }
         }
     }
 }
@@ -223,10 +253,11 @@ struct SelParams {
 // row mode: one workgroup per (KV head, request)
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
-    extern __shared__ float lds_scores[];
+    extern __shared__ __attribute__((aligned(16))) float lds_scores[];
     __shared__ uint32_t hist[256];
     __shared__ int sh[4];
     __shared__ int wsum[kWaves];
+    __shared__ u32x4 qstage[kThreads];
     const int n = blockIdx.x, b = blockIdx.y;
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
@@ -235,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
     if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
         score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
-                          lds_scores, false);
+                          lds_scores, false, qstage);
         __syncthreads();
         if (p.dbg_scores)
             for (int i = threadIdx.x; i < r.nb; i += kThreads)
@@ -243,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
         topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     } else {
         score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
-                          gscores, p.dbg_scores != nullptr);
+                          gscores, p.dbg_scores != nullptr, qstage);
         __syncthreads();
         topk_emit(gscores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     }
@@ -252,6 +283,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
 // split mode, step 1: scoring grid (chunk, KV head, request)
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int chunk) {
+    __shared__ u32x4 qstage[kThreads];
     const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int
     if (i0 >= r.nb) return;
     float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
     score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
-                      min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr);
+                      min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage);
 }
 
 // split mode, step 2: top-k per (KV head, request)
