@@ -139,6 +139,119 @@ def run_cpu_baseline(wl, qsets, tsmu_tab, n_req, min_seconds):
                       f"scaled by {wl.B}/{len(reqs)}; single-threaded C oracle (fp64)"}
 
 
+def _timed(fn, reps, stream):
+    """Average ms of fn() over reps back-to-back calls on the stream (after one warm call)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def other_workloads(qs, W, dev, stream, reps=50):
+    """The other configurations of the path, each timed on its own (ms per call and
+    algorithmic GB/s); they are parity-test cases too, these are measurements only."""
+    res = {}
+
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    def meta_buf(wl):
+        mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=wl.k_cache.dtype, device=dev)
+        return mx, torch.zeros_like(mx)
+
+    # config 1: tiny fp32 Quest select + attention
+    wl = W.config1().to(dev)
+    mx, mn = meta_buf(wl)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx, mn)
+    sel, ns = qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k)
+    t_sel = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, selected=sel,
+                                              n_selected=ns), reps, stream)
+    t_att = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                                    sel, ns), reps, stream)
+    res["config1_tiny_fp32"] = {"select_us": round(t_sel * 1e3, 2), "attention_us": round(t_att * 1e3, 2),
+                                "step_us": round((t_sel + t_att) * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
+    del wl, mx, mn
+
+    # config 2: page-3-shaped Quest select, bf16; metadata build timed too
+    wl = W.config2(device=dev)
+    mx, mn = meta_buf(wl)
+    t_build = _timed(lambda: qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx, mn),
+                     10, stream)
+    tz = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=dev)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+    t0 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, selected=sel,
+                                           n_selected=ns), reps, stream)
+    t1 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k,
+                                           tokens_since_update=tz, flags=3, selected=sel, n_selected=ns),
+                reps, stream)
+    es = 2
+    sel_bytes = wl.B * wl.N * 128 * 2 * wl.D * es + wl.B * wl.H * wl.D * es
+    build_bytes = wl.k_cache.numel() * es + wl.num_meta_blocks * wl.BS * wl.N * wl.D * es * 2
+    res["config2_p3_select_bf16"] = {"select_us": round(t0 * 1e3, 2), "select_gbps": gbps(sel_bytes, t0),
+                                     "select_window_us": round(t1 * 1e3, 2),
+                                     "metadata_build_us": round(t_build * 1e3, 2),
+                                     "metadata_build_gbps": gbps(build_bytes, t_build)}
+    del wl, mx, mn
+
+    # config 3: page-1 probe selection + fp32 / int8 attention at k = 32
+    wl = W.config3().to(dev)
+    psel, pns = qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
+                                   importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY)
+    t_probe = _timed(lambda: qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
+                                                importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY,
+                                                selected=psel, n_selected=pns), reps, stream)
+    t_f32 = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                                    psel, pns, sel_heads=wl.H), reps, stream)
+    t_i8 = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, psel,
+                                                   pns, sel_heads=wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale),
+                  reps, stream)
+    probe_bytes = wl.N * 128 * 8 * wl.D * 4 + 4096 * 4 + wl.H * wl.D * 4
+    res["config3_p1_probe_k32"] = {"probe_select_us": round(t_probe * 1e3, 2),
+                                   "probe_select_gbps": gbps(probe_bytes, t_probe),
+                                   "attention_fp32_us": round(t_f32 * 1e3, 2),
+                                   "attention_int8_us": round(t_i8 * 1e3, 2),
+                                   "step_fp32_us": round((t_probe + t_f32) * 1e3, 2),
+                                   "step_int8_us": round((t_probe + t_i8) * 1e3, 2),
+                                   "note": "latency-bound (a few MB a step)"}
+    del wl
+
+    # config 4: long-context paged decode, bf16 (rows split over workgroups + combine)
+    wl = W.config4(device=dev)
+    mx, mn = meta_buf(wl)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=dev)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.bfloat16, device=dev)
+
+    def c4_select():
+        qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, tokens_since_update=wl.tsmu,
+                           flags=wl.flags, selected=sel, n_selected=ns)
+
+    def c4_attend():
+        qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns, out=out)
+
+    t_s = _timed(c4_select, reps, stream)
+    t_a = _timed(c4_attend, reps, stream)
+    t_step = _timed(lambda: (c4_select(), c4_attend()), reps, stream)
+    sb, ab = step_bytes(wl, sel.cpu(), ns.cpu(), wl.tsmu.cpu())
+    res["config4_long_context_bf16"] = {
+        "step_us": round(t_step * 1e3, 2), "steps_per_s": round(1000.0 / t_step, 1),
+        "step_bytes": int(sb + ab), "step_gbps": gbps(sb + ab, t_step),
+        "select_us": round(t_s * 1e3, 2), "select_gbps": gbps(sb, t_s),
+        "attention_us": round(t_a * 1e3, 2), "attention_gbps": gbps(ab, t_a),
+        "needle_recall": sum(int((t // wl.BS) in set(sel[b, n, :ns[b, n]].cpu().tolist()))
+                             for b, t in wl.needles for n in range(wl.N)) / (wl.B * wl.N)}
+    del wl, mx, mn
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +261,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the other configurations (tiny, page-3 select, probe, long context)")
     ap.add_argument("--graph-steps", type=int, default=128,
                     help="steps captured in one HIP graph for the replay figure (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
@@ -340,6 +455,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_cpu_baseline(wl, qsets, tsmu_tab, args.cpu_sample, args.cpu_seconds)
+    if not args.no_other_workloads:
+        del wl, qsets, mx, mn
+        torch.cuda.empty_cache()
+        log("timing the other workloads")
+        result["other_workloads"] = other_workloads(qs, W, dev, stream)
     print(json.dumps(result), flush=True)
 
 

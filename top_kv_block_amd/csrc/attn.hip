@@ -38,7 +38,10 @@
 namespace qs {
 namespace {
 
-constexpr int kTargetWorkgroups = 2048;
+// Split rows until the grid fills the chip for one round: the matrix-core kernel keeps
+// 4 workgroups per CU (1024 on 256 CUs), the vector kernels up to 8.
+constexpr int kTargetWorkgroupsMfma = 1024;
+constexpr int kTargetWorkgroupsVec = 2048;
 constexpr int kNoSplitRows = 1024;   // rows at which each row gets one workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int D = 128;
@@ -466,25 +469,41 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-// combine pass for split rows: merges the splits' partials in split order
+// combine pass for split rows: merges the splits' partials in split order. One thread
+// per output element (request, head, channel); each split's (max, sum, acc) loads are
+// issued ahead of the merge so they are in flight together.
 // ------------------------------------------------------------------------------------
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, int hc_cap, bool out_bf16) {
-    const int hcix = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const int e = blockIdx.x * kThreads + threadIdx.x;  // (head, channel) of request b
+    const int b = blockIdx.y;
+    if (e >= p.H * D) return;
+    const int d = e % D, h = e / D;
+    const int s = h / p.hpr, hh = h % p.hpr;
+    const int hcix = hh / hc_cap, g = hh % hc_cap;
     const int row = b * p.sel_heads + s;
-    const int h0 = s * p.hpr + hcix * hc_cap;
-    const int nh = min(hc_cap, p.hpr - hcix * hc_cap);
-    for (int idx = threadIdx.x; idx < nh * D; idx += kThreads) {
-        const int g = idx / D, d = idx % D;
-        float M = -INFINITY, Ls = 0.f, A = 0.f;
-        for (int sp = 0; sp < p.splits; ++sp) {
-            const float* rec = p.part + (((size_t(row) * p.hchunks + hcix) * p.splits + sp) * hc_cap + g) * PSTRIDE;
-            merge_state(M, Ls, &A, 1, rec[D], rec[D + 1], &rec[d]);
+    const float* base = p.part + ((size_t(row) * p.hchunks + hcix) * p.splits) * hc_cap * PSTRIDE + size_t(g) * PSTRIDE;
+    const size_t sstride = size_t(hc_cap) * PSTRIDE;
+    float M = -INFINITY, Ls = 0.f, A = 0.f;
+    for (int sp0 = 0; sp0 < p.splits; sp0 += kCombineBatch) {
+        float mv[kCombineBatch], lv[kCombineBatch], av[kCombineBatch];
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t) {
+            const int sp = min(sp0 + t, p.splits - 1);
+            const float* rec = base + size_t(sp) * sstride;
+            mv[t] = rec[D];
+            lv[t] = rec[D + 1];
+            av[t] = rec[d];
         }
-        const float v = (Ls > 0.f) ? A / Ls : 0.f;
-        const size_t o = (size_t(b) * p.H + h0 + g) * D + d;
-        if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
-        else ((float*)p.out)[o] = v;
+#pragma unroll
+        for (int t = 0; t < kCombineBatch; ++t)
+            if (sp0 + t < p.splits) merge_state(M, Ls, &A, 1, mv[t], lv[t], &av[t]);
     }
+    const float v = (Ls > 0.f) ? A / Ls : 0.f;
+    const size_t o = (size_t(b) * p.H + h) * D + d;
+    if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
+    else ((float*)p.out)[o] = v;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -516,7 +535,8 @@ AttnPlan plan_sparse_attn(int B, int H, int N, int D_, int sel_heads, int k, int
     long long splits = 1;
     if (rows < kNoSplitRows) {
         const long long rows1 = rows > 0 ? rows : 1;
-        splits = (kTargetWorkgroups + rows1 - 1) / rows1;
+        const long long target = p.mfma ? kTargetWorkgroupsMfma : kTargetWorkgroupsVec;
+        splits = (target + rows1 - 1) / rows1;
         if (splits > k) splits = k;
         if (splits < 1) splits = 1;
     }
@@ -545,9 +565,10 @@ hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t
     } else {
         if (qb) launch_vec<2, true>(prm, pl, grid, s); else launch_vec<2, false>(prm, pl, grid, s);
     }
-    if (pl.splits > 1)
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(pl.hchunks), unsigned(a.sel_heads), unsigned(a.B)),
-                           dim3(kThreads), 0, s, prm, pl.hc, qb);
+    if (pl.splits > 1) {
+        const unsigned per_req = unsigned((size_t(a.H) * D + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(a.B)), dim3(kThreads), 0, s, prm, pl.hc, qb);
+    }
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ struct SelectPlan {
     bool row_mode;     // one workgroup per (request, KV head); else score grid + top-k kernel
     int chunk;         // blocks per scoring workgroup (split mode)
     int n_chunks;      // scoring workgroups per row (split mode)
-    size_t lds_bytes;  // dynamic LDS of the row-mode kernel (scores kept on chip)
+    size_t lds_bytes;  // dynamic LDS of the row-mode / top-k kernel (scores kept on chip)
     size_t scores_off, bytes;
 };
 SelectPlan plan_block_select(int B, int N, int BS, int mmbpr);

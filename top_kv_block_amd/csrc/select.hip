@@ -294,8 +294,10 @@ __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int
                       min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage);
 }
 
-// split mode, step 2: top-k per (KV head, request)
+// split mode, step 2: top-k per (KV head, request); the row's scores are first copied
+// into LDS (all loads in flight together) when they fit
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelParams p) {
+    extern __shared__ __attribute__((aligned(16))) float lds_scores[];
     __shared__ uint32_t hist[256];
     __shared__ int sh[4];
     __shared__ int wsum[kWaves];
@@ -303,8 +305,27 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelParams p) {
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
     const float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
-    topk_emit(scores, r.nb, r.F, p.k, p.selected + (size_t(b) * p.N + n) * p.k, p.n_selected + size_t(b) * p.N + n,
-              hist, sh, wsum);
+    int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
+    int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
+    if (cap <= kLdsScoreCap) {
+        for (int i0 = 0; i0 < r.nb; i0 += 4 * kThreads) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + threadIdx.x;
+                v[u] = i < r.nb ? scores[i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + threadIdx.x;
+                if (i < r.nb) lds_scores[i] = v[u];
+            }
+        }
+        __syncthreads();
+        topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
+    } else {
+        topk_emit(scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -318,7 +339,7 @@ SelectPlan plan_block_select(int B, int N, int BS, int mmbpr) {
     p.row_mode = rows >= kRowModeRows || cap <= size_t(kRowModeMaxCap);
     p.chunk = kChunk;
     p.n_chunks = int((cap + kChunk - 1) / kChunk);
-    p.lds_bytes = (p.row_mode && cap <= size_t(kLdsScoreCap)) ? cap * sizeof(float) : 0;
+    p.lds_bytes = cap <= size_t(kLdsScoreCap) ? cap * sizeof(float) : 0;  // row / top-k kernel
     p.scores_off = 0;
     p.bytes = align256(size_t(B) * N * cap * sizeof(float));
     if (p.bytes < 256) p.bytes = 256;
@@ -341,7 +362,7 @@ hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& pl, hipStr
             hipLaunchKernelGGL(select_score_kernel<true>, g1, dim3(kThreads), 0, s, p, pl.chunk);
         else
             hipLaunchKernelGGL(select_score_kernel<false>, g1, dim3(kThreads), 0, s, p, pl.chunk);
-        hipLaunchKernelGGL(select_topk_kernel, dim3(unsigned(a.N), unsigned(a.B)), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(select_topk_kernel, dim3(unsigned(a.N), unsigned(a.B)), dim3(kThreads), pl.lds_bytes, s, p);
     }
     return hipGetLastError();
 }
