@@ -111,21 +111,56 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* wsum, int& total
     return off + below;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (row shifts within each row
+// of 16, then the row broadcasts 15 and 31 carry the row totals forward).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum of a per-thread count over the workgroup in thread order; `total`
+// receives the sum. wsum: kWaves ints of LDS. Two barriers.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
+    const uint32_t incl = wave_incl_scan(uint32_t(v));
+    if (lane_id() == kWave - 1) wsum[wave_id()] = int(incl);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = wsum[w];
+        off += (w < wave_id()) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return off + int(incl) - v;
+}
+
 // Block-wide radix select over a virtual array of n keys.
 // kf(i, &key) returns true if index i is a candidate and sets its key.
 // Finds the R-th largest candidate key T (1 <= R <= #candidates); on return `need_eq`
 // holds how many candidates equal to T belong to the top R (R minus those above T).
-// LDS: hist[256], sh[4]. Contains barriers: every thread of the workgroup must call it.
+// LDS: hist[512] (two 256-bin histograms used alternately, so clearing the next one
+// needs no barrier of its own), sh[4]. Two barriers per 8-bit pass; every thread of the
+// workgroup must call it.
 template <class KeyFn>
 __device__ uint32_t block_radix_select(int n, int R, KeyFn kf, uint32_t* hist, int* sh, int& need_eq) {
     uint32_t prefix = 0, pmask = 0;
     int need = R;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int j = threadIdx.x; j < 256; j += kThreads) hist[j] = 0;
-        __syncthreads();
+    for (int j = threadIdx.x; j < 512; j += kThreads) hist[j] = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        uint32_t* h = hist + 256 * (pass & 1);
         for (int i = threadIdx.x; i < n; i += kThreads) {
             uint32_t key;
-            if (kf(i, key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            if (kf(i, key) && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
         if (wave_id() == 0) {
@@ -134,32 +169,28 @@ __device__ uint32_t block_radix_select(int n, int R, KeyFn kf, uint32_t* hist, i
             uint32_t c[4];
             uint32_t s = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * l - j]; s += c[j]; }
-            uint32_t incl = s;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t t = __shfl_up(incl, o, kWave);
-                if (l >= o) incl += t;
-            }
+            for (int j = 0; j < 4; ++j) { c[j] = h[255 - 4 * l - j]; s += c[j]; }
+            const uint32_t incl = wave_incl_scan(s);
             uint32_t run = incl - s;
             if (run < uint32_t(need) && uint32_t(need) <= incl) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (run + c[j] >= uint32_t(need)) {
-                        sh[0] = 255 - 4 * l - j;
-                        sh[1] = int(run);
+                        sh[2 * (pass & 1)] = 255 - 4 * l - j;
+                        sh[2 * (pass & 1) + 1] = int(run);
                         break;
                     }
                     run += c[j];
                 }
             }
         }
+        // the other histogram is free now: clear it for the next pass
+        for (int j = threadIdx.x; j < 256; j += kThreads) hist[256 * ((pass + 1) & 1) + j] = 0;
         __syncthreads();
-        const uint32_t d = uint32_t(sh[0]);
-        need -= sh[1];
+        const uint32_t d = uint32_t(sh[2 * (pass & 1)]);
+        need -= sh[2 * (pass & 1) + 1];
         prefix |= d << shift;
         pmask |= 255u << shift;
-        __syncthreads();
     }
     need_eq = need;
     return prefix;

@@ -196,15 +196,19 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
 }
 
 // Exact top-k of a row from its scores (LDS or global); writes selected / n_selected.
-__device__ __forceinline__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out, int32_t* n_out,
-                          uint32_t* hist, int* sh, int* wsum) {
+// The radix select finds the k-th best key T; then each thread takes a contiguous run of
+// blocks, and two block-wide scans (equal-to-T ranks, then output positions) keep every
+// block above T and the lowest-index blocks equal to T, written in ascending order.
+__device__ __forceinline__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out,
+                                          int32_t* n_out, uint32_t* hist, int* sh, int* wsum) {
     const int tid = threadIdx.x;
     const int R = max(0, min(k, nb) - F.count);  // fill picks
     const int nc = nb - F.count;                   // fill candidates
     const bool take_all = R >= nc;
+    const bool radix = R > 0 && !take_all;
     uint32_t T = 0;
     int need_eq = 0;
-    if (R > 0 && !take_all) {
+    if (radix) {
         auto kf = [&](int i, uint32_t& key) -> bool {
             if (F.has(i)) return false;
             key = f2key(scores[i]);
@@ -212,25 +216,48 @@ __device__ __forceinline__ void topk_emit(const float* scores, int nb, const For
         };
         T = block_radix_select(nb, R, kf, hist, sh, need_eq);
     }
-    int pos0 = 0, eq_seen = 0;
-    for (int ib = 0; ib < nb; ib += kThreads) {
-        const int i = ib + tid;
-        const bool valid = i < nb;
-        const bool frc = valid && F.has(i);
-        const bool cand = valid && !frc && R > 0;
-        const uint32_t key = cand ? f2key(scores[i]) : 0u;
-        const bool eq = cand && !take_all && key == T;
-        int eq_tot;
-        const int eq_rank = block_excl_count(eq, wsum, eq_tot) + eq_seen;
-        const bool pick = frc || (cand && (take_all || key > T || (eq && eq_rank < need_eq)));
-        int tot;
-        const int pos = block_excl_count(pick, wsum, tot) + pos0;
-        if (pick && pos < k) out[pos] = i;
-        pos0 += tot;
-        eq_seen += eq_tot;
+    const int E = (nb + kThreads - 1) / kThreads;  // blocks per thread, contiguous
+    const int i0 = min(nb, tid * E), i1 = min(nb, i0 + E);
+    int eq_off = 0, tot;
+    if (radix) {
+        int eq_local = 0;
+        for (int i = i0; i < i1; ++i) eq_local += (!F.has(i) && f2key(scores[i]) == T) ? 1 : 0;
+        eq_off = block_excl_scan(eq_local, wsum, tot);
     }
-    for (int j = pos0 + tid; j < k; j += kThreads) out[j] = -1;
-    if (tid == 0) *n_out = min(pos0, k);
+    int pick_local = 0;
+    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
+        bool pick = F.has(i);
+        if (!pick && R > 0) {
+            if (take_all) {
+                pick = true;
+            } else {
+                const uint32_t key = f2key(scores[i]);
+                pick = key > T || (key == T && eq_seen < need_eq);
+                eq_seen += key == T ? 1 : 0;
+            }
+        }
+        pick_local += pick ? 1 : 0;
+    }
+    int npick;
+    int pos = block_excl_scan(pick_local, wsum, npick);
+    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
+        bool pick = F.has(i);
+        if (!pick && R > 0) {
+            if (take_all) {
+                pick = true;
+            } else {
+                const uint32_t key = f2key(scores[i]);
+                pick = key > T || (key == T && eq_seen < need_eq);
+                eq_seen += key == T ? 1 : 0;
+            }
+        }
+        if (pick) {
+            if (pos < k) out[pos] = i;
+            ++pos;
+        }
+    }
+    for (int j = npick + tid; j < k; j += kThreads) out[j] = -1;
+    if (tid == 0) *n_out = min(npick, k);
 }
 
 struct SelParams {
@@ -254,7 +281,7 @@ struct SelParams {
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds_scores[];
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[512];
     __shared__ int sh[4];
     __shared__ int wsum[kWaves];
     __shared__ u32x4 qstage[kThreads];
@@ -298,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int
 // into LDS (all loads in flight together) when they fit
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds_scores[];
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[512];
     __shared__ int sh[4];
     __shared__ int wsum[kWaves];
     const int n = blockIdx.x, b = blockIdx.y;
