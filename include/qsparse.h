@@ -141,6 +141,10 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
                           int32_t* selected, int32_t* n_selected, float* block_scores,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* bytes of workspace qs_probe_select needs for these sizes (B * H *
+ * max_kv_blocks_per_req probe keys, rounded up to 256) */
+size_t qs_probe_select_workspace_bytes(int32_t B, int32_t H, int32_t max_kv_blocks_per_req);
+
 /*
  * qs_probe_select -- page 1's probe + importance + recency selection, per query head.
  * [P1] sections 1 and 2 (sparse_attn_head): for query head h (KV head h / G) the probe
@@ -162,6 +166,8 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
  *   selected       [B, H, k] int32 output (ascending, -1 padded); n_selected [B, H] int32
  *   probe_scores   [B, H, max_kv_blocks_per_req] fp32 output or NULL (entries i >= nb
  *                  are not written)
+ *   workspace      device scratch of at least qs_probe_select_workspace_bytes(), 256-byte
+ *                  aligned, contents ignored
  */
 qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
                           qs_dtype q_dtype, qs_dtype kv_dtype,
@@ -171,7 +177,7 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
                           const float* importance, int32_t importance_stride,
                           int32_t n_probe, int32_t k, uint32_t flags,
                           int32_t* selected, int32_t* n_selected, float* probe_scores,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* bytes of workspace qs_sparse_attn_decode needs for these sizes */
 size_t qs_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D, int32_t sel_heads,

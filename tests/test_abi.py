@@ -96,20 +96,30 @@ def test_block_select_workspace_size(qs):
 
 def _probe(qs, **kw):
     a = dict(B=0, H=16, N=8, D=128, BS=32, qd=qs.QS_F32, kd=qs.QS_F32, q=FAKE, kc=FAKE, nkv=128, bt=FAKE,
-             mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32, flags=qs.QS_RECENCY, sel=FAKE, nsel=FAKE, ps=None)
+             mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32, flags=qs.QS_RECENCY, sel=FAKE, nsel=FAKE, ps=None,
+             ws=WS, wsb=1 << 30)
     a.update(kw)
     return qs.lib.qs_probe_select(a["B"], a["H"], a["N"], a["D"], a["BS"], a["qd"], a["kd"], a["q"], a["kc"],
                                   a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["imp"], a["stride"], a["npb"], a["k"],
-                                  a["flags"], a["sel"], a["nsel"], a["ps"], None)
+                                  a["flags"], a["sel"], a["nsel"], a["ps"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(kd=2), 2), (dict(qd=2), 2), (dict(k=0), 1), (dict(flags=1), 1), (dict(mkbpr=5000), 2),
     (dict(imp=FAKE, stride=0), 1), (dict(kc=None), 1), (dict(H=12), 1), (dict(BS=8), 2),
+    (dict(ws=None), 1), (dict(ws=ctypes.c_void_p((1 << 20) + 64)), 1), (dict(wsb=16), 1),
 ])
 def test_probe_select_rejects(qs, kw, status):
     assert _probe(qs, **kw) == status
     assert qs.lib.qs_last_error().decode().startswith("qs_probe_select")
+
+
+def test_probe_select_workspace_size(qs):
+    b = qs.probe_select_workspace_bytes(64, 16, 128)
+    assert b == 64 * 16 * 128 * 4
+    assert qs.probe_select_workspace_bytes(1, 1, 1) == 256
+    assert qs.probe_select_workspace_bytes(1, 0, 1) == 0
+    assert _probe(qs, wsb=qs.probe_select_workspace_bytes(0, 16, 128)) == 0
 
 
 def _attn(qs, **kw):

@@ -91,26 +91,6 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
-// exclusive prefix count of `flag` over the workgroup's threads in thread order;
-// `total` receives the workgroup total. Uses wsum[kWaves] of LDS; contains barriers.
-__device__ __forceinline__ int block_excl_count(bool flag, int* wsum, int& total) {
-    const uint64_t m = __ballot(flag);
-    const int lane = lane_id();
-    const int below = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    if (lane == 0) wsum[wave_id()] = __popcll(m);
-    __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const int c = wsum[w];
-        off += (w < wave_id()) ? c : 0;
-        tot += c;
-    }
-    __syncthreads();
-    total = tot;
-    return off + below;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave with DPP (row shifts within each row
 // of 16, then the row broadcasts 15 and 31 carry the row totals forward).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {

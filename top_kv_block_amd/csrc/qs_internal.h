@@ -73,7 +73,9 @@ struct ProbeArgs {
     int32_t* selected;
     int32_t* n_selected;
     float* probe_scores;
+    void* workspace;  // B * H * mkbpr probe keys
 };
+size_t probe_workspace_bytes(int B, int H, int mkbpr);
 hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s);
 
 // ---- sparse attention --------------------------------------------------------------

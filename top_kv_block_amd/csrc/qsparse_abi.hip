@@ -119,21 +119,28 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     return hip_status(qs::launch_block_select(a, plan, (hipStream_t)stream), fn);
 }
 
+size_t qs_probe_select_workspace_bytes(int32_t B, int32_t H, int32_t max_kv_blocks_per_req) {
+    if (B < 0 || H < 1 || max_kv_blocks_per_req < 1) return 0;
+    return qs::probe_workspace_bytes(B, H, max_kv_blocks_per_req);
+}
+
 qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
                           qs_dtype kv_dtype, const void* query, const void* k_cache, int32_t num_kv_blocks,
                           const int32_t* block_tables, int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
                           const float* importance, int32_t importance_stride, int32_t n_probe, int32_t k,
                           uint32_t flags, int32_t* selected, int32_t* n_selected, float* probe_scores,
-                          void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "qs_probe_select";
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
     if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
     if ((q_dtype != QS_F32 && q_dtype != QS_BF16) || (kv_dtype != QS_F32 && kv_dtype != QS_BF16))
         return fail(QS_ERR_UNSUPPORTED, "%s: query and K must be QS_F32 or QS_BF16", fn);
-    if (!query || !k_cache || !block_tables || !seq_lens || !selected || !n_selected)
+    if (!query || !k_cache || !block_tables || !seq_lens || !selected || !n_selected || !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned16(k_cache)) return fail(QS_ERR_INVALID, "%s: k_cache must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
     if (flags & ~(uint32_t)QS_RECENCY) return fail(QS_ERR_INVALID, "%s: flags may only hold QS_RECENCY", fn);
     if (k < 1) return fail(QS_ERR_INVALID, "%s: k=%d must be >= 1", fn, k);
     if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
@@ -143,10 +150,13 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
                     qs::kProbeMaxBlocks);
     if (importance && importance_stride < 1)
         return fail(QS_ERR_INVALID, "%s: importance_stride must be >= 1 when importance is given", fn);
+    const size_t need = qs::probe_workspace_bytes(B, H, max_kv_blocks_per_req);
+    if (workspace_bytes < need)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if (B == 0) return ok();
     qs::ProbeArgs a{B, H, N, D, block_size, q_dtype == QS_BF16, kv_dtype == QS_BF16, query, k_cache, num_kv_blocks,
                     block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
-                    selected, n_selected, probe_scores};
+                    selected, n_selected, probe_scores, workspace};
     return hip_status(qs::launch_probe_select(a, (hipStream_t)stream), fn);
 }
 

@@ -21,7 +21,8 @@ QS_FORCE_SINK, QS_FORCE_WINDOW, QS_RECENCY = 1, 2, 4
 
 # the C ABI's exported functions (also checked by the ABI tests)
 EXPORTS = (
-    "qs_build_metadata", "qs_block_select_workspace_bytes", "qs_block_select", "qs_probe_select",
+    "qs_build_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
+    "qs_probe_select_workspace_bytes", "qs_probe_select",
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_last_error", "qs_version",
 )
 
@@ -44,7 +45,9 @@ def _load():
     lib.qs_block_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, u32, i32,
                                     P, P, P, P, sz, P]
     lib.qs_probe_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, i32, P, i32, P, P,
-                                    i32, i32, i32, u32, P, P, P, P]
+                                    i32, i32, i32, u32, P, P, P, P, sz, P]
+    lib.qs_probe_select_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.qs_probe_select_workspace_bytes.restype = sz
     lib.qs_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.qs_sparse_attn_workspace_bytes.restype = sz
     lib.qs_sparse_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, P, P, i32,
@@ -121,7 +124,7 @@ _workspaces = {}
 
 
 def workspace(nbytes, device, op):
-    """A zero-filled, 256-byte aligned workspace cached per (device, operation), grown on
+    """An uninitialised, 256-byte aligned workspace cached per (device, operation), grown on
     demand. Calls that share one must be ordered on one stream."""
     key = (torch.device(device).index or 0, op)
     ws = _workspaces.get(key)
@@ -194,8 +197,13 @@ def qs_block_select(query, maxblocks, minblocks, metadata_block_tables, seq_lens
     return selected, n_selected
 
 
+def probe_select_workspace_bytes(B, H, mkbpr):
+    return lib.qs_probe_select_workspace_bytes(B, H, mkbpr)
+
+
 def qs_probe_select(query, k_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
-                    flags=QS_RECENCY, selected=None, n_selected=None, probe_scores=None):
+                    flags=QS_RECENCY, selected=None, n_selected=None, probe_scores=None,
+                    workspace_buf=None):
     """Page 1's probe/importance/recency selection per query head.
     Returns (selected [B, H, k] int32, n_selected [B, H] int32)."""
     dev = _dev(query, k_cache, block_tables, seq_lens, importance, selected, n_selected, probe_scores)
@@ -218,10 +226,12 @@ def qs_probe_select(query, k_cache, block_tables, seq_lens, k, importance=None, 
     _need(probe_scores is None or (probe_scores.dtype == torch.float32 and probe_scores.numel() >= B * H * mkbpr),
           "probe_scores must be fp32 [B, H, MKBPR]")
     stride = 0 if importance is None else importance.shape[1]
+    nbytes = probe_select_workspace_bytes(B, H, mkbpr)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe")
     _check(lib.qs_probe_select(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
                                _ptr(k_cache), nkv, _ptr(block_tables), mkbpr, _ptr(seq_lens), _ptr(importance),
                                stride, int(n_probe), int(k), int(flags), _ptr(selected), _ptr(n_selected),
-                               _ptr(probe_scores), _stream(dev)))
+                               _ptr(probe_scores), _ptr(ws), ws.numel(), _stream(dev)))
     return selected, n_selected
 
 
