@@ -44,6 +44,7 @@ def lib():
         P = ctypes.c_void_p
         i = ctypes.c_int
         L.qso_build_metadata.argtypes = [i, i, i, i, i, P, i, P, i, P, P, i, P, P, i]
+        L.qso_update_metadata.argtypes = [i, i, i, i, i, P, i, P, i, P, P, i, P, i, P, P, i]
         L.qso_block_select.argtypes = [i, i, i, i, i, i, P, P, P, P, i, i, P, P, ctypes.c_uint, i, P, P, P]
         L.qso_probe_select.argtypes = [i, i, i, i, i, i, i, P, P, i, P, i, P, P, i, i, i, ctypes.c_uint,
                                        P, P, P, P, P, P]
@@ -117,6 +118,21 @@ def build_metadata(k_cache, block_tables, seq_lens, meta_tables, num_meta_blocks
     rc = lib().qso_build_metadata(B, N, D, BS, _dtype_code(kc), _p(kc), nkv, _p(bt), bt.shape[1],
                                   _p(sl), _p(mt), mt.shape[1], _p(mx), _p(mn), num_meta_blocks)
     _check(rc, "build_metadata")
+    return mx, mn
+
+
+def update_metadata(k_cache, block_tables, seq_lens, first_block, max_new_blocks, meta_tables, maxb, minb):
+    """O1' (refresh). Returns copies of (maxb, minb) with sequence blocks first_block[b] ..
+    min(nb, first_block[b] + max_new_blocks) - 1 of each request recomputed."""
+    kc = np.ascontiguousarray(_np(k_cache))
+    nkv, BS, N, D = kc.shape
+    bt, sl, mt, fb = _i32(block_tables), _i32(seq_lens), _i32(meta_tables), _i32(first_block)
+    B = sl.shape[0]
+    mx = np.array(_np(maxb), dtype=kc.dtype, copy=True)
+    mn = np.array(_np(minb), dtype=kc.dtype, copy=True)
+    rc = lib().qso_update_metadata(B, N, D, BS, _dtype_code(kc), _p(kc), nkv, _p(bt), bt.shape[1], _p(sl),
+                                   _p(fb), int(max_new_blocks), _p(mt), mt.shape[1], _p(mx), _p(mn), mx.shape[0])
+    _check(rc, "update_metadata")
     return mx, mn
 
 

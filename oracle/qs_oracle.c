@@ -91,6 +91,40 @@ static int total_greater(float a, float b) {
  * Layouts: k_cache [num_kv_blocks, BS, N, D]; maxb/minb [num_meta_blocks, BS, N, D] in
  * the same dtype as k_cache (f32 or bf16), written bit-exactly from the winning key.
  */
+/* max/min of one sequence block i of request b into its metadata row (O1's inner step) */
+static int reduce_block(int N, int D, int BS, int dtype, const void* k_cache, int num_kv_blocks,
+                        const int32_t* block_tables, int mkbpr, const int32_t* meta_tables, int mmbpr,
+                        void* maxb, void* minb, int num_meta_blocks, int b, int32_t L, int32_t i) {
+    const size_t row = (size_t)N * D;
+    const int32_t phys = block_tables[(size_t)b * mkbpr + i];
+    const int32_t m = meta_tables[(size_t)b * mmbpr + i / BS];
+    if (phys < 0 || phys >= num_kv_blocks || m < 0 || m >= num_meta_blocks) return QSO_BAD;
+    const int32_t r = i % BS;
+    int32_t nt = L - i * BS;
+    if (nt > BS) nt = BS;
+    for (int n = 0; n < N; ++n) {
+        for (int d = 0; d < D; ++d) {
+            size_t best_hi = ((size_t)phys * BS + 0) * row + (size_t)n * D + d;
+            size_t best_lo = best_hi;
+            for (int32_t t = 1; t < nt; ++t) {
+                const size_t idx = ((size_t)phys * BS + t) * row + (size_t)n * D + d;
+                const float x = elem_f(k_cache, dtype, idx);
+                if (total_greater(x, elem_f(k_cache, dtype, best_hi))) best_hi = idx;
+                if (total_greater(elem_f(k_cache, dtype, best_lo), x)) best_lo = idx;
+            }
+            const size_t o = ((size_t)m * BS + r) * row + (size_t)n * D + d;
+            if (dtype == QSO_F32) {
+                ((float*)maxb)[o] = ((const float*)k_cache)[best_hi];
+                ((float*)minb)[o] = ((const float*)k_cache)[best_lo];
+            } else {
+                ((uint16_t*)maxb)[o] = ((const uint16_t*)k_cache)[best_hi];
+                ((uint16_t*)minb)[o] = ((const uint16_t*)k_cache)[best_lo];
+            }
+        }
+    }
+    return QSO_OK;
+}
+
 int qso_build_metadata(int B, int N, int D, int BS, int dtype,
                        const void* k_cache, int num_kv_blocks,
                        const int32_t* block_tables, int mkbpr,
@@ -104,32 +138,9 @@ int qso_build_metadata(int B, int N, int D, int BS, int dtype,
         const int32_t nb = n_blocks_of(L, BS);
         if (nb > mkbpr || ceil_div64(nb, BS) > mmbpr) return QSO_BAD;
         for (int32_t i = 0; i < nb; ++i) {
-            const int32_t phys = block_tables[(size_t)b * mkbpr + i];
-            const int32_t m = meta_tables[(size_t)b * mmbpr + i / BS];
-            if (phys < 0 || phys >= num_kv_blocks || m < 0 || m >= num_meta_blocks) return QSO_BAD;
-            const int32_t r = i % BS;
-            int32_t nt = L - i * BS;
-            if (nt > BS) nt = BS;
-            for (int n = 0; n < N; ++n) {
-                for (int d = 0; d < D; ++d) {
-                    size_t best_hi = ((size_t)phys * BS + 0) * row + (size_t)n * D + d;
-                    size_t best_lo = best_hi;
-                    for (int32_t t = 1; t < nt; ++t) {
-                        const size_t idx = ((size_t)phys * BS + t) * row + (size_t)n * D + d;
-                        const float x = elem_f(k_cache, dtype, idx);
-                        if (total_greater(x, elem_f(k_cache, dtype, best_hi))) best_hi = idx;
-                        if (total_greater(elem_f(k_cache, dtype, best_lo), x)) best_lo = idx;
-                    }
-                    const size_t o = ((size_t)m * BS + r) * row + (size_t)n * D + d;
-                    if (dtype == QSO_F32) {
-                        ((float*)maxb)[o] = ((const float*)k_cache)[best_hi];
-                        ((float*)minb)[o] = ((const float*)k_cache)[best_lo];
-                    } else {
-                        ((uint16_t*)maxb)[o] = ((const uint16_t*)k_cache)[best_hi];
-                        ((uint16_t*)minb)[o] = ((const uint16_t*)k_cache)[best_lo];
-                    }
-                }
-            }
+            const int rc = reduce_block(N, D, BS, dtype, k_cache, num_kv_blocks, block_tables, mkbpr, meta_tables,
+                                        mmbpr, maxb, minb, num_meta_blocks, b, L, i);
+            if (rc != QSO_OK) return rc;
         }
         if (nb % BS != 0) {
             const int32_t m = meta_tables[(size_t)b * mmbpr + (nb - 1) / BS];
@@ -140,6 +151,36 @@ int qso_build_metadata(int B, int N, int D, int BS, int dtype,
                 memset((char*)maxb + o * (dtype == QSO_F32 ? 4 : 2), 0, bytes);
                 memset((char*)minb + o * (dtype == QSO_F32 ? 4 : 2), 0, bytes);
             }
+        }
+    }
+    return QSO_OK;
+}
+
+/*
+ * O1': refresh of the newest blocks.
+ * [P3] "生产实践建议": after prefill the metadata is built once, then refreshed every 128
+ * decoded tokens. reading: a refresh recomputes, with O1's own per-block step, only
+ * sequence blocks first_block[b] .. min(nb, first_block[b] + max_new) - 1 (negative
+ * first_block counts as 0) and writes nothing else (no tail fill: rows past nb keep what
+ * they held).
+ */
+int qso_update_metadata(int B, int N, int D, int BS, int dtype,
+                        const void* k_cache, int num_kv_blocks,
+                        const int32_t* block_tables, int mkbpr,
+                        const int32_t* seq_lens, const int32_t* first_block, int max_new,
+                        const int32_t* meta_tables, int mmbpr,
+                        void* maxb, void* minb, int num_meta_blocks) {
+    if (dtype != QSO_F32 && dtype != QSO_BF16) return QSO_BAD;
+    if (max_new < 1) return QSO_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t L = seq_lens[b];
+        const int32_t nb = n_blocks_of(L, BS);
+        if (nb > mkbpr || ceil_div64(nb, BS) > mmbpr) return QSO_BAD;
+        const int32_t i0 = first_block[b] > 0 ? first_block[b] : 0;
+        for (int64_t i = i0; i < nb && i < (int64_t)i0 + max_new; ++i) {
+            const int rc = reduce_block(N, D, BS, dtype, k_cache, num_kv_blocks, block_tables, mkbpr, meta_tables,
+                                        mmbpr, maxb, minb, num_meta_blocks, b, L, (int32_t)i);
+            if (rc != QSO_OK) return rc;
         }
     }
     return QSO_OK;

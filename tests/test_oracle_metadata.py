@@ -113,3 +113,74 @@ def test_metadata_capacity_matches_page3(oracle):
         sl1 = torch.tensor([max_tokens + 1], dtype=torch.int32)
         with pytest.raises(ValueError):
             oracle.build_metadata(kc, bt, sl1, mt, mmbpr)     # one token more does not
+
+
+# ---- refresh of the newest blocks (page 3, "生产实践建议": rebuilt every 128 tokens) ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_update_equals_library_amax_amin_and_writes_nothing_else(oracle, dtype):
+    BS = 16
+    lens = [0, 5, 3 * BS, 3 * BS + 7, BS * BS + 2 * BS + 3, 40]
+    first = [0, -4, 1, 2, BS - 2, 9]        # empty, negative (= 0), mid, last partial, spans two meta blocks, past nb
+    max_new = 3
+    wl = W.random_case(15, len(lens), 4, 2, BS, lens, k=4, dtype=dtype, D=128, with_v=False)
+    sentinel = torch.full((wl.num_meta_blocks, BS, wl.N, wl.D), 7.0, dtype=dtype)
+    mx, mn = oracle.update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens,
+                                    torch.tensor(first, dtype=torch.int32), max_new, wl.meta_tables,
+                                    sentinel, sentinel)
+    mxf, mnf = _as_float(mx), _as_float(mn)
+    touched = set()
+    for b, L in enumerate(lens):
+        nb = cdiv(L, BS)
+        i0 = max(first[b], 0)
+        for i in range(i0, min(nb, i0 + max_new)):
+            phys = int(wl.block_tables[b, i])
+            blk = wl.k_cache[phys, :min(BS, L - i * BS)].float()
+            np.testing.assert_array_equal(_meta_row(mxf, wl, b, i), torch.amax(blk, dim=0).numpy())
+            np.testing.assert_array_equal(_meta_row(mnf, wl, b, i), torch.amin(blk, dim=0).numpy())
+            touched.add((int(wl.meta_tables[b, i // BS]), i % BS))
+    assert len(touched) == 0 + 1 + 2 + 2 + 3 + 0
+    for m in range(wl.num_meta_blocks):
+        for r in range(BS):
+            if (m, r) not in touched:     # no tail fill, no other row
+                assert np.all(mxf[m, r] == 7.0) and np.all(mnf[m, r] == 7.0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_update_chain_reproduces_full_build(oracle, dtype):
+    """Serving loop: build after prefill, then refresh every BS tokens from the block that
+    was partial at the last refresh. From a zero-filled metadata pool the result equals a
+    full build at the final length, bit for bit, tail rows included."""
+    BS = 16
+    L0 = [37, 0, 16 * BS - 3, 5]
+    steps = 3 * BS + 2                               # the last refresh is not at a BS multiple
+    final = [x + steps for x in L0]
+    wl = W.random_case(16, len(L0), 4, 2, BS, final, k=4, dtype=dtype, D=128, with_v=False)
+    zeros = torch.zeros((wl.num_meta_blocks, BS, wl.N, wl.D), dtype=dtype)
+    cur = list(L0)
+    mx, mn = oracle.build_metadata(wl.k_cache, wl.block_tables, torch.tensor(cur, dtype=torch.int32),
+                                   wl.meta_tables, wl.num_meta_blocks, maxb=zeros, minb=zeros)
+    for t in range(BS, steps + 1, BS):
+        new = [x + BS for x in cur]
+        fb = torch.tensor([x // BS for x in cur], dtype=torch.int32)
+        mx, mn = oracle.update_metadata(wl.k_cache, wl.block_tables, torch.tensor(new, dtype=torch.int32), fb, 2,
+                                        wl.meta_tables, mx, mn)
+        cur = new
+    fb = torch.tensor([x // BS for x in cur], dtype=torch.int32)
+    mx, mn = oracle.update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, fb, 2, wl.meta_tables, mx, mn)
+    fx, fn = oracle.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables,
+                                   wl.num_meta_blocks, maxb=zeros, minb=zeros)
+    assert np.asarray(mx).tobytes() == np.asarray(fx).tobytes()
+    assert np.asarray(mn).tobytes() == np.asarray(fn).tobytes()
+
+
+def test_update_bound_stops_early(oracle):
+    """A refresh that covers fewer blocks than were added leaves the rest untouched."""
+    BS = 16
+    wl = W.random_case(17, 1, 4, 2, BS, [10 * BS], k=4, dtype=torch.float32, D=128, with_v=False)
+    zeros = torch.zeros((wl.num_meta_blocks, BS, wl.N, wl.D))
+    mx, _ = oracle.update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, torch.tensor([4], dtype=torch.int32),
+                                   2, wl.meta_tables, zeros, zeros)
+    m = int(wl.meta_tables[0, 0])
+    written = [r for r in range(BS) if np.any(mx[m, r] != 0)]
+    assert written == [4, 5]
