@@ -6,8 +6,10 @@ A step is one pass of the path over one batch: Quest block selection (grouped-qu
 scoring, top-k, sink/window forcing) followed by exact attention over the selected
 blocks. The default workload is the large-batch serving decode: B=128, H=64, N=8, D=128,
 BS=128, seq_len=32768, k=16, bf16 K/V (8 GiB each) in a shuffled paged pool; step s uses
-query set s mod 4 and tokens_since_metadata_update = s mod 128. The metadata rebuild
-(every 128 steps in that workload) is timed on its own and reported beside the step.
+query set s mod 4 and tokens_since_metadata_update = s mod 128. The full metadata
+rebuild and the refresh of each request's newest block (the every-128-tokens update) are
+timed on their own and reported beside the step, as is the step rate with the caches
+flushed (1 GiB written) before each step.
 
 Prints one JSON line: steps/s, ms/step, achieved algorithmic HBM GB/s of the step and of
 the attention kernel (HIP events around each attention launch on the launch stream),
@@ -261,6 +263,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flushed-steps", type=int, default=32,
+                    help="steps timed one by one after a 1 GiB cache flush each (0: skip)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the other configurations (tiny, page-3 select, probe, long context)")
     ap.add_argument("--graph-steps", type=int, default=128,
@@ -323,6 +327,21 @@ def main():
     meta_bytes = sum(L * N * D * es for L in mlens) + \
         sum(cdiv(cdiv(L, BS), BS) * BS * N * D * es * 2 for L in mlens)   # K read + max/min rows written
 
+    # refresh of the newest block of every request (the every-128-tokens metadata update)
+    first_blk = torch.tensor([max(cdiv(L, BS) - 1, 0) for L in mlens], dtype=torch.int32, device=dev)
+
+    def refresh():
+        qs.qs_update_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, first_blk, 1, wl.meta_tables, mx, mn)
+
+    refresh()
+    e0.record(stream)
+    for _ in range(20):
+        refresh()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    refresh_us = e0.elapsed_time(e1) / 20 * 1e3
+    refresh_bytes = sum((L - (cdiv(L, BS) - 1) * BS) * N * D * es + N * D * es * 2 for L in mlens if L > 0)
+
     copy_gbps = None
     if args.copy_calibration_mib > 0:
         # a plain device-to-device copy of known size: the bandwidth a simple streaming
@@ -358,6 +377,31 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+
+    # (1b) the same steps with the caches flushed before each one: reading a 1 GiB buffer
+    # evicts L2 and the 256 MB last-level cache, so nothing of the step's inputs is cache
+    # resident (a read, not a fill, so no dirty lines are left to be written back during
+    # the step); select and attention are bracketed by events separately
+    flushed = None
+    if args.flushed_steps > 0:
+        log(f"timing {args.flushed_steps} steps after a cache flush each")
+        junk = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        acc = torch.zeros((), dtype=torch.float32, device=dev)
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.flushed_steps)]
+        for s in range(args.flushed_steps):
+            acc += junk.sum()
+            fe[s][0].record(stream)
+            select(s)
+            fe[s][1].record(stream)
+            attend(s)
+            fe[s][2].record(stream)
+        torch.cuda.synchronize()
+        f_sel = float(np.mean([a.elapsed_time(b) for a, b, _ in fe]))
+        f_att = float(np.mean([b.elapsed_time(c) for _, b, c in fe]))
+        flushed = {"steps_per_s": round(1000.0 / (f_sel + f_att), 3), "select_us": round(f_sel * 1e3, 2),
+                   "attention_us": round(f_att * 1e3, 2), "steps": args.flushed_steps,
+                   "flush": "1 GiB read before each step; events around select and attention"}
+        del junk
 
     # (2) per-kernel durations: the same K steps with HIP events around every launch, on
     # the stream the kernels run on (the events themselves add a little time between
@@ -447,6 +491,10 @@ def main():
         "metadata_rebuild_ms": round(rebuild_ms, 4),
         "metadata_rebuild_gbps": round(meta_bytes / (rebuild_ms * 1e-3) / 1e9, 1),
         "steps_per_s_with_rebuild_every_128": round(128.0 / (128 * ms_per_step + rebuild_ms) * 1000.0, 3),
+        "metadata_refresh_us": round(refresh_us, 2),
+        "metadata_refresh_gbps": round(refresh_bytes / (refresh_us * 1e-6) / 1e9, 1),
+        "steps_per_s_with_refresh_every_128": round(128.0 / (128 * ms_per_step + refresh_us * 1e-3) * 1000.0, 3),
+        "flushed": flushed,
         "roofline": {"kernel": "attn_mfma_kernel (qs_sparse_attn_decode)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),

@@ -3,8 +3,9 @@
  * (libqsparse.so, HIP kernels for CDNA4 / gfx950).
  *
  * Four operations, run in this order on each decode step:
- *   qs_build_metadata      per-block, per-channel max/min of K (after prefill, and again
- *                          whenever the metadata is refreshed);
+ *   qs_build_metadata      per-block, per-channel max/min of K (after prefill);
+ *   qs_update_metadata     the same for only the blocks completed since the last
+ *                          refresh (every BS decoded tokens);
  *   qs_block_select        Quest top-k block selection on the grouped query, optional
  *                          sink / local-window forcing;   (or)
  *   qs_probe_select        probe + prefill-importance + recency block selection;
@@ -99,6 +100,32 @@ qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size,
                             const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
                             void* maxblocks, void* minblocks, int32_t num_meta_blocks,
                             void* stream);
+
+/*
+ * qs_update_metadata -- refresh the Quest metadata of the newest blocks only.
+ * [P3] "生产实践建议": the metadata is built once after prefill and then refreshed every
+ * 128 decoded tokens. A refresh needs only the blocks whose tokens changed since the
+ * last one, so this call recomputes, for each request b, the sequence blocks
+ *     i = first_block[b] ... min(nb_b, first_block[b] + max_new_blocks) - 1
+ * (negative first_block entries count as 0; nb_b = ceil(seq_lens[b] / BS)) with exactly
+ * the per-channel max/min qs_build_metadata writes for them, bit for bit. No other row is
+ * written: rows past nb_b are not zero-filled, so metadata blocks must start zeroed
+ * (as from a zero-filled pool) where a consumer needs the +0.0 rows of absent blocks.
+ * A refresh after the last one covered L_old tokens passes first_block = floor(L_old / BS)
+ * (the block that was partial then) and max_new_blocks >= the blocks added since.
+ *
+ *   arguments as qs_build_metadata, plus
+ *   first_block     [B] int32 (device), first sequence block to recompute per request
+ *   max_new_blocks  host bound on the blocks recomputed per request (>= 1)
+ */
+qs_status qs_update_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size, qs_dtype kv_dtype,
+                             const void* k_cache, int32_t num_kv_blocks,
+                             const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                             const int32_t* seq_lens, const int32_t* first_block,
+                             int32_t max_new_blocks,
+                             const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                             void* maxblocks, void* minblocks, int32_t num_meta_blocks,
+                             void* stream);
 
 /* bytes of workspace qs_block_select needs for these sizes */
 size_t qs_block_select_workspace_bytes(int32_t B, int32_t N, int32_t block_size,

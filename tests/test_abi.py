@@ -27,9 +27,10 @@ def _declared_functions():
     return sorted(set(re.findall(r"^\s*(?:qs_status|size_t|const char\s*\*)\s*(qs_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     names = _declared_functions()
-    for n in ("qs_build_metadata", "qs_block_select", "qs_probe_select", "qs_sparse_attn_decode"):
+    for n in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
+              "qs_sparse_attn_decode"):
         assert n in names
 
 
@@ -65,6 +66,30 @@ def test_build_metadata_rejects(qs, kw, status):
 
 def test_build_metadata_b0_is_noop(qs):
     assert _meta(qs, B=0) == 0
+    assert qs.lib.qs_last_error().decode() == ""
+
+
+def _update(qs, **kw):
+    a = dict(B=0, N=8, D=128, BS=128, dt=qs.QS_BF16, kc=FAKE, nkv=4, bt=FAKE, mkbpr=4, sl=FAKE, fb=FAKE, mnew=1,
+             mt=FAKE, mmbpr=1, mx=FAKE, mn=FAKE, nmeta=1)
+    a.update(kw)
+    return qs.lib.qs_update_metadata(a["B"], a["N"], a["D"], a["BS"], a["dt"], a["kc"], a["nkv"], a["bt"],
+                                     a["mkbpr"], a["sl"], a["fb"], a["mnew"], a["mt"], a["mmbpr"], a["mx"],
+                                     a["mn"], a["nmeta"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), 2), (dict(BS=100), 2), (dict(dt=2), 2), (dict(B=-1), 1), (dict(fb=None), 1),
+    (dict(mnew=0), 1), (dict(mnew=-3), 1), (dict(kc=None), 1), (dict(mn=ctypes.c_void_p((1 << 20) + 8)), 1),
+    (dict(nmeta=0), 1), (dict(mkbpr=0), 1),
+])
+def test_update_metadata_rejects(qs, kw, status):
+    assert _update(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_update_metadata")
+
+
+def test_update_metadata_b0_is_noop(qs):
+    assert _update(qs) == 0
     assert qs.lib.qs_last_error().decode() == ""
 
 

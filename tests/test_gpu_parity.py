@@ -199,6 +199,101 @@ def test_metadata_config1_and_config2(qs, oracle):
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
 
 
+# metadata refresh of the newest blocks
+UPDATE_CASES = [
+    # seed, B, N, BS, lens, first_block, max_new, dtype   (column slices per block in brackets)
+    (21, 2, 8, 128, [128 * 9 + 3, 128 * 4], [8, 2], 1, torch.bfloat16),                 # [8]
+    (22, 4, 2, 32, [0, 31, 32 * 33 + 7, 32 * 64], [0, -5, 30, 63], 4, torch.float32),   # [4]
+    (23, 3, 3, 16, [16 * 16 * 2 + 1, 5, 16 * 20], [31, 0, 14], 3, torch.bfloat16),       # N=3: [2]
+    (24, 2, 4, 64, [64 * 70, 64 * 3 - 1], [60, 1], 16, torch.float32),                   # [4]
+    (25, 3, 1, 128, [128 * 3 + 100, 128 * 2, 1], [1, 5, 0], 2, torch.bfloat16),          # N=1: [1]
+    (26, 8, 8, 16, [16 * 16 * 4] * 8, [0] * 8, 256, torch.bfloat16),                     # whole sequences: [1]
+]
+
+
+@pytest.mark.parametrize("case", UPDATE_CASES, ids=lambda c: f"seed{c[0]}")
+def test_update_metadata_random(qs, oracle, case):
+    seed, B, N, BS, lens, first, max_new, dtype = case
+    say(f"metadata refresh seed={seed} B={B} N={N} BS={BS} first={first} max_new={max_new} dtype={dtype}")
+    wl = W.random_case(seed, B, 2 * N, N, BS, lens, k=4, dtype=dtype, with_v=False)
+    shape = (wl.num_meta_blocks, BS, N, wl.D)
+    mx = torch.full(shape, 7.0, dtype=dtype, device=DEV)
+    mn = torch.full(shape, 7.0, dtype=dtype, device=DEV)
+    fb = torch.tensor(first, dtype=torch.int32)
+    qs.qs_update_metadata(wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV), fb.to(DEV), max_new,
+                          wl.meta_tables.to(DEV), mx, mn)
+    torch.cuda.synchronize()
+    s = torch.full(shape, 7.0, dtype=dtype)
+    omx, omn = oracle.update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, fb, max_new, wl.meta_tables, s, s)
+    assert np.array_equal(bits(tnp(mx)), bits(omx))
+    assert np.array_equal(bits(tnp(mn)), bits(omn))
+
+
+def test_update_metadata_serving_chain(qs, oracle):
+    """Build after prefill, then a refresh every BS decoded tokens (from the block that was
+    partial at the last refresh), on a zero-filled pool: the GPU pool equals the oracle's
+    full build at the final length, bit for bit."""
+    BS, N = 32, 8
+    L0 = [32 * 50 + 9, 32 * 3, 1, 32 * 31]
+    steps = 3 * BS + 11
+    final = [x + steps for x in L0]
+    say(f"metadata refresh chain BS={BS} L0={L0} steps={steps}")
+    wl = W.random_case(27, len(L0), 16, N, BS, final, k=4, dtype=torch.bfloat16, with_v=False)
+    kc, bt, mt = wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.meta_tables.to(DEV)
+    mx = torch.zeros((wl.num_meta_blocks, BS, N, wl.D), dtype=torch.bfloat16, device=DEV)
+    mn = torch.zeros_like(mx)
+    cur = list(L0)
+    qs.qs_build_metadata(kc, bt, torch.tensor(cur, dtype=torch.int32, device=DEV), mt, mx, mn)
+    while cur != final:
+        new = [min(x + BS, f) for x, f in zip(cur, final)]
+        fb = torch.tensor([x // BS for x in cur], dtype=torch.int32, device=DEV)
+        qs.qs_update_metadata(kc, bt, torch.tensor(new, dtype=torch.int32, device=DEV), fb, 2, mt, mx, mn)
+        cur = new
+    torch.cuda.synchronize()
+    z = torch.zeros((wl.num_meta_blocks, BS, N, wl.D), dtype=torch.bfloat16)
+    omx, omn = oracle.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, wl.num_meta_blocks,
+                                     maxb=z, minb=z)
+    assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
+
+
+def test_update_metadata_config5_newest_blocks(qs, oracle):
+    """Serving shape (B=128, N=8, BS=128, 256 blocks a request, 8 GiB K pool): refresh the
+    last blocks of every request in one call; sampled requests against the oracle, and no
+    row outside the refreshed blocks written anywhere in the pool."""
+    wl = W.config5(device=DEV)
+    first, max_new = 250, 8                 # blocks 250 .. 255 (nb = 256)
+    say(f"metadata refresh config5 first={first} max_new={max_new}")
+    shape = (wl.num_meta_blocks, wl.BS, wl.N, wl.D)
+    mx = torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV)
+    mn = torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV)
+    fb = torch.full((wl.B,), first, dtype=torch.int32, device=DEV)
+    qs.qs_update_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, fb, max_new, wl.meta_tables, mx, mn)
+    torch.cuda.synchronize()
+    # rows of blocks 250..255 live in each request's second metadata block, rows 122..127
+    nb = cdiv(int(wl.meta_seq_lens[0]), wl.BS)
+    assert nb == 256 and bool((wl.meta_seq_lens == wl.meta_seq_lens[0]).all())
+    sentinel = torch.tensor(7.0, dtype=torch.bfloat16)
+    written = torch.zeros((wl.num_meta_blocks, wl.BS), dtype=torch.bool, device=DEV)
+    mt = wl.meta_tables.cpu()
+    for b in range(wl.B):
+        written[int(mt[b, 1]), first - wl.BS:nb - wl.BS] = True
+    for t in (mx, mn):
+        is_sent = (t == sentinel.to(DEV)).flatten(2).all(dim=2)
+        assert bool(is_sent[~written].all()), "a row outside the refreshed blocks was written"
+    reqs = [0, 64, 127]
+    sub, nbs = sub_workload(wl, reqs)
+    s = torch.full((sub.num_meta_blocks, wl.BS, wl.N, wl.D), 7.0, dtype=torch.bfloat16)
+    omx, omn = oracle.update_metadata(sub.k_cache, sub.block_tables, sub.meta_seq_lens,
+                                      torch.full((len(reqs),), first, dtype=torch.int32), max_new,
+                                      sub.meta_tables, s, s)
+    gmx, gmn = mx.cpu(), mn.cpu()
+    for j, b in enumerate(reqs):
+        for m in range(cdiv(nbs[j], wl.BS)):
+            om = int(sub.meta_tables[j, m])
+            assert np.array_equal(bits(tnp(gmx[int(mt[b, m])])), bits(omx[om]))
+            assert np.array_equal(bits(tnp(gmn[int(mt[b, m])])), bits(omn[om]))
+
+
 # ------------------------------------------------------------------------------------------
 # Quest select
 # ------------------------------------------------------------------------------------------

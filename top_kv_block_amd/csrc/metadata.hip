@@ -83,27 +83,32 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
     const int32_t* __restrict__ sl,
     const int32_t* __restrict__ mt, int mmbpr,
     uint8_t* __restrict__ maxb, uint8_t* __restrict__ minb, int num_meta,
-    int BS, int row_vecs) {
+    int BS, int row_vecs, const int32_t* __restrict__ first) {
     using E = Ext<BF16>;
     __shared__ u32x4 red_hi[kThreads];
     __shared__ u32x4 red_lo[kThreads];
 
-    const int i = blockIdx.x;  // sequence block of request b
     const int b = blockIdx.y;
+    // sequence block of request b: the grid's x index, offset by the request's first
+    // block to refresh when only new blocks are reduced
+    const int i = int(blockIdx.x) + (first ? max(first[b], 0) : 0);
     const int L = max(sl[b], 0);
     const int nb = (L + BS - 1) / BS;
     const int nb_round = ((nb + BS - 1) / BS) * BS;
-    if (i >= nb_round) return;
+    if (i >= (first ? nb : nb_round) || i / BS >= mmbpr) return;
     const int m = mt[size_t(b) * mmbpr + i / BS];
     if (m < 0 || m >= num_meta) return;
+    // this workgroup's slice of the row: columns [c0, c0 + cv) of 16 bytes each
+    const int cv = row_vecs / int(gridDim.z);
+    const size_t c0b = size_t(blockIdx.z) * cv * 16;
     const size_t row_bytes = size_t(row_vecs) * 16;
-    uint8_t* omax = maxb + (size_t(m) * BS + (i % BS)) * row_bytes;
-    uint8_t* omin = minb + (size_t(m) * BS + (i % BS)) * row_bytes;
+    uint8_t* omax = maxb + (size_t(m) * BS + (i % BS)) * row_bytes + c0b;
+    uint8_t* omin = minb + (size_t(m) * BS + (i % BS)) * row_bytes + c0b;
     const int tid = threadIdx.x;
 
     if (i >= nb) {  // tail row of the last metadata block: +0.0
         const u32x4 z{0u, 0u, 0u, 0u};
-        for (int v = tid; v < row_vecs; v += kThreads) {
+        for (int v = tid; v < cv; v += kThreads) {
             st16(omax + size_t(v) * 16, z);
             st16(omin + size_t(v) * 16, z);
         }
@@ -113,12 +118,12 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
     const int phys = bt[size_t(b) * mkbpr + i];
     if (phys < 0 || phys >= num_kv_blocks) return;
     const int nt = min(BS, L - i * BS);
-    const uint8_t* src = kc + size_t(phys) * BS * row_bytes;
+    const uint8_t* src = kc + size_t(phys) * BS * row_bytes + c0b;
 
-    if (row_vecs <= kThreads) {
-        const int R = kThreads / row_vecs;  // token rows per pass
-        const int col = tid % row_vecs;
-        const int r0 = tid / row_vecs;
+    if (cv <= kThreads) {
+        const int R = kThreads / cv;  // token rows per pass
+        const int col = tid % cv;
+        const int r0 = tid / cv;
         u32x4 hi{E::hi_init, E::hi_init, E::hi_init, E::hi_init};
         u32x4 lo{E::lo_init, E::lo_init, E::lo_init, E::lo_init};
         if (r0 < R) {
@@ -136,10 +141,10 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
         red_hi[tid] = hi;
         red_lo[tid] = lo;
         __syncthreads();
-        if (tid < row_vecs) {
+        if (tid < cv) {
             for (int r = 1; r < R; ++r) {
-                const u32x4 h2 = red_hi[r * row_vecs + tid];
-                const u32x4 l2 = red_lo[r * row_vecs + tid];
+                const u32x4 h2 = red_hi[r * cv + tid];
+                const u32x4 l2 = red_lo[r * cv + tid];
                 hi.x = E::mx(hi.x, h2.x); hi.y = E::mx(hi.y, h2.y);
                 hi.z = E::mx(hi.z, h2.z); hi.w = E::mx(hi.w, h2.w);
                 lo.x = E::mn(lo.x, l2.x); lo.y = E::mn(lo.y, l2.y);
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
             st16(omin + size_t(tid) * 16, unord<BF16>(lo));
         }
     } else {
-        for (int col = tid; col < row_vecs; col += kThreads) {
+        for (int col = tid; col < cv; col += kThreads) {
             u32x4 hi{E::hi_init, E::hi_init, E::hi_init, E::hi_init};
             u32x4 lo{E::lo_init, E::lo_init, E::lo_init, E::lo_init};
             const uint8_t* p = src + size_t(col) * 16;
@@ -168,22 +173,43 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t launch_build_metadata(const MetaArgs& a, hipStream_t s) {
+void launch_meta(const MetaArgs& a, dim3 grid, const int32_t* first, hipStream_t s) {
     const int esize = a.bf16 ? 2 : 4;
     const int row_vecs = a.N * a.D * esize / 16;
-    dim3 grid(unsigned(a.mmbpr) * unsigned(a.BS), unsigned(a.B));
     if (a.bf16)
         hipLaunchKernelGGL(meta_kernel<true>, grid, dim3(kThreads), 0, s,
                            (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens,
                            a.meta_tables, a.mmbpr, (uint8_t*)a.maxb, (uint8_t*)a.minb, a.num_meta, a.BS,
-                           row_vecs);
+                           row_vecs, first);
     else
         hipLaunchKernelGGL(meta_kernel<false>, grid, dim3(kThreads), 0, s,
                            (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens,
                            a.meta_tables, a.mmbpr, (uint8_t*)a.maxb, (uint8_t*)a.minb, a.num_meta, a.BS,
-                           row_vecs);
+                           row_vecs, first);
+}
+
+}  // namespace
+
+hipError_t launch_build_metadata(const MetaArgs& a, hipStream_t s) {
+    launch_meta(a, dim3(unsigned(a.mmbpr) * unsigned(a.BS), unsigned(a.B), 1u), nullptr, s);
+    return hipGetLastError();
+}
+
+int update_col_slices(int B, int N, int D, bool bf16, int max_new_blocks) {
+    // A refresh touches few blocks (often one per request): split each block's row into
+    // column slices of at least one KV head (256 bytes or more) until the grid fills the chip.
+    const int row_vecs = N * D * (bf16 ? 2 : 4) / 16;
+    int slices = 1;
+    while ((long long)B * max_new_blocks * slices < 2048 && row_vecs / (slices * 2) >= 16 &&
+           (row_vecs % (slices * 2)) == 0)
+        slices *= 2;
+    return slices;
+}
+
+hipError_t launch_update_metadata(const MetaArgs& a, const int32_t* first_block, int max_new_blocks,
+                                  hipStream_t s) {
+    const int slices = update_col_slices(a.B, a.N, a.D, a.bf16, max_new_blocks);
+    launch_meta(a, dim3(unsigned(max_new_blocks), unsigned(a.B), unsigned(slices)), first_block, s);
     return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ struct MetaArgs {
     int num_meta;
 };
 hipError_t launch_build_metadata(const MetaArgs& a, hipStream_t s);
+int update_col_slices(int B, int N, int D, bool bf16, int max_new_blocks);
+hipError_t launch_update_metadata(const MetaArgs& a, const int32_t* first_block, int max_new_blocks,
+                                  hipStream_t s);
 
 // ---- Quest select ------------------------------------------------------------------
 struct SelectPlan {

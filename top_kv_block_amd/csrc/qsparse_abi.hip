@@ -80,6 +80,34 @@ qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size,
     return hip_status(qs::launch_build_metadata(a, (hipStream_t)stream), fn);
 }
 
+qs_status qs_update_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size, qs_dtype kv_dtype,
+                             const void* k_cache, int32_t num_kv_blocks, const int32_t* block_tables,
+                             int32_t max_kv_blocks_per_req, const int32_t* seq_lens, const int32_t* first_block,
+                             int32_t max_new_blocks, const int32_t* metadata_block_tables,
+                             int32_t max_meta_blocks_per_req, void* maxblocks, void* minblocks,
+                             int32_t num_meta_blocks, void* stream) {
+    const char* fn = "qs_update_metadata";
+    qs_status st = check_dims(fn, B, N, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32 or QS_BF16", fn);
+    if (!k_cache || !block_tables || !seq_lens || !first_block || !metadata_block_tables || !maxblocks ||
+        !minblocks)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(k_cache) || !aligned16(maxblocks) || !aligned16(minblocks))
+        return fail(QS_ERR_INVALID, "%s: k_cache, maxblocks and minblocks must be 16-byte aligned", fn);
+    if (num_kv_blocks < 1 || num_meta_blocks < 1 || max_kv_blocks_per_req < 1 || max_meta_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: block counts and table widths must be >= 1", fn);
+    if (max_new_blocks < 1) return fail(QS_ERR_INVALID, "%s: max_new_blocks=%d must be >= 1", fn, max_new_blocks);
+    if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
+        return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
+    if (B == 0) return ok();
+    qs::MetaArgs a{B, N, D, block_size, kv_dtype == QS_BF16, k_cache, num_kv_blocks, block_tables,
+                   max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
+                   maxblocks, minblocks, num_meta_blocks};
+    return hip_status(qs::launch_update_metadata(a, first_block, max_new_blocks, (hipStream_t)stream), fn);
+}
+
 size_t qs_block_select_workspace_bytes(int32_t B, int32_t N, int32_t block_size, int32_t max_meta_blocks_per_req) {
     if (B < 0 || N < 1 || block_size < 1 || max_meta_blocks_per_req < 1) return 0;
     return qs::plan_block_select(B, N, block_size, max_meta_blocks_per_req).bytes;

@@ -21,7 +21,7 @@ QS_FORCE_SINK, QS_FORCE_WINDOW, QS_RECENCY = 1, 2, 4
 
 # the C ABI's exported functions (also checked by the ABI tests)
 EXPORTS = (
-    "qs_build_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
+    "qs_build_metadata", "qs_update_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
     "qs_probe_select_workspace_bytes", "qs_probe_select",
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_last_error", "qs_version",
 )
@@ -40,6 +40,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
     lib.qs_build_metadata.argtypes = [i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, P, i32, P, P, i32, P]
+    lib.qs_update_metadata.argtypes = [i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, P, i32, P, i32, P, P,
+                                       i32, P]
     lib.qs_block_select_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.qs_block_select_workspace_bytes.restype = sz
     lib.qs_block_select.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, u32, i32,
@@ -52,7 +54,8 @@ def _load():
     lib.qs_sparse_attn_workspace_bytes.restype = sz
     lib.qs_sparse_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, P, P, i32,
                                           P, i32, P, P, P, i32, i32, ctypes.c_float, P, P, sz, P]
-    for f in ("qs_build_metadata", "qs_block_select", "qs_probe_select", "qs_sparse_attn_decode"):
+    for f in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
+              "qs_sparse_attn_decode"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
@@ -138,13 +141,10 @@ def workspace(nbytes, device, op):
 # the four operations (names and argument meaning as in include/qsparse.h)
 # ------------------------------------------------------------------------------------------
 
-def qs_build_metadata(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks):
-    """Per-block, per-channel max/min of K into the paged metadata blocks (in place)."""
-    dev = _dev(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks)
+def _meta_shapes(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks):
     for n, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
                  ("metadata_block_tables", metadata_block_tables)):
         _i32(t, n)
-    nkv, BS, N, D = k_cache.shape
     if maxblocks.shape != minblocks.shape or maxblocks.shape[1:] != k_cache.shape[1:]:
         raise ValueError("maxblocks/minblocks must be [num_meta_blocks, BS, N, D]")
     if maxblocks.dtype != k_cache.dtype or minblocks.dtype != k_cache.dtype:
@@ -152,10 +152,33 @@ def qs_build_metadata(k_cache, block_tables, seq_lens, metadata_block_tables, ma
     B = seq_lens.shape[0]
     _rows(block_tables, B, "block_tables")
     _rows(metadata_block_tables, B, "metadata_block_tables")
+    return B
+
+
+def qs_build_metadata(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks):
+    """Per-block, per-channel max/min of K into the paged metadata blocks (in place)."""
+    dev = _dev(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks)
+    B = _meta_shapes(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks)
+    nkv, BS, N, D = k_cache.shape
     _check(lib.qs_build_metadata(B, N, D, BS, _dtype_code(k_cache), _ptr(k_cache), nkv, _ptr(block_tables),
                                  block_tables.shape[1], _ptr(seq_lens), _ptr(metadata_block_tables),
                                  metadata_block_tables.shape[1], _ptr(maxblocks), _ptr(minblocks),
                                  maxblocks.shape[0], _stream(dev)))
+
+
+def qs_update_metadata(k_cache, block_tables, seq_lens, first_block, max_new_blocks, metadata_block_tables,
+                       maxblocks, minblocks):
+    """Recompute the metadata of blocks first_block[b] .. first_block[b] + max_new_blocks - 1
+    (those below ceil(seq_lens[b] / BS)) of each request, in place; nothing else is written."""
+    dev = _dev(k_cache, block_tables, seq_lens, first_block, metadata_block_tables, maxblocks, minblocks)
+    B = _meta_shapes(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks)
+    _i32(first_block, "first_block")
+    _rows(first_block, B, "first_block")
+    nkv, BS, N, D = k_cache.shape
+    _check(lib.qs_update_metadata(B, N, D, BS, _dtype_code(k_cache), _ptr(k_cache), nkv, _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(seq_lens), _ptr(first_block), int(max_new_blocks),
+                                  _ptr(metadata_block_tables), metadata_block_tables.shape[1], _ptr(maxblocks),
+                                  _ptr(minblocks), maxblocks.shape[0], _stream(dev)))
 
 
 def block_select_workspace_bytes(B, N, block_size, mmbpr):
