@@ -118,7 +118,8 @@ void attn_mfma_kernel(AttnParams p) {
     const int nh = min(16, p.hpr - hcix * 16);
     const int G = p.H / p.N;
     const int kh = (s * p.hpr) / G;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int c16 = lane & 15, j = lane >> 4;
 
     // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
@@ -141,6 +142,24 @@ void attn_mfma_kernel(AttnParams p) {
     const size_t tstride = size_t(p.N) * D;           // elements between tokens of one KV head
     uint8_t* vt = lds + w * kVtBytes;
 
+    // Slot table: lane t of every wave resolves slot slot0 + t once (selection entry, then
+    // block table) into (physical block, valid tokens), and the chunk loop reads it back
+    // with v_readlane. The loop then issues only K/V loads, never waiting on a dependent
+    // lookup with K/V loads in flight. Ranges longer than a wave look up in the loop.
+    const int nsl = max(0, slot1 - slot0);
+    const bool use_tab = nsl <= kWave;
+    int tab_phys = -1, tab_nt = 0;
+    if (use_tab && lane < nsl) {
+        const int blk = srow[slot0 + lane];
+        if (blk >= 0 && blk < nb && blk < p.mkbpr) {
+            const int ph = p.bt[size_t(b) * p.mkbpr + blk];
+            if (ph >= 0 && ph < p.num_kv_blocks) {
+                tab_phys = ph;
+                tab_nt = min(p.BS, L - blk * p.BS);
+            }
+        }
+    }
+
     float m = -INFINITY, lsum = 0.f;
     f32x4 o[8];
 #pragma unroll
@@ -148,11 +167,18 @@ void attn_mfma_kernel(AttnParams p) {
 
     for (int q = w; q < nq; q += kWaves) {
         const int slot = slot0 + q / cpb, cib = q % cpb;
-        const int blk = srow[slot];
-        if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
-        const int phys = p.bt[size_t(b) * p.mkbpr + blk];
-        if (phys < 0 || phys >= p.num_kv_blocks) continue;
-        const int nt = min(p.BS, L - blk * p.BS);
+        int phys, nt;
+        if (use_tab) {
+            phys = __builtin_amdgcn_readlane(tab_phys, slot - slot0);
+            nt = __builtin_amdgcn_readlane(tab_nt, slot - slot0);
+            if (phys < 0) continue;
+        } else {
+            const int blk = srow[slot];
+            if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
+            phys = p.bt[size_t(b) * p.mkbpr + blk];
+            if (phys < 0 || phys >= p.num_kv_blocks) continue;
+            nt = min(p.BS, L - blk * p.BS);
+        }
         const int tb = cib * 32;
         if (tb >= nt) continue;
         const uint16_t* kb = (const uint16_t*)p.kc + (size_t(phys) * p.BS * p.N + kh) * D;

@@ -22,6 +22,8 @@
 // ties"). Output is written in ascending block order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -32,6 +34,9 @@ constexpr int kChunk = 64;             // blocks per scoring workgroup in split 
 constexpr int kRowModeRows = 512;      // rows at which one workgroup per row fills the chip
 constexpr int kRowModeMaxCap = 256;    // rows this short always use row mode
 constexpr int kLdsScoreCap = 8192;     // row mode keeps up to this many scores in LDS
+constexpr int kMtStageCap = 256;       // metadata-table rows up to this long are staged in LDS
+static_assert(kMtStageCap <= kThreads, "one staging load per thread");
+static_assert(kChunk / 16 + 2 <= kMtStageCap, "a split-mode chunk's table entries fit the stage");
 
 struct Forced {
     int w_lo;   // blocks >= w_lo are forced (window); nb when none
@@ -79,14 +84,16 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 
 // Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
 // skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
-// qstage: kThreads 16-byte LDS slots used to stage the group's query rows. Contains a
-// barrier: every thread of the workgroup must call it.
-template <bool BF16>
+// qstage: kThreads 16-byte LDS slots used to stage the group's query rows; mt_stage:
+// kMtStageCap ints of LDS for the metadata-table entries of [i0, i_end) (MT_LDS: the
+// caller guarantees they fit). Contains a barrier: every thread of the workgroup must
+// call it.
+template <bool BF16, bool MT_LDS>
 __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
                                             const uint8_t* __restrict__ minb, int num_meta,
                                             const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
                                             int n, const Forced& F, int i0, int i_end, float* dst, bool nan_forced,
-                                            u32x4* qstage) {
+                                            u32x4* qstage, int32_t* mt_stage) {
     constexpr int esize = BF16 ? 2 : 4;
     constexpr int D = 128;
     constexpr int LPR = D * esize / 16;  // lanes per metadata row
@@ -98,16 +105,22 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
     const int G = H / N;
     const size_t row_bytes = size_t(N) * D * esize;
 
-    // One batch = U passes of RPP rows. The table lookups of a batch come first, then its
-    // metadata loads back to back (a lookup between them would wait for every load in
-    // flight); the next batch's loads are issued before the current batch is consumed.
-    auto issue = [&](int base, u32x4 (&vmx)[U], u32x4 (&vmn)[U], bool (&ok)[U]) {
+    // One batch = U passes of RPP rows; the next batch's loads are issued before the
+    // current batch is consumed. With MT_LDS the range's metadata-table entries are
+    // staged in LDS so that the lookups of later batches are LDS reads (a global lookup
+    // would have to wait for every load in flight before it); batch 0 looks up in global
+    // memory while the staging loads are in flight.
+    const int mbase = i0 / BS;
+    auto issue = [&](int base, u32x4 (&vmx)[U], u32x4 (&vmn)[U], bool (&ok)[U], auto from_lds) {
         int mrow[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = base + u * RPP + slot;
             ok[u] = i < i_end && !F.has(i);
-            mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
+            if constexpr (decltype(from_lds)::value)
+                mrow[u] = ok[u] ? mt_stage[i / BS - mbase] : 0;
+            else
+                mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -127,9 +140,13 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
     u32x4 qpiece{0u, 0u, 0u, 0u};
     if (staged && tid < npieces)
         qpiece = ld16(query + ((size_t(b) * H + size_t(n) * G + tid / LPR) * D + (tid % LPR) * EPL) * esize);
+    const int n_ent = i0 < i_end ? (i_end - 1) / BS - mbase + 1 : 0;  // table entries of the range
+    int32_t mt_piece = 0;
+    if (MT_LDS && tid < n_ent) mt_piece = mt[size_t(b) * mmbpr + mbase + tid];
     u32x4 vmx[U], vmn[U];
     bool ok[U];
-    if (i0 < i_end) issue(i0, vmx, vmn, ok);
+    if (i0 < i_end) issue(i0, vmx, vmn, ok, std::false_type{});
+    if (MT_LDS && tid < n_ent) mt_stage[tid] = mt_piece;
 
     // grouped query for this lane's channels: mean over the group's G heads
     float gq[EPL];
@@ -145,9 +162,9 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
             for (int j = 0; j < 4; ++j) gq[j] += __uint_as_float(w[j]);
         }
     };
+    if (staged && tid < npieces) qstage[tid] = qpiece;
+    __syncthreads();  // query pieces and the table row are in LDS
     if (staged) {
-        if (tid < npieces) qstage[tid] = qpiece;
-        __syncthreads();
         for (int g = 0; g < G; ++g) add_piece(qstage[g * LPR + lr]);
     } else {
         for (int g = 0; g < G; ++g)
@@ -156,11 +173,7 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
 #pragma unroll
     for (int e = 0; e < EPL; ++e) gq[e] = gq[e] / float(G);
 
-    for (int base = i0; base < i_end; base += RPP * U) {
-        u32x4 nmx[U], nmn[U];
-        bool nok[U];
-        const bool more = base + RPP * U < i_end;
-        if (more) issue(base + RPP * U, nmx, nmn, nok);
+    auto consume = [&](int base, const u32x4 (&vmx)[U], const u32x4 (&vmn)[U], const bool (&ok)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t a[4] = {vmx[u].x, vmx[u].y, vmx[u].z, vmx[u].w};
@@ -188,10 +201,19 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
                     dst[i] = __builtin_nanf("");
             }
         }
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) { vmx[u] = nmx[u]; vmn[u] = nmn[u]; ok[u] = nok[u]; }
-        }
+    };
+
+    // ping-pong over two register sets, so a batch's loads are in flight while the other
+    // batch is consumed, with no register copies between them
+    constexpr int STEP = RPP * U;
+    u32x4 wmx[U], wmn[U];
+    bool wok[U];
+    for (int base = i0; base < i_end; base += 2 * STEP) {
+        const bool more1 = base + STEP < i_end;
+        if (more1) issue(base + STEP, wmx, wmn, wok, std::integral_constant<bool, MT_LDS>{});
+        consume(base, vmx, vmn, ok);
+        if (base + 2 * STEP < i_end) issue(base + 2 * STEP, vmx, vmn, ok, std::integral_constant<bool, MT_LDS>{});
+        if (more1) consume(base + STEP, wmx, wmn, wok);
     }
 }
 
@@ -277,14 +299,16 @@ struct SelParams {
     float* ws_scores;
 };
 
-// row mode: one workgroup per (KV head, request)
-template <bool BF16>
+// row mode: one workgroup per (KV head, request); MT_LDS when the request's metadata
+// table row fits in LDS
+template <bool BF16, bool MT_LDS>
 __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds_scores[];
     __shared__ uint32_t hist[512];
     __shared__ int sh[4];
     __shared__ int wsum[kWaves];
     __shared__ u32x4 qstage[kThreads];
+    __shared__ int32_t mt_stage[kMtStageCap];
     const int n = blockIdx.x, b = blockIdx.y;
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
@@ -292,16 +316,16 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
     int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
     if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
-        score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
-                          lds_scores, false, qstage);
+        score_range<BF16, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+                                  0, r.nb, lds_scores, false, qstage, mt_stage);
         __syncthreads();
         if (p.dbg_scores)
             for (int i = threadIdx.x; i < r.nb; i += kThreads)
                 gscores[i] = r.F.has(i) ? __builtin_nanf("") : lds_scores[i];
         topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     } else {
-        score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0, r.nb,
-                          gscores, p.dbg_scores != nullptr, qstage);
+        score_range<BF16, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+                                  0, r.nb, gscores, p.dbg_scores != nullptr, qstage, mt_stage);
         __syncthreads();
         topk_emit(gscores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     }
@@ -311,14 +335,16 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int chunk) {
     __shared__ u32x4 qstage[kThreads];
+    __shared__ int32_t mt_stage[kMtStageCap];
     const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
     const int i0 = c * chunk;
     if (i0 >= r.nb) return;
     float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
-    score_range<BF16>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
-                      min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage);
+    // a chunk spans at most chunk / BS + 2 table entries, always within kMtStageCap
+    score_range<BF16, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
+                            min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage, mt_stage);
 }
 
 // split mode, step 2: top-k per (KV head, request); the row's scores are first copied
@@ -379,10 +405,14 @@ hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& pl, hipStr
                 a.block_scores, (float*)((uint8_t*)a.workspace + pl.scores_off)};
     if (pl.row_mode) {
         dim3 grid(unsigned(a.N), unsigned(a.B));
-        if (a.bf16)
-            hipLaunchKernelGGL(select_row_kernel<true>, grid, dim3(kThreads), pl.lds_bytes, s, p);
-        else
-            hipLaunchKernelGGL(select_row_kernel<false>, grid, dim3(kThreads), pl.lds_bytes, s, p);
+        const bool mt_lds = a.mmbpr <= kMtStageCap;
+        if (a.bf16) {
+            if (mt_lds) hipLaunchKernelGGL((select_row_kernel<true, true>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+            else hipLaunchKernelGGL((select_row_kernel<true, false>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+        } else {
+            if (mt_lds) hipLaunchKernelGGL((select_row_kernel<false, true>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+            else hipLaunchKernelGGL((select_row_kernel<false, false>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+        }
     } else {
         dim3 g1(unsigned(pl.n_chunks), unsigned(a.N), unsigned(a.B));
         if (a.bf16)
