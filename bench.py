@@ -6,14 +6,15 @@ A step is one pass of the path over one batch: Quest block selection (grouped-qu
 scoring, top-k, sink/window forcing) followed by exact attention over the selected
 blocks. The default workload is the large-batch serving decode: B=128, H=64, N=8, D=128,
 BS=128, seq_len=32768, k=16, bf16 K/V (8 GiB each) in a shuffled paged pool; step s uses
-query set s mod 4 and tokens_since_metadata_update = s mod 128. The full metadata
-rebuild and the refresh of each request's newest block (the every-128-tokens update) are
-timed on their own and reported beside the step, as is the step rate with the caches
-flushed (1 GiB written) before each step.
+query set s mod 4 and tokens_since_metadata_update = s mod 128. There the step is one
+qs_select_attn_decode call (one kernel); the two-call path (qs_block_select, then
+qs_sparse_attn_decode) is timed beside it. The full metadata rebuild and the refresh of
+each request's newest block (the every-128-tokens update) are timed on their own, as is
+the step rate with the caches flushed (1 GiB read) before each step.
 
 Prints one JSON line: steps/s, ms/step, achieved algorithmic HBM GB/s of the step and of
-the attention kernel (HIP events around each attention launch on the launch stream),
-and the CPU oracle's rate on a bounded sample of the same workload.
+its dominant kernel (HIP events around each launch on the launch stream), and the CPU
+oracle's rate on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -83,11 +84,11 @@ def step_bytes(wl, sel_h, ns_h, tsmu_h):
     return sel_b, att_b
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary, if it was taken
-    on the current kernel source (else None: the counters are stale)."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary,
+    if it was taken on the current kernel sources (else None: the counters are stale)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_attn_mfma_config5.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
@@ -175,8 +176,12 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                               n_selected=ns), reps, stream)
     t_att = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
                                                     sel, ns), reps, stream)
+    out1 = torch.empty_like(wl.query)
+    t_fused = _timed(lambda: qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
+                                                      wl.block_tables, wl.seq_lens, wl.k, out=out1), reps, stream)
     res["config1_tiny_fp32"] = {"select_us": round(t_sel * 1e3, 2), "attention_us": round(t_att * 1e3, 2),
-                                "step_us": round((t_sel + t_att) * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
+                                "step_us": round((t_sel + t_att) * 1e3, 2),
+                                "fused_step_us": round(t_fused * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
     del wl, mx, mn
 
     # config 2: page-3-shaped Quest select, bf16; metadata build timed too
@@ -262,6 +267,9 @@ def main():
     ap.add_argument("--workload", default="config5", choices=["config5", "config4"])
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=["fused", "separate"], default=None,
+                    help="step as one qs_select_attn_decode call (default for config5) or as "
+                         "qs_block_select + qs_sparse_attn_decode (default for config4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flushed-steps", type=int, default=32,
                     help="steps timed one by one after a 1 GiB cache flush each (0: skip)")
@@ -359,67 +367,87 @@ def main():
         copy_gbps = 2 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         del src, dst
 
-    log(f"warmup {args.warmup} steps")
-    for s in range(args.warmup):
+    ws_fused = torch.zeros(qs.select_attn_workspace_bytes(B, H, N, BS, wl.mmbpr, k, qs.QS_BF16), dtype=torch.uint8,
+                           device=dev)
+
+    def fused(s):
+        # the fused entry point: selection kept on chip and attention in one launch when the
+        # rows allow it (the serving shape does); the selection is still written out
+        qs.qs_select_attn_decode(qsets[s % qsets.shape[0]], mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
+                                 wl.block_tables, wl.seq_lens, k, tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]],
+                                 flags=wl.flags, out=out, selected=sel, n_selected=ns, workspace_buf=ws_fused)
+
+    def separate(s):
         select(s)
         attend(s)
+
+    path = args.path or ("fused" if args.workload == "config5" else "separate")
+    step = fused if path == "fused" else separate
+    other = separate if path == "fused" else fused
+
+    log(f"warmup {args.warmup} steps of each path")
+    for s in range(args.warmup):
+        fused(s)
+        separate(s)
     torch.cuda.synchronize()
 
     K = args.steps
+
+    def time_steps(fn):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(K):
+            fn(s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
     # (1) the step rate: K steps back to back, events only around the whole region
-    log(f"timing {K} steps")
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(K):
-        select(s)
-        attend(s)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    log(f"timing {K} steps ({path} path)")
+    total_ms = time_steps(step)
+    log(f"timing {K} steps (the other path)")
+    other_ms = time_steps(other) / K
 
     # (1b) the same steps with the caches flushed before each one: reading a 1 GiB buffer
     # evicts L2 and the 256 MB last-level cache, so nothing of the step's inputs is cache
     # resident (a read, not a fill, so no dirty lines are left to be written back during
-    # the step); select and attention are bracketed by events separately
+    # the step); events around each step
     flushed = None
     if args.flushed_steps > 0:
         log(f"timing {args.flushed_steps} steps after a cache flush each")
         junk = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         acc = torch.zeros((), dtype=torch.float32, device=dev)
-        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.flushed_steps)]
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.flushed_steps)]
         for s in range(args.flushed_steps):
             acc += junk.sum()
             fe[s][0].record(stream)
-            select(s)
+            step(s)
             fe[s][1].record(stream)
-            attend(s)
-            fe[s][2].record(stream)
         torch.cuda.synchronize()
-        f_sel = float(np.mean([a.elapsed_time(b) for a, b, _ in fe]))
-        f_att = float(np.mean([b.elapsed_time(c) for _, b, c in fe]))
-        flushed = {"steps_per_s": round(1000.0 / (f_sel + f_att), 3), "select_us": round(f_sel * 1e3, 2),
-                   "attention_us": round(f_att * 1e3, 2), "steps": args.flushed_steps,
-                   "flush": "1 GiB read before each step; events around select and attention"}
+        f_ms = float(np.mean([a.elapsed_time(b) for a, b in fe]))
+        flushed = {"steps_per_s": round(1000.0 / f_ms, 3), "step_us": round(f_ms * 1e3, 2),
+                   "steps": args.flushed_steps, "flush": "1 GiB read before each step; events around each step"}
         del junk
 
-    # (2) per-kernel durations: the same K steps with HIP events around every launch, on
+    # (2) per-launch durations: the same K steps with HIP events around every launch, on
     # the stream the kernels run on (the events themselves add a little time between
     # launches, so the step rate above is taken without them)
     log(f"timing {K} steps with per-launch events")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for s in range(K):
-        evs[s][0].record(stream)
-        select(s)
-        evs[s][1].record(stream)
-        ev[s][0].record(stream)
-        attend(s)
-        ev[s][1].record(stream)
-    torch.cuda.synchronize()
-    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    select_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    def per_launch(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for s in range(K):
+            ev[s][0].record(stream)
+            fn(s)
+            ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    fused_ms = per_launch(fused)
+    select_ms = per_launch(select)
+    attn_ms = per_launch(attend)
 
     # (3) the same steps replayed from one captured HIP graph (no host launch overhead)
     graph_ms = None
@@ -432,8 +460,7 @@ def main():
         with torch.cuda.stream(cs):
             with torch.cuda.graph(g, stream=cs):
                 for s in range(gs):
-                    select(s)
-                    attend(s)
+                    step(s)
         stream.wait_stream(cs)
         g.replay()
         torch.cuda.synchronize()
@@ -460,8 +487,13 @@ def main():
     att_bytes /= len(sample_steps)
     ms_per_step = total_ms / K
     step_gbps = (sel_bytes + att_bytes) / (ms_per_step * 1e-3) / 1e9
-    attn_avg_ms = float(attn_ms.mean())
-    attn_gbps = att_bytes / (attn_avg_ms * 1e-3) / 1e9
+    if path == "fused":
+        # one kernel per step in the serving shape: select_attn_mfma_kernel moves the whole step
+        dom_kernel, dom_ms, dom_bytes = "select_attn_mfma_kernel (qs_select_attn_decode)", fused_ms, sel_bytes + att_bytes
+    else:
+        dom_kernel, dom_ms, dom_bytes = "attn_mfma_kernel (qs_sparse_attn_decode)", attn_ms, att_bytes
+    dom_avg_ms = float(dom_ms.mean())
+    dom_gbps = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -478,15 +510,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "block_size": BS,
                    "seq_len": int(wl.seq_lens.max()), "k": k, "flags": "sink+window",
-                   "query_sets": int(qsets.shape[0])},
+                   "query_sets": int(qsets.shape[0]),
+                   "path": "qs_select_attn_decode" if path == "fused" else "qs_block_select + qs_sparse_attn_decode"},
         "step_bytes": int(sel_bytes + att_bytes),
         "step_gbps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "select_bytes": int(sel_bytes),
         "attention_bytes": int(att_bytes),
+        "other_path": {"path": "qs_block_select + qs_sparse_attn_decode" if path == "fused" else "qs_select_attn_decode",
+                       "steps_per_s": round(1000.0 / other_ms, 3), "ms_per_step": round(other_ms, 5)},
         "graph_replay_steps_per_s": None if graph_ms is None else round(1000.0 / graph_ms, 3),
+        "fused_call_avg_us": round(float(fused_ms.mean()) * 1000, 3),
         "select_avg_us": round(float(select_ms.mean()) * 1000, 3),
         "select_gbps": round(sel_bytes / (float(select_ms.mean()) * 1e-3) / 1e9, 1),
+        "attention_avg_us": round(float(attn_ms.mean()) * 1000, 3),
+        "attention_gbps": round(att_bytes / (float(attn_ms.mean()) * 1e-3) / 1e9, 1),
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
         "metadata_rebuild_ms": round(rebuild_ms, 4),
         "metadata_rebuild_gbps": round(meta_bytes / (rebuild_ms * 1e-3) / 1e9, 1),
@@ -495,11 +533,11 @@ def main():
         "metadata_refresh_gbps": round(refresh_bytes / (refresh_us * 1e-6) / 1e9, 1),
         "steps_per_s_with_refresh_every_128": round(128.0 / (128 * ms_per_step + refresh_us * 1e-3) * 1000.0, 3),
         "flushed": flushed,
-        "roofline": {"kernel": "attn_mfma_kernel (qs_sparse_attn_decode)", "bound": "hbm",
-                     "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic() if args.workload == "config5" else None,
-                     "avg_launch_us": round(attn_avg_ms * 1000, 3), "bytes_per_launch": int(att_bytes)},
+        "roofline": {"kernel": dom_kernel, "bound": "hbm",
+                     "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(dom_kernel.split()[0], wl.name),
+                     "avg_launch_us": round(dom_avg_ms * 1000, 3), "bytes_per_launch": int(dom_bytes)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_cpu_baseline(wl, qsets, tsmu_tab, args.cpu_sample, args.cpu_seconds)

@@ -9,7 +9,8 @@
  *   qs_block_select        Quest top-k block selection on the grouped query, optional
  *                          sink / local-window forcing;   (or)
  *   qs_probe_select        probe + prefill-importance + recency block selection;
- *   qs_sparse_attn_decode  exact softmax attention over the selected blocks only.
+ *   qs_sparse_attn_decode  exact softmax attention over the selected blocks only;
+ *   qs_select_attn_decode  qs_block_select followed by qs_sparse_attn_decode, fused.
  *
  * Sources, cited by page title and section:
  *   [P1] "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择"
@@ -242,6 +243,38 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                                 const int32_t* selected, const int32_t* n_selected,
                                 int32_t sel_heads, int32_t k, float softmax_scale,
                                 void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* bytes of workspace qs_select_attn_decode needs for these sizes (0 for invalid sizes) */
+size_t qs_select_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t block_size,
+                                      int32_t max_meta_blocks_per_req, int32_t k, qs_dtype dtype);
+
+/*
+ * qs_select_attn_decode -- Quest selection and the attention over the selected blocks in
+ * one call. [P3] "quest_block_select_paged: 解码期 top-k 预测算法" and "三个核心算子", [P1]
+ * section 2 (the attention loop runs over the blocks the selection points to). The
+ * result is, by definition, qs_block_select (flags, tokens_since_update and k as there)
+ * followed by qs_sparse_attn_decode with sel_heads = N on that selection: the same
+ * output and, when selected / n_selected are given, the same selection. Rows of up to 64
+ * selected blocks and 4096 candidate blocks run as one kernel that keeps the selection
+ * on chip; other sizes run the two operations' kernels back to back.
+ *
+ *   dtype          QS_BF16 or QS_F32, for query, metadata and K/V alike
+ *   query ... tokens_since_update, flags, k   as qs_block_select
+ *   k_cache ... max_kv_blocks_per_req, softmax_scale   as qs_sparse_attn_decode
+ *   out            [B, H, D] in dtype
+ *   selected       [B, N, k] int32 and n_selected [B, N] int32 outputs, or both NULL
+ *   workspace      at least qs_select_attn_workspace_bytes(); 256-byte aligned
+ */
+qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                                qs_dtype dtype, const void* query,
+                                const void* maxblocks, const void* minblocks, int32_t num_meta_blocks,
+                                const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                                const void* k_cache, const void* v_cache, int32_t num_kv_blocks,
+                                const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                const int32_t* seq_lens, const int32_t* tokens_since_update,
+                                uint32_t flags, int32_t k, float softmax_scale, void* out,
+                                int32_t* selected, int32_t* n_selected,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* message for the calling thread's last failed call ("" if none) */
 const char* qs_last_error(void);

@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode"):
         assert n in names
 
 
@@ -172,6 +172,39 @@ def test_sparse_attn_workspace_size(qs):
     assert b > 0 and b % 256 == 0
     assert _attn(qs, wsb=qs.sparse_attn_workspace_bytes(0, 32, 8, 128, 8, 16)) == 0
     assert qs.sparse_attn_workspace_bytes(1, 32, 8, 128, 5, 16) == 0     # H % sel_heads != 0
+
+
+def _fused(qs, **kw):
+    a = dict(B=0, H=32, N=8, D=128, BS=128, dt=qs.QS_BF16, q=FAKE, mx=FAKE, mn=FAKE, nmeta=1, mt=FAKE, mmbpr=1,
+             kc=FAKE, vc=FAKE, nkv=64, bt=FAKE, mkbpr=64, sl=FAKE, ts=None, flags=0, k=16, scale=0.0, out=FAKE,
+             sel=None, nsel=None, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qs.lib.qs_select_attn_decode(a["B"], a["H"], a["N"], a["D"], a["BS"], a["dt"], a["q"], a["mx"], a["mn"],
+                                        a["nmeta"], a["mt"], a["mmbpr"], a["kc"], a["vc"], a["nkv"], a["bt"],
+                                        a["mkbpr"], a["sl"], a["ts"], a["flags"], a["k"], a["scale"], a["out"],
+                                        a["sel"], a["nsel"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=30), 1), (dict(k=0), 1), (dict(flags=4), 1), (dict(dt=2), 2), (dict(D=64), 2), (dict(BS=48), 2),
+    (dict(q=None), 1), (dict(vc=None), 1), (dict(out=None), 1), (dict(ws=None), 1), (dict(wsb=16), 1),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 32)), 1), (dict(sel=FAKE), 1), (dict(nsel=FAKE), 1),
+    (dict(kc=ctypes.c_void_p((1 << 20) + 4)), 1), (dict(scale=float("nan")), 1), (dict(nkv=0), 1),
+])
+def test_select_attn_rejects(qs, kw, status):
+    assert _fused(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_select_attn_decode")
+
+
+def test_select_attn_workspace_size(qs):
+    fused = qs.select_attn_workspace_bytes(128, 64, 8, 128, 2, 16, qs.QS_BF16)     # one kernel, no partials
+    split = qs.select_attn_workspace_bytes(1, 4, 1, 32, 2, 8, qs.QS_F32)          # one kernel + combine
+    two = qs.select_attn_workspace_bytes(8, 32, 8, 128, 8, 128, qs.QS_BF16)        # k > 64: two operations
+    assert fused == 256 and split > 256 and two > 8 * 8 * 128 * 4
+    assert all(x % 256 == 0 for x in (fused, split, two))
+    assert qs.select_attn_workspace_bytes(1, 30, 8, 128, 1, 8, qs.QS_BF16) == 0
+    assert qs.select_attn_workspace_bytes(1, 32, 8, 128, 1, 8, qs.QS_I8) == 0
+    assert _fused(qs, sel=FAKE, nsel=FAKE) == 0
 
 
 def test_binding_refuses_cpu_tensors(qs):

@@ -550,6 +550,101 @@ def test_sparse_attn_config3(qs, oracle, int8):
 
 
 # ------------------------------------------------------------------------------------------
+# fused selection + attention (qs_select_attn_decode)
+# ------------------------------------------------------------------------------------------
+
+FUSED_CASES = [
+    # seed, B, H, N, BS, lens, k, dtype, flags, tsmu          path taken
+    (71, 2, 8, 2, 32, [32 * 40 + 5, 32 * 7], 5, torch.float32, 0, None),         # one kernel, slot splits
+    (72, 3, 32, 8, 128, [128 * 200 + 17, 128 * 64, 0], 8, torch.bfloat16, 3, [5, 0, 0]),   # one kernel, splits
+    (73, 2, 40, 2, 64, [64 * 100 + 9, 64 * 3], 12, torch.bfloat16, 3, [9, -1]),  # G=20: two head chunks
+    (74, 2, 40, 2, 16, [16 * 200 + 1, 16 * 20], 7, torch.float32, 1, None),       # fp32 G=20: three chunks
+    (75, 2, 16, 8, 128, [128 * 600, 128 * 300 + 3], 64, torch.bfloat16, 3, [127, 0]),  # long rows: two kernels
+    (76, 1, 8, 8, 32, [32 * 64], 65, torch.bfloat16, 0, None),                    # k > 64: two kernels
+    (77, 128, 16, 8, 16, [16 * (20 + (7 * b) % 23) + b % 5 for b in range(128)], 6, torch.bfloat16, 3,
+     [b % 16 for b in range(128)]),                                               # 1024 rows: one kernel, no split
+]
+
+
+def run_fused(qs, wl, mx, mn, want_sel=True):
+    B, N, k = wl.B, wl.N, wl.k
+    sel = torch.full((B, N, k), -7, dtype=torch.int32, device=DEV) if want_sel else None
+    ns = torch.full((B, N), -7, dtype=torch.int32, device=DEV) if want_sel else None
+    ts = None if wl.tsmu is None else wl.tsmu.to(DEV)
+    out = qs.qs_select_attn_decode(wl.query.to(DEV), mx, mn, wl.meta_tables.to(DEV), wl.k_cache.to(DEV),
+                                   wl.v_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV), k,
+                                   tokens_since_update=ts, flags=wl.flags, selected=sel, n_selected=ns)
+    return out, sel, ns
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"seed{c[0]}")
+def test_select_attn_random(qs, oracle, case):
+    seed, B, H, N, BS, lens, k, dtype, flags, tsmu = case
+    say(f"select+attention seed={seed} B={B} H={H} N={N} BS={BS} k={k} dtype={dtype} flags={flags}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=dtype, tsmu=tsmu, flags=flags)
+    mx, mn = run_meta(qs, wl, sentinel=0.0)
+    out, sel, ns = run_fused(qs, wl, mx, mn)
+    out2, _, _ = run_fused(qs, wl, mx, mn, want_sel=False)
+    torch.cuda.synchronize()
+    # the output does not depend on whether the selection is also written out
+    assert torch.equal(out.view(torch.int16) if dtype == torch.bfloat16 else out.view(torch.int32),
+                       out2.view(torch.int16) if dtype == torch.bfloat16 else out2.view(torch.int32))
+    omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k, tsmu=wl.tsmu,
+                                         flags=wl.flags)
+    gsel, gns = tnp(sel), tnp(ns)
+    compare_quest(gsel, gns, osel, ons, osc, nbs_of(wl), k)
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, gsel, gns, N)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= attn_tol(dtype), f"attention err {err:.3e}"
+    # consistency with the separate operations: the same selection, bit for bit
+    s2, n2, _ = run_select(qs, wl, mx, mn, k=k, scores=False)
+    assert np.array_equal(tnp(s2), gsel) and np.array_equal(tnp(n2), gns)
+
+
+def test_select_attn_config1(qs, oracle):
+    wl = W.config1()
+    say("select+attention config1")
+    mx, mn = run_meta(qs, wl, sentinel=0.0)
+    out, sel, ns = run_fused(qs, wl, mx, mn)
+    omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k)
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs_of(wl), wl.k)
+    assert 31 in set(tnp(sel)[0, 0].tolist())                       # the planted needle block
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(sel),
+                                    tnp(ns), wl.N)
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-4
+
+
+def test_select_attn_config5_sampled(qs, oracle):
+    """Serving shape through the fused path (1024 rows, one workgroup each): selection and
+    output of sampled requests against the oracle."""
+    wl = W.config5(device=DEV)
+    say("select+attention config5 (full size)")
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=DEV)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)
+    out = qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                   wl.seq_lens, wl.k, tokens_since_update=wl.tsmu, flags=wl.flags, selected=sel,
+                                   n_selected=ns)
+    torch.cuda.synchronize()
+    reqs = [0, 51, 127]
+    sub, nbs = sub_workload(wl, reqs)
+    omx, omn = oracle.build_metadata(sub.k_cache, sub.block_tables, sub.meta_seq_lens, sub.meta_tables,
+                                     sub.num_meta_blocks)
+    osel, ons, osc = oracle.block_select(sub.query, omx, omn, sub.meta_tables, sub.seq_lens, wl.k, tsmu=sub.tsmu,
+                                         flags=sub.flags)
+    gsel, gns = tnp(sel)[reqs], tnp(ns)[reqs]
+    compare_quest(gsel, gns, osel, ons, osc, nbs, wl.k)
+    ref = oracle.sparse_attn_decode(sub.query, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens, gsel, gns,
+                                    wl.N)
+    err = np.abs(out.float().cpu().numpy()[reqs] - ref).max()
+    assert err <= 2e-2, f"attention err {err:.3e}"
+
+
+# ------------------------------------------------------------------------------------------
 # large configurations: full-size launch, outputs checked on sampled requests
 # ------------------------------------------------------------------------------------------
 

@@ -32,466 +32,36 @@
 // order (no cross-workgroup synchronisation inside a kernel).
 #include <math.h>
 
+#include "attn_dev.h"
 #include "qs_device.h"
 #include "qs_internal.h"
 
 namespace qs {
 namespace {
 
-// Split rows until the grid fills the chip for one round: the matrix-core kernel keeps
-// 4 workgroups per CU (1024 on 256 CUs), the vector kernels up to 8.
+using namespace attn;
+
 constexpr int kTargetWorkgroupsMfma = 1024;
 constexpr int kTargetWorkgroupsVec = 2048;
 constexpr int kNoSplitRows = 1024;   // rows at which each row gets one workgroup
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int D = 128;
-constexpr int PSTRIDE = D + 2;       // partial record: acc[D], max, sum
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void merge_state(float& m, float& l, float* a, int n, float m2, float l2,
-                                            const float* a2) {
-    const float M = fmaxf(m, m2);
-    if (M == -INFINITY) return;
-    const float c1 = exp2f(m - M), c2 = exp2f(m2 - M);
-    l = l * c1 + l2 * c2;
-    for (int e = 0; e < n; ++e) a[e] = a[e] * c1 + a2[e] * c2;
-    m = M;
-}
-
-struct AttnParams {
-    const uint8_t* query;
-    const uint8_t* kc;
-    const uint8_t* vc;
-    const float* ksc;
-    const float* vsc;
-    int num_kv_blocks;
-    const int32_t* bt;
-    int mkbpr;
-    const int32_t* sl;
-    const int32_t* sel;
-    const int32_t* nsel;
-    int H, N, BS, sel_heads, k;
-    int hpr, hchunks, splits, spb;
-    float scale_log2;
-    uint8_t* out;
-    float* part;
-};
-
-// result of one workgroup for head g, channel d: either the output or a partial record
-__device__ __forceinline__ void emit(const AttnParams& p, int b, int row, int hcix, int split, int hc_cap, int h0,
-                                     int g, int d, float M, float Ls, float A, bool out_bf16) {
-    if (p.splits == 1) {
-        const float v = (Ls > 0.f) ? A / Ls : 0.f;
-        const size_t o = (size_t(b) * p.H + h0 + g) * D + d;
-        if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
-        else ((float*)p.out)[o] = v;
-    } else {
-        float* rec = p.part + (((size_t(row) * p.hchunks + hcix) * p.splits + split) * hc_cap + g) * PSTRIDE;
-        rec[d] = A;
-        if (d == 0) { rec[D] = M; rec[D + 1] = Ls; }
-    }
-}
-
-// ------------------------------------------------------------------------------------
-// bf16 matrix-core kernel
-// ------------------------------------------------------------------------------------
-constexpr int kVtPitch = 80;             // bytes per V^T row in LDS: 32 tokens (64 B) + pad
-constexpr int kVtBytes = D * kVtPitch;   // one wave's V^T tile
-
-__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) {
-    u32v4 t = {v.x, v.y, v.z, v.w};
-    return __builtin_bit_cast(bf16x8, t);
-}
-
-// 128 VGPRs: four workgroups (16 waves) per CU, which the 1024-row serving batch fills
-// in one round; LDS is 40 KiB per workgroup, 160 KiB per CU.
+// the attention kernels: one workgroup per (slot split x head chunk, selection row, request)
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attn_mfma_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kVtBytes];  // 40 KiB
-
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMfmaLdsBytes];  // 40 KiB
     const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
     const int s = blockIdx.y, b = blockIdx.z;
-    const int h0 = s * p.hpr + hcix * 16;
-    const int nh = min(16, p.hpr - hcix * 16);
-    const int G = p.H / p.N;
-    const int kh = (s * p.hpr) / G;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int c16 = lane & 15, j = lane >> 4;
-
-    // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
-    bf16x8 qb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v{0u, 0u, 0u, 0u};
-        if (c16 < nh) v = ld16(p.query + ((size_t(b) * p.H + h0 + c16) * D + 32 * ks + 8 * j) * 2);
-        qb[ks] = as_bf8(v);
-    }
-
-    const int L = max(p.sl[b], 0);
-    const int nb = (L + p.BS - 1) / p.BS;
     const int row = b * p.sel_heads + s;
-    const int ns = min(max(p.nsel[row], 0), p.k);
-    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
-    const int32_t* srow = p.sel + size_t(row) * p.k;
-    const int cpb = (p.BS + 31) / 32;                 // 32-token chunks per block
-    const int nq = max(0, slot1 - slot0) * cpb;
-    const size_t tstride = size_t(p.N) * D;           // elements between tokens of one KV head
-    uint8_t* vt = lds + w * kVtBytes;
-
-    // Slot table: lane t of every wave resolves slot slot0 + t once (selection entry, then
-    // block table) into (physical block, valid tokens), and the chunk loop reads it back
-    // with v_readlane. The loop then issues only K/V loads, never waiting on a dependent
-    // lookup with K/V loads in flight. Ranges longer than a wave look up in the loop.
-    const int nsl = max(0, slot1 - slot0);
-    const bool use_tab = nsl <= kWave;
-    int tab_phys = -1, tab_nt = 0;
-    if (use_tab && lane < nsl) {
-        const int blk = srow[slot0 + lane];
-        if (blk >= 0 && blk < nb && blk < p.mkbpr) {
-            const int ph = p.bt[size_t(b) * p.mkbpr + blk];
-            if (ph >= 0 && ph < p.num_kv_blocks) {
-                tab_phys = ph;
-                tab_nt = min(p.BS, L - blk * p.BS);
-            }
-        }
-    }
-
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 o[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int q = w; q < nq; q += kWaves) {
-        const int slot = slot0 + q / cpb, cib = q % cpb;
-        int phys, nt;
-        if (use_tab) {
-            phys = __builtin_amdgcn_readlane(tab_phys, slot - slot0);
-            nt = __builtin_amdgcn_readlane(tab_nt, slot - slot0);
-            if (phys < 0) continue;
-        } else {
-            const int blk = srow[slot];
-            if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
-            phys = p.bt[size_t(b) * p.mkbpr + blk];
-            if (phys < 0 || phys >= p.num_kv_blocks) continue;
-            nt = min(p.BS, L - blk * p.BS);
-        }
-        const int tb = cib * 32;
-        if (tb >= nt) continue;
-        const uint16_t* kb = (const uint16_t*)p.kc + (size_t(phys) * p.BS * p.N + kh) * D;
-        const uint16_t* vb = (const uint16_t*)p.vc + (size_t(phys) * p.BS * p.N + kh) * D;
-
-        // K: tile tau row r = c16 is token tb + 8*(r/4) + 4*tau + r%4 (so that lane group j
-        // ends up holding tokens tb + 8j .. 8j+7 in its accumulators)
-        u32x4 kr[2][4];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            const int t = tb + 8 * (c16 >> 2) + 4 * tau + (c16 & 3);
-            const int tl = t < nt ? t : 0;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kr[tau][ks] = ld16(kb + size_t(tl) * tstride + 32 * ks + 8 * j);
-        }
-        // V: lane (c16, j) loads tokens tb + 8j + u, channels 8*c16 .. +7
-        u32x4 vr[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int t = tb + 8 * j + u;
-            const int tl = t < nt ? t : 0;
-            vr[u] = ld16(vb + size_t(tl) * tstride + 8 * c16);
-        }
-
-        // S^T (tokens x heads): lane holds tokens tb + 8j + 4*tau + i for head c16
-        f32x4 sacc[2];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[tau][ks]), qb[ks], sacc[tau], 0, 0, 0);
-        }
-        float sv[8];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int tau = e >> 2, i = e & 3;
-            const float x = sacc[tau][i] * p.scale_log2;
-            sv[e] = (tb + 8 * j + e < nt) ? x : -INFINITY;
-            cmax = fmaxf(cmax, sv[e]);
-        }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-        const float mn = fmaxf(m, cmax);
-        const float cf = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-        bf16x8 pv;
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mn);
-            const __bf16 pb = (__bf16)pe;
-            pv[e] = pb;
-            psum += (float)pb;
-        }
-        lsum = lsum * cf + psum;
-        m = mn;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] *= cf;
-
-        // V^T tile: row d = 8*c16 + e holds tokens 8j .. 8j+7 at byte 16*j
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int wsel = e >> 1;
-            uint32_t x[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const u32x4 r = vr[u];
-                x[u] = wsel == 0 ? r.x : wsel == 1 ? r.y : wsel == 2 ? r.z : r.w;
-            }
-            u32x4 t;
-            if (e & 1) {
-                t.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
-                t.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
-                t.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
-                t.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
-            } else {
-                t.x = (x[0] & 0xffffu) | (x[1] << 16);
-                t.y = (x[2] & 0xffffu) | (x[3] << 16);
-                t.z = (x[4] & 0xffffu) | (x[5] << 16);
-                t.w = (x[6] & 0xffffu) | (x[7] << 16);
-            }
-            st16(vt + (8 * c16 + e) * kVtPitch + 16 * j, t);
-        }
-        // this wave's V^T stores must land before its lanes read other lanes' rows
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // O^T (channels x heads) += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const u32x4 a = ld16(vt + (16 * dt + c16) * kVtPitch + 16 * j);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), pv, o[dt], 0, 0, 0);
-        }
-        // the next chunk overwrites the tile only after every lane has read it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-
-    // per-head sum over the four lane groups
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
-
-    // merge the four waves through LDS: red_o[w][head][channel], red_m/red_l[w][head]
-    __syncthreads();
-    float* red_o = (float*)lds;                        // 4 * 16 * 128 floats = 32 KiB
-    float* red_m = red_o + kWaves * 16 * D;
-    float* red_l = red_m + kWaves * 16;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[(w * 16 + c16) * D + 16 * dt + 4 * j + i] = o[dt][i];
-    if (j == 0) { red_m[w * 16 + c16] = m; red_l[w * 16 + c16] = lsum; }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * D; idx += kThreads) {
-        const int g = idx / D, d = idx % D;
-        if (g >= nh) continue;
-        float M = -INFINITY, Ls = 0.f, A = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww)
-            merge_state(M, Ls, &A, 1, red_m[ww * 16 + g], red_l[ww * 16 + g], &red_o[(ww * 16 + g) * D + d]);
-        emit(p, b, row, hcix, split, 16, h0, g, d, M, Ls, A, true);
-    }
+    mfma_body(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
 }
 
-// ------------------------------------------------------------------------------------
-// vector-ALU kernel (fp32 / bf16 with fp32 query / int8 KV)
-// ------------------------------------------------------------------------------------
 template <int KV, bool QBF16, int HC>
 __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
-    constexpr int ke = KV == 0 ? 4 : (KV == 1 ? 2 : 1);
-    constexpr int qe = QBF16 ? 2 : 4;
-    constexpr int LPR = D * ke / 16;    // lanes per K/V row
-    constexpr int EPL = 16 / ke;        // channels per lane
-    constexpr int NG = kThreads / LPR;  // independent lane groups per workgroup
-    constexpr int U = 2;                // tokens in flight per group
-
-    __shared__ float red_m[kWaves][HC];
-    __shared__ float red_l[kWaves][HC];
-    __shared__ float red_a[kWaves][HC][D];
-
+    __shared__ float red[vec_red_floats<HC>()];
     const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
     const int s = blockIdx.y, b = blockIdx.z;
-    const int h0 = s * p.hpr + hcix * HC;
-    const int nh = min(HC, p.hpr - hcix * HC);
-    const int G = p.H / p.N;
-    const int kh = (s * p.hpr) / G;
-    const int tid = threadIdx.x, lr = tid % LPR, grp = tid / LPR;
-
-    // query: fp32 (pre-scaled by softmax_scale * log2 e) or int8 codes
-    float qf[HC][EPL];
-    int32_t q8[HC][EPL / 4 > 0 ? EPL / 4 : 1];
-    float qscale[HC];
-#pragma unroll
-    for (int g = 0; g < HC; ++g) {
-        const int hh = h0 + (g < nh ? g : 0);
-        const uint8_t* qp = p.query + (size_t(b) * p.H + hh) * D * qe;
-        float x[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int d = lr * EPL + e;
-            x[e] = QBF16 ? bf16_to_f32(((const uint16_t*)qp)[d]) : ((const float*)qp)[d];
-        }
-        if constexpr (KV == 2) {
-            float amax = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-            amax = group_max<LPR>(amax);
-            const float sq = amax / 127.0f;
-            qscale[g] = sq * p.scale_log2;
-#pragma unroll
-            for (int wd = 0; wd < EPL / 4; ++wd) {
-                uint32_t packed = 0;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float r = 0.f;
-                    if (sq != 0.f) r = fminf(fmaxf(rintf(x[4 * wd + jj] / sq), -127.f), 127.f);
-                    packed |= (uint32_t(int32_t(r)) & 0xffu) << (8 * jj);
-                }
-                q8[g][wd] = int32_t(packed);
-            }
-        } else {
-            qscale[g] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) qf[g][e] = x[e] * p.scale_log2;
-        }
-    }
-
-    const int L = max(p.sl[b], 0);
-    const int nb = (L + p.BS - 1) / p.BS;
     const int row = b * p.sel_heads + s;
-    const int ns = min(max(p.nsel[row], 0), p.k);
-    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
-    const int32_t* srow = p.sel + size_t(row) * p.k;
-    const size_t tok_bytes = size_t(p.N) * D * ke;
-
-    float m[HC], l[HC], acc[HC][EPL];
-#pragma unroll
-    for (int g = 0; g < HC; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-    }
-
-    for (int slot = slot0; slot < slot1; ++slot) {
-        const int blk = srow[slot];
-        if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
-        const int phys = p.bt[size_t(b) * p.mkbpr + blk];
-        if (phys < 0 || phys >= p.num_kv_blocks) continue;
-        const int nt = min(p.BS, L - blk * p.BS);
-        const size_t tok0 = size_t(phys) * p.BS;
-        const uint8_t* kb = p.kc + (tok0 * p.N + kh) * D * ke + lr * 16;
-        const uint8_t* vb = p.vc + (tok0 * p.N + kh) * D * ke + lr * 16;
-        for (int t0 = 0; t0 < nt; t0 += NG * U) {
-            u32x4 kv[U], vv[U];
-            float ks[U], vs[U];
-            bool ok[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int t = t0 + u * NG + grp;
-                ok[u] = t < nt;
-                const int tt = ok[u] ? t : 0;
-                kv[u] = ld16(kb + size_t(tt) * tok_bytes);
-                vv[u] = ld16(vb + size_t(tt) * tok_bytes);
-                if constexpr (KV == 2) {
-                    ks[u] = p.ksc[(tok0 + tt) * p.N + kh];
-                    vs[u] = p.vsc[(tok0 + tt) * p.N + kh];
-                } else {
-                    ks[u] = vs[u] = 1.f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
-                const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-                float vf[EPL];
-                if constexpr (KV == 0) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) vf[jj] = __uint_as_float(vw[jj]);
-                } else if constexpr (KV == 1) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) { vf[2 * jj] = bf_lo(vw[jj]); vf[2 * jj + 1] = bf_hi(vw[jj]); }
-                } else {
-#pragma unroll
-                    for (int jj = 0; jj < 16; ++jj) vf[jj] = float(int8_t(vw[jj / 4] >> (8 * (jj % 4)))) * vs[u];
-                }
-#pragma unroll
-                for (int g = 0; g < HC; ++g) {
-                    float sc;
-                    if constexpr (KV == 2) {
-                        int dot = 0;
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) dot = __builtin_amdgcn_sdot4(q8[g][jj], int32_t(kw[jj]), dot, false);
-                        dot = group_sum_i<LPR>(dot);
-                        sc = float(dot) * (qscale[g] * ks[u]);
-                    } else {
-                        float pp = 0.f;
-                        if constexpr (KV == 0) {
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) pp += qf[g][jj] * __uint_as_float(kw[jj]);
-                        } else {
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj)
-                                pp += qf[g][2 * jj] * bf_lo(kw[jj]) + qf[g][2 * jj + 1] * bf_hi(kw[jj]);
-                        }
-                        sc = group_sum<LPR>(pp);
-                    }
-                    if (ok[u]) {
-                        const float mn = fmaxf(m[g], sc);
-                        const float cf = exp2f(m[g] - mn);
-                        const float pw = exp2f(sc - mn);
-                        l[g] = l[g] * cf + pw;
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * cf + pw * vf[e];
-                        m[g] = mn;
-                    }
-                }
-            }
-        }
-    }
-
-    // merge the lane groups of each wave (same lr = same channels)
-#pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) {
-#pragma unroll
-        for (int g = 0; g < HC; ++g) {
-            const float m2 = __shfl_xor(m[g], o, kWave);
-            const float l2 = __shfl_xor(l[g], o, kWave);
-            float a2[EPL];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(acc[g][e], o, kWave);
-            merge_state(m[g], l[g], acc[g], EPL, m2, l2, a2);
-        }
-    }
-    const int w = wave_id();
-    if (lane_id() < LPR) {
-#pragma unroll
-        for (int g = 0; g < HC; ++g) {
-            if (lr == 0) { red_m[w][g] = m[g]; red_l[w][g] = l[g]; }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) red_a[w][g][lr * EPL + e] = acc[g][e];
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < HC * D; idx += kThreads) {
-        const int g = idx / D, d = idx % D;
-        if (g >= nh) continue;
-        float M = -INFINITY, Ls = 0.f, A = 0.f;
-        for (int ww = 0; ww < kWaves; ++ww) merge_state(M, Ls, &A, 1, red_m[ww][g], red_l[ww][g], &red_a[ww][g][d]);
-        emit(p, b, row, hcix, split, HC, h0, g, d, M, Ls, A, QBF16);
-    }
+    vec_body<KV, QBF16, HC>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], red);
 }
 
 // ------------------------------------------------------------------------------------
@@ -591,10 +161,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t
     } else {
         if (qb) launch_vec<2, true>(prm, pl, grid, s); else launch_vec<2, false>(prm, pl, grid, s);
     }
-    if (pl.splits > 1) {
-        const unsigned per_req = unsigned((size_t(a.H) * D + kThreads - 1) / kThreads);
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(a.B)), dim3(kThreads), 0, s, prm, pl.hc, qb);
-    }
+    if (pl.splits > 1) return attn::launch_combine(prm, a.B, pl.hc, qb, s);
+    return hipGetLastError();
+}
+
+hipError_t attn::launch_combine(const AttnParams& p, int B, int hc_cap, bool out_bf16, hipStream_t s) {
+    const unsigned per_req = unsigned((size_t(p.H) * D + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(B)), dim3(kThreads), 0, s, p, hc_cap, out_bf16);
     return hipGetLastError();
 }
 

@@ -115,4 +115,14 @@ struct AttnArgs {
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 
+// ---- fused select + attention -------------------------------------------------------
+struct FusedPlan {
+    bool fused;        // one kernel (selection into LDS, then attention); else the two paths
+    SelectPlan sel;
+    AttnPlan attn;
+    size_t sel_off, attn_off, idx_off, nidx_off, bytes;  // workspace regions
+};
+FusedPlan plan_select_attn(int B, int H, int N, int BS, int mmbpr, int k, int dtype);
+hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const FusedPlan& p, hipStream_t st);
+
 }  // namespace qs

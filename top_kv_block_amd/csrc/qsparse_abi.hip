@@ -238,4 +238,58 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     return hip_status(qs::launch_sparse_attn(a, plan, (hipStream_t)stream), fn);
 }
 
+size_t qs_select_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t block_size,
+                                      int32_t max_meta_blocks_per_req, int32_t k, qs_dtype dtype) {
+    if (B < 0 || N < 1 || H < N || H % N != 0 || block_size < 1 || max_meta_blocks_per_req < 1 || k < 1 ||
+        (dtype != QS_F32 && dtype != QS_BF16))
+        return 0;
+    return qs::plan_select_attn(B, H, N, block_size, max_meta_blocks_per_req, k, int(dtype)).bytes;
+}
+
+qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
+                                const void* query, const void* maxblocks, const void* minblocks,
+                                int32_t num_meta_blocks, const int32_t* metadata_block_tables,
+                                int32_t max_meta_blocks_per_req, const void* k_cache, const void* v_cache,
+                                int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags,
+                                int32_t k, float softmax_scale, void* out, int32_t* selected, int32_t* n_selected,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "qs_select_attn_decode";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (dtype != QS_F32 && dtype != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32 or QS_BF16", fn);
+    if (!query || !maxblocks || !minblocks || !metadata_block_tables || !k_cache || !v_cache || !block_tables ||
+        !seq_lens || !out || !workspace)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if ((selected == nullptr) != (n_selected == nullptr))
+        return fail(QS_ERR_INVALID, "%s: selected and n_selected must both be given or both be NULL", fn);
+    if (!aligned16(query) || !aligned16(maxblocks) || !aligned16(minblocks) || !aligned16(k_cache) ||
+        !aligned16(v_cache))
+        return fail(QS_ERR_INVALID, "%s: query, metadata and K/V caches must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (flags & ~(uint32_t)(QS_FORCE_SINK | QS_FORCE_WINDOW))
+        return fail(QS_ERR_INVALID, "%s: flags may only hold QS_FORCE_SINK | QS_FORCE_WINDOW", fn);
+    if (k < 1) return fail(QS_ERR_INVALID, "%s: k=%d must be >= 1", fn, k);
+    if (num_meta_blocks < 1 || max_meta_blocks_per_req < 1 || num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: block counts and table widths must be >= 1", fn);
+    if ((long long)max_meta_blocks_per_req * block_size > (1LL << 24))
+        return fail(QS_ERR_UNSUPPORTED, "%s: more than 2^24 blocks per request", fn);
+    if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
+    const qs::FusedPlan plan = qs::plan_select_attn(B, H, N, block_size, max_meta_blocks_per_req, k, int(dtype));
+    if (workspace_bytes < plan.bytes)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
+    if ((long long)plan.attn.splits * plan.attn.hchunks > 0x7fffffffLL)
+        return fail(QS_ERR_INVALID, "%s: grid too large", fn);
+    if (B == 0) return ok();
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
+    qs::SelectArgs sa{B, H, N, D, block_size, dtype == QS_BF16, query, maxblocks, minblocks, num_meta_blocks,
+                      metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
+                      selected, n_selected, nullptr, workspace};
+    qs::AttnArgs aa{B, H, N, D, block_size, int(dtype), int(dtype), query, k_cache, v_cache, nullptr, nullptr,
+                    num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, selected, n_selected, N, k,
+                    scale, out, workspace};
+    return hip_status(qs::launch_select_attn(sa, aa, plan, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

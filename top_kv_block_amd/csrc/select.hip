@@ -22,282 +22,19 @@
 // ties"). Output is written in ascending block order.
 #include <math.h>
 
-#include <type_traits>
-
 #include "qs_device.h"
 #include "qs_internal.h"
+#include "select_dev.h"
 
 namespace qs {
 namespace {
 
+using namespace sel;
+
 constexpr int kChunk = 64;             // blocks per scoring workgroup in split mode
 constexpr int kRowModeRows = 512;      // rows at which one workgroup per row fills the chip
 constexpr int kRowModeMaxCap = 256;    // rows this short always use row mode
-constexpr int kLdsScoreCap = 8192;     // row mode keeps up to this many scores in LDS
-constexpr int kMtStageCap = 256;       // metadata-table rows up to this long are staged in LDS
-static_assert(kMtStageCap <= kThreads, "one staging load per thread");
-static_assert(kChunk / 16 + 2 <= kMtStageCap, "a split-mode chunk's table entries fit the stage");
-
-struct Forced {
-    int w_lo;   // blocks >= w_lo are forced (window); nb when none
-    bool sink;  // block 0 forced
-    int count;
-    __device__ bool has(int i) const { return i >= w_lo || (sink && i == 0); }
-};
-
-__device__ __forceinline__ Forced forced_set(int L, int nb, int BS, int k, const int32_t* tsmu, int b,
-                                             uint32_t flags) {
-    Forced f{nb, false, 0};
-    const bool active = (tsmu == nullptr) || (tsmu[b] >= 0);
-    if (!active || nb <= 0) return f;
-    if (flags & 2u) {  // window: the last block and every block without metadata
-        const long long u = tsmu ? tsmu[b] : 0;
-        const long long num = (long long)L - u;
-        long long n_meta = (num >= 0) ? num / BS : -((-num + BS - 1) / BS);
-        if (n_meta < 0) n_meta = 0;
-        if (n_meta > nb - 1) n_meta = nb - 1;
-        int lo = int(n_meta);
-        if (lo < nb - k) lo = nb - k;
-        f.w_lo = lo;
-        f.count = nb - lo;
-    }
-    if ((flags & 1u) && f.count < k && f.w_lo > 0) {
-        f.sink = true;
-        f.count += 1;
-    }
-    return f;
-}
-
-struct RowInfo {
-    int L, nb;
-    Forced F;
-};
-
-__device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* tsmu, uint32_t flags, int k, int b,
-                                            int BS, int cap) {
-    RowInfo r;
-    r.L = max(sl[b], 0);
-    r.nb = min((r.L + BS - 1) / BS, cap);
-    r.F = forced_set(r.L, r.nb, BS, k, tsmu, b, flags);
-    return r;
-}
-
-// Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
-// skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
-// qstage: kThreads 16-byte LDS slots used to stage the group's query rows; mt_stage:
-// kMtStageCap ints of LDS for the metadata-table entries of [i0, i_end) (MT_LDS: the
-// caller guarantees they fit). Contains a barrier: every thread of the workgroup must
-// call it.
-template <bool BF16, bool MT_LDS>
-__device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
-                                            const uint8_t* __restrict__ minb, int num_meta,
-                                            const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
-                                            int n, const Forced& F, int i0, int i_end, float* dst, bool nan_forced,
-                                            u32x4* qstage, int32_t* mt_stage) {
-    constexpr int esize = BF16 ? 2 : 4;
-    constexpr int D = 128;
-    constexpr int LPR = D * esize / 16;  // lanes per metadata row
-    constexpr int EPL = 16 / esize;      // channels per lane
-    constexpr int RPP = kThreads / LPR;  // rows per pass
-    constexpr int U = 4;                 // passes per batch
-    const int tid = threadIdx.x;
-    const int lr = tid % LPR, slot = tid / LPR;
-    const int G = H / N;
-    const size_t row_bytes = size_t(N) * D * esize;
-
-    // One batch = U passes of RPP rows; the next batch's loads are issued before the
-    // current batch is consumed. With MT_LDS the range's metadata-table entries are
-    // staged in LDS so that the lookups of later batches are LDS reads (a global lookup
-    // would have to wait for every load in flight before it); batch 0 looks up in global
-    // memory while the staging loads are in flight.
-    const int mbase = i0 / BS;
-    auto issue = [&](int base, u32x4 (&vmx)[U], u32x4 (&vmn)[U], bool (&ok)[U], auto from_lds) {
-        int mrow[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base + u * RPP + slot;
-            ok[u] = i < i_end && !F.has(i);
-            if constexpr (decltype(from_lds)::value)
-                mrow[u] = ok[u] ? mt_stage[i / BS - mbase] : 0;
-            else
-                mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = base + u * RPP + slot;
-            ok[u] = ok[u] && mrow[u] >= 0 && mrow[u] < num_meta;
-            // rows that are not scored read the first row (always valid) and are masked
-            const size_t off = ok[u] ? (size_t(mrow[u]) * BS + (i % BS)) * row_bytes + size_t(n) * D * esize + lr * 16
-                                     : size_t(lr) * 16;
-            vmx[u] = ld16(maxb + off);
-            vmn[u] = ld16(minb + off);
-        }
-    };
-
-    // the group's query rows: one 16-byte piece per thread, loaded ahead of batch 0
-    const int npieces = G * LPR;
-    const bool staged = npieces <= kThreads;
-    u32x4 qpiece{0u, 0u, 0u, 0u};
-    if (staged && tid < npieces)
-        qpiece = ld16(query + ((size_t(b) * H + size_t(n) * G + tid / LPR) * D + (tid % LPR) * EPL) * esize);
-    const int n_ent = i0 < i_end ? (i_end - 1) / BS - mbase + 1 : 0;  // table entries of the range
-    int32_t mt_piece = 0;
-    if (MT_LDS && tid < n_ent) mt_piece = mt[size_t(b) * mmbpr + mbase + tid];
-    u32x4 vmx[U], vmn[U];
-    bool ok[U];
-    if (i0 < i_end) issue(i0, vmx, vmn, ok, std::false_type{});
-    if (MT_LDS && tid < n_ent) mt_stage[tid] = mt_piece;
-
-    // grouped query for this lane's channels: mean over the group's G heads
-    float gq[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) gq[e] = 0.f;
-    auto add_piece = [&](const u32x4& v) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (BF16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { gq[2 * j] += bf_lo(w[j]); gq[2 * j + 1] += bf_hi(w[j]); }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gq[j] += __uint_as_float(w[j]);
-        }
-    };
-    if (staged && tid < npieces) qstage[tid] = qpiece;
-    __syncthreads();  // query pieces and the table row are in LDS
-    if (staged) {
-        for (int g = 0; g < G; ++g) add_piece(qstage[g * LPR + lr]);
-    } else {
-        for (int g = 0; g < G; ++g)
-            add_piece(ld16(query + ((size_t(b) * H + size_t(n) * G + g) * D + lr * EPL) * esize));
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) gq[e] = gq[e] / float(G);
-
-    auto consume = [&](int base, const u32x4 (&vmx)[U], const u32x4 (&vmn)[U], const bool (&ok)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t a[4] = {vmx[u].x, vmx[u].y, vmx[u].z, vmx[u].w};
-            const uint32_t z[4] = {vmn[u].x, vmn[u].y, vmn[u].z, vmn[u].w};
-            float part = 0.f;
-            if constexpr (BF16) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    part += fmaxf(gq[2 * j] * bf_lo(a[j]), gq[2 * j] * bf_lo(z[j]));
-                    part += fmaxf(gq[2 * j + 1] * bf_hi(a[j]), gq[2 * j + 1] * bf_hi(z[j]));
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    part += fmaxf(gq[j] * __uint_as_float(a[j]), gq[j] * __uint_as_float(z[j]));
-            }
-            const float s = group_sum<LPR>(part);
-            const int i = base + u * RPP + slot;
-            if (lr == 0 && i < i_end) {
-                if (ok[u])
-                    dst[i] = s;
-                else if (!F.has(i))
-                    dst[i] = -INFINITY;
-                else if (nan_forced)
-                    dst[i] = __builtin_nanf("");
-            }
-        }
-    };
-
-    // ping-pong over two register sets, so a batch's loads are in flight while the other
-    // batch is consumed, with no register copies between them
-    constexpr int STEP = RPP * U;
-    u32x4 wmx[U], wmn[U];
-    bool wok[U];
-    for (int base = i0; base < i_end; base += 2 * STEP) {
-        const bool more1 = base + STEP < i_end;
-        if (more1) issue(base + STEP, wmx, wmn, wok, std::integral_constant<bool, MT_LDS>{});
-        consume(base, vmx, vmn, ok);
-        if (base + 2 * STEP < i_end) issue(base + 2 * STEP, vmx, vmn, ok, std::integral_constant<bool, MT_LDS>{});
-        if (more1) consume(base + STEP, wmx, wmn, wok);
-    }
-}
-
-// Exact top-k of a row from its scores (LDS or global); writes selected / n_selected.
-// The radix select finds the k-th best key T; then each thread takes a contiguous run of
-// blocks, and two block-wide scans (equal-to-T ranks, then output positions) keep every
-// block above T and the lowest-index blocks equal to T, written in ascending order.
-__device__ __forceinline__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out,
-                                          int32_t* n_out, uint32_t* hist, int* sh, int* wsum) {
-    const int tid = threadIdx.x;
-    const int R = max(0, min(k, nb) - F.count);  // fill picks
-    const int nc = nb - F.count;                   // fill candidates
-    const bool take_all = R >= nc;
-    const bool radix = R > 0 && !take_all;
-    uint32_t T = 0;
-    int need_eq = 0;
-    if (radix) {
-        auto kf = [&](int i, uint32_t& key) -> bool {
-            if (F.has(i)) return false;
-            key = f2key(scores[i]);
-            return true;
-        };
-        T = block_radix_select(nb, R, kf, hist, sh, need_eq);
-    }
-    const int E = (nb + kThreads - 1) / kThreads;  // blocks per thread, contiguous
-    const int i0 = min(nb, tid * E), i1 = min(nb, i0 + E);
-    int eq_off = 0, tot;
-    if (radix) {
-        int eq_local = 0;
-        for (int i = i0; i < i1; ++i) eq_local += (!F.has(i) && f2key(scores[i]) == T) ? 1 : 0;
-        eq_off = block_excl_scan(eq_local, wsum, tot);
-    }
-    int pick_local = 0;
-    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
-        bool pick = F.has(i);
-        if (!pick && R > 0) {
-            if (take_all) {
-                pick = true;
-            } else {
-                const uint32_t key = f2key(scores[i]);
-                pick = key > T || (key == T && eq_seen < need_eq);
-                eq_seen += key == T ? 1 : 0;
-            }
-        }
-        pick_local += pick ? 1 : 0;
-    }
-    int npick;
-    int pos = block_excl_scan(pick_local, wsum, npick);
-    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
-        bool pick = F.has(i);
-        if (!pick && R > 0) {
-            if (take_all) {
-                pick = true;
-            } else {
-                const uint32_t key = f2key(scores[i]);
-                pick = key > T || (key == T && eq_seen < need_eq);
-                eq_seen += key == T ? 1 : 0;
-            }
-        }
-        if (pick) {
-            if (pos < k) out[pos] = i;
-            ++pos;
-        }
-    }
-    for (int j = npick + tid; j < k; j += kThreads) out[j] = -1;
-    if (tid == 0) *n_out = min(npick, k);
-}
-
-struct SelParams {
-    const uint8_t* query;
-    const uint8_t* maxb;
-    const uint8_t* minb;
-    int num_meta;
-    const int32_t* mt;
-    int mmbpr;
-    const int32_t* sl;
-    const int32_t* tsmu;
-    uint32_t flags;
-    int k, H, N, BS;
-    int32_t* selected;
-    int32_t* n_selected;
-    float* dbg_scores;
-    float* ws_scores;
-};
+static_assert(kChunk / 16 + 2 <= sel::kMtStageCap, "a split-mode chunk's table entries fit the stage");
 
 // row mode: one workgroup per (KV head, request); MT_LDS when the request's metadata
 // table row fits in LDS

@@ -23,7 +23,8 @@ QS_FORCE_SINK, QS_FORCE_WINDOW, QS_RECENCY = 1, 2, 4
 EXPORTS = (
     "qs_build_metadata", "qs_update_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
     "qs_probe_select_workspace_bytes", "qs_probe_select",
-    "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_last_error", "qs_version",
+    "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_select_attn_workspace_bytes",
+    "qs_select_attn_decode", "qs_last_error", "qs_version",
 )
 
 
@@ -54,8 +55,12 @@ def _load():
     lib.qs_sparse_attn_workspace_bytes.restype = sz
     lib.qs_sparse_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, P, P, i32,
                                           P, i32, P, P, P, i32, i32, ctypes.c_float, P, P, sz, P]
+    lib.qs_select_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.qs_select_attn_workspace_bytes.restype = sz
+    lib.qs_select_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, i32, P,
+                                          i32, P, P, u32, i32, ctypes.c_float, P, P, P, P, sz, P]
     for f in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
@@ -138,7 +143,7 @@ def workspace(nbytes, device, op):
 
 
 # ------------------------------------------------------------------------------------------
-# the four operations (names and argument meaning as in include/qsparse.h)
+# the operations (names and argument meaning as in include/qsparse.h)
 # ------------------------------------------------------------------------------------------
 
 def _meta_shapes(k_cache, block_tables, seq_lens, metadata_block_tables, maxblocks, minblocks):
@@ -297,4 +302,49 @@ def qs_sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selec
                                      _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(selected),
                                      _ptr(n_selected), int(sel_heads), int(k), float(softmax_scale), _ptr(out),
                                      _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype):
+    return lib.qs_select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype)
+
+
+def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                          seq_lens, k, tokens_since_update=None, flags=0, softmax_scale=0.0, out=None,
+                          selected=None, n_selected=None, workspace_buf=None):
+    """Quest selection and attention over the selected blocks in one call (qs_block_select
+    then qs_sparse_attn_decode with one selection row per KV head). Returns out [B, H, D];
+    pass selected [B, N, k] / n_selected [B, N] to receive the selection too."""
+    dev = _dev(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables, seq_lens,
+               tokens_since_update, out, selected, n_selected)
+    for n, t in (("metadata_block_tables", metadata_block_tables), ("block_tables", block_tables),
+                 ("seq_lens", seq_lens), ("tokens_since_update", tokens_since_update), ("selected", selected),
+                 ("n_selected", n_selected)):
+        _i32(t, n)
+    B, H, D = query.shape
+    nmeta, BS, N, D2 = maxblocks.shape
+    nkv = k_cache.shape[0]
+    mmbpr = metadata_block_tables.shape[1]
+    _need(D2 == D and H % N == 0, "query and metadata shapes disagree")
+    _need(maxblocks.shape == minblocks.shape and maxblocks.dtype == minblocks.dtype == query.dtype,
+          "maxblocks/minblocks must match each other and the query dtype")
+    _need(k_cache.shape[1:] == maxblocks.shape[1:] and v_cache.shape == k_cache.shape and
+          k_cache.dtype == v_cache.dtype == query.dtype, "K/V caches must be [num_kv_blocks, BS, N, D] in the query dtype")
+    _need((selected is None) == (n_selected is None), "give both selected and n_selected, or neither")
+    if selected is not None:
+        _need(selected.numel() >= B * N * k and n_selected.numel() >= B * N, "selected must hold [B, N, k]")
+    for name, t in (("metadata_block_tables", metadata_block_tables), ("block_tables", block_tables),
+                    ("seq_lens", seq_lens), ("tokens_since_update", tokens_since_update)):
+        _rows(t, B, name)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=query.dtype, device=dev)
+    _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
+    dt = _dtype_code(query)
+    nbytes = select_attn_workspace_bytes(B, H, N, BS, mmbpr, k, dt)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select_attn")
+    _check(lib.qs_select_attn_decode(B, H, N, D, BS, dt, _ptr(query), _ptr(maxblocks), _ptr(minblocks), nmeta,
+                                     _ptr(metadata_block_tables), mmbpr, _ptr(k_cache), _ptr(v_cache), nkv,
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                                     _ptr(tokens_since_update), int(flags), int(k), float(softmax_scale), _ptr(out),
+                                     _ptr(selected), _ptr(n_selected), _ptr(ws), ws.numel(), _stream(dev)))
     return out
