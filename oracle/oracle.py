@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qs_oracle.c")
 LIB = os.path.join(HERE, "libqsoracle.so")
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, F16 = 0, 1, 2, 3
 FORCE_SINK, FORCE_WINDOW, RECENCY = 1, 2, 4
 
 
@@ -51,6 +51,8 @@ def lib():
         L.qso_sparse_attn_decode.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, i, P, i, P, P, P, i, i,
                                              ctypes.c_double, P]
         L.qso_quantize_row_i8.argtypes = [P, i, P, P]
+        L.qso_widen.argtypes = [i, P, i, P]
+        L.qso_widen.restype = None
         for f in (L.qso_build_metadata, L.qso_block_select, L.qso_probe_select, L.qso_sparse_attn_decode):
             f.restype = ctypes.c_int
         L.qso_quantize_row_i8.restype = None
@@ -83,6 +85,8 @@ def _dtype_code(a) -> int:
         return BF16
     if a.dtype == np.int8:
         return I8
+    if a.dtype == np.float16:
+        return F16
     raise TypeError(f"unsupported dtype {a.dtype}")
 
 
@@ -201,6 +205,14 @@ def sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selected
                                       _p(sel), _p(nsel), sel_heads, k, float(softmax_scale), _p(out))
     _check(rc, "sparse_attn_decode")
     return out
+
+
+def widen(a):
+    """The oracle's exact widening of stored elements (f32, bf16 bits, f16, int8) to float64."""
+    a = np.ascontiguousarray(_np(a))
+    out = np.empty(a.size, np.float64)
+    lib().qso_widen(_dtype_code(a), _p(a), a.size, _p(out))
+    return out.reshape(a.shape)
 
 
 def quantize_row_i8(x):

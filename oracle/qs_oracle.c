@@ -19,7 +19,8 @@
  * the path must reproduce bit for bit are computed in the precision the path uses:
  * max/min of stored keys (exact), the fp32 running sum of prefill importance per block
  * ([P1] section 2 probe loop accumulates a float per block), and the fp32 int8
- * quantiser of the query. bf16 values are widened exactly (bits << 16).
+ * quantiser of the query. bf16 values are widened exactly (bits << 16); IEEE binary16
+ * values are decoded exactly from their sign, exponent and fraction fields.
  *
  * Readings where the pages are silent or ambiguous are marked "reading:" below.
  *
@@ -31,7 +32,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { QSO_F32 = 0, QSO_BF16 = 1, QSO_I8 = 2 };
+enum { QSO_F32 = 0, QSO_BF16 = 1, QSO_I8 = 2, QSO_F16 = 3 };
 enum { QSO_FORCE_SINK = 1u, QSO_FORCE_WINDOW = 2u, QSO_RECENCY = 4u };
 enum { QSO_OK = 0, QSO_BAD = -1 };
 
@@ -46,11 +47,32 @@ static float bf16_bits_to_float(uint16_t h) {
     return f;
 }
 
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0
+ * holds zeros and subnormals (fraction * 2^-24), exponent 31 infinities and NaNs. Every
+ * binary16 value is exactly representable as a float. */
+static float f16_bits_to_float(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    float v;
+    if (e == 0) v = ldexpf((float)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexpf((float)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+static int is_half(int dtype) { return dtype == QSO_BF16 || dtype == QSO_F16; }
+static int is_float(int dtype) { return dtype == QSO_F32 || is_half(dtype); }
+
 /* value of element idx of an array of the given dtype, as float (exact widening) */
 static float elem_f(const void* base, int dtype, size_t idx) {
     if (dtype == QSO_F32) return ((const float*)base)[idx];
     if (dtype == QSO_BF16) return bf16_bits_to_float(((const uint16_t*)base)[idx]);
+    if (dtype == QSO_F16) return f16_bits_to_float(((const uint16_t*)base)[idx]);
     return (float)((const int8_t*)base)[idx];
+}
+
+/* the element widening above, exported so that tests can pin it against a library decoder */
+void qso_widen(int dtype, const void* in, int n, double* out) {
+    for (int i = 0; i < n; ++i) out[i] = (double)elem_f(in, dtype, (size_t)i);
 }
 
 static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -131,7 +153,7 @@ int qso_build_metadata(int B, int N, int D, int BS, int dtype,
                        const int32_t* seq_lens,
                        const int32_t* meta_tables, int mmbpr,
                        void* maxb, void* minb, int num_meta_blocks) {
-    if (dtype != QSO_F32 && dtype != QSO_BF16) return QSO_BAD;
+    if (!is_float(dtype)) return QSO_BAD;
     const size_t row = (size_t)N * D;
     for (int b = 0; b < B; ++b) {
         const int32_t L = seq_lens[b];
@@ -170,7 +192,7 @@ int qso_update_metadata(int B, int N, int D, int BS, int dtype,
                         const int32_t* seq_lens, const int32_t* first_block, int max_new,
                         const int32_t* meta_tables, int mmbpr,
                         void* maxb, void* minb, int num_meta_blocks) {
-    if (dtype != QSO_F32 && dtype != QSO_BF16) return QSO_BAD;
+    if (!is_float(dtype)) return QSO_BAD;
     if (max_new < 1) return QSO_BAD;
     for (int b = 0; b < B; ++b) {
         const int32_t L = seq_lens[b];
@@ -246,7 +268,7 @@ int qso_block_select(int B, int H, int N, int D, int BS, int dtype,
                      const int32_t* seq_lens, const int32_t* tsmu,
                      unsigned flags, int k,
                      int32_t* selected, int32_t* n_selected, double* scores) {
-    if (dtype != QSO_F32 && dtype != QSO_BF16) return QSO_BAD;
+    if (!is_float(dtype)) return QSO_BAD;
     if (N <= 0 || H % N != 0 || k < 1) return QSO_BAD;
     const int G = H / N;
     const int cap = mmbpr * BS;
@@ -358,7 +380,7 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
                      int n_probe, int k, unsigned flags,
                      int32_t* selected, int32_t* n_selected,
                      double* probe_out, float* imp_out, int32_t* n_imp_out, int8_t* kind_out) {
-    if ((q_dtype != QSO_F32 && q_dtype != QSO_BF16) || (kv_dtype != QSO_F32 && kv_dtype != QSO_BF16))
+    if (!is_float(q_dtype) || !is_float(kv_dtype))
         return QSO_BAD;
     if (N <= 0 || H % N != 0 || k < 1) return QSO_BAD;
     const int G = H / N;
@@ -516,8 +538,8 @@ int qso_sparse_attn_decode(int B, int H, int N, int D, int BS, int q_dtype, int 
                            const int32_t* seq_lens,
                            const int32_t* selected, const int32_t* n_selected,
                            int sel_heads, int k, double softmax_scale, double* out) {
-    if (q_dtype != QSO_F32 && q_dtype != QSO_BF16) return QSO_BAD;
-    if (kv_dtype != QSO_F32 && kv_dtype != QSO_BF16 && kv_dtype != QSO_I8) return QSO_BAD;
+    if (!is_float(q_dtype)) return QSO_BAD;
+    if (!is_float(kv_dtype) && kv_dtype != QSO_I8) return QSO_BAD;
     if (N <= 0 || H % N != 0 || sel_heads <= 0 || H % sel_heads != 0 || sel_heads % N != 0) return QSO_BAD;
     if (kv_dtype == QSO_I8 && (k_scale == NULL || v_scale == NULL)) return QSO_BAD;
     const int G = H / N;

@@ -31,7 +31,7 @@ def _all_blocks(wl):
     return sel, ns
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_all_blocks_selected_is_dense_attention(oracle, dtype):
     lens = [3 * 32 + 11, 5 * 32, 1]
     wl = W.random_case(41, 3, 8, 2, 32, lens, k=8, dtype=dtype)
@@ -145,3 +145,22 @@ def test_bf16_is_exact_widening(oracle):
     b = oracle.sparse_attn_decode(wl.query.float(), wl.k_cache.float(), wl.v_cache.float(), wl.block_tables,
                                   wl.seq_lens, sel, ns, 2)
     assert np.array_equal(a, b)
+
+
+def test_widening_matches_library_decoders(oracle):
+    """Every stored element the oracle reads is widened exactly: all 65536 binary16 and
+    bfloat16 bit patterns against numpy's and torch's own conversions, and int8."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    got = oracle.widen(h)
+    want = h.astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))      # -0 stays -0
+    bf = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    got = oracle.widen(bf)
+    want = bf.float().double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], want[~nan])
+    i8 = np.arange(-128, 128, dtype=np.int8)
+    assert np.array_equal(oracle.widen(i8), i8.astype(np.float64))

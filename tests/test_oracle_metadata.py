@@ -22,10 +22,10 @@ def _as_float(a):
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32)
-    return a
+    return a.astype(np.float32) if a.dtype == np.float16 else a
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("BS", [16, 32])
 def test_metadata_equals_library_amax_amin(oracle, dtype, BS):
     lens = [0, 1, BS - 1, BS, 3 * BS + 5, BS * BS + 2 * BS + 7]  # empty, tiny, ragged, >1 meta block
@@ -84,7 +84,7 @@ def test_metadata_single_token_tail(oracle):
     np.testing.assert_array_equal(_meta_row(mn, wl, 0, 2), key)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_metadata_signed_zero_total_order(oracle, dtype):
     wl = W.random_case(14, 1, 1, 1, 16, [16], k=1, dtype=dtype, with_v=False)
     kc = wl.k_cache.clone()

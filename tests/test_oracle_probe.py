@@ -53,9 +53,10 @@ def test_probe_positions(oracle):
             np.testing.assert_allclose(r["probe"][0, h, i], dots.max(), rtol=1e-12)
 
 
-def test_full_sampling_equals_block_max_and_lower_bound(oracle):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_full_sampling_equals_block_max_and_lower_bound(oracle, dtype):
     lens = [10 * 32 + 7, 96]
-    wl = W.random_case(34, 2, 8, 4, 32, lens, k=3)
+    wl = W.random_case(34, 2, 8, 4, 32, lens, k=3, dtype=dtype)
     full = _run(oracle, wl, 3, importance=False, n_probe=32)["probe"]
     part = _run(oracle, wl, 3, importance=False, n_probe=8)["probe"]
     for b, L in enumerate(lens):

@@ -49,12 +49,13 @@ def test_quest_upper_bound(oracle):
                 assert sc[b, n, i] >= dots.max() - margin
 
 
-def test_single_key_metadata_is_dot(oracle):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_single_key_metadata_is_dot(oracle, dtype):
     """max == min == k  =>  score = gq . k exactly."""
     B, H, N, D, BS = 2, 8, 4, 128, 16
     g = torch.Generator().manual_seed(5)
-    keys = torch.randn((2, BS, N, D), generator=g)
-    q = torch.randn((B, H, D), generator=g)
+    keys = torch.randn((2, BS, N, D), generator=g).to(dtype)
+    q = torch.randn((B, H, D), generator=g).to(dtype)
     for n in range(N):
         q[:, n * 2:(n + 1) * 2] = q[:, n * 2:n * 2 + 1]
     mt = torch.tensor([[0], [1]], dtype=torch.int32)
