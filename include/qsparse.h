@@ -65,7 +65,8 @@ typedef enum {
 typedef enum {
     QS_F32 = 0,  /* IEEE binary32 */
     QS_BF16 = 1, /* bfloat16 (upper half of a binary32) */
-    QS_I8 = 2    /* int8 codes with fp32 per-row scales (KV caches only) */
+    QS_I8 = 2,   /* int8 codes with fp32 per-row scales (KV caches only) */
+    QS_F16 = 3   /* IEEE binary16 */
 } qs_dtype;
 
 /* flag bits of the selection calls */
@@ -84,7 +85,7 @@ enum {
  * metadata_block_tables; the unused rows of a request's last metadata block are set
  * to +0.0 ([P3] "三个核心算子": absent blocks' metadata must be 0).
  *
- *   k_cache                [num_kv_blocks, BS, N, D], kv_dtype QS_F32 or QS_BF16
+ *   k_cache                [num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_F16
  *   block_tables           [B, max_kv_blocks_per_req] int32, physical KV block of
  *                          sequence block i of request b
  *   seq_lens               [B] int32, tokens the metadata covers for each request
@@ -141,7 +142,7 @@ size_t qs_block_select_workspace_bytes(int32_t B, int32_t N, int32_t block_size,
  * as sequence-relative indices. [P3] "三个核心算子", variant _w: the sink block and the
  * local-window blocks can be forced in; [P1] section 1: ties go to the lower index.
  *
- *   query                  [B, H, D], dtype QS_F32 or QS_BF16 (metadata has the same dtype)
+ *   query                  [B, H, D], dtype QS_F32, QS_BF16 or QS_F16 (metadata has the same dtype)
  *   maxblocks, minblocks   [num_meta_blocks, BS, N, D] (as written by qs_build_metadata)
  *   metadata_block_tables  [B, max_meta_blocks_per_req] int32
  *   seq_lens               [B] int32, tokens in each request (blocks 0..nb-1 are candidates)
@@ -182,8 +183,8 @@ size_t qs_probe_select_workspace_bytes(int32_t B, int32_t H, int32_t max_kv_bloc
  * to the best probe scores (ties: lower index); with QS_RECENCY, if the last block is
  * not picked it replaces the lowest-scoring probe pick (never an importance pick).
  *
- *   query          [B, H, D], q_dtype QS_F32 or QS_BF16
- *   k_cache        [num_kv_blocks, BS, N, D], kv_dtype QS_F32 or QS_BF16
+ *   query          [B, H, D], q_dtype QS_F32, QS_BF16 or QS_F16
+ *   k_cache        [num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_F16
  *   block_tables   [B, max_kv_blocks_per_req] int32 (max_kv_blocks_per_req <= 4096)
  *   seq_lens       [B] int32
  *   importance     [B, importance_stride] fp32 per-token prefill importance, or NULL
@@ -218,8 +219,10 @@ size_t qs_sparse_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t D
  * selected tokens only, then the weighted sum of V. [P3] "quest_block_select_paged"
  * notes: selected indices are sequence-relative and go through block_tables.
  *
- *   query          [B, H, D], q_dtype QS_F32 or QS_BF16; out [B, H, D] in q_dtype
- *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_I8
+ *   query          [B, H, D], q_dtype QS_F32, QS_BF16 or QS_F16; out [B, H, D] in q_dtype
+ *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16, QS_F16 or QS_I8
+ *                  (bf16 and f16 with a query of the same dtype run on the matrix cores,
+ *                  with P rounded to that format; other pairs on the vector ALU in fp32)
  *   k_scale/v_scale[num_kv_blocks, BS, N] fp32 per-row scales (QS_I8 only, else ignored)
  *   block_tables   [B, max_kv_blocks_per_req] int32; seq_lens [B] int32
  *   selected       [B, sel_heads, k] int32; n_selected [B, sel_heads] int32 (entries
@@ -258,7 +261,7 @@ size_t qs_select_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t b
  * selected blocks and 4096 candidate blocks run as one kernel that keeps the selection
  * on chip; other sizes run the two operations' kernels back to back.
  *
- *   dtype          QS_BF16 or QS_F32, for query, metadata and K/V alike
+ *   dtype          QS_BF16, QS_F16 or QS_F32, for query, metadata and K/V alike
  *   query ... tokens_since_update, flags, k   as qs_block_select
  *   k_cache ... max_kv_blocks_per_req, softmax_scale   as qs_sparse_attn_decode
  *   out            [B, H, D] in dtype

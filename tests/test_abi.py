@@ -214,3 +214,16 @@ def test_binding_refuses_cpu_tensors(qs):
         qs.qs_sparse_attn_decode(x, torch.zeros((1, 32, 1, 128)), torch.zeros((1, 32, 1, 128)),
                                  torch.zeros((1, 1), dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
                                  torch.zeros((1, 1, 1), dtype=torch.int32), torch.zeros((1, 1), dtype=torch.int32))
+
+
+def test_page3_wrappers_exist_and_refuse_cpu_tensors(qs):
+    import torch
+    from top_kv_block_amd import quest_ops as Q
+    for name in ("quest_prefill_metadata", "quest_block_select_paged", "quest_block_select_paged_in_out",
+                 "quest_block_select_paged_in_out_w"):
+        assert callable(getattr(Q, name))
+    q = torch.zeros((1, 8, 128), dtype=torch.float16)
+    m = torch.zeros((1, 128, 2, 128), dtype=torch.float16)
+    t = torch.zeros((1, 1), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        Q.quest_block_select_paged(q, m, m, t, torch.ones(1, dtype=torch.int32), 4)

@@ -109,7 +109,7 @@ def compare_probe(gsel, gns, o, nbs, k):
 
 
 def attn_tol(q_dtype):
-    return 2e-2 if q_dtype == torch.bfloat16 else 1e-4
+    return {torch.bfloat16: 2e-2, torch.float16: 5e-3}.get(q_dtype, 1e-4)
 
 
 # ------------------------------------------------------------------------------------------
@@ -157,6 +157,7 @@ META_CASES = [
     (3, 2, 1, 16, [16 * 16 * 2 + 1, 5], torch.bfloat16),
     (4, 2, 4, 64, [64 * 70, 64 * 3 - 1], torch.float32),
     (5, 1, 16, 128, [128 * 3 + 100], torch.bfloat16),
+    (6, 2, 4, 64, [64 * 20 + 5, 64 * 3], torch.float16),
 ]
 
 
@@ -208,6 +209,7 @@ UPDATE_CASES = [
     (24, 2, 4, 64, [64 * 70, 64 * 3 - 1], [60, 1], 16, torch.float32),                   # [4]
     (25, 3, 1, 128, [128 * 3 + 100, 128 * 2, 1], [1, 5, 0], 2, torch.bfloat16),          # N=1: [1]
     (26, 8, 8, 16, [16 * 16 * 4] * 8, [0] * 8, 256, torch.bfloat16),                     # whole sequences: [1]
+    (28, 2, 4, 32, [32 * 40 + 9, 32 * 7], [39, 3], 2, torch.float16),                    # [4]
 ]
 
 
@@ -308,6 +310,7 @@ SELECT_CASES = [
     (16, 2, 8, 8, 32, [32 * 100, 32 * 2], 1, torch.float32, 2, [0, 64]),
     (17, 1, 64, 8, 128, [128 * 1024], 64, torch.bfloat16, 3, [127]),
     (18, 2, 24, 8, 64, [64 * 130 + 1, 64 * 66], 9, torch.bfloat16, 3, [1, 0]),
+    (19, 3, 16, 4, 64, [64 * 90 + 3, 64 * 17, 64 * 200], 10, torch.float16, 3, [3, 0, 70]),
 ]
 
 
@@ -407,6 +410,7 @@ PROBE_CASES = [
     (24, 3, 4, 4, 16, [16 * 30, 0, 16 * 7 + 5], 9, torch.float32, True, 0, 3),
     (25, 1, 4, 2, 32, [32 * 70], 4, torch.bfloat16, True, 4, 64),
     (26, 1, 2, 1, 128, [128 * 40 + 77], 3, torch.float32, True, 4, 0),
+    (27, 2, 8, 4, 32, [32 * 60 + 9, 32 * 5], 7, torch.float16, True, 4, 8),
 ]
 
 
@@ -480,6 +484,9 @@ ATTN_CASES = [
     (38, 1, 40, 2, 16, [16 * 50 + 1], 9, torch.float32, torch.float32, 1),     # 20 heads per row
     (39, 4, 4, 1, 128, [128 * 64, 1, 128 * 2, 0], 64, torch.bfloat16, torch.bfloat16, 1),
     (40, 1, 8, 8, 16, [16 * 8], 1, torch.float32, torch.float32, 1),
+    (42, 2, 32, 8, 128, [128 * 40 + 5, 128 * 9], 12, torch.float16, torch.float16, 1),   # f16 matrix cores
+    (43, 2, 16, 8, 32, [32 * 50 + 1, 32 * 7], 9, torch.float16, torch.float32, 0),       # f16 KV, fp32 query
+    (44, 2, 8, 2, 32, [32 * 30, 32 * 4 + 2], 5, torch.float32, torch.float16, 1),        # fp32 KV, f16 query
 ]
 
 
@@ -563,6 +570,7 @@ FUSED_CASES = [
     (76, 1, 8, 8, 32, [32 * 64], 65, torch.bfloat16, 0, None),                    # k > 64: two kernels
     (77, 128, 16, 8, 16, [16 * (20 + (7 * b) % 23) + b % 5 for b in range(128)], 6, torch.bfloat16, 3,
      [b % 16 for b in range(128)]),                                               # 1024 rows: one kernel, no split
+    (78, 2, 32, 8, 128, [128 * 150 + 3, 128 * 20], 8, torch.float16, 3, [2, 0]),  # f16, one kernel, splits
 ]
 
 
@@ -587,8 +595,8 @@ def test_select_attn_random(qs, oracle, case):
     out2, _, _ = run_fused(qs, wl, mx, mn, want_sel=False)
     torch.cuda.synchronize()
     # the output does not depend on whether the selection is also written out
-    assert torch.equal(out.view(torch.int16) if dtype == torch.bfloat16 else out.view(torch.int32),
-                       out2.view(torch.int16) if dtype == torch.bfloat16 else out2.view(torch.int32))
+    ib = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.equal(out.view(ib), out2.view(ib))
     omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
     osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k, tsmu=wl.tsmu,
                                          flags=wl.flags)
@@ -811,3 +819,41 @@ def test_graph_replay_matches_eager(qs):
         step()   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))
+
+
+# ------------------------------------------------------------------------------------------
+# page-3 call shapes (top_kv_block_amd.quest_ops)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_page3_wrappers(qs, oracle, dtype):
+    """The page's example shapes (B=20, H=32, N=8, BS=128, MMBPR=1, k=8) through the page-3
+    names, in fp16 and bf16, against the oracle; the forcing variant with a scalar
+    tokens_since_metadata_update of 0 and of -1 (off)."""
+    from top_kv_block_amd import quest_ops as Q
+    say(f"page-3 wrappers dtype={dtype}")
+    B, H, N, BS, k = 20, 32, 8, 128, 8
+    wl = W.random_case(81, B, H, N, BS, [BS * BS] * 10 + [BS * 100 + 17] * 10, k=k, dtype=dtype, dist="uniform",
+                       with_v=False)
+    kc, bt, mt, sl = wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.meta_tables.to(DEV), wl.seq_lens.to(DEV)
+    mx = torch.zeros((wl.num_meta_blocks, BS, N, wl.D), dtype=dtype, device=DEV)
+    mn = torch.zeros_like(mx)
+    Q.quest_prefill_metadata(kc, sl, bt, mt, mx, mn)
+    omx, omn = oracle.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, wl.num_meta_blocks)
+    assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
+    q = wl.query.to(DEV)
+    ids = Q.quest_block_select_paged(q, mx, mn, mt, sl, k)
+    assert ids.shape == (B, N, k) and ids.dtype == torch.int32
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k)
+    compare_quest(tnp(ids), ons, osel, ons, osc, nbs_of(wl), k)
+    ids2 = torch.zeros((B, N, k), dtype=torch.int32, device=DEV)
+    Q.quest_block_select_paged_in_out(q, mx, mn, mt, sl, ids2)
+    assert torch.equal(ids, ids2)
+    for tsmu in (0, -1):
+        Q.quest_block_select_paged_in_out_w(q, mx, mn, mt, sl, tsmu, ids2)
+        osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, k,
+                                             tsmu=torch.full((B,), tsmu, dtype=torch.int32),
+                                             flags=W.FORCE_SINK | W.FORCE_WINDOW)
+        compare_quest(tnp(ids2), ons, osel, ons, osc, nbs_of(wl), k)
+        if tsmu == 0:
+            assert all(0 in set(r.tolist()) for r in tnp(ids2).reshape(-1, k))      # sink forced

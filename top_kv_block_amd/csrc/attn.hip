@@ -32,6 +32,8 @@
 // order (no cross-workgroup synchronisation inside a kernel).
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_dev.h"
 #include "qs_device.h"
 #include "qs_internal.h"
@@ -46,22 +48,23 @@ constexpr int kTargetWorkgroupsVec = 2048;
 constexpr int kNoSplitRows = 1024;   // rows at which each row gets one workgroup
 
 // the attention kernels: one workgroup per (slot split x head chunk, selection row, request)
+template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attn_mfma_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMfmaLdsBytes];  // 40 KiB
     const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
     const int s = blockIdx.y, b = blockIdx.z;
     const int row = b * p.sel_heads + s;
-    mfma_body(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
+    mfma_body<DT>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
 }
 
-template <int KV, bool QBF16, int HC>
+template <int KV, int QDT, int HC>
 __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
     __shared__ float red[vec_red_floats<HC>()];
     const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
     const int s = blockIdx.y, b = blockIdx.z;
     const int row = b * p.sel_heads + s;
-    vec_body<KV, QBF16, HC>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], red);
+    vec_body<KV, QDT, HC>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], red);
 }
 
 // ------------------------------------------------------------------------------------
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 // ------------------------------------------------------------------------------------
 constexpr int kCombineBatch = 8;
 
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, int hc_cap, bool out_bf16) {
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, int hc_cap, int out_dt) {
     const int e = blockIdx.x * kThreads + threadIdx.x;  // (head, channel) of request b
     const int b = blockIdx.y;
     if (e >= p.H * D) return;
@@ -98,13 +101,12 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, in
     }
     const float v = (Ls > 0.f) ? A / Ls : 0.f;
     const size_t o = (size_t(b) * p.H + h) * D + d;
-    if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
-    else ((float*)p.out)[o] = v;
+    store_out(p.out, o, v, out_dt);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int KV, bool QB>
+template <int KV, int QB>
 void launch_vec(const AttnParams& prm, const AttnPlan& pl, dim3 grid, hipStream_t s) {
     switch (pl.hc) {
         case 1: hipLaunchKernelGGL((attn_vec_kernel<KV, QB, 1>), grid, dim3(kThreads), 0, s, prm); break;
@@ -120,7 +122,7 @@ AttnPlan plan_sparse_attn(int B, int H, int N, int D_, int sel_heads, int k, int
     (void)N;
     (void)D_;
     AttnPlan p;
-    p.mfma = (q_dtype == 1 && kv_dtype == 1);
+    p.mfma = q_dtype == kv_dtype && (q_dtype == kBF16 || q_dtype == kF16);
     p.hpr = H / sel_heads;
     if (p.mfma)
         p.hc = 16;
@@ -151,23 +153,28 @@ hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t
                    a.H, a.N, a.BS, a.sel_heads, a.k, pl.hpr, pl.hchunks, pl.splits, pl.spb, a.scale * kLog2e,
                    (uint8_t*)a.out, (float*)((uint8_t*)a.workspace + pl.part_off)};
     dim3 grid(unsigned(pl.splits * pl.hchunks), unsigned(a.sel_heads), unsigned(a.B));
-    const bool qb = a.q_dtype == 1;
     if (pl.mfma) {
-        hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kThreads), 0, s, prm);
-    } else if (a.kv_dtype == 0) {
-        if (qb) launch_vec<0, true>(prm, pl, grid, s); else launch_vec<0, false>(prm, pl, grid, s);
-    } else if (a.kv_dtype == 1) {
-        if (qb) launch_vec<1, true>(prm, pl, grid, s); else launch_vec<1, false>(prm, pl, grid, s);
+        if (a.q_dtype == kF16) hipLaunchKernelGGL(attn_mfma_kernel<kF16>, grid, dim3(kThreads), 0, s, prm);
+        else hipLaunchKernelGGL(attn_mfma_kernel<kBF16>, grid, dim3(kThreads), 0, s, prm);
     } else {
-        if (qb) launch_vec<2, true>(prm, pl, grid, s); else launch_vec<2, false>(prm, pl, grid, s);
+        auto by_q = [&](auto kv) {
+            constexpr int KV = decltype(kv)::value;
+            if (a.q_dtype == kBF16) launch_vec<KV, kBF16>(prm, pl, grid, s);
+            else if (a.q_dtype == kF16) launch_vec<KV, kF16>(prm, pl, grid, s);
+            else launch_vec<KV, kF32>(prm, pl, grid, s);
+        };
+        if (a.kv_dtype == kF32) by_q(std::integral_constant<int, kF32>{});
+        else if (a.kv_dtype == kBF16) by_q(std::integral_constant<int, kBF16>{});
+        else if (a.kv_dtype == kF16) by_q(std::integral_constant<int, kF16>{});
+        else by_q(std::integral_constant<int, kI8>{});
     }
-    if (pl.splits > 1) return attn::launch_combine(prm, a.B, pl.hc, qb, s);
+    if (pl.splits > 1) return attn::launch_combine(prm, a.B, pl.hc, a.q_dtype, s);
     return hipGetLastError();
 }
 
-hipError_t attn::launch_combine(const AttnParams& p, int B, int hc_cap, bool out_bf16, hipStream_t s) {
+hipError_t attn::launch_combine(const AttnParams& p, int B, int hc_cap, int out_dt, hipStream_t s) {
     const unsigned per_req = unsigned((size_t(p.H) * D + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(B)), dim3(kThreads), 0, s, p, hc_cap, out_bf16);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(B)), dim3(kThreads), 0, s, p, hc_cap, out_dt);
     return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -16,6 +18,7 @@ constexpr int D = 128;
 constexpr int PSTRIDE = D + 2;       // partial record: acc[D], max, sum
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 
@@ -48,14 +51,19 @@ struct AttnParams {
     float* part;
 };
 
+// stores output element o in the query dtype (F32, BF16 or F16; 16-bit: round to nearest even)
+__device__ __forceinline__ void store_out(uint8_t* out, size_t o, float v, int out_dt) {
+    if (out_dt == kBF16) ((uint16_t*)out)[o] = f32_to_half<kBF16>(v);
+    else if (out_dt == kF16) ((uint16_t*)out)[o] = f32_to_half<kF16>(v);
+    else ((float*)out)[o] = v;
+}
+
 // result of one workgroup for head g, channel d: either the output or a partial record
 __device__ __forceinline__ void emit(const AttnParams& p, int b, int row, int hcix, int split, int hc_cap, int h0,
-                                     int g, int d, float M, float Ls, float A, bool out_bf16) {
+                                     int g, int d, float M, float Ls, float A, int out_dt) {
     if (p.splits == 1) {
         const float v = (Ls > 0.f) ? A / Ls : 0.f;
-        const size_t o = (size_t(b) * p.H + h0 + g) * D + d;
-        if (out_bf16) ((uint16_t*)p.out)[o] = f32_to_bf16_rne(v);
-        else ((float*)p.out)[o] = v;
+        store_out(p.out, (size_t(b) * p.H + h0 + g) * D + d, v, out_dt);
     } else {
         float* rec = p.part + (((size_t(row) * p.hchunks + hcix) * p.splits + split) * hc_cap + g) * PSTRIDE;
         rec[d] = A;
@@ -64,14 +72,25 @@ __device__ __forceinline__ void emit(const AttnParams& p, int b, int row, int hc
 }
 
 // ------------------------------------------------------------------------------------
-// bf16 matrix-core kernel
+// matrix-core kernel (bf16 or f16 query and KV)
 // ------------------------------------------------------------------------------------
 constexpr int kVtPitch = 80;             // bytes per V^T row in LDS: 32 tokens (64 B) + pad
 constexpr int kVtBytes = D * kVtPitch;   // one wave's V^T tile
 
-__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) {
+// the MFMA operand type of a 16-bit format, and v_mfma_f32_16x16x32 on it
+template <int DT>
+using op8 = typename std::conditional<DT == kBF16, bf16x8, f16x8>::type;
+template <int DT>
+using op1 = typename std::conditional<DT == kBF16, __bf16, _Float16>::type;
+template <int DT>
+__device__ __forceinline__ op8<DT> as_op8(u32x4 v) {
     u32v4 t = {v.x, v.y, v.z, v.w};
-    return __builtin_bit_cast(bf16x8, t);
+    return __builtin_bit_cast(op8<DT>, t);
+}
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(op8<DT> a, op8<DT> b, f32x4 c) {
+    if constexpr (DT == kBF16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // 128 VGPRs: four workgroups (16 waves) per CU, which the 1024-row serving batch fills
@@ -80,6 +99,7 @@ __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) {
 // count ns_raw, in global memory or LDS), head chunk hcix, slot range `split`. lds: the
 // kMfmaLdsBytes work area. With sync_after_table the workgroup synchronises once every
 // wave has read its slot table, so the selection may live inside the work area.
+template <int DT>
 __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hcix, int s, int b,
                                           const int32_t* srow, int ns_raw, uint8_t* lds, bool sync_after_table) {
     const int h0 = s * p.hpr + hcix * 16;
@@ -91,12 +111,12 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
     const int c16 = lane & 15, j = lane >> 4;
 
     // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
-    bf16x8 qb[4];
+    op8<DT> qb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4 v{0u, 0u, 0u, 0u};
         if (c16 < nh) v = ld16(p.query + ((size_t(b) * p.H + h0 + c16) * D + 32 * ks + 8 * j) * 2);
-        qb[ks] = as_bf8(v);
+        qb[ks] = as_op8<DT>(v);
     }
 
     const int L = max(p.sl[b], 0);
@@ -178,7 +198,7 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
             sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(kr[tau][ks]), qb[ks], sacc[tau], 0, 0, 0);
+                sacc[tau] = mfma16x16x32<DT>(as_op8<DT>(kr[tau][ks]), qb[ks], sacc[tau]);
         }
         float sv[8];
         float cmax = -INFINITY;
@@ -193,12 +213,12 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
         const float mn = fmaxf(m, cmax);
         const float cf = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-        bf16x8 pv;
+        op8<DT> pv;
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float pe = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mn);
-            const __bf16 pb = (__bf16)pe;
+            const op1<DT> pb = (op1<DT>)pe;  // P in the operand format; the sum takes the rounded value
             pv[e] = pb;
             psum += (float)pb;
         }
@@ -239,7 +259,7 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const u32x4 a = ld16(vt + (16 * dt + c16) * kVtPitch + 16 * j);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), pv, o[dt], 0, 0, 0);
+            o[dt] = mfma16x16x32<DT>(as_op8<DT>(a), pv, o[dt]);
         }
         // the next chunk overwrites the tile only after every lane has read it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -269,7 +289,7 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww)
             merge_state(M, Ls, &A, 1, red_m[ww * 16 + g], red_l[ww * 16 + g], &red_o[(ww * 16 + g) * D + d]);
-        emit(p, b, row, hcix, split, 16, h0, g, d, M, Ls, A, true);
+        emit(p, b, row, hcix, split, 16, h0, g, d, M, Ls, A, DT);
     }
 }
 
@@ -278,11 +298,11 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
 // ------------------------------------------------------------------------------------
 // Vector-ALU attention of one workgroup (arguments as mfma_body). red: kWaves * HC *
 // (D + 2) floats of LDS for the cross-wave merge.
-template <int KV, bool QBF16, int HC>
+template <int KV, int QDT, int HC>
 __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hcix, int s, int b,
                                          const int32_t* srow, int ns_raw, float* red) {
-    constexpr int ke = KV == 0 ? 4 : (KV == 1 ? 2 : 1);
-    constexpr int qe = QBF16 ? 2 : 4;
+    constexpr int ke = elem_bytes(KV);
+    constexpr int qe = elem_bytes(QDT);
     constexpr int LPR = D * ke / 16;    // lanes per K/V row
     constexpr int EPL = 16 / ke;        // channels per lane
     constexpr int NG = kThreads / LPR;  // independent lane groups per workgroup
@@ -310,9 +330,9 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const int d = lr * EPL + e;
-            x[e] = QBF16 ? bf16_to_f32(((const uint16_t*)qp)[d]) : ((const float*)qp)[d];
+            x[e] = load_elem<QDT>(qp, d);
         }
-        if constexpr (KV == 2) {
+        if constexpr (KV == kI8) {
             float amax = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -373,7 +393,7 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
                 const int tt = ok[u] ? t : 0;
                 kv[u] = ld16(kb + size_t(tt) * tok_bytes);
                 vv[u] = ld16(vb + size_t(tt) * tok_bytes);
-                if constexpr (KV == 2) {
+                if constexpr (KV == kI8) {
                     ks[u] = p.ksc[(tok0 + tt) * p.N + kh];
                     vs[u] = p.vsc[(tok0 + tt) * p.N + kh];
                 } else {
@@ -385,12 +405,12 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
                 const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
                 const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
                 float vf[EPL];
-                if constexpr (KV == 0) {
+                if constexpr (KV == kF32) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) vf[jj] = __uint_as_float(vw[jj]);
-                } else if constexpr (KV == 1) {
+                } else if constexpr (KV == kBF16 || KV == kF16) {
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) { vf[2 * jj] = bf_lo(vw[jj]); vf[2 * jj + 1] = bf_hi(vw[jj]); }
+                    for (int jj = 0; jj < 4; ++jj) { vf[2 * jj] = lo16<KV>(vw[jj]); vf[2 * jj + 1] = hi16<KV>(vw[jj]); }
                 } else {
 #pragma unroll
                     for (int jj = 0; jj < 16; ++jj) vf[jj] = float(int8_t(vw[jj / 4] >> (8 * (jj % 4)))) * vs[u];
@@ -398,7 +418,7 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
 #pragma unroll
                 for (int g = 0; g < HC; ++g) {
                     float sc;
-                    if constexpr (KV == 2) {
+                    if constexpr (KV == kI8) {
                         int dot = 0;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) dot = __builtin_amdgcn_sdot4(q8[g][jj], int32_t(kw[jj]), dot, false);
@@ -406,13 +426,13 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
                         sc = float(dot) * (qscale[g] * ks[u]);
                     } else {
                         float pp = 0.f;
-                        if constexpr (KV == 0) {
+                        if constexpr (KV == kF32) {
 #pragma unroll
                             for (int jj = 0; jj < 4; ++jj) pp += qf[g][jj] * __uint_as_float(kw[jj]);
                         } else {
 #pragma unroll
                             for (int jj = 0; jj < 4; ++jj)
-                                pp += qf[g][2 * jj] * bf_lo(kw[jj]) + qf[g][2 * jj + 1] * bf_hi(kw[jj]);
+                                pp += qf[g][2 * jj] * lo16<KV>(kw[jj]) + qf[g][2 * jj + 1] * hi16<KV>(kw[jj]);
                         }
                         sc = group_sum<LPR>(pp);
                     }
@@ -459,7 +479,7 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
         float M = -INFINITY, Ls = 0.f, A = 0.f;
         for (int ww = 0; ww < kWaves; ++ww)
             merge_state(M, Ls, &A, 1, red_m[ww * HC + g], red_l[ww * HC + g], &red_a[(ww * HC + g) * D + d]);
-        emit(p, b, row, hcix, split, HC, h0, g, d, M, Ls, A, QBF16);
+        emit(p, b, row, hcix, split, HC, h0, g, d, M, Ls, A, QDT);
     }
 }
 
@@ -468,7 +488,7 @@ template <int HC>
 constexpr int vec_red_floats() { return kWaves * HC * (D + 2); }
 
 // merges split partials into the output (attn.hip)
-hipError_t launch_combine(const AttnParams& p, int B, int hc_cap, bool out_bf16, hipStream_t s);
+hipError_t launch_combine(const AttnParams& p, int B, int hc_cap, int out_dt, hipStream_t s);
 
 }  // namespace attn
 }  // namespace qs

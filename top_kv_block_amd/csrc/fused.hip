@@ -54,7 +54,7 @@ static_assert(kFusedMaxCap <= sel::kLdsScoreCap, "scores stay on chip");
 // Selection of row (b, n) into LDS (every thread must call it). Returns n_selected; the
 // entries are at lds + kOffSel. Split 0 of head chunk 0 also writes them to the caller's
 // selected / n_selected when those are given.
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int n, uint8_t* lds, bool publish) {
     float* scores = (float*)(lds + kOffScores);
     uint32_t* hist = (uint32_t*)(lds + kOffHist);
@@ -66,7 +66,7 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     int32_t* nsel = (int32_t*)(lds + kOffNsel);
     const int cap = p.mmbpr * p.BS;
     const sel::RowInfo r = sel::row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
-    sel::score_range<BF16, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0,
+    sel::score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0,
                                  r.nb, scores, false, qstage, mt_stage);
     __syncthreads();
     sel::topk_emit(scores, r.nb, r.F, p.k, selv, nsel, hist, sh, wsum);
@@ -80,17 +80,18 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     return ns;
 }
 
-// bf16: grid (splits x head chunks, KV head, request)
+// bf16 / f16: grid (splits x head chunks, KV head, request)
+template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void select_attn_mfma_kernel(sel::SelParams sp, attn::AttnParams ap) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[attn::kMfmaLdsBytes];
     const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
     const int n = blockIdx.y, b = blockIdx.z;
-    const int ns = select_phase<true>(sp, b, n, lds, split == 0 && hcix == 0);
-    attn::mfma_body(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
+    const int ns = select_phase<DT>(sp, b, n, lds, split == 0 && hcix == 0);
+    attn::mfma_body<DT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
 }
 
-// fp32: the vector-ALU attention; its merge buffer overlays the dead scoring scratch
+// f32: the vector-ALU attention; its merge buffer overlays the dead scoring scratch
 template <int HC>
 __global__ __launch_bounds__(kThreads) void select_attn_vec_kernel(sel::SelParams sp, attn::AttnParams ap) {
     constexpr int kRedBytes = attn::vec_red_floats<HC>() * 4;
@@ -98,9 +99,9 @@ __global__ __launch_bounds__(kThreads) void select_attn_vec_kernel(sel::SelParam
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
     const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
     const int n = blockIdx.y, b = blockIdx.z;
-    const int ns = select_phase<false>(sp, b, n, lds, split == 0 && hcix == 0);
-    attn::vec_body<0, false, HC>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns,
-                                 (float*)(lds + kOffScores));
+    const int ns = select_phase<kF32>(sp, b, n, lds, split == 0 && hcix == 0);
+    attn::vec_body<kF32, kF32, HC>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns,
+                                   (float*)(lds + kOffScores));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -171,7 +172,8 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
                          (uint8_t*)a.out, (float*)(ws + ap.part_off)};
     dim3 grid(unsigned(ap.splits * ap.hchunks), unsigned(a.N), unsigned(a.B));
     if (ap.mfma) {
-        hipLaunchKernelGGL(select_attn_mfma_kernel, grid, dim3(kThreads), 0, st, sp, prm);
+        if (a.q_dtype == kF16) hipLaunchKernelGGL(select_attn_mfma_kernel<kF16>, grid, dim3(kThreads), 0, st, sp, prm);
+        else hipLaunchKernelGGL(select_attn_mfma_kernel<kBF16>, grid, dim3(kThreads), 0, st, sp, prm);
     } else {
         switch (ap.hc) {
             case 1: hipLaunchKernelGGL(select_attn_vec_kernel<1>, grid, dim3(kThreads), 0, st, sp, prm); break;
@@ -180,7 +182,7 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
             default: hipLaunchKernelGGL(select_attn_vec_kernel<8>, grid, dim3(kThreads), 0, st, sp, prm); break;
         }
     }
-    if (ap.splits > 1) return attn::launch_combine(prm, a.B, ap.hc, ap.mfma, st);
+    if (ap.splits > 1) return attn::launch_combine(prm, a.B, ap.hc, a.q_dtype, st);
     return hipGetLastError();
 }
 

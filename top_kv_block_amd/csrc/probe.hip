@@ -18,6 +18,8 @@
 // with the block-wide radix select plus one ordered pass.
 #include <math.h>
 
+#include <type_traits>
+
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -75,14 +77,14 @@ constexpr int kProbeHeads = 8;   // query heads scored per pass over the sampled
 // row of its blocks once and scores it against every query head of the group (so each
 // key row is read once for all of them), folding the dot into the block's probe score
 // with an LDS atomic max on the order-preserving key. Results go to keys[b][h][block].
-template <bool QBF16, bool KBF16>
+template <int QDT, int KDT>
 __global__ __launch_bounds__(kThreads) void probe_score_kernel(
     const uint8_t* __restrict__ query, const uint8_t* __restrict__ kc, int num_kv_blocks,
     const int32_t* __restrict__ bt, int mkbpr, const int32_t* __restrict__ sl, int n_probe, int H, int N, int BS,
     uint32_t* __restrict__ keys) {
     constexpr int D = 128;
-    constexpr int ke = KBF16 ? 2 : 4;
-    constexpr int qe = QBF16 ? 2 : 4;
+    constexpr int ke = elem_bytes(KDT);
+    constexpr int qe = elem_bytes(QDT);
     constexpr int LPR = D * ke / 16;  // lanes per key row
     constexpr int EPL = 16 / ke;      // channels per lane
     constexpr int GRP = kThreads / LPR;
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void probe_score_kernel(
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 const int d = lr * EPL + e;
-                q[g][e] = QBF16 ? bf16_to_f32(((const uint16_t*)qp)[d]) : ((const float*)qp)[d];
+                q[g][e] = load_elem<QDT>(qp, d);
             }
         }
         __syncthreads();
@@ -159,9 +161,9 @@ __global__ __launch_bounds__(kThreads) void probe_score_kernel(
             for (int u = 0; u < U; ++u) {
                 const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
                 float kf[EPL];
-                if constexpr (KBF16) {
+                if constexpr (KDT != kF32) {
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) { kf[2 * jj] = bf_lo(w[jj]); kf[2 * jj + 1] = bf_hi(w[jj]); }
+                    for (int jj = 0; jj < 4; ++jj) { kf[2 * jj] = lo16<KDT>(w[jj]); kf[2 * jj + 1] = hi16<KDT>(w[jj]); }
                 } else {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) kf[jj] = __uint_as_float(w[jj]);
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void probe_pick_kernel(
         for (int i = tid; i < nb; i += kThreads) probe_scores[(size_t(b) * H + h) * mkbpr + i] = key2f(pkey[i]);
 }
 
-template <bool QB, bool KB>
+template <int QB, int KB>
 void launch_score(const ProbeArgs& a, uint32_t* keys, hipStream_t s) {
     const unsigned chunks = unsigned((a.mkbpr + kProbeChunk - 1) / kProbeChunk);
     hipLaunchKernelGGL((probe_score_kernel<QB, KB>), dim3(chunks, unsigned(a.N), unsigned(a.B)), dim3(kThreads), 0, s,
@@ -304,11 +306,15 @@ size_t probe_workspace_bytes(int B, int H, int mkbpr) {
 
 hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s) {
     uint32_t* keys = (uint32_t*)a.workspace;
-    if (a.q_bf16) {
-        if (a.kv_bf16) launch_score<true, true>(a, keys, s); else launch_score<true, false>(a, keys, s);
-    } else {
-        if (a.kv_bf16) launch_score<false, true>(a, keys, s); else launch_score<false, false>(a, keys, s);
-    }
+    auto by_k = [&](auto q) {
+        constexpr int QD = decltype(q)::value;
+        if (a.kv_dtype == kBF16) launch_score<QD, kBF16>(a, keys, s);
+        else if (a.kv_dtype == kF16) launch_score<QD, kF16>(a, keys, s);
+        else launch_score<QD, kF32>(a, keys, s);
+    };
+    if (a.q_dtype == kBF16) by_k(std::integral_constant<int, kBF16>{});
+    else if (a.q_dtype == kF16) by_k(std::integral_constant<int, kF16>{});
+    else by_k(std::integral_constant<int, kF32>{});
     hipLaunchKernelGGL(probe_pick_kernel, dim3(unsigned(a.H), unsigned(a.B)), dim3(kThreads), 0, s, keys, a.mkbpr,
                        a.seq_lens, a.importance, a.imp_stride, a.k, a.flags, a.H, a.BS, a.selected, a.n_selected,
                        a.probe_scores);

@@ -27,6 +27,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return uint16_t(u >> 16);
 }
 
+// Element types (the qs_dtype values) and the two 16-bit float formats: bf16 is the upper
+// half of a binary32; f16 is IEEE binary16 (converted by the hardware, round to nearest even).
+constexpr int kF32 = 0, kBF16 = 1, kI8 = 2, kF16 = 3;
+__host__ __device__ constexpr int elem_bytes(int dt) { return dt == kF32 ? 4 : (dt == kI8 ? 1 : 2); }
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+    static_assert(DT == kBF16 || DT == kF16, "16-bit float formats only");
+    if constexpr (DT == kBF16) return __uint_as_float(w << 16);
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    static_assert(DT == kBF16 || DT == kF16, "16-bit float formats only");
+    if constexpr (DT == kBF16) return __uint_as_float(w & 0xffff0000u);
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+template <int DT>
+__device__ __forceinline__ float half_to_f32(uint16_t h) { return lo16<DT>(uint32_t(h)); }
+template <int DT>
+__device__ __forceinline__ uint16_t f32_to_half(float f) {
+    if constexpr (DT == kBF16) return f32_to_bf16_rne(f);
+    else return __builtin_bit_cast(unsigned short, (_Float16)f);
+}
+// element e of a row as fp32 (DT f32, bf16 or f16)
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* row, int e) {
+    if constexpr (DT == kF32) return ((const float*)row)[e];
+    else return half_to_f32<DT>(((const uint16_t*)row)[e]);
+}
+
 // Monotone map from finite floats to uint32: a < b (IEEE total order, -0 < +0)
 // iff key(a) < key(b). Used for exact, deterministic top-k on scores.
 __device__ __forceinline__ uint32_t f2key(float f) {

@@ -10,7 +10,7 @@ namespace qs {
 // ---- metadata ----------------------------------------------------------------------
 struct MetaArgs {
     int B, N, D, BS;
-    bool bf16;
+    bool bf16;  // any 16-bit float format (bf16 or f16): the reduction only orders bit patterns
     const void* k_cache;
     int num_kv_blocks;
     const int32_t* block_tables;
@@ -39,7 +39,7 @@ SelectPlan plan_block_select(int B, int N, int BS, int mmbpr);
 
 struct SelectArgs {
     int B, H, N, D, BS;
-    bool bf16;
+    int dtype;  // qs_dtype of the query and metadata (F32, BF16 or F16)
     const void* query;
     const void* maxb;
     const void* minb;
@@ -61,7 +61,7 @@ hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& p, hipStre
 constexpr int kProbeMaxBlocks = 4096;
 struct ProbeArgs {
     int B, H, N, D, BS;
-    bool q_bf16, kv_bf16;
+    int q_dtype, kv_dtype;  // F32, BF16 or F16
     const void* query;
     const void* k_cache;
     int num_kv_blocks;

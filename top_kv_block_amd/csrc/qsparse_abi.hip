@@ -63,8 +63,8 @@ qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size,
     const char* fn = "qs_build_metadata";
     qs_status st = check_dims(fn, B, N, N, D, block_size);
     if (st != QS_OK) return st;
-    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16)
-        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32 or QS_BF16", fn);
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!k_cache || !block_tables || !seq_lens || !metadata_block_tables || !maxblocks || !minblocks)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned16(k_cache) || !aligned16(maxblocks) || !aligned16(minblocks))
@@ -74,7 +74,7 @@ qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size,
     if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
     if (B == 0) return ok();
-    qs::MetaArgs a{B, N, D, block_size, kv_dtype == QS_BF16, k_cache, num_kv_blocks, block_tables,
+    qs::MetaArgs a{B, N, D, block_size, kv_dtype != QS_F32, k_cache, num_kv_blocks, block_tables,
                    max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
                    maxblocks, minblocks, num_meta_blocks};
     return hip_status(qs::launch_build_metadata(a, (hipStream_t)stream), fn);
@@ -89,8 +89,8 @@ qs_status qs_update_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size
     const char* fn = "qs_update_metadata";
     qs_status st = check_dims(fn, B, N, N, D, block_size);
     if (st != QS_OK) return st;
-    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16)
-        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32 or QS_BF16", fn);
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!k_cache || !block_tables || !seq_lens || !first_block || !metadata_block_tables || !maxblocks ||
         !minblocks)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
@@ -102,7 +102,7 @@ qs_status qs_update_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size
     if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
     if (B == 0) return ok();
-    qs::MetaArgs a{B, N, D, block_size, kv_dtype == QS_BF16, k_cache, num_kv_blocks, block_tables,
+    qs::MetaArgs a{B, N, D, block_size, kv_dtype != QS_F32, k_cache, num_kv_blocks, block_tables,
                    max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
                    maxblocks, minblocks, num_meta_blocks};
     return hip_status(qs::launch_update_metadata(a, first_block, max_new_blocks, (hipStream_t)stream), fn);
@@ -122,7 +122,8 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     const char* fn = "qs_block_select";
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
-    if (dtype != QS_F32 && dtype != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32 or QS_BF16", fn);
+    if (dtype != QS_F32 && dtype != QS_BF16 && dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!query || !maxblocks || !minblocks || !metadata_block_tables || !seq_lens || !selected || !n_selected ||
         !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
@@ -141,7 +142,7 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     if (workspace_bytes < plan.bytes)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if (B == 0) return ok();
-    qs::SelectArgs a{B, H, N, D, block_size, dtype == QS_BF16, query, maxblocks, minblocks, num_meta_blocks,
+    qs::SelectArgs a{B, H, N, D, block_size, int(dtype), query, maxblocks, minblocks, num_meta_blocks,
                      metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
                      selected, n_selected, block_scores, workspace};
     return hip_status(qs::launch_block_select(a, plan, (hipStream_t)stream), fn);
@@ -162,8 +163,9 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
     if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
-    if ((q_dtype != QS_F32 && q_dtype != QS_BF16) || (kv_dtype != QS_F32 && kv_dtype != QS_BF16))
-        return fail(QS_ERR_UNSUPPORTED, "%s: query and K must be QS_F32 or QS_BF16", fn);
+    if ((q_dtype != QS_F32 && q_dtype != QS_BF16 && q_dtype != QS_F16) ||
+        (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16))
+        return fail(QS_ERR_UNSUPPORTED, "%s: query and K must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!query || !k_cache || !block_tables || !seq_lens || !selected || !n_selected || !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
     if (!aligned16(k_cache)) return fail(QS_ERR_INVALID, "%s: k_cache must be 16-byte aligned", fn);
@@ -182,7 +184,7 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     if (workspace_bytes < need)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if (B == 0) return ok();
-    qs::ProbeArgs a{B, H, N, D, block_size, q_dtype == QS_BF16, kv_dtype == QS_BF16, query, k_cache, num_kv_blocks,
+    qs::ProbeArgs a{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, num_kv_blocks,
                     block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
                     selected, n_selected, probe_scores, workspace};
     return hip_status(qs::launch_probe_select(a, (hipStream_t)stream), fn);
@@ -206,10 +208,10 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     const char* fn = "qs_sparse_attn_decode";
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
-    if (q_dtype != QS_F32 && q_dtype != QS_BF16)
-        return fail(QS_ERR_UNSUPPORTED, "%s: q_dtype must be QS_F32 or QS_BF16", fn);
-    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_I8)
-        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32, QS_BF16 or QS_I8", fn);
+    if (q_dtype != QS_F32 && q_dtype != QS_BF16 && q_dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: q_dtype must be QS_F32, QS_BF16 or QS_F16", fn);
+    if (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_I8 && kv_dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: kv_dtype must be QS_F32, QS_BF16, QS_F16 or QS_I8", fn);
     if (!query || !k_cache || !v_cache || !block_tables || !seq_lens || !selected || !n_selected || !out ||
         !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
@@ -241,7 +243,7 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
 size_t qs_select_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t block_size,
                                       int32_t max_meta_blocks_per_req, int32_t k, qs_dtype dtype) {
     if (B < 0 || N < 1 || H < N || H % N != 0 || block_size < 1 || max_meta_blocks_per_req < 1 || k < 1 ||
-        (dtype != QS_F32 && dtype != QS_BF16))
+        (dtype != QS_F32 && dtype != QS_BF16 && dtype != QS_F16))
         return 0;
     return qs::plan_select_attn(B, H, N, block_size, max_meta_blocks_per_req, k, int(dtype)).bytes;
 }
@@ -257,7 +259,8 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     const char* fn = "qs_select_attn_decode";
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
-    if (dtype != QS_F32 && dtype != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32 or QS_BF16", fn);
+    if (dtype != QS_F32 && dtype != QS_BF16 && dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!query || !maxblocks || !minblocks || !metadata_block_tables || !k_cache || !v_cache || !block_tables ||
         !seq_lens || !out || !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
@@ -283,7 +286,7 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
         return fail(QS_ERR_INVALID, "%s: grid too large", fn);
     if (B == 0) return ok();
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
-    qs::SelectArgs sa{B, H, N, D, block_size, dtype == QS_BF16, query, maxblocks, minblocks, num_meta_blocks,
+    qs::SelectArgs sa{B, H, N, D, block_size, int(dtype), query, maxblocks, minblocks, num_meta_blocks,
                       metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
                       selected, n_selected, nullptr, workspace};
     qs::AttnArgs aa{B, H, N, D, block_size, int(dtype), int(dtype), query, k_cache, v_cache, nullptr, nullptr,

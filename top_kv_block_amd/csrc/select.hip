@@ -22,6 +22,8 @@
 // ties"). Output is written in ascending block order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "qs_device.h"
 #include "qs_internal.h"
 #include "select_dev.h"
@@ -38,7 +40,7 @@ static_assert(kChunk / 16 + 2 <= sel::kMtStageCap, "a split-mode chunk's table e
 
 // row mode: one workgroup per (KV head, request); MT_LDS when the request's metadata
 // table row fits in LDS
-template <bool BF16, bool MT_LDS>
+template <int DT, bool MT_LDS>
 __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds_scores[];
     __shared__ uint32_t hist[512];
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
     int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
     if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
-        score_range<BF16, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+        score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
                                   0, r.nb, lds_scores, false, qstage, mt_stage);
         __syncthreads();
         if (p.dbg_scores)
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
                 gscores[i] = r.F.has(i) ? __builtin_nanf("") : lds_scores[i];
         topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     } else {
-        score_range<BF16, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+        score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
                                   0, r.nb, gscores, p.dbg_scores != nullptr, qstage, mt_stage);
         __syncthreads();
         topk_emit(gscores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
 }
 
 // split mode, step 1: scoring grid (chunk, KV head, request)
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int chunk) {
     __shared__ u32x4 qstage[kThreads];
     __shared__ int32_t mt_stage[kMtStageCap];
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int
     if (i0 >= r.nb) return;
     float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
     // a chunk spans at most chunk / BS + 2 table entries, always within kMtStageCap
-    score_range<BF16, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
+    score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
                             min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage, mt_stage);
 }
 
@@ -143,19 +145,22 @@ hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& pl, hipStr
     if (pl.row_mode) {
         dim3 grid(unsigned(a.N), unsigned(a.B));
         const bool mt_lds = a.mmbpr <= kMtStageCap;
-        if (a.bf16) {
-            if (mt_lds) hipLaunchKernelGGL((select_row_kernel<true, true>), grid, dim3(kThreads), pl.lds_bytes, s, p);
-            else hipLaunchKernelGGL((select_row_kernel<true, false>), grid, dim3(kThreads), pl.lds_bytes, s, p);
-        } else {
-            if (mt_lds) hipLaunchKernelGGL((select_row_kernel<false, true>), grid, dim3(kThreads), pl.lds_bytes, s, p);
-            else hipLaunchKernelGGL((select_row_kernel<false, false>), grid, dim3(kThreads), pl.lds_bytes, s, p);
-        }
+        auto row = [&](auto dt) {
+            constexpr int DT = decltype(dt)::value;
+            if (mt_lds) hipLaunchKernelGGL((select_row_kernel<DT, true>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+            else hipLaunchKernelGGL((select_row_kernel<DT, false>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+        };
+        if (a.dtype == kBF16) row(std::integral_constant<int, kBF16>{});
+        else if (a.dtype == kF16) row(std::integral_constant<int, kF16>{});
+        else row(std::integral_constant<int, kF32>{});
     } else {
         dim3 g1(unsigned(pl.n_chunks), unsigned(a.N), unsigned(a.B));
-        if (a.bf16)
-            hipLaunchKernelGGL(select_score_kernel<true>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+        if (a.dtype == kBF16)
+            hipLaunchKernelGGL(select_score_kernel<kBF16>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+        else if (a.dtype == kF16)
+            hipLaunchKernelGGL(select_score_kernel<kF16>, g1, dim3(kThreads), 0, s, p, pl.chunk);
         else
-            hipLaunchKernelGGL(select_score_kernel<false>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+            hipLaunchKernelGGL(select_score_kernel<kF32>, g1, dim3(kThreads), 0, s, p, pl.chunk);
         hipLaunchKernelGGL(select_topk_kernel, dim3(unsigned(a.N), unsigned(a.B)), dim3(kThreads), pl.lds_bytes, s, p);
     }
     return hipGetLastError();

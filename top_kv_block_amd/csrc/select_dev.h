@@ -67,13 +67,13 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 // kMtStageCap ints of LDS for the metadata-table entries of [i0, i_end) (MT_LDS: the
 // caller guarantees they fit). Contains a barrier: every thread of the workgroup must
 // call it.
-template <bool BF16, bool MT_LDS>
+template <int DT, bool MT_LDS>
 __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
                                             const uint8_t* __restrict__ minb, int num_meta,
                                             const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
                                             int n, const Forced& F, int i0, int i_end, float* dst, bool nan_forced,
                                             u32x4* qstage, int32_t* mt_stage) {
-    constexpr int esize = BF16 ? 2 : 4;
+    constexpr int esize = elem_bytes(DT);
     constexpr int D = 128;
     constexpr int LPR = D * esize / 16;  // lanes per metadata row
     constexpr int EPL = 16 / esize;      // channels per lane
@@ -133,9 +133,9 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
     for (int e = 0; e < EPL; ++e) gq[e] = 0.f;
     auto add_piece = [&](const u32x4& v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (BF16) {
+        if constexpr (DT != kF32) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { gq[2 * j] += bf_lo(w[j]); gq[2 * j + 1] += bf_hi(w[j]); }
+            for (int j = 0; j < 4; ++j) { gq[2 * j] += lo16<DT>(w[j]); gq[2 * j + 1] += hi16<DT>(w[j]); }
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) gq[j] += __uint_as_float(w[j]);
@@ -158,11 +158,11 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
             const uint32_t a[4] = {vmx[u].x, vmx[u].y, vmx[u].z, vmx[u].w};
             const uint32_t z[4] = {vmn[u].x, vmn[u].y, vmn[u].z, vmn[u].w};
             float part = 0.f;
-            if constexpr (BF16) {
+            if constexpr (DT != kF32) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    part += fmaxf(gq[2 * j] * bf_lo(a[j]), gq[2 * j] * bf_lo(z[j]));
-                    part += fmaxf(gq[2 * j + 1] * bf_hi(a[j]), gq[2 * j + 1] * bf_hi(z[j]));
+                    part += fmaxf(gq[2 * j] * lo16<DT>(a[j]), gq[2 * j] * lo16<DT>(z[j]));
+                    part += fmaxf(gq[2 * j + 1] * hi16<DT>(a[j]), gq[2 * j + 1] * hi16<DT>(z[j]));
                 }
             } else {
 #pragma unroll

@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsparse.so")
 
 QS_OK, QS_ERR_INVALID, QS_ERR_UNSUPPORTED, QS_ERR_HIP = 0, 1, 2, 3
-QS_F32, QS_BF16, QS_I8 = 0, 1, 2
+QS_F32, QS_BF16, QS_I8, QS_F16 = 0, 1, 2, 3
 QS_FORCE_SINK, QS_FORCE_WINDOW, QS_RECENCY = 1, 2, 4
 
 # the C ABI's exported functions (also checked by the ABI tests)
@@ -86,6 +86,8 @@ def _dtype_code(t):
         return QS_BF16
     if t.dtype == torch.int8:
         return QS_I8
+    if t.dtype == torch.float16:
+        return QS_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
