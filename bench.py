@@ -184,27 +184,28 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                 "fused_step_us": round(t_fused * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
     del wl, mx, mn
 
-    # config 2: page-3-shaped Quest select, bf16; metadata build timed too
-    wl = W.config2(device=dev)
-    mx, mn = meta_buf(wl)
-    t_build = _timed(lambda: qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx, mn),
-                     10, stream)
-    tz = torch.zeros(wl.B, dtype=torch.int32, device=dev)
-    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=dev)
-    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
-    t0 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, selected=sel,
-                                           n_selected=ns), reps, stream)
-    t1 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k,
-                                           tokens_since_update=tz, flags=3, selected=sel, n_selected=ns),
-                reps, stream)
-    es = 2
-    sel_bytes = wl.B * wl.N * 128 * 2 * wl.D * es + wl.B * wl.H * wl.D * es
-    build_bytes = wl.k_cache.numel() * es + wl.num_meta_blocks * wl.BS * wl.N * wl.D * es * 2
-    res["config2_p3_select_bf16"] = {"select_us": round(t0 * 1e3, 2), "select_gbps": gbps(sel_bytes, t0),
-                                     "select_window_us": round(t1 * 1e3, 2),
-                                     "metadata_build_us": round(t_build * 1e3, 2),
-                                     "metadata_build_gbps": gbps(build_bytes, t_build)}
-    del wl, mx, mn
+    # config 2: page-3-shaped Quest select, bf16 and fp16 (the page's metadata example is
+    # fp16); metadata build timed too
+    for dt in (torch.bfloat16, torch.float16):
+        wl = W.config2(device=dev, dtype=dt)
+        mx, mn = meta_buf(wl)
+        t_build = _timed(lambda: qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx,
+                                                      mn), 10, stream)
+        tz = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+        sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=dev)
+        ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=dev)
+        t0 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, selected=sel,
+                                               n_selected=ns), reps, stream)
+        t1 = _timed(lambda: qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k,
+                                               tokens_since_update=tz, flags=3, selected=sel, n_selected=ns),
+                    reps, stream)
+        es = 2
+        sel_bytes = wl.B * wl.N * 128 * 2 * wl.D * es + wl.B * wl.H * wl.D * es
+        build_bytes = wl.k_cache.numel() * es + wl.num_meta_blocks * wl.BS * wl.N * wl.D * es * 2
+        res[wl.name] = {"select_us": round(t0 * 1e3, 2), "select_gbps": gbps(sel_bytes, t0),
+                        "select_window_us": round(t1 * 1e3, 2), "metadata_build_us": round(t_build * 1e3, 2),
+                        "metadata_build_gbps": gbps(build_bytes, t_build)}
+        del wl, mx, mn
 
     # config 3: page-1 probe selection + fp32 / int8 attention at k = 32
     wl = W.config3().to(dev)

@@ -177,8 +177,8 @@ def config1(seed: int = 0) -> Workload:
                     sl.clone(), tsmu=None, flags=0, sel_heads=N, needles=[(0, t)])
 
 
-def config2(device="cpu", seed: int = 1, B: int = 20, nb: int = 128) -> Workload:
-    """Quest select shaped like page 3's usage example, bf16.
+def config2(device="cpu", seed: int = 1, B: int = 20, nb: int = 128, dtype=torch.bfloat16) -> Workload:
+    """Quest select shaped like page 3's usage example, bf16 (or ``dtype``, e.g. fp16).
 
     B=20, H=32, N=8, D=128, BS=128, MMBPR=1, seq_len=16384 (128 blocks), k=8.
     K ~ U(-1,1) in a pool of B*128 physical blocks with a random-permutation block
@@ -189,14 +189,15 @@ def config2(device="cpu", seed: int = 1, B: int = 20, nb: int = 128) -> Workload
     L = nb * BS
     g = _gen(seed, device)
     n_kv = B * nb
-    kc = _fill_blocks(n_kv, BS, N, D, g, device, "uniform", torch.bfloat16)
+    kc = _fill_blocks(n_kv, BS, N, D, g, device, "uniform", dtype)
     bt = torch.randperm(n_kv, generator=g, device=device).to(torch.int32).reshape(B, nb)
     mmbpr = _cdiv(nb, BS)
     n_meta = B * mmbpr
     mt = torch.randperm(n_meta, generator=g, device=device).to(torch.int32).reshape(B, mmbpr)
-    q = _uniform((B, H, D), g, device).to(torch.bfloat16)
+    q = _uniform((B, H, D), g, device).to(dtype)
     sl = torch.full((B,), L, dtype=torch.int32, device=device)
-    return Workload("config2_p3_select_bf16", B, H, N, D, BS, k, q, kc, None, bt, sl, mt,
+    name = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(dtype, str(dtype))
+    return Workload(f"config2_p3_select_{name}", B, H, N, D, BS, k, q, kc, None, bt, sl, mt,
                     n_meta, sl.clone(), tsmu=None, flags=0, sel_heads=N)
 
 
