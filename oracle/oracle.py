@@ -52,6 +52,8 @@ def lib():
                                              ctypes.c_double, P]
         L.qso_quantize_row_i8.argtypes = [P, i, P, P]
         L.qso_widen.argtypes = [i, P, i, P]
+        L.qso_prefill_importance.argtypes = [i, i, i, i, i, i, P, i, P, i, P, i, P, ctypes.c_double, i, i, P, P, i]
+        L.qso_prefill_importance.restype = ctypes.c_int
         L.qso_widen.restype = None
         for f in (L.qso_build_metadata, L.qso_block_select, L.qso_probe_select, L.qso_sparse_attn_decode):
             f.restype = ctypes.c_int
@@ -205,6 +207,26 @@ def sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selected
                                       _p(sel), _p(nsel), sel_heads, k, float(softmax_scale), _p(out))
     _check(rc, "sparse_attn_decode")
     return out
+
+
+def prefill_importance(query, k_cache, block_tables, seq_lens, N, softmax_scale=0.0, heads=None, stride=None):
+    """O5. query [B, max_len, H, D]. Returns (importance [B, stride] f64, head_imp [B, H, stride] f64);
+    ``heads`` = (lo, hi) restricts the computation to heads lo .. hi-1 (importance then sums those)."""
+    q = np.ascontiguousarray(_np(query))
+    kc = np.ascontiguousarray(_np(k_cache))
+    assert q.dtype == kc.dtype
+    B, max_len, H, D = q.shape
+    nkv, BS, N2, D2 = kc.shape
+    assert N2 == N and D2 == D
+    bt, sl = _i32(block_tables), _i32(seq_lens)
+    stride = max_len if stride is None else stride
+    lo, hi = (0, H) if heads is None else heads
+    imp = np.zeros((B, stride), np.float64)
+    himp = np.zeros((B, H, stride), np.float64)
+    rc = lib().qso_prefill_importance(B, H, N, D, BS, _dtype_code(q), _p(q), max_len, _p(kc), nkv, _p(bt),
+                                      bt.shape[1], _p(sl), float(softmax_scale), lo, hi, _p(imp), _p(himp), stride)
+    _check(rc, "prefill_importance")
+    return imp, himp
 
 
 def widen(a):

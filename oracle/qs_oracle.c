@@ -616,3 +616,79 @@ int qso_sparse_attn_decode(int B, int H, int N, int D, int BS, int q_dtype, int 
     free(q8);
     return rc;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* O5: prefill importance                                                                */
+/* ------------------------------------------------------------------------------------ */
+/*
+ * [P1] section 1 "知识点", signal 2: the prefill importance of a token is how much
+ * attention the prefill actually gave it, recorded per head (imp_head) and reduced over
+ * heads into prefill_importance[s] when the prefill ends ([P1] section 2, closing
+ * paragraph: every head's imp_head is added into prefill_importance[s]); with exact
+ * prefill attention it is exact.
+ *
+ * reading: causal prefill of L = seq_lens[b] tokens; head h (KV head h / (H / N)) gives
+ * token s the weight p_h[t][s] = exp(c q_{t,h}.k_s) / sum_{s' <= t} exp(c q_{t,h}.k_{s'})
+ * in query row t >= s, c = softmax_scale (1/sqrt(D) when <= 0); imp_head[h][s] is the sum
+ * of p_h[t][s] over the rows t = s .. L-1, and prefill_importance[s] the sum of
+ * imp_head[h][s] over all heads. Entries s >= L are 0.
+ * Layouts: query [B, max_len, H, D] (row t of request b, head h); K through the paged
+ * cache [num_kv_blocks, BS, N, D] and block_tables. Heads h_lo .. h_hi-1 are computed
+ * (the others are left 0 in head_imp and not added): a range lets a test evaluate a few
+ * heads of a long prefill. Outputs in double: importance [B, stride] (may be NULL),
+ * head_imp [B, H, stride] (may be NULL).
+ */
+int qso_prefill_importance(int B, int H, int N, int D, int BS, int dtype, const void* query, int max_len,
+                           const void* k_cache, int num_kv_blocks, const int32_t* block_tables, int mkbpr,
+                           const int32_t* seq_lens, double softmax_scale, int h_lo, int h_hi,
+                           double* importance, double* head_imp, int stride) {
+    if (!is_float(dtype) || H % N != 0 || h_lo < 0 || h_hi > H || h_lo > h_hi) return QSO_BAD;
+    const int G = H / N;
+    const double c = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)D);
+    const size_t row = (size_t)N * D;
+    if (importance) memset(importance, 0, sizeof(double) * (size_t)B * stride);
+    if (head_imp) memset(head_imp, 0, sizeof(double) * (size_t)B * H * stride);
+    double* x = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    size_t* krow = (size_t*)malloc(sizeof(size_t) * (size_t)(max_len > 0 ? max_len : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    int rc = QSO_OK;
+    for (int b = 0; b < B && rc == QSO_OK; ++b) {
+        const int L = seq_lens[b] > 0 ? seq_lens[b] : 0;
+        if (L > max_len || ceil_div64(L, BS) > mkbpr) { rc = QSO_BAD; break; }
+        for (int s = 0; s < L; ++s) {
+            const int32_t phys = block_tables[(size_t)b * mkbpr + s / BS];
+            if (phys < 0 || phys >= num_kv_blocks) { rc = QSO_BAD; break; }
+            krow[s] = ((size_t)phys * BS + (size_t)(s % BS)) * row;
+        }
+        if (rc != QSO_OK) break;
+        for (int h = h_lo; h < h_hi; ++h) {
+            const int kh = h / G;
+            for (int s = 0; s < L; ++s) acc[s] = 0.0;
+            for (int t = 0; t < L; ++t) {
+                const size_t qb = (((size_t)b * max_len + t) * H + h) * D;
+                double m = -INFINITY;
+                for (int s = 0; s <= t; ++s) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += (double)elem_f(query, dtype, qb + d) * (double)elem_f(k_cache, dtype, krow[s] + (size_t)kh * D + d);
+                    x[s] = c * dot;
+                    if (x[s] > m) m = x[s];
+                }
+                double z = 0.0;
+                for (int s = 0; s <= t; ++s) {
+                    x[s] = exp(x[s] - m);
+                    z += x[s];
+                }
+                for (int s = 0; s <= t; ++s) acc[s] += x[s] / z;
+            }
+            for (int s = 0; s < L && s < stride; ++s) {
+                if (head_imp) head_imp[((size_t)b * H + h) * stride + s] = acc[s];
+                if (importance) importance[(size_t)b * stride + s] += acc[s];
+            }
+        }
+    }
+    free(x);
+    free(krow);
+    free(acc);
+    return rc;
+}

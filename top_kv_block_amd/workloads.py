@@ -364,3 +364,23 @@ def random_case(seed: int, B: int, H: int, N: int, BS: int, seq_lens, k: int,
         wl.k_i8, wl.k_scale = quantize_rows_int8(kc.float())
         wl.v_i8, wl.v_scale = quantize_rows_int8(vc.float())
     return wl
+
+
+def prefill_queries(wl: Workload, seed: int, max_len: int = 0, dist: str = "normal") -> torch.Tensor:
+    """Prefill query rows for ``wl``'s requests: [B, max_len, H, D] in the workload's float
+    dtype (fp32 for an int8 workload), drawn on the workload's device. ``max_len``
+    defaults to the longest request. Rows past a request's length are drawn too (unused)."""
+    device = wl.k_cache.device
+    L = max_len or max(1, int(wl.seq_lens.max()))
+    g = _gen(seed, device)
+    x = _uniform((wl.B, L, wl.H, wl.D), g, device) if dist == "uniform" else _normal((wl.B, L, wl.H, wl.D), g, device)
+    dt = wl.k_cache.dtype if wl.k_cache.dtype != torch.int8 else torch.float32
+    return x.to(dt)
+
+
+def config3_prefill(seed: int = 5):
+    """The prefill that produces page 1's importance for config 3: config 3's requests and
+    K cache (B=1, H=16, N=8, D=128, BS=32, 4096 tokens, fp32) with 4096 prefill query rows
+    ~ N(0,1). Returns (workload, queries [1, 4096, 16, 128])."""
+    wl = config3()
+    return wl, prefill_queries(wl, seed)
