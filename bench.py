@@ -229,6 +229,21 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                    "note": "latency-bound (a few MB a step)"}
     del wl
 
+    # the prefill that produces config 3's importance: two causal QK^T passes on the matrix
+    # cores (fp32 inputs); algorithmic flops 2 passes x H x L(L+1) x D multiply-adds
+    wl, pq = W.config3_prefill()
+    wl, pq = wl.to(dev), pq.to(dev)
+    imp = torch.empty((wl.B, int(wl.seq_lens.max())), dtype=torch.float32, device=dev)
+    t_imp = _timed(lambda: qs.qs_prefill_importance(pq, wl.k_cache, wl.block_tables, wl.seq_lens, importance=imp),
+                   10, stream)
+    L = int(wl.seq_lens.max())
+    flops = 2 * wl.H * L * (L + 1) * wl.D * 2
+    res["config3_prefill_importance_fp32"] = {
+        "us": round(t_imp * 1e3, 2), "tflops": round(flops / (t_imp * 1e-3) / 1e12, 2),
+        "mfma_fp32_peak_tflops": 157.3, "frac": round(flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),
+        "note": "B=1, L=4096, H=16, N=8; row pass + column pass + head reduction"}
+    del wl, pq, imp
+
     # config 4: long-context paged decode, bf16 (rows split over workgroups + combine)
     wl = W.config4(device=dev)
     mx, mn = meta_buf(wl)

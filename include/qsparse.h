@@ -10,7 +10,8 @@
  *                          sink / local-window forcing;   (or)
  *   qs_probe_select        probe + prefill-importance + recency block selection;
  *   qs_sparse_attn_decode  exact softmax attention over the selected blocks only;
- *   qs_select_attn_decode  qs_block_select followed by qs_sparse_attn_decode, fused.
+ *   qs_select_attn_decode  qs_block_select followed by qs_sparse_attn_decode, fused;
+ *   qs_prefill_importance  (at prefill) page 1's per-token importance for qs_probe_select.
  *
  * Sources, cited by page title and section:
  *   [P1] "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择"
@@ -277,6 +278,40 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                                 const int32_t* seq_lens, const int32_t* tokens_since_update,
                                 uint32_t flags, int32_t k, float softmax_scale, void* out,
                                 int32_t* selected, int32_t* n_selected,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* bytes of workspace qs_prefill_importance needs (0 for invalid sizes) */
+size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_len);
+
+/*
+ * qs_prefill_importance -- the prefill importance that qs_probe_select consumes.
+ * [P1] section 1, signal 2 (how much attention the prefill really gave each token,
+ * recorded per head, reduced over heads) and section 2's closing note (each head's record
+ * is added into prefill_importance[s] when the prefill ends). With exact causal prefill
+ * attention, head h (KV head h / (H / N)) gives key s the weight
+ *     p_h[t][s] = exp(c q_{t,h} . k_s) / sum_{s' <= t} exp(c q_{t,h} . k_{s'})   (s <= t < L)
+ * in query row t; head_importance[b][h][s] = sum over t of p_h[t][s] and
+ * importance[b][s] = sum over h of head_importance[b][h][s], for s < L = seq_lens[b];
+ * entries s >= L (up to importance_stride) are written as 0.
+ *
+ *   query              [B, max_len, H, D] prefill query rows, dtype QS_F32, QS_BF16 or QS_F16
+ *   k_cache            [num_kv_blocks, BS, N, D] in the same dtype, the prompt's keys through
+ *                      block_tables [B, max_kv_blocks_per_req]; seq_lens [B] prompt lengths
+ *                      (clamped to max_len and to the table's capacity)
+ *   softmax_scale      c; <= 0 selects 1/sqrt(D)
+ *   importance         [B, importance_stride] fp32 output, or NULL
+ *   head_importance    [B, H, importance_stride] fp32 output, or NULL (not both NULL)
+ *   workspace          at least qs_prefill_importance_workspace_bytes(); 256-byte aligned
+ * Dot products run on the matrix cores in fp32 accumulation from exactly widened inputs;
+ * the heads are summed in head order, so results are deterministic.
+ */
+qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                                qs_dtype dtype, const void* query, int32_t max_len,
+                                const void* k_cache, int32_t num_kv_blocks,
+                                const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                const int32_t* seq_lens, float softmax_scale,
+                                float* importance, int32_t importance_stride,
+                                float* head_importance,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* message for the calling thread's last failed call ("" if none) */

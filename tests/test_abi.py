@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode", "qs_select_attn_decode"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_prefill_importance"):
         assert n in names
 
 
@@ -205,6 +205,32 @@ def test_select_attn_workspace_size(qs):
     assert qs.select_attn_workspace_bytes(1, 30, 8, 128, 1, 8, qs.QS_BF16) == 0
     assert qs.select_attn_workspace_bytes(1, 32, 8, 128, 1, 8, qs.QS_I8) == 0
     assert _fused(qs, sel=FAKE, nsel=FAKE) == 0
+
+
+def _imp(qs, **kw):
+    a = dict(B=0, H=16, N=8, D=128, BS=32, dt=qs.QS_F32, q=FAKE, ml=4096, kc=FAKE, nkv=128, bt=FAKE, mkbpr=128,
+             sl=FAKE, scale=0.0, imp=FAKE, stride=4096, himp=None, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qs.lib.qs_prefill_importance(a["B"], a["H"], a["N"], a["D"], a["BS"], a["dt"], a["q"], a["ml"], a["kc"],
+                                        a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["scale"], a["imp"], a["stride"],
+                                        a["himp"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), 2), (dict(D=64), 2), (dict(H=12), 1), (dict(q=None), 1), (dict(imp=None), 1),
+    (dict(ws=None), 1), (dict(wsb=16), 1), (dict(ml=-1), 1), (dict(stride=0), 1), (dict(nkv=0), 1),
+    (dict(kc=ctypes.c_void_p((1 << 20) + 8)), 1), (dict(scale=float("nan")), 1), (dict(BS=24), 2),
+])
+def test_prefill_importance_rejects(qs, kw, status):
+    assert _imp(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_prefill_importance")
+
+
+def test_prefill_importance_workspace_size(qs):
+    assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == 2 * 16 * 4096 * 4
+    assert qs.prefill_importance_workspace_bytes(0, 16, 4096) == 256
+    assert qs.prefill_importance_workspace_bytes(1, 0, 4096) == 0
+    assert _imp(qs, imp=None, himp=FAKE, wsb=qs.prefill_importance_workspace_bytes(0, 16, 4096)) == 0
 
 
 def test_binding_refuses_cpu_tensors(qs):

@@ -857,3 +857,61 @@ def test_page3_wrappers(qs, oracle, dtype):
         compare_quest(tnp(ids2), ons, osel, ons, osc, nbs_of(wl), k)
         if tsmu == 0:
             assert all(0 in set(r.tolist()) for r in tnp(ids2).reshape(-1, k))      # sink forced
+
+
+# ------------------------------------------------------------------------------------------
+# prefill importance (qs_prefill_importance)
+# ------------------------------------------------------------------------------------------
+
+def check_importance(got, want, what):
+    """fp32 matrix-core evaluation against the fp64 oracle: relative 2e-4 plus 1e-6."""
+    err = np.abs(got.astype(np.float64) - want)
+    bad = err > 2e-4 * np.abs(want) + 1e-6
+    assert not bad.any(), f"{what}: {bad.sum()} entries off, worst {err.max():.3e}"
+
+
+IMP_CASES = [
+    # seed, B, H, N, BS, lens, dtype, max_len, stride, scale
+    (101, 2, 4, 2, 16, [37, 50], torch.float32, 50, 64, 0.0),
+    (102, 3, 8, 4, 32, [200, 1, 0], torch.bfloat16, 203, 203, 0.0),
+    (103, 1, 16, 8, 32, [640], torch.float16, 640, 700, 0.2),
+    (104, 2, 6, 3, 64, [129, 300], torch.float32, 301, 250, 0.0),   # stride shorter than a prompt
+    (105, 1, 2, 1, 128, [1000], torch.bfloat16, 1000, 1000, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", IMP_CASES, ids=lambda c: f"seed{c[0]}")
+def test_prefill_importance_random(qs, oracle, case):
+    seed, B, H, N, BS, lens, dtype, max_len, stride, scale = case
+    say(f"prefill importance seed={seed} B={B} H={H} N={N} BS={BS} lens={lens} dtype={dtype}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=2, dtype=dtype, with_v=False)
+    q = W.prefill_queries(wl, seed, max_len=max_len)
+    imp, himp = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                         softmax_scale=scale, importance_stride=stride, with_heads=True)
+    torch.cuda.synchronize()
+    oimp, ohimp = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, N, softmax_scale=scale,
+                                            stride=stride)
+    check_importance(tnp(imp), oimp, "importance")
+    check_importance(tnp(himp), ohimp, "head importance")
+    for b, L in enumerate(lens):
+        assert not tnp(imp)[b, L:].any() and not tnp(himp)[b, :, L:].any()
+    # deterministic: a second run is bitwise identical
+    imp2 = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                    softmax_scale=scale, importance_stride=stride)
+    assert torch.equal(imp, imp2)
+
+
+def test_prefill_importance_config3_sampled_heads(qs, oracle):
+    """Config 3's prefill (4096 tokens, 16 heads, fp32): every head on the GPU, heads 0 and 15
+    against the oracle, and the row-mass identity (the importance sums to H * L)."""
+    wl, q = W.config3_prefill()
+    say("prefill importance config3 (4096 tokens)")
+    imp, himp = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                         with_heads=True)
+    torch.cuda.synchronize()
+    g, gh = tnp(imp), tnp(himp)
+    L = int(wl.seq_lens[0])
+    assert abs(g[0].astype(np.float64).sum() - wl.H * L) <= 1e-4 * wl.H * L
+    for lo in (0, 15):
+        _, oh = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, wl.N, heads=(lo, lo + 1))
+        check_importance(gh[:, lo], oh[:, lo], f"head {lo}")

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsparse.so")
-SOURCES = ["metadata.hip", "select.hip", "probe.hip", "attn.hip", "fused.hip", "qsparse_abi.hip"]
+SOURCES = ["metadata.hip", "select.hip", "probe.hip", "attn.hip", "fused.hip", "importance.hip", "qsparse_abi.hip"]
 ARCH = os.environ.get("QSPARSE_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,222 @@
+// importance.hip -- page 1's prefill importance: the attention mass each prompt token
+// receives from the causal prefill, per head and summed over heads.
+//
+// Source: "0.8MB 跑通 Qwen | 第 10-2 篇" (page 1), section 1 "知识点", signal 2 (how much
+// attention the prefill actually gave each token, recorded per head and reduced over
+// heads) and section 2's closing note (each head's imp_head is added into
+// prefill_importance[s] when the prefill ends). With p_h[t][s] the causal softmax weight
+// of key s in query row t of head h, imp_head[h][s] = sum over t >= s of p_h[t][s] and
+// prefill_importance[s] = sum over heads of imp_head[h][s].
+//
+// Design (CDNA4). The weights need each row's softmax normaliser before any column can
+// be summed, so there are two passes over the causal score matrix, both dense
+// contractions on the matrix cores (the scores are never stored):
+//   row pass     grid (64-row query tile, head, request): each wave takes 16 query rows
+//                and walks the 16-key tiles up to its last row, S = Q K^T on
+//                v_mfma_f32_16x16x4_f32 (fp32 inputs) or v_mfma_f32_16x16x32_{bf16,f16};
+//                each lane keeps an online (max, sum) of its key column for its 4 rows and
+//                the 16 lanes of a row merge once at the end into log2-sum-exp per row;
+//   column pass  grid (64-key tile, head, request): each wave takes 16 keys and walks the
+//                16-row query tiles from its first key to the end, S^T = K Q^T, adds
+//                2^(x - lse_row) into per-lane column sums, merges the 16 lanes at the end;
+//   reduce       sums the heads in a fixed order (deterministic) and writes the outputs.
+// Operand layout: a lane (row r = lane % 16, group j = lane / 16) holds channels
+// 32j .. 32j+31 of its row, contiguous in memory (16-byte loads). The contraction order
+// over channels is free, so both operands use that same channel order: at step ks the
+// f32 MFMA pairs channel 32j + ks, the 16-bit one channels 32j + 8ks .. 8ks + 7.
+#include <math.h>
+
+#include "attn_dev.h"
+#include "qs_device.h"
+#include "qs_internal.h"
+
+namespace qs {
+namespace {
+
+constexpr int D = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct ImpParams {
+    const uint8_t* q;   // [B, max_len, H, D]
+    const uint8_t* kc;  // [num_kv_blocks, BS, N, D]
+    int num_kv_blocks;
+    const int32_t* bt;
+    int mkbpr;
+    const int32_t* sl;
+    int B, H, N, BS, max_len;
+    float scale2;  // softmax scale * log2(e)
+    float* lse;    // [B, H, max_len] workspace: log2-sum-exp2 of each row
+    float* himp;   // [B, H, max_len] workspace: per-head column sums
+};
+
+// one row's channels 32j .. 32j+31 (this lane's operand slice)
+template <int DT>
+struct Frag {
+    static constexpr int kVecs = DT == kF32 ? 8 : 4;  // 16-byte pieces
+    u32x4 v[kVecs];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* row, int j) {
+    const uint8_t* p = row + size_t(32 * j) * elem_bytes(DT);
+#pragma unroll
+    for (int i = 0; i < Frag<DT>::kVecs; ++i) f.v[i] = ld16(p + 16 * i);
+}
+
+// C[m][n] = sum over the 128 channels of A-row m times B-row n (16 x 16 tile, fp32)
+template <int DT>
+__device__ __forceinline__ attn::f32x4 dot_tile(const Frag<DT>& a, const Frag<DT>& b) {
+    attn::f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t aw[4] = {a.v[i].x, a.v[i].y, a.v[i].z, a.v[i].w};
+            const uint32_t bw[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(bw[e]), c, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b.v[i]), c);
+    }
+    return c;
+}
+
+// address of key s (head kh) of request b, or nullptr when its block is out of range
+__device__ __forceinline__ const uint8_t* key_row(const ImpParams& p, int b, int s, int kh, int esize) {
+    const int phys = p.bt[size_t(b) * p.mkbpr + s / p.BS];
+    if (phys < 0 || phys >= p.num_kv_blocks) return nullptr;
+    return p.kc + ((size_t(phys) * p.BS + s % p.BS) * p.N + kh) * D * esize;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
+    constexpr int es = elem_bytes(DT);
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, j = lane >> 4;
+    const int t0 = blockIdx.x * 64 + 16 * w;  // this wave's rows t0 .. t0+15
+    if (t0 >= L) return;                      // no barriers in this kernel
+    const int kh = h / (p.H / p.N);
+    Frag<DT> qf;
+    load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
+
+    float m[4], l[4];  // online max / sum of 2^x over this lane's key column, rows 4j + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
+    const int t_last = min(t0 + 15, L - 1);
+    for (int s0 = 0; s0 <= t_last; s0 += 16) {
+        const uint8_t* kr = key_row(p, b, s0, kh, es);  // the 16 keys share one block
+        if (kr == nullptr) continue;
+        const int s = s0 + r;
+        Frag<DT> kf;
+        load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+        const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * j + i;
+            if (s <= t && s < L) {
+                const float x = c[i] * p.scale2;
+                const float mn = fmaxf(m[i], x);
+                l[i] = l[i] * exp2f(m[i] - mn) + exp2f(x - mn);
+                m[i] = mn;
+            }
+        }
+    }
+    // merge the 16 key columns of each row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float M = group_max<16>(m[i]);
+        const float part = (m[i] == -INFINITY) ? 0.f : l[i] * exp2f(m[i] - M);
+        const float S = group_sum<16>(part);
+        const int t = t0 + 4 * j + i;
+        if (r == 0 && t < L) p.lse[(size_t(b) * p.H + h) * p.max_len + t] = M + log2f(S);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
+    constexpr int es = elem_bytes(DT);
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, j = lane >> 4;
+    const int s0 = blockIdx.x * 64 + 16 * w;  // this wave's keys s0 .. s0+15
+    if (s0 >= L) return;
+    const int kh = h / (p.H / p.N);
+    const uint8_t* kr = key_row(p, b, s0, kh, es);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // keys 4j + i, partial over this lane's query column
+    if (kr != nullptr) {
+        Frag<DT> kf;
+        load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+        const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
+        for (int t0 = s0; t0 < L; t0 += 16) {
+            const int t = t0 + r;
+            Frag<DT> qf;
+            load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t, L - 1)) * p.H + h) * D * es, j);
+            const float lt = t < L ? lse[t] : 0.f;
+            const attn::f32x4 c = dot_tile<DT>(kf, qf);  // C[key 4j+i][row r]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = s0 + 4 * j + i;
+                if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float tot = group_sum<16>(acc[i]);
+        const int s = s0 + 4 * j + i;
+        if (r == 0 && s < L) p.himp[(size_t(b) * p.H + h) * p.max_len + s] = tot;
+    }
+}
+
+// importance[b][s] = sum over heads (in head order) for s < L; 0 elsewhere
+__global__ __launch_bounds__(kThreads) void imp_reduce_kernel(ImpParams p, float* importance, int stride,
+                                                              float* head_importance) {
+    const int s = blockIdx.x * kThreads + threadIdx.x, b = blockIdx.y;
+    if (s >= stride) return;
+    const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    float tot = 0.f;
+    for (int h = 0; h < p.H; ++h) {
+        const float v = s < L ? p.himp[(size_t(b) * p.H + h) * p.max_len + s] : 0.f;
+        tot += v;
+        if (head_importance) head_importance[(size_t(b) * p.H + h) * stride + s] = v;
+    }
+    if (importance) importance[size_t(b) * stride + s] = tot;
+}
+
+}  // namespace
+
+size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
+    size_t bytes = size_t(B) * H * max_len * sizeof(float) * 2;
+    bytes = (bytes + 255) & ~size_t(255);
+    return bytes < 256 ? 256 : bytes;
+}
+
+hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s) {
+    float* ws = (float*)a.workspace;
+    ImpParams p{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr,
+                a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, ws,
+                ws + size_t(a.B) * a.H * a.max_len};
+    const dim3 grid(unsigned((a.max_len + 63) / 64), unsigned(a.H), unsigned(a.B));
+    if (a.max_len > 0) {
+        if (a.dtype == kBF16) {
+            hipLaunchKernelGGL(imp_row_kernel<kBF16>, grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL(imp_col_kernel<kBF16>, grid, dim3(kThreads), 0, s, p);
+        } else if (a.dtype == kF16) {
+            hipLaunchKernelGGL(imp_row_kernel<kF16>, grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL(imp_col_kernel<kF16>, grid, dim3(kThreads), 0, s, p);
+        } else {
+            hipLaunchKernelGGL(imp_row_kernel<kF32>, grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL(imp_col_kernel<kF32>, grid, dim3(kThreads), 0, s, p);
+        }
+    }
+    hipLaunchKernelGGL(imp_reduce_kernel, dim3(unsigned((a.stride + kThreads - 1) / kThreads), unsigned(a.B)),
+                       dim3(kThreads), 0, s, p, a.importance, a.stride, a.head_importance);
+    return hipGetLastError();
+}
+
+}  // namespace qs

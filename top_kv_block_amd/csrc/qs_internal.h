@@ -115,6 +115,26 @@ struct AttnArgs {
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 
+// ---- prefill importance -------------------------------------------------------------
+struct ImportanceArgs {
+    int B, H, N, D, BS;
+    int dtype;  // F32, BF16 or F16 (query and K)
+    const void* query;  // [B, max_len, H, D]
+    int max_len;
+    const void* k_cache;
+    int num_kv_blocks;
+    const int32_t* block_tables;
+    int mkbpr;
+    const int32_t* seq_lens;
+    float scale;
+    float* importance;       // [B, stride] or null
+    int stride;
+    float* head_importance;  // [B, H, stride] or null
+    void* workspace;
+};
+size_t prefill_importance_workspace_bytes(int B, int H, int max_len);
+hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s);
+
 // ---- fused select + attention -------------------------------------------------------
 struct FusedPlan {
     bool fused;        // one kernel (selection into LDS, then attention); else the two paths

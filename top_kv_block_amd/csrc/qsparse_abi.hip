@@ -295,4 +295,44 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     return hip_status(qs::launch_select_attn(sa, aa, plan, (hipStream_t)stream), fn);
 }
 
+size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_len) {
+    if (B < 0 || H < 1 || max_len < 0) return 0;
+    return qs::prefill_importance_workspace_bytes(B, H, max_len);
+}
+
+qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
+                                const void* query, int32_t max_len, const void* k_cache, int32_t num_kv_blocks,
+                                const int32_t* block_tables, int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
+                                float softmax_scale, float* importance, int32_t importance_stride,
+                                float* head_importance, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "qs_prefill_importance";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
+    if (dtype != QS_F32 && dtype != QS_BF16 && dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32, QS_BF16 or QS_F16", fn);
+    if (!query || !k_cache || !block_tables || !seq_lens || !workspace)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!importance && !head_importance)
+        return fail(QS_ERR_INVALID, "%s: importance and head_importance are both NULL", fn);
+    if (!aligned16(query) || !aligned16(k_cache))
+        return fail(QS_ERR_INVALID, "%s: query and k_cache must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (max_len < 0 || importance_stride < 1)
+        return fail(QS_ERR_INVALID, "%s: max_len must be >= 0 and importance_stride >= 1", fn);
+    if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
+    if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
+    const size_t need = qs::prefill_importance_workspace_bytes(B, H, max_len);
+    if (workspace_bytes < need)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (B == 0) return ok();
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
+    qs::ImportanceArgs a{B, H, N, D, block_size, int(dtype), query, max_len, k_cache, num_kv_blocks, block_tables,
+                         max_kv_blocks_per_req, seq_lens, scale, importance, importance_stride, head_importance,
+                         workspace};
+    return hip_status(qs::launch_prefill_importance(a, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

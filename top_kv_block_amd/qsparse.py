@@ -24,7 +24,8 @@ EXPORTS = (
     "qs_build_metadata", "qs_update_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
     "qs_probe_select_workspace_bytes", "qs_probe_select",
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_select_attn_workspace_bytes",
-    "qs_select_attn_decode", "qs_last_error", "qs_version",
+    "qs_select_attn_decode", "qs_prefill_importance_workspace_bytes", "qs_prefill_importance",
+    "qs_last_error", "qs_version",
 )
 
 
@@ -59,8 +60,12 @@ def _load():
     lib.qs_select_attn_workspace_bytes.restype = sz
     lib.qs_select_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, i32, P,
                                           i32, P, P, u32, i32, ctypes.c_float, P, P, P, P, sz, P]
+    lib.qs_prefill_importance_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.qs_prefill_importance_workspace_bytes.restype = sz
+    lib.qs_prefill_importance.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, i32, P,
+                                          ctypes.c_float, P, i32, P, P, sz, P]
     for f in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode", "qs_select_attn_decode"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_prefill_importance"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
@@ -350,3 +355,38 @@ def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_
                                      _ptr(tokens_since_update), int(flags), int(k), float(softmax_scale), _ptr(out),
                                      _ptr(selected), _ptr(n_selected), _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def prefill_importance_workspace_bytes(B, H, max_len):
+    return lib.qs_prefill_importance_workspace_bytes(B, H, max_len)
+
+
+def qs_prefill_importance(query, k_cache, block_tables, seq_lens, softmax_scale=0.0, importance=None,
+                          importance_stride=None, head_importance=None, with_heads=False, workspace_buf=None):
+    """Page 1's prefill importance from the prefill queries [B, max_len, H, D] and the paged
+    K cache. Returns importance [B, stride] fp32 (and head_importance [B, H, stride] when
+    with_heads or given)."""
+    dev = _dev(query, k_cache, block_tables, seq_lens, importance, head_importance)
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    B, max_len, H, D = query.shape
+    nkv, BS, N, D2 = k_cache.shape
+    _need(D2 == D and H % N == 0 and k_cache.dtype == query.dtype, "query and k_cache shapes/dtypes disagree")
+    _rows(block_tables, B, "block_tables")
+    _rows(seq_lens, B, "seq_lens")
+    stride = importance_stride or (importance.shape[-1] if importance is not None else max(1, max_len))
+    if importance is None:
+        importance = torch.empty((B, stride), dtype=torch.float32, device=dev)
+    _need(importance.dtype == torch.float32 and importance.numel() >= B * stride, "importance must be fp32 [B, stride]")
+    if head_importance is None and with_heads:
+        head_importance = torch.empty((B, H, stride), dtype=torch.float32, device=dev)
+    if head_importance is not None:
+        _need(head_importance.dtype == torch.float32 and head_importance.numel() >= B * H * stride,
+              "head_importance must be fp32 [B, H, stride]")
+    nbytes = prefill_importance_workspace_bytes(B, H, max_len)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "importance")
+    _check(lib.qs_prefill_importance(B, H, N, D, BS, _dtype_code(query), _ptr(query), max_len, _ptr(k_cache), nkv,
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), float(softmax_scale),
+                                     _ptr(importance), int(stride), _ptr(head_importance), _ptr(ws), ws.numel(),
+                                     _stream(dev)))
+    return (importance, head_importance) if head_importance is not None else importance
