@@ -230,14 +230,14 @@ def other_workloads(qs, W, dev, stream, reps=50):
     del wl
 
     # the prefill that produces config 3's importance: two causal QK^T passes on the matrix
-    # cores (fp32 inputs); algorithmic flops 2 passes x H x L(L+1) x D multiply-adds
+    # cores (fp32 inputs); algorithmic flops: 2 passes x H heads x L(L+1)/2 causal dots x 2D
     wl, pq = W.config3_prefill()
     wl, pq = wl.to(dev), pq.to(dev)
     imp = torch.empty((wl.B, int(wl.seq_lens.max())), dtype=torch.float32, device=dev)
     t_imp = _timed(lambda: qs.qs_prefill_importance(pq, wl.k_cache, wl.block_tables, wl.seq_lens, importance=imp),
                    10, stream)
     L = int(wl.seq_lens.max())
-    flops = 2 * wl.H * L * (L + 1) * wl.D * 2
+    flops = 2 * wl.H * L * (L + 1) * wl.D
     res["config3_prefill_importance_fp32"] = {
         "us": round(t_imp * 1e3, 2), "tflops": round(flops / (t_imp * 1e-3) / 1e12, 2),
         "mfma_fp32_peak_tflops": 157.3, "frac": round(flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),

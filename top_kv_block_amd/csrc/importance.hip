@@ -63,24 +63,31 @@ __device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* row, int j
     for (int i = 0; i < Frag<DT>::kVecs; ++i) f.v[i] = ld16(p + 16 * i);
 }
 
-// C[m][n] = sum over the 128 channels of A-row m times B-row n (16 x 16 tile, fp32)
+// C[m][n] = sum over the 128 channels of A-row m times B-row n (16 x 16 tile, fp32). Two
+// independent accumulation chains (even and odd steps) halve the dependent MFMA latency.
 template <int DT>
 __device__ __forceinline__ attn::f32x4 dot_tile(const Frag<DT>& a, const Frag<DT>& b) {
-    attn::f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    attn::f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == kF32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t aw[4] = {a.v[i].x, a.v[i].y, a.v[i].z, a.v[i].w};
             const uint32_t bw[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(bw[e]), c, 0, 0, 0);
+            for (int e = 0; e < 4; e += 2) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(bw[e]), c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e + 1]), __uint_as_float(bw[e + 1]), c1,
+                                                          0, 0, 0);
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b.v[i]), c);
+        for (int i = 0; i < 4; i += 2) {
+            c0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b.v[i]), c0);
+            c1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i + 1]), attn::as_op8<DT>(b.v[i + 1]), c1);
+        }
     }
-    return c;
+    return c0 + c1;
 }
 
 // address of key s (head kh) of request b, or nullptr when its block is out of range
@@ -97,8 +104,9 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int t0 = blockIdx.x * 64 + 16 * w;  // this wave's rows t0 .. t0+15
-    if (t0 >= L) return;                      // no barriers in this kernel
+    // the last query tiles have the most keys: dispatch them first
+    const int t0 = (gridDim.x - 1 - blockIdx.x) * 64 + 16 * w;  // this wave's rows t0 .. t0+15
+    if (t0 >= L) return;                                        // no barriers in this kernel
     const int kh = h / (p.H / p.N);
     Frag<DT> qf;
     load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
@@ -107,12 +115,20 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
     const int t_last = min(t0 + 15, L - 1);
-    for (int s0 = 0; s0 <= t_last; s0 += 16) {
-        const uint8_t* kr = key_row(p, b, s0, kh, es);  // the 16 keys share one block
-        if (kr == nullptr) continue;
-        const int s = s0 + r;
-        Frag<DT> kf;
+    // key tile s0 (16 keys in one block) with the next tile's keys loaded ahead
+    auto fetch = [&](int s0, Frag<DT>& kf) -> bool {
+        const uint8_t* kr = key_row(p, b, s0, kh, es);
+        if (kr == nullptr) return false;
         load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+        return true;
+    };
+    Frag<DT> kf;
+    bool have = fetch(0, kf);
+    for (int s0 = 0; s0 <= t_last; s0 += 16) {
+        Frag<DT> kn;
+        const bool next = s0 + 16 <= t_last && fetch(s0 + 16, kn);
+        if (have) {
+        const int s = s0 + r;
         const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -124,6 +140,9 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
                 m[i] = mn;
             }
         }
+        }
+        kf = kn;
+        have = next;
     }
     // merge the 16 key columns of each row
 #pragma unroll
@@ -143,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int s0 = blockIdx.x * 64 + 16 * w;  // this wave's keys s0 .. s0+15
+    const int s0 = blockIdx.x * 64 + 16 * w;  // this wave's keys s0 .. s0+15 (the first keys have the most rows)
     if (s0 >= L) return;
     const int kh = h / (p.H / p.N);
     const uint8_t* kr = key_row(p, b, s0, kh, es);
@@ -152,17 +171,28 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
         Frag<DT> kf;
         load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
         const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
+        // query tile t0 with the next tile's rows loaded ahead
+        auto fetch = [&](int t0, Frag<DT>& qf, float& lt) {
+            const int t = t0 + r;
+            load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t, L - 1)) * p.H + h) * D * es, j);
+            lt = t < L ? lse[t] : 0.f;
+        };
+        Frag<DT> qf;
+        float lt;
+        fetch(s0, qf, lt);
         for (int t0 = s0; t0 < L; t0 += 16) {
             const int t = t0 + r;
-            Frag<DT> qf;
-            load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t, L - 1)) * p.H + h) * D * es, j);
-            const float lt = t < L ? lse[t] : 0.f;
+            Frag<DT> qn;
+            float ln = 0.f;
+            if (t0 + 16 < L) fetch(t0 + 16, qn, ln);
             const attn::f32x4 c = dot_tile<DT>(kf, qf);  // C[key 4j+i][row r]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + 4 * j + i;
                 if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
             }
+            qf = qn;
+            lt = ln;
         }
     }
 #pragma unroll
