@@ -262,9 +262,14 @@ def other_workloads(qs, W, dev, stream, reps=50):
     t_s = _timed(c4_select, reps, stream)
     t_a = _timed(c4_attend, reps, stream)
     t_step = _timed(lambda: (c4_select(), c4_attend()), reps, stream)
+    t_fused = _timed(lambda: qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
+                                                      wl.block_tables, wl.seq_lens, wl.k,
+                                                      tokens_since_update=wl.tsmu, flags=wl.flags, out=out,
+                                                      selected=sel, n_selected=ns), reps, stream)
     sb, ab = step_bytes(wl, sel.cpu(), ns.cpu(), wl.tsmu.cpu())
     res["config4_long_context_bf16"] = {
         "step_us": round(t_step * 1e3, 2), "steps_per_s": round(1000.0 / t_step, 1),
+        "fused_step_us": round(t_fused * 1e3, 2), "fused_steps_per_s": round(1000.0 / t_fused, 1),
         "step_bytes": int(sb + ab), "step_gbps": gbps(sb + ab, t_step),
         "select_us": round(t_s * 1e3, 2), "select_gbps": gbps(sb, t_s),
         "attention_us": round(t_a * 1e3, 2), "attention_gbps": gbps(ab, t_a),

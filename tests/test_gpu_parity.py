@@ -566,7 +566,8 @@ FUSED_CASES = [
     (72, 3, 32, 8, 128, [128 * 200 + 17, 128 * 64, 0], 8, torch.bfloat16, 3, [5, 0, 0]),   # one kernel, splits
     (73, 2, 40, 2, 64, [64 * 100 + 9, 64 * 3], 12, torch.bfloat16, 3, [9, -1]),  # G=20: two head chunks
     (74, 2, 40, 2, 16, [16 * 200 + 1, 16 * 20], 7, torch.float32, 1, None),       # fp32 G=20: three chunks
-    (75, 2, 16, 8, 128, [128 * 600, 128 * 300 + 3], 64, torch.bfloat16, 3, [127, 0]),  # long rows: two kernels
+    (75, 2, 16, 8, 128, [128 * 600, 128 * 300 + 3], 64, torch.bfloat16, 3, [127, 0]),  # long rows: prescored
+    (79, 3, 8, 2, 32, [32 * 400 + 5, 32 * 90, 1], 20, torch.float32, 3, [4, 0, 0]),   # fp32 prescored
     (76, 1, 8, 8, 32, [32 * 64], 65, torch.bfloat16, 0, None),                    # k > 64: two kernels
     (77, 128, 16, 8, 16, [16 * (20 + (7 * b) % 23) + b % 5 for b in range(128)], 6, torch.bfloat16, 3,
      [b % 16 for b in range(128)]),                                               # 1024 rows: one kernel, no split
@@ -622,6 +623,34 @@ def test_select_attn_config1(qs, oracle):
     ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(sel),
                                     tnp(ns), wl.N)
     assert np.abs(out.cpu().numpy() - ref).max() <= 1e-4
+
+
+def test_select_attn_config4_sampled(qs, oracle):
+    """Long-context shape through qs_select_attn_decode (scoring grid, then per-split top-k
+    + attention, then combine): sampled requests against the oracle."""
+    wl = W.config4(device=DEV)
+    say("select+attention config4 (full size)")
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=DEV)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)
+    out = qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                   wl.seq_lens, wl.k, tokens_since_update=wl.tsmu, flags=wl.flags, selected=sel,
+                                   n_selected=ns)
+    torch.cuda.synchronize()
+    reqs = [1, 6]
+    sub, nbs = sub_workload(wl, reqs)
+    omx, omn = oracle.build_metadata(sub.k_cache, sub.block_tables, sub.meta_seq_lens, sub.meta_tables,
+                                     sub.num_meta_blocks)
+    osel, ons, osc = oracle.block_select(sub.query, omx, omn, sub.meta_tables, sub.seq_lens, wl.k, tsmu=sub.tsmu,
+                                         flags=sub.flags)
+    gsel, gns = tnp(sel)[reqs], tnp(ns)[reqs]
+    compare_quest(gsel, gns, osel, ons, osc, nbs, wl.k)
+    ref = oracle.sparse_attn_decode(sub.query, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens, gsel, gns,
+                                    wl.N)
+    err = np.abs(out.float().cpu().numpy()[reqs] - ref).max()
+    assert err <= 2e-2, f"attention err {err:.3e}"
 
 
 def test_select_attn_config5_sampled(qs, oracle):

@@ -19,8 +19,13 @@
 // too few rows to fill the chip and the rows are short, each of a row's slot splits
 // recomputes the (deterministic, hence identical) selection from L2-resident metadata and
 // the splits' partials are merged by the attention combine pass. Long rows with few
-// requests go through the separate kernels instead (a split scoring grid, then attention).
+// requests are scored first by the selection's wide scoring grid (the scores go to the
+// workspace); each attention workgroup then stages its row's scores in LDS and runs the
+// top-k itself, so the separate top-k launch and the selection's round trip through HBM
+// disappear. Rows with more than 64 selected blocks use the two operations' kernels.
 #include <math.h>
+
+#include <type_traits>
 
 #include "attn_dev.h"
 #include "qs_device.h"
@@ -52,9 +57,10 @@ static_assert(kFusedMaxK <= kWave, "the selection fits one slot table");
 static_assert(kFusedMaxCap <= sel::kLdsScoreCap, "scores stay on chip");
 
 // Selection of row (b, n) into LDS (every thread must call it). Returns n_selected; the
-// entries are at lds + kOffSel. Split 0 of head chunk 0 also writes them to the caller's
-// selected / n_selected when those are given.
-template <int DT>
+// entries are at lds + kOffSel. With PRESCORED the row's scores come from the scoring
+// grid's output (p.ws_scores) instead of being computed here. Split 0 of head chunk 0
+// also writes the selection to the caller's selected / n_selected when those are given.
+template <int DT, bool PRESCORED>
 __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int n, uint8_t* lds, bool publish) {
     float* scores = (float*)(lds + kOffScores);
     uint32_t* hist = (uint32_t*)(lds + kOffHist);
@@ -66,8 +72,26 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     int32_t* nsel = (int32_t*)(lds + kOffNsel);
     const int cap = p.mmbpr * p.BS;
     const sel::RowInfo r = sel::row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
-    sel::score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, 0,
-                                 r.nb, scores, false, qstage, mt_stage);
+    if constexpr (PRESCORED) {
+        // all loads of a thread's entries in flight together, then into LDS
+        const float* src = p.ws_scores + (size_t(b) * p.N + n) * cap;
+        for (int i0 = 0; i0 < r.nb; i0 += 4 * kThreads) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + threadIdx.x;
+                v[u] = i < r.nb ? src[i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + threadIdx.x;
+                if (i < r.nb) scores[i] = v[u];
+            }
+        }
+    } else {
+        sel::score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+                                   0, r.nb, scores, false, qstage, mt_stage);
+    }
     __syncthreads();
     sel::topk_emit(scores, r.nb, r.F, p.k, selv, nsel, hist, sh, wsum);
     __syncthreads();
@@ -81,25 +105,25 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
 }
 
 // bf16 / f16: grid (splits x head chunks, KV head, request)
-template <int DT>
+template <int DT, bool PRESCORED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void select_attn_mfma_kernel(sel::SelParams sp, attn::AttnParams ap) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[attn::kMfmaLdsBytes];
     const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
     const int n = blockIdx.y, b = blockIdx.z;
-    const int ns = select_phase<DT>(sp, b, n, lds, split == 0 && hcix == 0);
+    const int ns = select_phase<DT, PRESCORED>(sp, b, n, lds, split == 0 && hcix == 0);
     attn::mfma_body<DT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
 }
 
 // f32: the vector-ALU attention; its merge buffer overlays the dead scoring scratch
-template <int HC>
+template <int HC, bool PRESCORED>
 __global__ __launch_bounds__(kThreads) void select_attn_vec_kernel(sel::SelParams sp, attn::AttnParams ap) {
     constexpr int kRedBytes = attn::vec_red_floats<HC>() * 4;
     constexpr int kLds = kSelectLds > kOffScores + kRedBytes ? kSelectLds : kOffScores + kRedBytes;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
     const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
     const int n = blockIdx.y, b = blockIdx.z;
-    const int ns = select_phase<kF32>(sp, b, n, lds, split == 0 && hcix == 0);
+    const int ns = select_phase<kF32, PRESCORED>(sp, b, n, lds, split == 0 && hcix == 0);
     attn::vec_body<kF32, kF32, HC>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns,
                                    (float*)(lds + kOffScores));
 }
@@ -112,10 +136,13 @@ FusedPlan plan_select_attn(int B, int H, int N, int BS, int mmbpr, int k, int dt
     FusedPlan f{};
     const long long cap = (long long)mmbpr * BS;
     f.attn = plan_sparse_attn(B, H, N, 128, N, k, dtype, dtype);
+    f.sel = plan_block_select(B, N, BS, mmbpr);
     const long long rows = (long long)B * N * f.attn.hchunks;
-    f.fused = k <= kFusedMaxK && cap <= kFusedMaxCap && mmbpr <= sel::kMtStageCap &&
-              (rows >= kFusedRows || cap <= kFusedSplitMaxCap);
-    if (f.fused) {
+    const bool fits = k <= kFusedMaxK && cap <= kFusedMaxCap && mmbpr <= sel::kMtStageCap;
+    if (fits && (rows >= kFusedRows || cap <= kFusedSplitMaxCap)) f.mode = FusedPlan::kOneKernel;
+    else if (fits) f.mode = FusedPlan::kPrescored;
+    else f.mode = FusedPlan::kSeparate;
+    if (f.mode != FusedPlan::kSeparate) {
         long long splits = 1;
         if (rows < kFusedRows) {
             const long long rows1 = rows > 0 ? rows : 1;
@@ -126,14 +153,14 @@ FusedPlan plan_select_attn(int B, int H, int N, int BS, int mmbpr, int k, int dt
         f.attn.spb = int((k + splits - 1) / splits);
         f.attn.splits = (k + f.attn.spb - 1) / f.attn.spb;
         const size_t part = f.attn.splits > 1 ? size_t(rows) * f.attn.splits * f.attn.hc * attn::PSTRIDE * 4 : 0;
-        f.attn.part_off = 0;
+        const size_t scores = f.mode == FusedPlan::kPrescored ? size_t(B) * N * cap * 4 : 0;
+        f.sel_off = 0;                      // prescored: the scores
+        f.attn.part_off = align256(scores);  // the attention partials
         f.attn.bytes = align256(part);
-        f.bytes = f.attn.bytes < 256 ? 256 : f.attn.bytes;
-        f.sel = plan_block_select(B, N, BS, mmbpr);
-        f.sel_off = f.idx_off = f.nidx_off = 0;
+        f.bytes = f.attn.part_off + f.attn.bytes;
+        f.attn_off = f.idx_off = f.nidx_off = 0;
     } else {
         // separate kernels: select into workspace-held (or the caller's) selection, then attend
-        f.sel = plan_block_select(B, N, BS, mmbpr);
         f.sel_off = 0;
         f.attn.part_off = 0;
         f.attn_off = align256(f.sel.bytes);
@@ -147,7 +174,7 @@ FusedPlan plan_select_attn(int B, int H, int N, int BS, int mmbpr, int k, int dt
 
 hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const FusedPlan& pl, hipStream_t st) {
     uint8_t* ws = (uint8_t*)a.workspace;
-    if (!pl.fused) {
+    if (pl.mode == FusedPlan::kSeparate) {
         SelectArgs s2 = s;
         AttnArgs a2 = a;
         if (!s2.selected) {
@@ -162,26 +189,39 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
         if (e != hipSuccess) return e;
         return launch_sparse_attn(a2, pl.attn, st);
     }
+    const bool pre = pl.mode == FusedPlan::kPrescored;
+    float* scores = (float*)(ws + pl.sel_off);
+    if (pre) {
+        hipError_t e = launch_select_scores(s, pl.sel, scores, st);
+        if (e != hipSuccess) return e;
+    }
     const AttnPlan& ap = pl.attn;
     sel::SelParams sp{(const uint8_t*)s.query, (const uint8_t*)s.maxb, (const uint8_t*)s.minb, s.num_meta,
                       s.meta_tables, s.mmbpr, s.seq_lens, s.tsmu, s.flags, s.k, s.H, s.N, s.BS, s.selected,
-                      s.n_selected, nullptr, nullptr};
+                      s.n_selected, nullptr, pre ? scores : nullptr};
     attn::AttnParams prm{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache, nullptr,
                          nullptr, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens, nullptr, nullptr, a.H, a.N,
                          a.BS, a.N, a.k, ap.hpr, ap.hchunks, ap.splits, ap.spb, a.scale * attn::kLog2e,
                          (uint8_t*)a.out, (float*)(ws + ap.part_off)};
     dim3 grid(unsigned(ap.splits * ap.hchunks), unsigned(a.N), unsigned(a.B));
-    if (ap.mfma) {
-        if (a.q_dtype == kF16) hipLaunchKernelGGL(select_attn_mfma_kernel<kF16>, grid, dim3(kThreads), 0, st, sp, prm);
-        else hipLaunchKernelGGL(select_attn_mfma_kernel<kBF16>, grid, dim3(kThreads), 0, st, sp, prm);
-    } else {
-        switch (ap.hc) {
-            case 1: hipLaunchKernelGGL(select_attn_vec_kernel<1>, grid, dim3(kThreads), 0, st, sp, prm); break;
-            case 2: hipLaunchKernelGGL(select_attn_vec_kernel<2>, grid, dim3(kThreads), 0, st, sp, prm); break;
-            case 4: hipLaunchKernelGGL(select_attn_vec_kernel<4>, grid, dim3(kThreads), 0, st, sp, prm); break;
-            default: hipLaunchKernelGGL(select_attn_vec_kernel<8>, grid, dim3(kThreads), 0, st, sp, prm); break;
+    auto launch = [&](auto pre_c) {
+        constexpr bool P = decltype(pre_c)::value;
+        if (ap.mfma) {
+            if (a.q_dtype == kF16)
+                hipLaunchKernelGGL((select_attn_mfma_kernel<kF16, P>), grid, dim3(kThreads), 0, st, sp, prm);
+            else
+                hipLaunchKernelGGL((select_attn_mfma_kernel<kBF16, P>), grid, dim3(kThreads), 0, st, sp, prm);
+        } else {
+            switch (ap.hc) {
+                case 1: hipLaunchKernelGGL((select_attn_vec_kernel<1, P>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                case 2: hipLaunchKernelGGL((select_attn_vec_kernel<2, P>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                case 4: hipLaunchKernelGGL((select_attn_vec_kernel<4, P>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                default: hipLaunchKernelGGL((select_attn_vec_kernel<8, P>), grid, dim3(kThreads), 0, st, sp, prm); break;
+            }
         }
-    }
+    };
+    if (pre) launch(std::true_type{});
+    else launch(std::false_type{});
     if (ap.splits > 1) return attn::launch_combine(prm, a.B, ap.hc, a.q_dtype, st);
     return hipGetLastError();
 }

@@ -56,6 +56,8 @@ struct SelectArgs {
     void* workspace;
 };
 hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& p, hipStream_t s);
+// the split-mode scoring grid alone: scores [B, N, mmbpr * BS] (forced blocks not written)
+hipError_t launch_select_scores(const SelectArgs& a, const SelectPlan& p, float* scores, hipStream_t s);
 
 // ---- probe select ------------------------------------------------------------------
 constexpr int kProbeMaxBlocks = 4096;
@@ -137,7 +139,10 @@ hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s);
 
 // ---- fused select + attention -------------------------------------------------------
 struct FusedPlan {
-    bool fused;        // one kernel (selection into LDS, then attention); else the two paths
+    // kOneKernel: each workgroup scores its row into LDS, selects and attends;
+    // kPrescored: a scoring grid writes the scores, then each attention workgroup selects
+    // from them in LDS and attends; kSeparate: the two operations' kernels
+    enum Mode { kOneKernel, kPrescored, kSeparate } mode;
     SelectPlan sel;
     AttnPlan attn;
     size_t sel_off, attn_off, idx_off, nidx_off, bytes;  // workspace regions

@@ -138,6 +138,19 @@ SelectPlan plan_block_select(int B, int N, int BS, int mmbpr) {
     return p;
 }
 
+hipError_t launch_select_scores(const SelectArgs& a, const SelectPlan& pl, float* scores, hipStream_t s) {
+    SelParams p{(const uint8_t*)a.query, (const uint8_t*)a.maxb, (const uint8_t*)a.minb, a.num_meta, a.meta_tables,
+                a.mmbpr, a.seq_lens, a.tsmu, a.flags, a.k, a.H, a.N, a.BS, nullptr, nullptr, nullptr, scores};
+    dim3 g1(unsigned(pl.n_chunks), unsigned(a.N), unsigned(a.B));
+    if (a.dtype == kBF16)
+        hipLaunchKernelGGL(select_score_kernel<kBF16>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+    else if (a.dtype == kF16)
+        hipLaunchKernelGGL(select_score_kernel<kF16>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+    else
+        hipLaunchKernelGGL(select_score_kernel<kF32>, g1, dim3(kThreads), 0, s, p, pl.chunk);
+    return hipGetLastError();
+}
+
 hipError_t launch_block_select(const SelectArgs& a, const SelectPlan& pl, hipStream_t s) {
     SelParams p{(const uint8_t*)a.query, (const uint8_t*)a.maxb, (const uint8_t*)a.minb, a.num_meta, a.meta_tables,
                 a.mmbpr, a.seq_lens, a.tsmu, a.flags, a.k, a.H, a.N, a.BS, a.selected, a.n_selected,
