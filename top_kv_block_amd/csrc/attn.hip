@@ -15,8 +15,10 @@
 // G query heads per KV head the work per token is a [G x 128] x [128 x T] product and on
 // the vector ALU (no packed fp32 here) it would cost about as many cycles as the HBM
 // stream: per 32-token chunk a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
-// (K rows load straight from HBM into the A operand, 16 B per lane; the heads are the
-// 16 columns), does the online softmax on the accumulator registers (each lane owns one
+// (K rows are loaded as whole 256-B rows, 16 lanes each, staged through the wave's LDS
+// tile and read back in the A-operand layout: a direct A-operand load would touch 16 rows
+// x 64 B per instruction and streams ~2% slower; the heads are the 16 columns), does the
+// online softmax on the accumulator registers (each lane owns one
 // head, so the running max/sum and the output rescale need no lane exchange), rounds P
 // to bf16 and accumulates O^T = V^T P^T with 8 more MFMAs. V^T comes from a per-wave
 // LDS tile that the wave writes transposed (8x8 register transposes + 16-byte stores).

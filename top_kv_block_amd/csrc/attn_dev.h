@@ -172,15 +172,16 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
         const uint16_t* kb = (const uint16_t*)p.kc + (size_t(phys) * p.BS * p.N + kh) * D;
         const uint16_t* vb = (const uint16_t*)p.vc + (size_t(phys) * p.BS * p.N + kh) * D;
 
-        // K: tile tau row r = c16 is token tb + 8*(r/4) + 4*tau + r%4 (so that lane group j
-        // ends up holding tokens tb + 8j .. 8j+7 in its accumulators)
-        u32x4 kr[2][4];
+        // K: loaded like V (16 lanes per 256-B token row, whole cache lines per instruction)
+        // and staged through this wave's LDS tile, from which each lane reads its MFMA A
+        // operand. Tile tau row r = c16 is token tb + 8*(r/4) + 4*tau + r%4 (so that lane
+        // group j ends up holding tokens tb + 8j .. 8j+7 in its accumulators).
+        u32x4 kn[8];
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            const int t = tb + 8 * (c16 >> 2) + 4 * tau + (c16 & 3);
+        for (int u = 0; u < 8; ++u) {
+            const int t = tb + 8 * j + u;
             const int tl = t < nt ? t : 0;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kr[tau][ks] = ld16(kb + size_t(tl) * tstride + 32 * ks + 8 * j);
+            kn[u] = ld16(kb + size_t(tl) * tstride + 8 * c16);
         }
         // V: lane (c16, j) loads tokens tb + 8j + u, channels 8*c16 .. +7
         u32x4 vr[8];
@@ -191,15 +192,25 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
             vr[u] = ld16(vb + size_t(tl) * tstride + 8 * c16);
         }
 
-        // S^T (tokens x heads): lane holds tokens tb + 8j + 4*tau + i for head c16
+        constexpr int KP = 272;  // K tile pitch: a 256-B token row + 16 B
+        static_assert(32 * KP <= kVtBytes, "the K tile fits the wave's LDS tile");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) st16(vt + (8 * j + u) * KP + 16 * c16, kn[u]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         f32x4 sacc[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int tr = 8 * (c16 >> 2) + 4 * tau + (c16 & 3);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                sacc[tau] = mfma16x16x32<DT>(as_op8<DT>(kr[tau][ks]), qb[ks], sacc[tau]);
+                sacc[tau] = mfma16x16x32<DT>(as_op8<DT>(ld16(vt + tr * KP + 64 * ks + 16 * j)), qb[ks], sacc[tau]);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         float sv[8];
         float cmax = -INFINITY;
 #pragma unroll
