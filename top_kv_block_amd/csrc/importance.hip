@@ -97,16 +97,59 @@ __device__ __forceinline__ const uint8_t* key_row(const ImpParams& p, int b, int
     return p.kc + ((size_t(phys) * p.BS + s % p.BS) * p.N + kh) * D * esize;
 }
 
+// A 16-row operand tile shared by the workgroup's four waves through LDS: the workgroup
+// loads it once (each thread 16-byte pieces of whole rows), every wave reads its
+// fragment from LDS. Rows are padded by 16 B against bank conflicts. Two buffers: the
+// next tile is fetched into registers while the current one is multiplied.
+template <int DT>
+struct Tile {
+    static constexpr int kRowBytes = D * elem_bytes(DT);        // 512 (fp32) or 256
+    static constexpr int kPitch = kRowBytes + 16;
+    static constexpr int kPieces = 16 * kRowBytes / 16;         // 16-byte pieces per tile
+    static constexpr int kPerThread = kPieces / kThreads;       // 2 (fp32) or 1
+    static constexpr int kBytes = 16 * kPitch;
+    static_assert(kPieces % kThreads == 0, "whole pieces per thread");
+};
+
+// this thread's pieces of a 16-row tile: row i of the tile starts at row_ptr(i)
+template <int DT, class RowPtr>
+__device__ __forceinline__ void tile_fetch(u32x4 (&v)[Tile<DT>::kPerThread], RowPtr row_ptr) {
+    constexpr int ppr = Tile<DT>::kRowBytes / 16;  // pieces per row
+#pragma unroll
+    for (int u = 0; u < Tile<DT>::kPerThread; ++u) {
+        const int piece = threadIdx.x + u * kThreads;
+        v[u] = ld16(row_ptr(piece / ppr) + 16 * (piece % ppr));
+    }
+}
+template <int DT>
+__device__ __forceinline__ void tile_store(uint8_t* buf, const u32x4 (&v)[Tile<DT>::kPerThread]) {
+    constexpr int ppr = Tile<DT>::kRowBytes / 16;
+#pragma unroll
+    for (int u = 0; u < Tile<DT>::kPerThread; ++u) {
+        const int piece = threadIdx.x + u * kThreads;
+        st16(buf + (piece / ppr) * Tile<DT>::kPitch + 16 * (piece % ppr), v[u]);
+    }
+}
+// this lane's operand slice (row r, channels 32j .. 32j+31) from an LDS tile
+template <int DT>
+__device__ __forceinline__ void frag_from_tile(Frag<DT>& f, const uint8_t* buf, int r, int j) {
+    const uint8_t* q = buf + r * Tile<DT>::kPitch + 32 * j * elem_bytes(DT);
+#pragma unroll
+    for (int i = 0; i < Frag<DT>::kVecs; ++i) f.v[i] = ld16(q + 16 * i);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][Tile<DT>::kBytes];
     const int b = blockIdx.z, h = blockIdx.y;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
     // the last query tiles have the most keys: dispatch them first
-    const int t0 = (gridDim.x - 1 - blockIdx.x) * 64 + 16 * w;  // this wave's rows t0 .. t0+15
-    if (t0 >= L) return;                                        // no barriers in this kernel
+    const int tw = (gridDim.x - 1 - blockIdx.x) * 64;  // the workgroup's rows tw .. tw+63
+    if (tw >= L) return;                              // whole workgroup
+    const int t0 = tw + 16 * w;                       // this wave's rows t0 .. t0+15
     const int kh = h / (p.H / p.N);
     Frag<DT> qf;
     load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
@@ -114,35 +157,40 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     float m[4], l[4];  // online max / sum of 2^x over this lane's key column, rows 4j + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
-    const int t_last = min(t0 + 15, L - 1);
-    // key tile s0 (16 keys in one block) with the next tile's keys loaded ahead
-    auto fetch = [&](int s0, Frag<DT>& kf) -> bool {
+    const int s_end = min(tw + 63, L - 1);  // last key any wave needs
+    // key tile s0 (16 keys in one block): rows past L repeat the last key (masked)
+    auto fetch = [&](int s0, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
         const uint8_t* kr = key_row(p, b, s0, kh, es);
         if (kr == nullptr) return false;
-        load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+        tile_fetch<DT>(v, [&](int i) { return kr + size_t(min(i, L - 1 - s0)) * p.N * D * es; });
         return true;
     };
-    Frag<DT> kf;
-    bool have = fetch(0, kf);
-    for (int s0 = 0; s0 <= t_last; s0 += 16) {
-        Frag<DT> kn;
-        const bool next = s0 + 16 <= t_last && fetch(s0 + 16, kn);
-        if (have) {
-        const int s = s0 + r;
-        const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
+    u32x4 nv[Tile<DT>::kPerThread];
+    bool have = fetch(0, nv);
+    int buf = 0;
+    for (int s0 = 0; s0 <= s_end; s0 += 16, buf ^= 1) {
+        if (have) tile_store<DT>(kt[buf], nv);
+        const bool cur = have;
+        __syncthreads();  // tile s0 is in kt[buf]; the reads of kt[buf] two tiles ago are done
+        have = s0 + 16 <= s_end && fetch(s0 + 16, nv);
+        if (cur && s0 <= t0 + 15 && t0 < L) {  // this wave has rows that see these keys
+            Frag<DT> kf;
+            frag_from_tile<DT>(kf, kt[buf], r, j);
+            const int s = s0 + r;
+            const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 4 * j + i;
-            if (s <= t && s < L) {
-                const float x = c[i] * p.scale2;
-                const float mn = fmaxf(m[i], x);
-                l[i] = l[i] * exp2f(m[i] - mn) + exp2f(x - mn);
-                m[i] = mn;
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 4 * j + i;
+                if (s <= t && s < L) {
+                    // one exp2 per score: a new maximum rescales the sum, any other score adds
+                    const float x = c[i] * p.scale2;
+                    const float d = x - m[i];
+                    const float e = exp2f(-fabsf(d));  // m = -inf: d = +inf, e = 0
+                    l[i] = d > 0.f ? l[i] * e + 1.f : l[i] + e;
+                    m[i] = fmaxf(m[i], x);
+                }
             }
         }
-        }
-        kf = kn;
-        have = next;
     }
     // merge the 16 key columns of each row
 #pragma unroll
@@ -158,41 +206,49 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
+    __shared__ __attribute__((aligned(16))) uint8_t qt[2][Tile<DT>::kBytes];
+    __shared__ float lt_s[2][16];
     const int b = blockIdx.z, h = blockIdx.y;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int s0 = blockIdx.x * 64 + 16 * w;  // this wave's keys s0 .. s0+15 (the first keys have the most rows)
-    if (s0 >= L) return;
+    const int sw = blockIdx.x * 64;  // the workgroup's keys sw .. sw+63 (the first keys have the most rows)
+    if (sw >= L) return;
+    const int s0 = sw + 16 * w;      // this wave's keys s0 .. s0+15
     const int kh = h / (p.H / p.N);
-    const uint8_t* kr = key_row(p, b, s0, kh, es);
+    const bool live = s0 < L;
+    const uint8_t* kr = live ? key_row(p, b, s0, kh, es) : nullptr;
+    Frag<DT> kf;
+    if (kr != nullptr) load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+    const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};  // keys 4j + i, partial over this lane's query column
-    if (kr != nullptr) {
-        Frag<DT> kf;
-        load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
-        const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
-        // query tile t0 with the next tile's rows loaded ahead
-        auto fetch = [&](int t0, Frag<DT>& qf, float& lt) {
+    // query tile t0: 16 rows of head h (rows past L repeat the last row, masked) and their lse
+    auto fetch = [&](int t0, u32x4 (&v)[Tile<DT>::kPerThread], float& lv) {
+        tile_fetch<DT>(v, [&](int i) {
+            return p.q + ((size_t(b) * p.max_len + min(t0 + i, L - 1)) * p.H + h) * D * es;
+        });
+        lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
+    };
+    u32x4 nv[Tile<DT>::kPerThread];
+    float nl;
+    fetch(sw, nv, nl);
+    int buf = 0;
+    for (int t0 = sw; t0 < L; t0 += 16, buf ^= 1) {
+        tile_store<DT>(qt[buf], nv);
+        if (threadIdx.x < 16) lt_s[buf][threadIdx.x] = nl;
+        __syncthreads();
+        if (t0 + 16 < L) fetch(t0 + 16, nv, nl);
+        if (kr != nullptr && t0 + 15 >= s0) {  // some row of the tile sees this wave's keys
+            Frag<DT> qf;
+            frag_from_tile<DT>(qf, qt[buf], r, j);
             const int t = t0 + r;
-            load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t, L - 1)) * p.H + h) * D * es, j);
-            lt = t < L ? lse[t] : 0.f;
-        };
-        Frag<DT> qf;
-        float lt;
-        fetch(s0, qf, lt);
-        for (int t0 = s0; t0 < L; t0 += 16) {
-            const int t = t0 + r;
-            Frag<DT> qn;
-            float ln = 0.f;
-            if (t0 + 16 < L) fetch(t0 + 16, qn, ln);
+            const float lt = lt_s[buf][r];
             const attn::f32x4 c = dot_tile<DT>(kf, qf);  // C[key 4j+i][row r]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + 4 * j + i;
                 if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
             }
-            qf = qn;
-            lt = ln;
         }
     }
 #pragma unroll
