@@ -70,28 +70,34 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-// combine pass for split rows: merges the splits' partials in split order. One thread
-// per output element (request, head, channel); each split's (max, sum, acc) loads are
-// issued ahead of the merge so they are in flight together.
+// combine pass for split rows: merges the splits' partials. Four lanes per output
+// element (request, head, channel): lane u merges splits u, u+4, u+8, ... (their loads
+// issued together), then the four states are merged across the lanes with two xor
+// shuffles. The pairwise merge is symmetric in its operands (max, and sums of products,
+// whose fp additions commute), so both lanes of a pair hold bitwise the same state and
+// the result does not depend on scheduling.
 // ------------------------------------------------------------------------------------
+constexpr int kCombineLanes = 4;
 constexpr int kCombineBatch = 8;
 
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, int hc_cap, int out_dt) {
-    const int e = blockIdx.x * kThreads + threadIdx.x;  // (head, channel) of request b
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    const int e = gid / kCombineLanes, u = gid % kCombineLanes;  // (head, channel) of request b
     const int b = blockIdx.y;
-    if (e >= p.H * D) return;
-    const int d = e % D, h = e / D;
+    const bool live = e < p.H * D;  // no early return: the lanes of an element shuffle together
+    const int ee = live ? e : 0;
+    const int d = ee % D, h = ee / D;
     const int s = h / p.hpr, hh = h % p.hpr;
     const int hcix = hh / hc_cap, g = hh % hc_cap;
     const int row = b * p.sel_heads + s;
     const float* base = p.part + ((size_t(row) * p.hchunks + hcix) * p.splits) * hc_cap * PSTRIDE + size_t(g) * PSTRIDE;
     const size_t sstride = size_t(hc_cap) * PSTRIDE;
     float M = -INFINITY, Ls = 0.f, A = 0.f;
-    for (int sp0 = 0; sp0 < p.splits; sp0 += kCombineBatch) {
+    for (int sp0 = u; sp0 < p.splits; sp0 += kCombineLanes * kCombineBatch) {
         float mv[kCombineBatch], lv[kCombineBatch], av[kCombineBatch];
 #pragma unroll
         for (int t = 0; t < kCombineBatch; ++t) {
-            const int sp = min(sp0 + t, p.splits - 1);
+            const int sp = min(sp0 + t * kCombineLanes, p.splits - 1);
             const float* rec = base + size_t(sp) * sstride;
             mv[t] = rec[D];
             lv[t] = rec[D + 1];
@@ -99,11 +105,14 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p, in
         }
 #pragma unroll
         for (int t = 0; t < kCombineBatch; ++t)
-            if (sp0 + t < p.splits) merge_state(M, Ls, &A, 1, mv[t], lv[t], &av[t]);
+            if (sp0 + t * kCombineLanes < p.splits) merge_state(M, Ls, &A, 1, mv[t], lv[t], &av[t]);
     }
-    const float v = (Ls > 0.f) ? A / Ls : 0.f;
-    const size_t o = (size_t(b) * p.H + h) * D + d;
-    store_out(p.out, o, v, out_dt);
+#pragma unroll
+    for (int o = 1; o < kCombineLanes; o <<= 1) {
+        const float m2 = __shfl_xor(M, o, kWave), l2 = __shfl_xor(Ls, o, kWave), a2 = __shfl_xor(A, o, kWave);
+        merge_state(M, Ls, &A, 1, m2, l2, &a2);
+    }
+    if (live && u == 0) store_out(p.out, (size_t(b) * p.H + h) * D + d, (Ls > 0.f) ? A / Ls : 0.f, out_dt);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -175,7 +184,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t
 }
 
 hipError_t attn::launch_combine(const AttnParams& p, int B, int hc_cap, int out_dt, hipStream_t s) {
-    const unsigned per_req = unsigned((size_t(p.H) * D + kThreads - 1) / kThreads);
+    const unsigned per_req = unsigned((size_t(p.H) * D * kCombineLanes + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(per_req, unsigned(B)), dim3(kThreads), 0, s, p, hc_cap, out_dt);
     return hipGetLastError();
 }
