@@ -944,3 +944,50 @@ def test_prefill_importance_config3_sampled_heads(qs, oracle):
     for lo in (0, 15):
         _, oh = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, wl.N, heads=(lo, lo + 1))
         check_importance(gh[:, lo], oh[:, lo], f"head {lo}")
+
+
+@pytest.mark.parametrize("lens,k", [([128 * 100 + 5] * 4 + [128 * 40] * 4, 16),        # one kernel, slot splits
+                                    ([128 * 700, 128 * 300 + 9], 48)],                  # scoring grid + top-k/attention
+                         ids=["one_kernel", "prescored"])
+def test_graph_replay_fused_matches_eager(qs, lens, k):
+    """qs_select_attn_decode captured in a HIP graph (each mode, with the combine pass) and
+    replayed with eager work in between: bitwise the eager results every time."""
+    say(f"graph replay fused k={k}")
+    B = len(lens)
+    wl = W.random_case(62, B, 64, 8, 128, lens, k=k, dtype=torch.bfloat16, flags=W.FORCE_SINK | W.FORCE_WINDOW,
+                       tsmu=[5] * B).to(DEV)
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=DEV)
+    ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)
+    out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(qs.select_attn_workspace_bytes(wl.B, wl.H, wl.N, wl.BS, wl.mmbpr, wl.k, qs.QS_BF16),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                 wl.seq_lens, wl.k, tokens_since_update=wl.tsmu, flags=wl.flags, out=out,
+                                 selected=sel, n_selected=ns, workspace_buf=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = (sel.clone(), ns.clone(), out.clone())
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    for rep in range(3):
+        sel.fill_(-7)
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, want[0]) and torch.equal(ns, want[1]), rep
+        assert torch.equal(out.view(torch.int16), want[2].view(torch.int16)), rep
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))
