@@ -2,16 +2,18 @@
  * qsparse.h -- C ABI of the decode-time sparse top-k KV-block attention library
  * (libqsparse.so, HIP kernels for CDNA4 / gfx950).
  *
- * Four operations, run in this order on each decode step:
- *   qs_build_metadata      per-block, per-channel max/min of K (after prefill);
- *   qs_update_metadata     the same for only the blocks completed since the last
- *                          refresh (every BS decoded tokens);
- *   qs_block_select        Quest top-k block selection on the grouped query, optional
- *                          sink / local-window forcing;   (or)
- *   qs_probe_select        probe + prefill-importance + recency block selection;
- *   qs_sparse_attn_decode  exact softmax attention over the selected blocks only;
- *   qs_select_attn_decode  qs_block_select followed by qs_sparse_attn_decode, fused;
- *   qs_prefill_importance  (at prefill) page 1's per-token importance for qs_probe_select.
+ * The operations, in the order a serving loop uses them:
+ *   at prefill
+ *     qs_build_metadata      per-block, per-channel max/min of K;
+ *     qs_prefill_importance  page 1's per-token importance (for qs_probe_select);
+ *   every BS decoded tokens
+ *     qs_update_metadata     max/min of only the blocks completed since the last refresh;
+ *   every decode step
+ *     qs_block_select        Quest top-k block selection on the grouped query, optional
+ *                            sink / local-window forcing;   (or)
+ *     qs_probe_select        probe + prefill-importance + recency block selection;
+ *     qs_sparse_attn_decode  exact softmax attention over the selected blocks only;
+ *     qs_select_attn_decode  qs_block_select then qs_sparse_attn_decode in one call.
  *
  * Sources, cited by page title and section:
  *   [P1] "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择"
@@ -44,7 +46,7 @@
  *     results; its contents on entry are ignored. It must be 256-byte aligned, at least
  *     the size the matching *_workspace_bytes() returns, and not used by calls that may
  *     run concurrently (calls on one stream are ordered). Kernels never synchronise
- *     across workgroups; a call may run as two stream-ordered kernels.
+ *     across workgroups; a call may run as several stream-ordered kernels.
  */
 #ifndef QSPARSE_H
 #define QSPARSE_H
