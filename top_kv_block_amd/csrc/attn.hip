@@ -11,7 +11,8 @@
 // bound. A workgroup takes one selection row (all query heads sharing a KV head, so
 // each K/V row is fetched once for all of them) and a range of its selection slots.
 //
-// bf16 KV with a bf16 query (the serving path) runs on the matrix cores, because with
+// bf16 (or fp16) KV with a query of the same type (the serving path) runs on the matrix
+// cores, because with
 // G query heads per KV head the work per token is a [G x 128] x [128 x T] product and on
 // the vector ALU (no packed fp32 here) it would cost about as many cycles as the HBM
 // stream: per 32-token chunk a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
@@ -20,18 +21,19 @@
 // x 64 B per instruction and streams ~2% slower; the heads are the 16 columns), does the
 // online softmax on the accumulator registers (each lane owns one
 // head, so the running max/sum and the output rescale need no lane exchange), rounds P
-// to bf16 and accumulates O^T = V^T P^T with 8 more MFMAs. V^T comes from a per-wave
+// to the operand format and accumulates O^T = V^T P^T with 8 more MFMAs. V^T comes from a per-wave
 // LDS tile that the wave writes transposed (8x8 register transposes + 16-byte stores).
 // Four waves take interleaved 32-token chunks and merge (max, sum, acc) through LDS.
 //
-// fp32 and int8 KV (small, latency-bound workloads) run on the vector ALU: a token row
+// fp32 and int8 KV, and mixed query / KV types (small, latency-bound workloads), run on
+// the vector ALU in fp32: a token row
 // is read by LPR lanes with 16-byte loads, dots reduce by shuffles, each lane group is an
 // independent online-softmax worker. int8: the query row is quantised in fp32 (absmax /
 // 127, half-to-even, clamp +-127) and dots use v_dot4_i32_i8 with exact int32 sums.
 //
 // When there are too few rows to fill the chip the slots are split over workgroups,
-// each writing (max, sum, acc) partials, and a small second kernel merges them in split
-// order (no cross-workgroup synchronisation inside a kernel).
+// each writing (max, sum, acc) partials, and a small second kernel merges them in a
+// fixed order (no cross-workgroup synchronisation inside a kernel).
 #include <math.h>
 
 #include <type_traits>
