@@ -572,6 +572,8 @@ FUSED_CASES = [
     (77, 128, 16, 8, 16, [16 * (20 + (7 * b) % 23) + b % 5 for b in range(128)], 6, torch.bfloat16, 3,
      [b % 16 for b in range(128)]),                                               # 1024 rows: one kernel, no split
     (78, 2, 32, 8, 128, [128 * 150 + 3, 128 * 20], 8, torch.float16, 3, [2, 0]),  # f16, one kernel, splits
+    (80, 3, 8, 2, 16, [16 * 3 + 1, 1, 0], 9, torch.float32, 3, [0, 0, 0]),       # k > nb, 1 token, empty
+    (81, 3, 16, 8, 64, [64 * 300 + 1, 64 * 2, 0], 64, torch.bfloat16, 3, [0, 0, 0]),  # prescored, k > nb, empty
 ]
 
 
