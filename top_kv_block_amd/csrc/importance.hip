@@ -90,6 +90,24 @@ __device__ __forceinline__ attn::f32x4 dot_tile(const Frag<DT>& a, const Frag<DT
     return c0 + c1;
 }
 
+// Work item of this workgroup in a 1-D grid of tiles x heads x requests, in decreasing
+// order of work (longest_first: tile gx-1 first, else tile 0 first). All workgroups are
+// resident at once and the dispatcher hands linear ids to the CUs round-robin, so CU c
+// holds ids c, c + kCus, c + 2 kCus, ...; a snake order over those rounds (round r
+// takes ranks r*kCus .. in forward order when r is even, backward when odd) gives every
+// CU a mix of long and short tiles instead of four equal ones.
+constexpr int kCus = 256;
+struct WorkItem { int tile, h, b; };
+__device__ __forceinline__ WorkItem work_item(int gx, int H, int B, bool longest_first) {
+    const int T = gx * H * B;
+    const int id = blockIdx.x;
+    const int rnd = id / kCus, pos = id % kCus;
+    const int cnt = min(kCus, T - rnd * kCus);  // ids in this round
+    const int rank = rnd * kCus + ((rnd & 1) ? cnt - 1 - pos : pos);
+    const int hb = rank % (H * B), k = rank / (H * B);
+    return WorkItem{longest_first ? gx - 1 - k : k, hb % H, hb / H};
+}
+
 // address of key s (head kh) of request b, or nullptr when its block is out of range
 __device__ __forceinline__ const uint8_t* key_row(const ImpParams& p, int b, int s, int kh, int esize) {
     const int phys = p.bt[size_t(b) * p.mkbpr + s / p.BS];
@@ -142,12 +160,12 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
     __shared__ __attribute__((aligned(16))) uint8_t kt[2][Tile<DT>::kBytes];
-    const int b = blockIdx.z, h = blockIdx.y;
+    const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, true);  // the last rows see the most keys
+    const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    // the last query tiles have the most keys: dispatch them first
-    const int tw = (gridDim.x - 1 - blockIdx.x) * 64;  // the workgroup's rows tw .. tw+63
+    const int tw = wi.tile * 64;  // the workgroup's rows tw .. tw+63
     if (tw >= L) return;                              // whole workgroup
     const int t0 = tw + 16 * w;                       // this wave's rows t0 .. t0+15
     const int kh = h / (p.H / p.N);
@@ -165,17 +183,16 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         tile_fetch<DT>(v, [&](int i) { return kr + size_t(min(i, L - 1 - s0)) * p.N * D * es; });
         return true;
     };
-    u32x4 nv[Tile<DT>::kPerThread];
-    bool have = fetch(0, nv);
-    int buf = 0;
-    for (int s0 = 0; s0 <= s_end; s0 += 16, buf ^= 1) {
-        if (have) tile_store<DT>(kt[buf], nv);
+    // tiles alternate between two register sets and two LDS buffers; each set is refilled
+    // with the tile two steps ahead as soon as it has been stored
+    auto step = [&](int s0, uint8_t* buf, u32x4 (&nv)[Tile<DT>::kPerThread], bool& have) {
+        if (have) tile_store<DT>(buf, nv);
         const bool cur = have;
-        __syncthreads();  // tile s0 is in kt[buf]; the reads of kt[buf] two tiles ago are done
-        have = s0 + 16 <= s_end && fetch(s0 + 16, nv);
+        __syncthreads();  // tile s0 is in buf; the reads of buf two tiles ago are done
+        have = s0 + 32 <= s_end && fetch(s0 + 32, nv);
         if (cur && s0 <= t0 + 15 && t0 < L) {  // this wave has rows that see these keys
             Frag<DT> kf;
-            frag_from_tile<DT>(kf, kt[buf], r, j);
+            frag_from_tile<DT>(kf, buf, r, j);
             const int s = s0 + r;
             const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
 #pragma unroll
@@ -191,6 +208,13 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
                 }
             }
         }
+    };
+    u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
+    bool ha = fetch(0, na);
+    bool hb = 16 <= s_end && fetch(16, nb);
+    for (int s0 = 0; s0 <= s_end; s0 += 32) {
+        step(s0, kt[0], na, ha);
+        if (s0 + 16 <= s_end) step(s0 + 16, kt[1], nb, hb);
     }
     // merge the 16 key columns of each row
 #pragma unroll
@@ -208,11 +232,12 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
     __shared__ __attribute__((aligned(16))) uint8_t qt[2][Tile<DT>::kBytes];
     __shared__ float lt_s[2][16];
-    const int b = blockIdx.z, h = blockIdx.y;
+    const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, false);  // the first keys have the most rows
+    const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int sw = blockIdx.x * 64;  // the workgroup's keys sw .. sw+63 (the first keys have the most rows)
+    const int sw = wi.tile * 64;  // the workgroup's keys sw .. sw+63
     if (sw >= L) return;
     const int s0 = sw + 16 * w;      // this wave's keys s0 .. s0+15
     const int kh = h / (p.H / p.N);
@@ -229,20 +254,17 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
         });
         lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
     };
-    u32x4 nv[Tile<DT>::kPerThread];
-    float nl;
-    fetch(sw, nv, nl);
-    int buf = 0;
-    for (int t0 = sw; t0 < L; t0 += 16, buf ^= 1) {
-        tile_store<DT>(qt[buf], nv);
-        if (threadIdx.x < 16) lt_s[buf][threadIdx.x] = nl;
+    // as in the row pass: two register sets and two LDS buffers, two tiles ahead
+    auto step = [&](int t0, int bi, u32x4 (&nv)[Tile<DT>::kPerThread], float& nl) {
+        tile_store<DT>(qt[bi], nv);
+        if (threadIdx.x < 16) lt_s[bi][threadIdx.x] = nl;
         __syncthreads();
-        if (t0 + 16 < L) fetch(t0 + 16, nv, nl);
+        if (t0 + 32 < L) fetch(t0 + 32, nv, nl);
         if (kr != nullptr && t0 + 15 >= s0) {  // some row of the tile sees this wave's keys
             Frag<DT> qf;
-            frag_from_tile<DT>(qf, qt[buf], r, j);
+            frag_from_tile<DT>(qf, qt[bi], r, j);
             const int t = t0 + r;
-            const float lt = lt_s[buf][r];
+            const float lt = lt_s[bi][r];
             const attn::f32x4 c = dot_tile<DT>(kf, qf);  // C[key 4j+i][row r]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -250,6 +272,14 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
                 if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
             }
         }
+    };
+    u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
+    float la = 0.f, lb = 0.f;
+    fetch(sw, na, la);
+    if (sw + 16 < L) fetch(sw + 16, nb, lb);
+    for (int t0 = sw; t0 < L; t0 += 32) {
+        step(t0, 0, na, la);
+        if (t0 + 16 < L) step(t0 + 16, 1, nb, lb);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -287,7 +317,7 @@ hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s) {
     ImpParams p{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr,
                 a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, ws,
                 ws + size_t(a.B) * a.H * a.max_len};
-    const dim3 grid(unsigned((a.max_len + 63) / 64), unsigned(a.H), unsigned(a.B));
+    const dim3 grid(unsigned((a.max_len + 63) / 64 * a.H * a.B));  // tiles x heads x requests, see work_item
     if (a.max_len > 0) {
         if (a.dtype == kBF16) {
             hipLaunchKernelGGL(imp_row_kernel<kBF16>, grid, dim3(kThreads), 0, s, p);

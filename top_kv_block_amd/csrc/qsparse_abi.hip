@@ -324,6 +324,8 @@ qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int3
     if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
         return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
     if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
+    if ((long long)((max_len + 63) / 64) * H * B > 0x7fffffffLL)
+        return fail(QS_ERR_INVALID, "%s: max_len * H * B too large for one grid", fn);
     const size_t need = qs::prefill_importance_workspace_bytes(B, H, max_len);
     if (workspace_bytes < need)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
