@@ -338,6 +338,39 @@ def test_block_select_random(qs, oracle, case):
     compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs, k)
 
 
+def test_block_select_long_row_scores_in_global_memory(qs, oracle):
+    """One request of 9001 blocks at BS=16: more candidates than the LDS score capacity, so
+    the top-k kernel selects from the workspace scores; 563 metadata-table entries."""
+    say("select long row (9001 blocks)")
+    wl = W.random_case(19, 1, 4, 1, 16, [16 * 9000 + 7], k=100, dtype=torch.bfloat16, with_v=False,
+                       tsmu=[5], flags=W.FORCE_SINK | W.FORCE_WINDOW)
+    assert wl.mmbpr * wl.BS > 8192
+    mx, mn = run_meta(qs, wl)
+    sel, ns, sc = run_select(qs, wl, mx, mn)
+    omx, omn = oracle_meta(oracle, wl)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k, tsmu=wl.tsmu,
+                                         flags=wl.flags)
+    nbs = nbs_of(wl)
+    mask = np.zeros_like(osc, dtype=bool)
+    mask[0, :, :nbs[0]] = ~np.isnan(osc[0, :, :nbs[0]])
+    check_scores(tnp(sc), osc, mask)
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs, wl.k)
+
+
+def test_block_select_row_mode_with_wide_table(qs, oracle):
+    """512 rows (row mode) with a 257-entry metadata table (too wide to stage in LDS, so the
+    lookups go to global memory): one long request among short ones."""
+    say("select row mode, 257 metadata blocks")
+    lens = [16 * (256 * 16 + 1)] + [16 * (1 + b % 5) + b % 7 for b in range(63)]
+    wl = W.random_case(20, 64, 8, 8, 16, lens, k=12, dtype=torch.bfloat16, with_v=False)
+    assert wl.mmbpr == 257 and wl.B * wl.N >= 512
+    mx, mn = run_meta(qs, wl)
+    sel, ns, sc = run_select(qs, wl, mx, mn)
+    omx, omn = oracle_meta(oracle, wl)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k)
+    compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs_of(wl), wl.k)
+
+
 def test_block_select_exact_ties(qs, oracle):
     """Metadata with few distinct values: many exactly equal scores; the lower index
     must win every tie (the oracle and the GPU then agree exactly)."""
@@ -434,6 +467,23 @@ def test_probe_select_random(qs, oracle, case):
     compare_probe(tnp(sel), tnp(ns), o, nbs, k)
 
 
+def test_probe_select_at_block_capacity(qs, oracle):
+    """The probe selection's largest row: 4096 blocks (BS=16, 65536 tokens), with importance,
+    recency and k=200."""
+    say("probe select at 4096 blocks")
+    wl = W.random_case(28, 1, 2, 1, 16, [16 * 4096], k=200, dtype=torch.float32, with_v=False,
+                       with_importance=True)
+    assert wl.mkbpr == 4096
+    ps = torch.full((1, 2, 4096), float("inf"), device=DEV)
+    sel, ns = qs.qs_probe_select(wl.query.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                 200, importance=wl.importance.to(DEV), n_probe=8, flags=W.RECENCY,
+                                 probe_scores=ps)
+    o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 200, 1, importance=wl.importance,
+                            n_probe=8, flags=W.RECENCY)
+    check_scores(tnp(ps), o["probe"], np.ones(o["probe"].shape, dtype=bool))
+    compare_probe(tnp(sel), tnp(ns), o, nbs_of(wl), 200)
+
+
 def test_probe_select_config3_sweep(qs, oracle):
     wl = W.config3()
     for k in (1, 2, 4, 8, 16, 32):
@@ -487,6 +537,8 @@ ATTN_CASES = [
     (42, 2, 32, 8, 128, [128 * 40 + 5, 128 * 9], 12, torch.float16, torch.float16, 1),   # f16 matrix cores
     (43, 2, 16, 8, 32, [32 * 50 + 1, 32 * 7], 9, torch.float16, torch.float32, 0),       # f16 KV, fp32 query
     (44, 2, 8, 2, 32, [32 * 30, 32 * 4 + 2], 5, torch.float32, torch.float16, 1),        # fp32 KV, f16 query
+    # 512 rows -> 2 splits of 100 slots: longer than one wave's slot table (lookups in the loop)
+    (45, 8, 64, 8, 16, [16 * 210 + (7 * b) % 16 for b in range(8)], 200, torch.bfloat16, torch.bfloat16, 0),
 ]
 
 
