@@ -390,6 +390,34 @@ def test_block_select_exact_ties(qs, oracle):
         np.testing.assert_array_equal(tnp(ns), ons)
 
 
+def test_block_select_topk_uniform_and_clustered(qs, oracle):
+    """Score distributions that reach every branch of the exact top-k: all candidates equal
+    (only the index order decides), and one outlier above a tight cluster with repeated
+    values, where far more than 256 candidates share the histogram bin of the k-th best
+    score. A one-hot query makes each block's score exactly its channel-0 metadata value,
+    so the GPU (fp32) and the oracle (fp64) see identical scores and must agree exactly."""
+    BS, D, nb = 32, 128, 2000
+    nmeta = cdiv(nb, BS)
+    q = torch.zeros((1, 1, D))
+    q[0, 0, 0] = 1.0
+    mt = torch.arange(nmeta, dtype=torch.int32)[None]
+    sl = torch.tensor([nb * BS], dtype=torch.int32)
+    j = torch.arange(nb)
+    uniform = torch.zeros(nb)
+    clustered = 1.0 + ((j * 37) % 500).float() * 2.0 ** -20   # each value on 4 blocks
+    clustered[0] = 1.0e4
+    for name, v in (("uniform", uniform), ("clustered", clustered)):
+        mx = torch.zeros((nmeta * BS, 1, D))
+        mx[:nb, 0, 0] = v
+        mx = mx.reshape(nmeta, BS, 1, D)
+        for k in (1, 2, 10, 300):
+            say(f"select top-k {name} k={k}")
+            sel, ns = qs.qs_block_select(q.to(DEV), mx.to(DEV), mx.to(DEV), mt.to(DEV), sl.to(DEV), k)
+            osel, ons, _ = oracle.block_select(q, mx, mx, mt, sl, k)
+            np.testing.assert_array_equal(tnp(sel), osel)
+            np.testing.assert_array_equal(tnp(ns), ons)
+
+
 def test_block_select_config1_needle(qs, oracle):
     say("select config1")
     wl = W.config1()

@@ -71,6 +71,28 @@ __device__ __forceinline__ void emit(const AttnParams& p, int b, int row, int hc
     }
 }
 
+// Slot table of one wave (used when a split has at most 64 slots): lane t resolves slot
+// slot0 + t of the selection row into (physical block, valid tokens), or (-1, 0) for a
+// slot past the count, a negative or out-of-range entry, or an out-of-range table entry.
+// The entry is read before the selection count is known (a selection row always holds k
+// entries), so the count, the sequence length and the entries are in flight together and
+// only the block-table lookup waits on them; the slot loops then read the table back with
+// v_readlane and issue nothing but K/V loads.
+__device__ __forceinline__ void slot_table(const AttnParams& p, int b, const int32_t* srow, int slot0, int nsl,
+                                           int nb, int L, int lane, int& tab_phys, int& tab_nt) {
+    const int blk_raw = (lane < p.spb && slot0 + lane < p.k) ? srow[slot0 + lane] : -1;
+    const int blk = lane < nsl ? blk_raw : -1;
+    tab_phys = -1;
+    tab_nt = 0;
+    if (blk >= 0 && blk < nb && blk < p.mkbpr) {
+        const int ph = p.bt[size_t(b) * p.mkbpr + blk];
+        if (ph >= 0 && ph < p.num_kv_blocks) {
+            tab_phys = ph;
+            tab_nt = min(p.BS, L - blk * p.BS);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // matrix-core kernel (bf16 or f16 query and KV)
 // ------------------------------------------------------------------------------------
@@ -110,15 +132,6 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int c16 = lane & 15, j = lane >> 4;
 
-    // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
-    op8<DT> qb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v{0u, 0u, 0u, 0u};
-        if (c16 < nh) v = ld16(p.query + ((size_t(b) * p.H + h0 + c16) * D + 32 * ks + 8 * j) * 2);
-        qb[ks] = as_op8<DT>(v);
-    }
-
     const int L = max(p.sl[b], 0);
     const int nb = (L + p.BS - 1) / p.BS;
     const int row = b * p.sel_heads + s;
@@ -129,23 +142,21 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
     const size_t tstride = size_t(p.N) * D;           // elements between tokens of one KV head
     uint8_t* vt = lds + w * kVtBytes;
 
-    // Slot table: lane t of every wave resolves slot slot0 + t once (selection entry, then
-    // block table) into (physical block, valid tokens), and the chunk loop reads it back
-    // with v_readlane. The loop then issues only K/V loads, never waiting on a dependent
-    // lookup with K/V loads in flight. Ranges longer than a wave look up in the loop.
+    // slot table (splits of up to 64 slots; longer ranges look up in the loop)
     const int nsl = max(0, slot1 - slot0);
-    const bool use_tab = nsl <= kWave;
+    const bool use_tab = p.spb <= kWave;
     int tab_phys = -1, tab_nt = 0;
-    if (use_tab && lane < nsl) {
-        const int blk = srow[slot0 + lane];
-        if (blk >= 0 && blk < nb && blk < p.mkbpr) {
-            const int ph = p.bt[size_t(b) * p.mkbpr + blk];
-            if (ph >= 0 && ph < p.num_kv_blocks) {
-                tab_phys = ph;
-                tab_nt = min(p.BS, L - blk * p.BS);
-            }
-        }
+    if (use_tab) slot_table(p, b, srow, slot0, nsl, nb, L, lane, tab_phys, tab_nt);
+
+    // B operand of S^T = K Q^T: lane holds Q[head c16][32*ks + 8*j .. +7]
+    op8<DT> qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        u32x4 v{0u, 0u, 0u, 0u};
+        if (c16 < nh) v = ld16(p.query + ((size_t(b) * p.H + h0 + c16) * D + 32 * ks + 8 * j) * 2);
+        qb[ks] = as_op8<DT>(v);
     }
+
     if (sync_after_table) __syncthreads();
 
     float m = -INFINITY, lsum = 0.f;
@@ -329,6 +340,19 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
     const int kh = (s * p.hpr) / G;
     const int tid = threadIdx.x, lr = tid % LPR, grp = tid / LPR;
 
+    const int L = max(p.sl[b], 0);
+    const int nb = (L + p.BS - 1) / p.BS;
+    const int row = b * p.sel_heads + s;
+    const int ns = min(max(ns_raw, 0), p.k);
+    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
+    const size_t tok_bytes = size_t(p.N) * D * ke;
+
+    // slot table (splits of up to 64 slots; longer ranges look up in the loop)
+    const int nsl = max(0, slot1 - slot0);
+    const bool use_tab = p.spb <= kWave;
+    int tab_phys = -1, tab_nt = 0;
+    if (use_tab) slot_table(p, b, srow, slot0, nsl, nb, L, tid & (kWave - 1), tab_phys, tab_nt);
+
     // query: fp32 (pre-scaled by softmax_scale * log2 e) or int8 codes
     float qf[HC][EPL];
     int32_t q8[HC][EPL / 4 > 0 ? EPL / 4 : 1];
@@ -368,13 +392,6 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
         }
     }
 
-    const int L = max(p.sl[b], 0);
-    const int nb = (L + p.BS - 1) / p.BS;
-    const int row = b * p.sel_heads + s;
-    const int ns = min(max(ns_raw, 0), p.k);
-    const int slot0 = split * p.spb, slot1 = min(ns, slot0 + p.spb);
-    const size_t tok_bytes = size_t(p.N) * D * ke;
-
     float m[HC], l[HC], acc[HC][EPL];
 #pragma unroll
     for (int g = 0; g < HC; ++g) {
@@ -385,11 +402,18 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
     }
 
     for (int slot = slot0; slot < slot1; ++slot) {
-        const int blk = srow[slot];
-        if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
-        const int phys = p.bt[size_t(b) * p.mkbpr + blk];
-        if (phys < 0 || phys >= p.num_kv_blocks) continue;
-        const int nt = min(p.BS, L - blk * p.BS);
+        int phys, nt;
+        if (use_tab) {
+            phys = __builtin_amdgcn_readlane(tab_phys, slot - slot0);
+            nt = __builtin_amdgcn_readlane(tab_nt, slot - slot0);
+            if (phys < 0) continue;
+        } else {
+            const int blk = srow[slot];
+            if (blk < 0 || blk >= nb || blk >= p.mkbpr) continue;
+            phys = p.bt[size_t(b) * p.mkbpr + blk];
+            if (phys < 0 || phys >= p.num_kv_blocks) continue;
+            nt = min(p.BS, L - blk * p.BS);
+        }
         const size_t tok0 = size_t(phys) * p.BS;
         const uint8_t* kb = p.kc + (tok0 * p.N + kh) * D * ke + lr * 16;
         const uint8_t* vb = p.vc + (tok0 * p.N + kh) * D * ke + lr * 16;

@@ -15,7 +15,7 @@
 // in fp32, exactly as the page's loop does, so the importance stage is bit-exact. Each
 // greedy stage ("repeatedly take the best unused block, lower index on ties") selects
 // the same set as taking the top-r keys under (value desc, index asc); that is computed
-// with the block-wide radix select plus one ordered pass.
+// with the block-wide threshold select plus one ordered pass.
 #include <math.h>
 
 #include <type_traits>
@@ -28,8 +28,8 @@ namespace {
 
 constexpr uint8_t kImp = 1, kProbe = 2;
 
-// Marks the r best candidates (value desc, index asc), r >= 1: a radix select finds the
-// r-th best key T, then each thread takes a contiguous run of blocks and one block-wide
+// Marks the r best candidates (value desc, index asc), r >= 1: a threshold select finds
+// the r-th best key T, then each thread takes a contiguous run of blocks and one block-wide
 // scan ranks the candidates equal to T by index. Every thread must call it.
 template <class Pred, class KeyOf>
 __device__ void mark_top(int nb, int r, Pred cand, KeyOf key_of, uint8_t* flag, uint8_t mark, uint32_t* hist,
@@ -52,7 +52,7 @@ __device__ void mark_top(int nb, int r, Pred cand, KeyOf key_of, uint8_t* flag, 
         key = key_of(i);
         return true;
     };
-    const uint32_t T = block_radix_select(nb, r, kf, hist, sh, need_eq);
+    const uint32_t T = block_topk_threshold(nb, r, kf, hist, sh, need_eq);
     int eq_local = 0;
     for (int i = i0; i < i1; ++i) eq_local += (cand(i) && key_of(i) == T) ? 1 : 0;
     int eq_tot;

@@ -148,6 +148,30 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     return off + int(incl) - v;
 }
 
+// Wave 0 scans the 256-bin histogram h from the highest bin down and finds the bin that
+// holds the need-th largest element (1 <= need <= total): out[0] = that bin, out[1] = the
+// count in the bins above it. Lane l owns bins 255-4l .. 252-4l.
+__device__ __forceinline__ void find_desc_bin(const uint32_t* h, int need, int* out) {
+    const int l = lane_id();
+    uint32_t c[4];
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c[j] = h[255 - 4 * l - j]; s += c[j]; }
+    const uint32_t incl = wave_incl_scan(s);
+    uint32_t run = incl - s;
+    if (run < uint32_t(need) && uint32_t(need) <= incl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (run + c[j] >= uint32_t(need)) {
+                out[0] = 255 - 4 * l - j;
+                out[1] = int(run);
+                break;
+            }
+            run += c[j];
+        }
+    }
+}
+
 // Block-wide radix select over a virtual array of n keys.
 // kf(i, &key) returns true if index i is a candidate and sets its key.
 // Finds the R-th largest candidate key T (1 <= R <= #candidates); on return `need_eq`
@@ -170,27 +194,7 @@ __device__ uint32_t block_radix_select(int n, int R, KeyFn kf, uint32_t* hist, i
             if (kf(i, key) && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (wave_id() == 0) {
-            // lane l owns bins 255-4l .. 252-4l (descending digit order across lanes)
-            const int l = lane_id();
-            uint32_t c[4];
-            uint32_t s = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { c[j] = h[255 - 4 * l - j]; s += c[j]; }
-            const uint32_t incl = wave_incl_scan(s);
-            uint32_t run = incl - s;
-            if (run < uint32_t(need) && uint32_t(need) <= incl) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (run + c[j] >= uint32_t(need)) {
-                        sh[2 * (pass & 1)] = 255 - 4 * l - j;
-                        sh[2 * (pass & 1) + 1] = int(run);
-                        break;
-                    }
-                    run += c[j];
-                }
-            }
-        }
+        if (wave_id() == 0) find_desc_bin(h, need, sh + 2 * (pass & 1));
         // the other histogram is free now: clear it for the next pass
         for (int j = threadIdx.x; j < 256; j += kThreads) hist[256 * ((pass + 1) & 1) + j] = 0;
         __syncthreads();
@@ -203,4 +207,86 @@ __device__ uint32_t block_radix_select(int n, int R, KeyFn kf, uint32_t* hist, i
     return prefix;
 }
 
+
+// The same result as block_radix_select (the R-th largest candidate key T, and need_eq),
+// in one histogram pass for keys that are spread out: the block's key range [kmin, kmax]
+// is cut into 256 bins by the top 8 significant bits of key - kmin (a monotone map, so
+// every key in a higher bin is larger), the bin holding the R-th largest key is found,
+// its keys are gathered into a list, and T is the key whose rank in that list is right
+// (counted against the whole list). Five barriers and no contended LDS atomics when the
+// keys spread over the bins; when more than 256 keys share the boundary bin (heavy
+// clustering or ties) it falls back to the radix select. Same LDS as
+// block_radix_select: hist[512] (bins in the first half, the boundary list and the
+// per-wave range in the second), sh[4]. Every thread of the workgroup must call it.
+template <class KeyFn>
+__device__ uint32_t block_topk_threshold(int n, int R, KeyFn kf, uint32_t* hist, int* sh, int& need_eq) {
+    const int tid = threadIdx.x;
+    uint32_t* list = hist + 256;
+    for (int j = tid; j < 256; j += kThreads) hist[j] = 0;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int i = tid; i < n; i += kThreads) {
+        uint32_t key;
+        if (kf(i, key)) { kmin = min(kmin, key); kmax = max(kmax, key); }
+    }
+    // wave range: DPP inside each row of 16 lanes (every lane active), then the four row
+    // results, so that every lane holds the wave's range
+    kmin = min(kmin, uint32_t(dpp_i<kDppXor1>(int(kmin))));
+    kmax = max(kmax, uint32_t(dpp_i<kDppXor1>(int(kmax))));
+    kmin = min(kmin, uint32_t(dpp_i<kDppXor2>(int(kmin))));
+    kmax = max(kmax, uint32_t(dpp_i<kDppXor2>(int(kmax))));
+    kmin = min(kmin, uint32_t(dpp_i<kDppHalfMirror>(int(kmin))));
+    kmax = max(kmax, uint32_t(dpp_i<kDppHalfMirror>(int(kmax))));
+    kmin = min(kmin, uint32_t(dpp_i<kDppMirror>(int(kmin))));
+    kmax = max(kmax, uint32_t(dpp_i<kDppMirror>(int(kmax))));
+#pragma unroll
+    for (int r = 0; r < kWave; r += 16) {
+        kmin = min(kmin, uint32_t(__builtin_amdgcn_readlane(int(kmin), r)));
+        kmax = max(kmax, uint32_t(__builtin_amdgcn_readlane(int(kmax), r)));
+    }
+    if (lane_id() == 0) { list[wave_id()] = kmin; list[kWaves + wave_id()] = kmax; }
+    if (tid == 0) sh[3] = 0;  // boundary list length
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { kmin = min(kmin, list[w]); kmax = max(kmax, list[kWaves + w]); }
+    if (kmin == kmax) {  // every candidate has the same key
+        need_eq = R;
+        return kmin;
+    }
+    const uint32_t d = kmax - kmin;
+    const int shift = max(0, (32 - __clz(d)) - 8);  // (key - kmin) >> shift is in [0, 255]
+    for (int i = tid; i < n; i += kThreads) {
+        uint32_t key;
+        if (kf(i, key)) atomicAdd(&hist[(key - kmin) >> shift], 1u);
+    }
+    __syncthreads();
+    if (wave_id() == 0) find_desc_bin(hist, R, sh);
+    __syncthreads();
+    const uint32_t bs = uint32_t(sh[0]);
+    const int need = R - sh[1];  // 1 <= need <= the boundary bin's count
+    for (int i = tid; i < n; i += kThreads) {
+        uint32_t key;
+        if (kf(i, key) && ((key - kmin) >> shift) == bs) {
+            const int pos = atomicAdd(&sh[3], 1);
+            if (pos < 256) list[pos] = key;
+        }
+    }
+    __syncthreads();
+    const int m = sh[3];
+    if (m > 256) return block_radix_select(n, R, kf, hist, sh, need_eq);
+    if (tid < m) {
+        const uint32_t mk = list[tid];
+        int gt = 0, ge = 0;
+        for (int e = 0; e < m; ++e) {
+            const uint32_t o = list[e];
+            gt += o > mk ? 1 : 0;
+            ge += o >= mk ? 1 : 0;
+        }
+        // T has fewer than `need` larger keys and at least `need` keys >= it; every thread
+        // holding T writes the same two values
+        if (gt < need && need <= ge) { sh[0] = int(mk); sh[1] = need - gt; }
+    }
+    __syncthreads();
+    need_eq = sh[1];
+    return uint32_t(sh[0]);
+}
 }  // namespace qs

@@ -16,8 +16,10 @@
 //              selects from there -- used when there are enough rows to fill the GPU;
 //   split mode a scoring grid (chunk, KV head, request) writes the scores to the
 //              workspace, then a second kernel selects per row -- used for few, long rows.
-// The top-k is exact: a 4-pass, 8-bit radix select on an order-preserving integer image
-// of the scores finds the k-th best value T, then one ordered pass keeps every block
+// The top-k is exact. On an order-preserving integer image of the scores, one 256-bin
+// histogram over the row's key range finds the bin holding the k-th best key, and the
+// keys of that bin alone are ranked to give the k-th best value T (an 8-bit radix
+// select takes over when the bin is crowded); then one ordered pass keeps every block
 // above T and the lowest-index blocks equal to T ("higher score first, lower index on
 // ties"). Output is written in ascending block order.
 #include <math.h>

@@ -197,60 +197,65 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
 }
 
 // Exact top-k of a row from its scores (LDS or global); writes selected / n_selected.
-// The radix select finds the k-th best key T; then each thread takes a contiguous run of
-// blocks, and two block-wide scans (equal-to-T ranks, then output positions) keep every
-// block above T and the lowest-index blocks equal to T, written in ascending order.
+// A threshold select finds the k-th best key T among the fill candidates and how many
+// candidates equal to T are taken (the lowest-index ones). Each thread then takes a
+// contiguous run of blocks and counts, in its run, the sure picks (forced, or above T)
+// and the candidates equal to T; one block-wide scan of the two counts (packed in one
+// word while the row is shorter than 65536 blocks) gives every thread its output
+// position, and the picks are written in ascending block order.
 __device__ __forceinline__ void topk_emit(const float* scores, int nb, const Forced& F, int k, int32_t* out,
                                           int32_t* n_out, uint32_t* hist, int* sh, int* wsum) {
     const int tid = threadIdx.x;
     const int R = max(0, min(k, nb) - F.count);  // fill picks
     const int nc = nb - F.count;                   // fill candidates
     const bool take_all = R >= nc;
-    const bool radix = R > 0 && !take_all;
+    const bool thresh = R > 0 && !take_all;
     uint32_t T = 0;
     int need_eq = 0;
-    if (radix) {
+    if (thresh) {
         auto kf = [&](int i, uint32_t& key) -> bool {
             if (F.has(i)) return false;
             key = f2key(scores[i]);
             return true;
         };
-        T = block_radix_select(nb, R, kf, hist, sh, need_eq);
+        T = block_topk_threshold(nb, R, kf, hist, sh, need_eq);
     }
+    // 0: not picked, 1: picked for sure, 2: equal to T (picked while the quota lasts)
+    auto cls = [&](int i) -> int {
+        if (F.has(i)) return 1;
+        if (R == 0) return 0;
+        if (take_all) return 1;
+        const uint32_t key = f2key(scores[i]);
+        return key > T ? 1 : (key == T ? 2 : 0);
+    };
     const int E = (nb + kThreads - 1) / kThreads;  // blocks per thread, contiguous
     const int i0 = min(nb, tid * E), i1 = min(nb, i0 + E);
-    int eq_off = 0, tot;
-    if (radix) {
-        int eq_local = 0;
-        for (int i = i0; i < i1; ++i) eq_local += (!F.has(i) && f2key(scores[i]) == T) ? 1 : 0;
-        eq_off = block_excl_scan(eq_local, wsum, tot);
+    int sure = 0, eq = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int c = cls(i);
+        sure += c == 1 ? 1 : 0;
+        eq += c == 2 ? 1 : 0;
     }
-    int pick_local = 0;
-    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
-        bool pick = F.has(i);
-        if (!pick && R > 0) {
-            if (take_all) {
-                pick = true;
-            } else {
-                const uint32_t key = f2key(scores[i]);
-                pick = key > T || (key == T && eq_seen < need_eq);
-                eq_seen += key == T ? 1 : 0;
-            }
-        }
-        pick_local += pick ? 1 : 0;
+    int sure_before, eq_before, sure_tot, eq_tot;
+    if (nb < 65536) {
+        int tot;
+        const int ex = block_excl_scan((sure << 16) | eq, wsum, tot);
+        sure_before = ex >> 16;
+        eq_before = ex & 0xffff;
+        sure_tot = tot >> 16;
+        eq_tot = tot & 0xffff;
+    } else {
+        sure_before = block_excl_scan(sure, wsum, sure_tot);
+        eq_before = block_excl_scan(eq, wsum, eq_tot);
     }
-    int npick;
-    int pos = block_excl_scan(pick_local, wsum, npick);
-    for (int i = i0, eq_seen = eq_off; i < i1; ++i) {
-        bool pick = F.has(i);
-        if (!pick && R > 0) {
-            if (take_all) {
-                pick = true;
-            } else {
-                const uint32_t key = f2key(scores[i]);
-                pick = key > T || (key == T && eq_seen < need_eq);
-                eq_seen += key == T ? 1 : 0;
-            }
+    const int npick = sure_tot + min(eq_tot, need_eq);
+    int pos = sure_before + min(eq_before, need_eq);
+    for (int i = i0, eq_seen = eq_before; i < i1; ++i) {
+        const int c = cls(i);
+        bool pick = c == 1;
+        if (c == 2) {
+            pick = eq_seen < need_eq;
+            ++eq_seen;
         }
         if (pick) {
             if (pos < k) out[pos] = i;
