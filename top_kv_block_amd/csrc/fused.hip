@@ -73,24 +73,26 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     const int cap = p.mmbpr * p.BS;
     const sel::RowInfo r = sel::row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
     if constexpr (PRESCORED) {
-        // all loads of a thread's entries in flight together, then into LDS
+        // the whole workspace row (cap <= kFusedMaxCap entries) into LDS, all loads of a
+        // thread in flight together and issued without waiting for the row length; entries
+        // at or past the row's block count are never read
         const float* src = p.ws_scores + (size_t(b) * p.N + n) * cap;
-        for (int i0 = 0; i0 < r.nb; i0 += 4 * kThreads) {
+        for (int i0 = 0; i0 < cap; i0 += 4 * kThreads) {
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * kThreads + threadIdx.x;
-                v[u] = i < r.nb ? src[i] : 0.f;
+                v[u] = i < cap ? src[i] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * kThreads + threadIdx.x;
-                if (i < r.nb) scores[i] = v[u];
+                if (i < cap) scores[i] = v[u];
             }
         }
     } else {
         sel::score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
-                                   0, r.nb, scores, false, qstage, mt_stage);
+                                   0, r.nb, cap, scores, false, qstage, mt_stage);
     }
     __syncthreads();
     sel::topk_emit(scores, r.nb, r.F, p.k, selv, nsel, hist, sh, wsum);

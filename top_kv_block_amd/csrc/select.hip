@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
     if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
         score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
-                                  0, r.nb, lds_scores, false, qstage, mt_stage);
+                                  0, r.nb, cap, lds_scores, false, qstage, mt_stage);
         __syncthreads();
         if (p.dbg_scores)
             for (int i = threadIdx.x; i < r.nb; i += kThreads)
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
         topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     } else {
         score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
-                                  0, r.nb, gscores, p.dbg_scores != nullptr, qstage, mt_stage);
+                                  0, r.nb, cap, gscores, p.dbg_scores != nullptr, qstage, mt_stage);
         __syncthreads();
         topk_emit(gscores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     }
@@ -80,12 +80,14 @@ __global__ __launch_bounds__(kThreads) void select_score_kernel(SelParams p, int
     const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
     const int cap = p.mmbpr * p.BS;
     const RowInfo r = row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
-    const int i0 = c * chunk;
-    if (i0 >= r.nb) return;
+    const int i0 = c * chunk;  // < cap: the grid has ceil(cap / chunk) chunks
     float* scores = (p.dbg_scores ? p.dbg_scores : p.ws_scores) + (size_t(b) * p.N + n) * cap;
-    // a chunk spans at most chunk / BS + 2 table entries, always within kMtStageCap
+    // a chunk spans at most chunk / BS + 2 table entries, always within kMtStageCap. A
+    // chunk past the row's blocks scores nothing; it is not cut short before the call, so
+    // that the table lookups of the others do not wait for the row length.
     score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F, i0,
-                            min(r.nb, i0 + chunk), scores, p.dbg_scores != nullptr, qstage, mt_stage);
+                            min(r.nb, i0 + chunk), min(cap, i0 + chunk), scores, p.dbg_scores != nullptr, qstage,
+                            mt_stage);
 }
 
 // split mode, step 2: top-k per (KV head, request); the row's scores are first copied

@@ -63,16 +63,18 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 
 // Scores blocks [i0, i_end) of row (b, n) into dst[i] (LDS or global). Forced blocks are
 // skipped (NaN written when nan_forced); an out-of-range metadata entry scores -inf.
-// qstage: kThreads 16-byte LDS slots used to stage the group's query rows; mt_stage:
-// kMtStageCap ints of LDS for the metadata-table entries of [i0, i_end) (MT_LDS: the
-// caller guarantees they fit). Contains a barrier: every thread of the workgroup must
-// call it.
+// i_lim (i_end <= i_lim <= the row capacity mmbpr * BS) bounds the range's table entries
+// without the row length, so the table lookups are issued together with the loads of the
+// row length instead of after them; i_end may be <= i0 (nothing scored). qstage: kThreads
+// 16-byte LDS slots used to stage the group's query rows; mt_stage: kMtStageCap ints of LDS
+// for the metadata-table entries of [i0, i_lim) (MT_LDS: the caller guarantees they fit).
+// Contains a barrier: every thread of the workgroup must call it.
 template <int DT, bool MT_LDS>
 __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
                                             const uint8_t* __restrict__ minb, int num_meta,
                                             const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
-                                            int n, const Forced& F, int i0, int i_end, float* dst, bool nan_forced,
-                                            u32x4* qstage, int32_t* mt_stage) {
+                                            int n, const Forced& F, int i0, int i_end, int i_lim, float* dst,
+                                            bool nan_forced, u32x4* qstage, int32_t* mt_stage) {
     constexpr int esize = elem_bytes(DT);
     constexpr int D = 128;
     constexpr int LPR = D * esize / 16;  // lanes per metadata row
@@ -98,8 +100,8 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
             ok[u] = i < i_end && !F.has(i);
             if constexpr (decltype(from_lds)::value)
                 mrow[u] = ok[u] ? mt_stage[i / BS - mbase] : 0;
-            else
-                mrow[u] = ok[u] ? mt[size_t(b) * mmbpr + i / BS] : 0;
+            else  // not gated on ok: the entry of any i < i_lim is in the table
+                mrow[u] = i < i_lim ? mt[size_t(b) * mmbpr + i / BS] : 0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -119,12 +121,14 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
     u32x4 qpiece{0u, 0u, 0u, 0u};
     if (staged && tid < npieces)
         qpiece = ld16(query + ((size_t(b) * H + size_t(n) * G + tid / LPR) * D + (tid % LPR) * EPL) * esize);
-    const int n_ent = i0 < i_end ? (i_end - 1) / BS - mbase + 1 : 0;  // table entries of the range
+    const int n_ent = i0 < i_lim ? (i_lim - 1) / BS - mbase + 1 : 0;  // table entries of [i0, i_lim)
     int32_t mt_piece = 0;
     if (MT_LDS && tid < n_ent) mt_piece = mt[size_t(b) * mmbpr + mbase + tid];
     u32x4 vmx[U], vmn[U];
     bool ok[U];
-    if (i0 < i_end) issue(i0, vmx, vmn, ok, std::false_type{});
+    // batch 0 is issued even for an empty range (its rows then read the first metadata row
+    // and are masked), so that nothing before the loads waits for the row length
+    issue(i0, vmx, vmn, ok, std::false_type{});
     if (MT_LDS && tid < n_ent) mt_stage[tid] = mt_piece;
 
     // grouped query for this lane's channels: mean over the group's G heads
