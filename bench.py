@@ -512,7 +512,10 @@ def main():
         # one kernel per step in the serving shape: select_attn_mfma_kernel moves the whole step
         dom_kernel, dom_ms, dom_bytes = "select_attn_mfma_kernel (qs_select_attn_decode)", fused_ms, sel_bytes + att_bytes
     else:
-        dom_kernel, dom_ms, dom_bytes = "attn_mfma_kernel (qs_sparse_attn_decode)", attn_ms, att_bytes
+        # the events bracket the whole qs_sparse_attn_decode call: with split rows (the
+        # long-context shape) that is attn_mfma_kernel plus attn_combine_kernel
+        dom_kernel, dom_ms, dom_bytes = ("attn_mfma_kernel + attn_combine_kernel (qs_sparse_attn_decode)", attn_ms,
+                                         att_bytes)
     dom_avg_ms = float(dom_ms.mean())
     dom_gbps = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
 
