@@ -136,15 +136,22 @@ def _stream(dev):
 
 
 _workspaces = {}
+_retired = []
 
 
 def workspace(nbytes, device, op):
-    """An uninitialised, 256-byte aligned workspace cached per (device, operation), grown on
-    demand. Calls that share one must be ordered on one stream."""
-    key = (torch.device(device).index or 0, op)
+    """An uninitialised, 256-byte aligned workspace cached per (device, stream, operation)
+    and grown on demand, so that calls of one operation on different streams never share
+    scratch memory (calls on one stream are ordered). A workspace that is replaced by a
+    larger one stays allocated: a HIP graph captured with it keeps a valid address."""
+    dev = torch.device(device)
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        if ws is not None:
+            _retired.append(ws)
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
