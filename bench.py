@@ -1,6 +1,6 @@
 """Decode-step benchmark of the sparse top-k KV-block attention path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload config5|config4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serving|long_context]
 
 A step is one pass of the path over one batch: Quest block selection (grouped-query
 scoring, top-k, sink/window forcing) followed by exact attention over the selected
@@ -167,8 +167,8 @@ def other_workloads(qs, W, dev, stream, reps=50):
         mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=wl.k_cache.dtype, device=dev)
         return mx, torch.zeros_like(mx)
 
-    # config 1: tiny fp32 Quest select + attention
-    wl = W.config1().to(dev)
+    # the tiny fp32 workload: Quest select + attention
+    wl = W.tiny_needle().to(dev)
     mx, mn = meta_buf(wl)
     qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx, mn)
     sel, ns = qs.qs_block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k)
@@ -179,15 +179,15 @@ def other_workloads(qs, W, dev, stream, reps=50):
     out1 = torch.empty_like(wl.query)
     t_fused = _timed(lambda: qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
                                                       wl.block_tables, wl.seq_lens, wl.k, out=out1), reps, stream)
-    res["config1_tiny_fp32"] = {"select_us": round(t_sel * 1e3, 2), "attention_us": round(t_att * 1e3, 2),
+    res[wl.name] = {"select_us": round(t_sel * 1e3, 2), "attention_us": round(t_att * 1e3, 2),
                                 "step_us": round((t_sel + t_att) * 1e3, 2),
                                 "fused_step_us": round(t_fused * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
     del wl, mx, mn
 
-    # config 2: page-3-shaped Quest select, bf16 and fp16 (the page's metadata example is
+    # page-3-shaped Quest select, bf16 and fp16 (the page's metadata example is
     # fp16); metadata build timed too
     for dt in (torch.bfloat16, torch.float16):
-        wl = W.config2(device=dev, dtype=dt)
+        wl = W.page3_select(device=dev, dtype=dt)
         mx, mn = meta_buf(wl)
         t_build = _timed(lambda: qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, mx,
                                                       mn), 10, stream)
@@ -207,8 +207,8 @@ def other_workloads(qs, W, dev, stream, reps=50):
                         "metadata_build_gbps": gbps(build_bytes, t_build)}
         del wl, mx, mn
 
-    # config 3: page-1 probe selection + fp32 / int8 attention at k = 32
-    wl = W.config3().to(dev)
+    # page-1 probe selection + fp32 / int8 attention at k = 32
+    wl = W.page1_probe().to(dev)
     psel, pns = qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
                                    importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY)
     t_probe = _timed(lambda: qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
@@ -220,7 +220,7 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                                    pns, sel_heads=wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale),
                   reps, stream)
     probe_bytes = wl.N * 128 * 8 * wl.D * 4 + 4096 * 4 + wl.H * wl.D * 4
-    res["config3_p1_probe_k32"] = {"probe_select_us": round(t_probe * 1e3, 2),
+    res["page1_probe_b1_h16_l4096_k32"] = {"probe_select_us": round(t_probe * 1e3, 2),
                                    "probe_select_gbps": gbps(probe_bytes, t_probe),
                                    "attention_fp32_us": round(t_f32 * 1e3, 2),
                                    "attention_int8_us": round(t_i8 * 1e3, 2),
@@ -229,23 +229,23 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                    "note": "latency-bound (a few MB a step)"}
     del wl
 
-    # the prefill that produces config 3's importance: two causal QK^T passes on the matrix
+    # the prefill that produces the probe workload's importance: two causal QK^T passes on the matrix
     # cores (fp32 inputs); algorithmic flops: 2 passes x H heads x L(L+1)/2 causal dots x 2D
-    wl, pq = W.config3_prefill()
+    wl, pq = W.page1_probe_prefill()
     wl, pq = wl.to(dev), pq.to(dev)
     imp = torch.empty((wl.B, int(wl.seq_lens.max())), dtype=torch.float32, device=dev)
     t_imp = _timed(lambda: qs.qs_prefill_importance(pq, wl.k_cache, wl.block_tables, wl.seq_lens, importance=imp),
                    10, stream)
     L = int(wl.seq_lens.max())
     flops = 2 * wl.H * L * (L + 1) * wl.D
-    res["config3_prefill_importance_fp32"] = {
+    res["page1_prefill_importance_b1_h16_l4096_fp32"] = {
         "us": round(t_imp * 1e3, 2), "tflops": round(flops / (t_imp * 1e-3) / 1e12, 2),
         "mfma_fp32_peak_tflops": 157.3, "frac": round(flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),
         "note": "B=1, L=4096, H=16, N=8; row pass + column pass + head reduction"}
     del wl, pq, imp
 
-    # config 4: long-context paged decode, bf16 (rows split over workgroups + combine)
-    wl = W.config4(device=dev)
+    # long-context paged decode, bf16 (rows split over workgroups + combine)
+    wl = W.long_context(device=dev)
     mx, mn = meta_buf(wl)
     qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
     sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=dev)
@@ -267,7 +267,7 @@ def other_workloads(qs, W, dev, stream, reps=50):
                                                       tokens_since_update=wl.tsmu, flags=wl.flags, out=out,
                                                       selected=sel, n_selected=ns), reps, stream)
     sb, ab = step_bytes(wl, sel.cpu(), ns.cpu(), wl.tsmu.cpu())
-    res["config4_long_context_bf16"] = {
+    res[wl.name] = {
         "step_us": round(t_step * 1e3, 2), "steps_per_s": round(1000.0 / t_step, 1),
         "fused_step_us": round(t_fused * 1e3, 2), "fused_steps_per_s": round(1000.0 / t_fused, 1),
         "step_bytes": int(sb + ab), "step_gbps": gbps(sb + ab, t_step),
@@ -285,12 +285,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="config5", choices=["config5", "config4"])
+    ap.add_argument("--workload", default="serving", choices=["serving", "long_context"])
     ap.add_argument("--cpu-sample", type=int, default=4, help="requests in the CPU-baseline sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=["fused", "separate"], default=None,
-                    help="step as one qs_select_attn_decode call (default for config5) or as "
-                         "qs_block_select + qs_sparse_attn_decode (default for config4)")
+                    help="step as one qs_select_attn_decode call (default for the serving workload) or as "
+                         "qs_block_select + qs_sparse_attn_decode (default for the long-context workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flushed-steps", type=int, default=32,
                     help="steps timed one by one after a 1 GiB cache flush each (0: skip)")
@@ -312,10 +312,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"generating {args.workload} on the GPU")
-    wl = W.config5(device=dev) if args.workload == "config5" else W.config4(device=dev)
+    wl = W.serving(device=dev) if args.workload == "serving" else W.long_context(device=dev)
     qsets = wl.extra.get("query_sets", wl.query[None])
     B, H, N, D, BS, k = wl.B, wl.H, wl.N, wl.D, wl.BS, wl.k
-    if args.workload == "config5":
+    if args.workload == "serving":
         tsmu_tab = (torch.arange(128, dtype=torch.int32, device=dev)[:, None] % 128).repeat(1, B).contiguous()
     else:
         tsmu_tab = wl.tsmu[None].contiguous()
@@ -402,7 +402,7 @@ def main():
         select(s)
         attend(s)
 
-    path = args.path or ("fused" if args.workload == "config5" else "separate")
+    path = args.path or ("fused" if args.workload == "serving" else "separate")
     step = fused if path == "fused" else separate
     other = separate if path == "fused" else fused
 

@@ -190,14 +190,14 @@ def test_metadata_signed_zeros(qs, oracle):
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
 
 
-def test_metadata_config1_and_config2(qs, oracle):
-    wl = W.config1()
-    say("metadata config1")
+def test_metadata_tiny_and_page3_example(qs, oracle):
+    wl = W.tiny_needle()
+    say("metadata, tiny workload")
     mx, mn = run_meta(qs, wl)
     omx, omn = oracle_meta(oracle, wl)
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
-    say("metadata config2 (full size, 640 MiB K cache)")
-    wl = W.config2(device=DEV)
+    say("metadata, page-3 example (full size, 640 MiB K cache)")
+    wl = W.page3_select(device=DEV)
     mx, mn = run_meta(qs, wl)
     omx, omn = oracle_meta(oracle, wl)
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
@@ -261,13 +261,13 @@ def test_update_metadata_serving_chain(qs, oracle):
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
 
 
-def test_update_metadata_config5_newest_blocks(qs, oracle):
+def test_update_metadata_serving_newest_blocks(qs, oracle):
     """Serving shape (B=128, N=8, BS=128, 256 blocks a request, 8 GiB K pool): refresh the
     last blocks of every request in one call; sampled requests against the oracle, and no
     row outside the refreshed blocks written anywhere in the pool."""
-    wl = W.config5(device=DEV)
+    wl = W.serving(device=DEV)
     first, max_new = 250, 8                 # blocks 250 .. 255 (nb = 256)
-    say(f"metadata refresh config5 first={first} max_new={max_new}")
+    say(f"metadata refresh, serving shape, first={first} max_new={max_new}")
     shape = (wl.num_meta_blocks, wl.BS, wl.N, wl.D)
     mx = torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV)
     mn = torch.full(shape, 7.0, dtype=torch.bfloat16, device=DEV)
@@ -421,9 +421,9 @@ def test_block_select_topk_uniform_and_clustered(qs, oracle):
             np.testing.assert_array_equal(tnp(ns), ons)
 
 
-def test_block_select_config1_needle(qs, oracle):
-    say("select config1")
-    wl = W.config1()
+def test_block_select_tiny_needle(qs, oracle):
+    say("select, tiny workload")
+    wl = W.tiny_needle()
     mx, mn = run_meta(qs, wl)
     sel, ns, sc = run_select(qs, wl, mx, mn)
     omx, omn = oracle_meta(oracle, wl)
@@ -434,9 +434,9 @@ def test_block_select_config1_needle(qs, oracle):
 
 
 @pytest.mark.parametrize("flags", [0, W.FORCE_SINK | W.FORCE_WINDOW])
-def test_block_select_config2_full(qs, oracle, flags):
-    say(f"select config2 full flags={flags}")
-    wl = W.config2(device=DEV)
+def test_block_select_page3_example_full(qs, oracle, flags):
+    say(f"select, page-3 example, full size, flags={flags}")
+    wl = W.page3_select(device=DEV)
     wl.flags = flags
     if flags:
         wl.tsmu = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
@@ -515,10 +515,10 @@ def test_probe_select_at_block_capacity(qs, oracle):
     compare_probe(tnp(sel), tnp(ns), o, nbs_of(wl), 200)
 
 
-def test_probe_select_config3_sweep(qs, oracle):
-    wl = W.config3()
+def test_probe_select_page1_k_sweep(qs, oracle):
+    wl = W.page1_probe()
     for k in (1, 2, 4, 8, 16, 32):
-        say(f"probe config3 k={k}")
+        say(f"probe, page-1 workload, k={k}")
         sel, ns = qs.qs_probe_select(wl.query.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV),
                                      wl.seq_lens.to(DEV), k, importance=wl.importance.to(DEV), n_probe=8,
                                      flags=W.RECENCY)
@@ -608,9 +608,9 @@ def test_sparse_attn_empty_rows_write_zeros(qs):
     assert torch.all(out == 0)
 
 
-def test_sparse_attn_config1(qs, oracle):
-    say("attn config1 (oracle selection)")
-    wl = W.config1()
+def test_sparse_attn_tiny(qs, oracle):
+    say("attn, tiny workload (oracle selection)")
+    wl = W.tiny_needle()
     omx, omn = oracle_meta(oracle, wl)
     osel, ons, _ = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k)
     out = qs.qs_sparse_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV),
@@ -621,11 +621,11 @@ def test_sparse_attn_config1(qs, oracle):
 
 
 @pytest.mark.parametrize("int8", [False, True])
-def test_sparse_attn_config3(qs, oracle, int8):
-    wl = W.config3()
+def test_sparse_attn_page1_probe(qs, oracle, int8):
+    wl = W.page1_probe()
     kc, vc = (wl.k_i8, wl.v_i8) if int8 else (wl.k_cache, wl.v_cache)
     for k in (1, 2, 4, 8, 16, 32):
-        say(f"attn config3 k={k} int8={int8}")
+        say(f"attn, page-1 workload, k={k} int8={int8}")
         o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, wl.N,
                                 importance=wl.importance, n_probe=8, flags=W.RECENCY)
         sel, ns = torch.from_numpy(o["selected"]), torch.from_numpy(o["n_selected"])
@@ -696,9 +696,9 @@ def test_select_attn_random(qs, oracle, case):
     assert np.array_equal(tnp(s2), gsel) and np.array_equal(tnp(n2), gns)
 
 
-def test_select_attn_config1(qs, oracle):
-    wl = W.config1()
-    say("select+attention config1")
+def test_select_attn_tiny(qs, oracle):
+    wl = W.tiny_needle()
+    say("select+attention, tiny workload")
     mx, mn = run_meta(qs, wl, sentinel=0.0)
     out, sel, ns = run_fused(qs, wl, mx, mn)
     omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
@@ -710,11 +710,11 @@ def test_select_attn_config1(qs, oracle):
     assert np.abs(out.cpu().numpy() - ref).max() <= 1e-4
 
 
-def test_select_attn_config4_sampled(qs, oracle):
+def test_select_attn_long_context_sampled(qs, oracle):
     """Long-context shape through qs_select_attn_decode (scoring grid, then per-split top-k
     + attention, then combine): sampled requests against the oracle."""
-    wl = W.config4(device=DEV)
-    say("select+attention config4 (full size)")
+    wl = W.long_context(device=DEV)
+    say("select+attention, long context (full size)")
     mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
     mn = torch.zeros_like(mx)
     qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
@@ -738,11 +738,11 @@ def test_select_attn_config4_sampled(qs, oracle):
     assert err <= 2e-2, f"attention err {err:.3e}"
 
 
-def test_select_attn_config5_sampled(qs, oracle):
+def test_select_attn_serving_sampled(qs, oracle):
     """Serving shape through the fused path (1024 rows, one workgroup each): selection and
     output of sampled requests against the oracle."""
-    wl = W.config5(device=DEV)
-    say("select+attention config5 (full size)")
+    wl = W.serving(device=DEV)
+    say("select+attention, serving (full size)")
     mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=torch.bfloat16, device=DEV)
     mn = torch.zeros_like(mx)
     qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
@@ -846,17 +846,17 @@ def check_large(qs, oracle, wl, reqs, label):
     return tnp(sel), tnp(ns)
 
 
-def test_config4_full_size_sampled(qs, oracle):
-    wl = W.config4(device=DEV)
-    sel, ns = check_large(qs, oracle, wl, [0, 3, 7], "config4")
+def test_long_context_full_size_sampled(qs, oracle):
+    wl = W.long_context(device=DEV)
+    sel, ns = check_large(qs, oracle, wl, [0, 3, 7], "long context")
     # needle recall is reported, not gated
     hits = sum(int((t // wl.BS) in set(sel[b, n, :ns[b, n]].tolist())) for b, t in wl.needles for n in range(wl.N))
-    say(f"config4 needle recall {hits}/{wl.B * wl.N}")
+    say(f"long-context needle recall {hits}/{wl.B * wl.N}")
 
 
-def test_config5_full_size_sampled(qs, oracle):
-    wl = W.config5(device=DEV)
-    check_large(qs, oracle, wl, [0, 77, 127], "config5")
+def test_serving_full_size_sampled(qs, oracle):
+    wl = W.serving(device=DEV)
+    check_large(qs, oracle, wl, [0, 77, 127], "serving")
 
 
 def test_workspace_shared_across_shapes_and_operations(qs, oracle):
@@ -1015,11 +1015,11 @@ def test_prefill_importance_random(qs, oracle, case):
     assert torch.equal(imp, imp2)
 
 
-def test_prefill_importance_config3_sampled_heads(qs, oracle):
-    """Config 3's prefill (4096 tokens, 16 heads, fp32): every head on the GPU, heads 0 and 15
+def test_prefill_importance_page1_prompt_sampled_heads(qs, oracle):
+    """The page-1 probe workload's prefill (4096 tokens, 16 heads, fp32): every head on the GPU, heads 0 and 15
     against the oracle, and the row-mass identity (the importance sums to H * L)."""
-    wl, q = W.config3_prefill()
-    say("prefill importance config3 (4096 tokens)")
+    wl, q = W.page1_probe_prefill()
+    say("prefill importance, page-1 prompt (4096 tokens)")
     imp, himp = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
                                          with_heads=True)
     torch.cuda.synchronize()

@@ -3,7 +3,7 @@ budget (k+1)/2, probe fill, recency insurance).
 
 Pinned against: page 1's printed budget values, the probe positions the printed loop
 visits, numpy matmul block maxima, numpy argmax / lexsort / float32 cumsum, brute force
-on tiny inputs in a sort-based two-stage form, and config 3's needle and k=1 behaviour.
+on tiny inputs in a sort-based two-stage form, and the page-1 probe workload's needle and k=1 behaviour.
 """
 
 import numpy as np
@@ -137,11 +137,11 @@ def test_recency_never_evicts_importance(oracle):
         assert {0, 1, 63} <= s
 
 
-def test_config3_k_sweep(oracle):
+def test_page1_probe_k_sweep(oracle):
     """k=1 takes the top importance block only; from k=4 on the needle block is in
     every head's selection (k=2 shows page 1's small-k failure: recency evicts the
     single probe pick); the most recent block is always kept when k > 1."""
-    base = W.config3()
+    base = W.page1_probe()
     needle_block = base.needles[0][1] // base.BS
     nb = int(base.seq_lens[0]) // base.BS
     for k in (1, 2, 4, 8, 16, 32):

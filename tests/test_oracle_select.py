@@ -4,7 +4,7 @@ top-k with lower-index ties, sink/window forcing).
 Pinned against: the Quest upper bound checked with numpy dot products, closed forms
 (single-key metadata, non-negative query, absent blocks), the GQA mean on exactly
 representable queries, numpy.lexsort as the ordering, brute force over subsets, and
-config 1's planted needle.
+the tiny workload's planted needle.
 """
 
 import itertools
@@ -224,9 +224,9 @@ def test_window_only_when_aligned_is_last_block(oracle):
         assert np.isnan(sc[0, n, 19]) and not np.isnan(sc[0, n, :19]).any()
 
 
-def test_config1_needle_selected(oracle):
-    (tok, bs, want_block), = [tuple(int(x) for x in r) for r in golden_rows("config1_needle.txt")]
-    wl = W.config1()
+def test_tiny_needle_selected(oracle):
+    (tok, bs, want_block), = [tuple(int(x) for x in r) for r in golden_rows("tiny_needle.txt")]
+    wl = W.tiny_needle()
     assert tok // bs == want_block and wl.BS == bs
     mx, mn = _build(oracle, wl)
     sel, ns, sc = oracle.block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k)

@@ -15,7 +15,7 @@ Shapes follow the two pages' workloads:
   per-token prefill importance, an fp32 KV cache with an int8 copy.
 
 Small cases are drawn on the CPU (identical on every machine). The large cases
-(config 2, 4, 5 below) are drawn on the device the caller names, with a seeded
+(the page-3 example, long-context and serving workloads below) are drawn on the device the caller names, with a seeded
 ``torch.Generator`` there, and copied to the host when the oracle needs them.
 """
 
@@ -154,7 +154,7 @@ def _cdiv(a, b):
 # the five benchmark / parity configurations
 # ----------------------------------------------------------------------------------------
 
-def config1(seed: int = 0) -> Workload:
+def tiny_needle(seed: int = 0) -> Workload:
     """Tiny Quest select + sparse attention, fp32 (CPU-drawn).
 
     B=1, H=4, N=1, D=128, BS=32, seq_len=2048 (64 blocks), k=8. Query, K and V are
@@ -173,11 +173,11 @@ def config1(seed: int = 0) -> Workload:
     mmbpr = _cdiv(nb, BS)
     mt = torch.arange(mmbpr, dtype=torch.int32).reshape(1, mmbpr)
     sl = torch.full((B,), L, dtype=torch.int32)
-    return Workload("config1_tiny_fp32", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt, mmbpr,
+    return Workload("tiny_b1_h4_l2048_fp32", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt, mmbpr,
                     sl.clone(), tsmu=None, flags=0, sel_heads=N, needles=[(0, t)])
 
 
-def config2(device="cpu", seed: int = 1, B: int = 20, nb: int = 128, dtype=torch.bfloat16) -> Workload:
+def page3_select(device="cpu", seed: int = 1, B: int = 20, nb: int = 128, dtype=torch.bfloat16) -> Workload:
     """Quest select shaped like page 3's usage example, bf16 (or ``dtype``, e.g. fp16).
 
     B=20, H=32, N=8, D=128, BS=128, MMBPR=1, seq_len=16384 (128 blocks), k=8.
@@ -197,11 +197,11 @@ def config2(device="cpu", seed: int = 1, B: int = 20, nb: int = 128, dtype=torch
     q = _uniform((B, H, D), g, device).to(dtype)
     sl = torch.full((B,), L, dtype=torch.int32, device=device)
     name = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(dtype, str(dtype))
-    return Workload(f"config2_p3_select_{name}", B, H, N, D, BS, k, q, kc, None, bt, sl, mt,
+    return Workload(f"page3_select_b{B}_l{L}_{name}", B, H, N, D, BS, k, q, kc, None, bt, sl, mt,
                     n_meta, sl.clone(), tsmu=None, flags=0, sel_heads=N)
 
 
-def config3(seed: int = 3, k: int = 32) -> Workload:
+def page1_probe(seed: int = 3, k: int = 32) -> Workload:
     """Page 1's probe selection, fp32 with an int8 copy (CPU-drawn).
 
     B=1, H=16, N=8 (group 2), D=128, BS=32, seq_len=4096 (128 blocks), n_probe=8.
@@ -231,13 +231,13 @@ def config3(seed: int = 3, k: int = 32) -> Workload:
     bt = torch.arange(nb, dtype=torch.int32).reshape(1, nb)
     mt = torch.zeros((1, 1), dtype=torch.int32)
     sl = torch.full((B,), L, dtype=torch.int32)
-    return Workload("config3_p1_probe_fp32_int8", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt, 1,
+    return Workload("page1_probe_b1_h16_l4096_fp32_int8", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt, 1,
                     sl.clone(), tsmu=None, flags=RECENCY, sel_heads=H, n_probe=8,
                     importance=importance, k_i8=k8, v_i8=v8, k_scale=ks, v_scale=vs,
                     needles=[(0, t)])
 
 
-def config4(device="cpu", seed: int = 2, B: int = 8, min_len: int = 8192,
+def long_context(device="cpu", seed: int = 2, B: int = 8, min_len: int = 8192,
             max_len: int = 131072) -> Workload:
     """Long-context paged decode, bf16.
 
@@ -276,12 +276,12 @@ def config4(device="cpu", seed: int = 2, B: int = 8, min_len: int = 8192,
         dirn = qb / qb.norm(dim=-1, keepdim=True)
         phys = int(bt_h[b, t // BS])
         kc[phys, t % BS] = (4.0 * math.sqrt(D) * dirn).to(torch.bfloat16)
-    return Workload("config4_long_context_bf16", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt,
+    return Workload(f"long_context_b{B}_l{min_len // 1024}k_{max_len // 1024}k_bf16", B, H, N, D, BS, k, q, kc, vc, bt, sl, mt,
                     n_meta, msl, tsmu=tsmu, flags=FORCE_SINK | FORCE_WINDOW, sel_heads=N,
                     needles=needles)
 
 
-def config5(device="cpu", seed: int = 4, B: int = 128, nb: int = 256,
+def serving(device="cpu", seed: int = 4, B: int = 128, nb: int = 256,
             n_query_sets: int = 4) -> Workload:
     """Large-batch serving decode, bf16.
 
@@ -305,7 +305,7 @@ def config5(device="cpu", seed: int = 4, B: int = 128, nb: int = 256,
     mt = torch.randperm(n_meta, generator=g, device=device).to(torch.int32).reshape(B, mmbpr)
     sl = torch.full((B,), L, dtype=torch.int32, device=device)
     tsmu = torch.zeros((B,), dtype=torch.int32, device=device)
-    return Workload("config5_serving_bf16", B, H, N, D, BS, k, qs[0].contiguous(), kc, vc, bt,
+    return Workload(f"serving_b{B}_h{H}_l{L}_bf16", B, H, N, D, BS, k, qs[0].contiguous(), kc, vc, bt,
                     sl, mt, n_meta, sl.clone(), tsmu=tsmu, flags=FORCE_SINK | FORCE_WINDOW,
                     sel_heads=N, extra={"query_sets": qs})
 
@@ -378,9 +378,9 @@ def prefill_queries(wl: Workload, seed: int, max_len: int = 0, dist: str = "norm
     return x.to(dt)
 
 
-def config3_prefill(seed: int = 5):
-    """The prefill that produces page 1's importance for config 3: config 3's requests and
+def page1_probe_prefill(seed: int = 5):
+    """The prefill that produces page 1's importance for the page-1 probe workload: its requests and
     K cache (B=1, H=16, N=8, D=128, BS=32, 4096 tokens, fp32) with 4096 prefill query rows
     ~ N(0,1). Returns (workload, queries [1, 4096, 16, 128])."""
-    wl = config3()
+    wl = page1_probe()
     return wl, prefill_queries(wl, seed)
