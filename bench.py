@@ -302,8 +302,8 @@ def main():
                     help="size of the plain device copy timed beside the step (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the path has no cross-GPU step in this build (see the sharding "
-              "design); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path has no cross-GPU step (each GPU runs these kernels "
+              "on its own share of the requests); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     from top_kv_block_amd import qsparse as qs
