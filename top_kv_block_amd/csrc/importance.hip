@@ -90,6 +90,38 @@ __device__ __forceinline__ attn::f32x4 dot_tile(const Frag<DT>& a, const Frag<DT
     return c0 + c1;
 }
 
+// two tiles sharing the operand a: four independent accumulation chains
+template <int DT>
+__device__ __forceinline__ void dot_tile2(const Frag<DT>& a, const Frag<DT>& b0, const Frag<DT>& b1,
+                                          attn::f32x4& r0, attn::f32x4& r1) {
+    attn::f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, d0 = c0, d1 = c0;
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t aw[4] = {a.v[i].x, a.v[i].y, a.v[i].z, a.v[i].w};
+            const uint32_t bw[4] = {b0.v[i].x, b0.v[i].y, b0.v[i].z, b0.v[i].w};
+            const uint32_t ew[4] = {b1.v[i].x, b1.v[i].y, b1.v[i].z, b1.v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(bw[e]), c0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(ew[e]), d0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e + 1]), __uint_as_float(bw[e + 1]), c1, 0, 0, 0);
+                d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e + 1]), __uint_as_float(ew[e + 1]), d1, 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            c0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b0.v[i]), c0);
+            d0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b1.v[i]), d0);
+            c1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i + 1]), attn::as_op8<DT>(b0.v[i + 1]), c1);
+            d1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i + 1]), attn::as_op8<DT>(b1.v[i + 1]), d1);
+        }
+    }
+    r0 = c0 + c1;
+    r1 = d0 + d1;
+}
+
 // Work item of this workgroup in a 1-D grid of tiles x heads x requests, in decreasing
 // order of work (longest_first: tile gx-1 first, else tile 0 first). All workgroups are
 // resident at once and the dispatcher hands linear ids to the CUs round-robin, so CU c
@@ -117,8 +149,10 @@ __device__ __forceinline__ const uint8_t* key_row(const ImpParams& p, int b, int
 
 // A 16-row operand tile shared by the workgroup's four waves through LDS: the workgroup
 // loads it once (each thread 16-byte pieces of whole rows), every wave reads its
-// fragment from LDS. Rows are padded by 16 B against bank conflicts. Two buffers: the
-// next tile is fetched into registers while the current one is multiplied.
+// fragment from LDS. Rows are padded by 16 B against bank conflicts. The passes take two
+// tiles per workgroup barrier (four buffers, two pairs in turn): while a pair is
+// multiplied, the next pair is already in flight into registers, and the waves run four
+// independent accumulation chains (dot_tile2).
 template <int DT>
 struct Tile {
     static constexpr int kRowBytes = D * elem_bytes(DT);        // 512 (fp32) or 256
@@ -159,7 +193,7 @@ __device__ __forceinline__ void frag_from_tile(Frag<DT>& f, const uint8_t* buf, 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
-    __shared__ __attribute__((aligned(16))) uint8_t kt[2][Tile<DT>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t kt[4][Tile<DT>::kBytes];
     const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, true);  // the last rows see the most keys
     const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
@@ -183,39 +217,50 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         tile_fetch<DT>(v, [&](int i) { return kr + size_t(min(i, L - 1 - s0)) * p.N * D * es; });
         return true;
     };
-    // tiles alternate between two register sets and two LDS buffers; each set is refilled
-    // with the tile two steps ahead as soon as it has been stored
-    auto step = [&](int s0, uint8_t* buf, u32x4 (&nv)[Tile<DT>::kPerThread], bool& have) {
-        if (have) tile_store<DT>(buf, nv);
-        const bool cur = have;
-        __syncthreads();  // tile s0 is in buf; the reads of buf two tiles ago are done
-        have = s0 + 32 <= s_end && fetch(s0 + 32, nv);
-        if (cur && s0 <= t0 + 15 && t0 < L) {  // this wave has rows that see these keys
-            Frag<DT> kf;
-            frag_from_tile<DT>(kf, buf, r, j);
-            const int s = s0 + r;
-            const attn::f32x4 c = dot_tile<DT>(qf, kf);  // C[row 4j+i][key r]
+    // the softmax update of this lane's 4 rows with one 16-key tile's scores
+    auto upd = [&](const attn::f32x4& c, int s) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 4 * j + i;
-                if (s <= t && s < L) {
-                    // one exp2 per score: a new maximum rescales the sum, any other score adds
-                    const float x = c[i] * p.scale2;
-                    const float d = x - m[i];
-                    const float e = exp2f(-fabsf(d));  // m = -inf: d = +inf, e = 0
-                    l[i] = d > 0.f ? l[i] * e + 1.f : l[i] + e;
-                    m[i] = fmaxf(m[i], x);
-                }
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * j + i;
+            if (s <= t && s < L) {
+                // one exp2 per score: a new maximum rescales the sum, any other score adds
+                const float x = c[i] * p.scale2;
+                const float d = x - m[i];
+                const float e = exp2f(-fabsf(d));  // m = -inf: d = +inf, e = 0
+                l[i] = d > 0.f ? l[i] * e + 1.f : l[i] + e;
+                m[i] = fmaxf(m[i], x);
             }
+        }
+    };
+    // a step takes two key tiles (32 keys): both go to LDS, one barrier, then the next two
+    // are fetched into the freed register sets and the pair is multiplied; four LDS
+    // buffers, so a pair's stores never meet the previous pair's reads
+    auto step2 = [&](int s0, uint8_t* b0, uint8_t* b1, u32x4 (&va)[Tile<DT>::kPerThread], bool& ha,
+                     u32x4 (&vb)[Tile<DT>::kPerThread], bool& hb) {
+        if (ha) tile_store<DT>(b0, va);
+        if (hb) tile_store<DT>(b1, vb);
+        const bool c0 = ha && s0 <= t0 + 15 && t0 < L, c1 = hb && s0 + 16 <= t0 + 15 && t0 < L;
+        __syncthreads();
+        ha = s0 + 32 <= s_end && fetch(s0 + 32, va);
+        hb = s0 + 48 <= s_end && fetch(s0 + 48, vb);
+        if (c0 && c1) {
+            Frag<DT> k0, k1;
+            frag_from_tile<DT>(k0, b0, r, j);
+            frag_from_tile<DT>(k1, b1, r, j);
+            attn::f32x4 r0, r1;
+            dot_tile2<DT>(qf, k0, k1, r0, r1);
+            upd(r0, s0 + r);
+            upd(r1, s0 + 16 + r);
+        } else if (c0 || c1) {
+            Frag<DT> kf;
+            frag_from_tile<DT>(kf, c0 ? b0 : b1, r, j);
+            upd(dot_tile<DT>(qf, kf), (c0 ? s0 : s0 + 16) + r);
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
     bool ha = fetch(0, na);
     bool hb = 16 <= s_end && fetch(16, nb);
-    for (int s0 = 0; s0 <= s_end; s0 += 32) {
-        step(s0, kt[0], na, ha);
-        if (s0 + 16 <= s_end) step(s0 + 16, kt[1], nb, hb);
-    }
+    for (int s0 = 0, pb = 0; s0 <= s_end; s0 += 32, pb ^= 2) step2(s0, kt[pb], kt[pb + 1], na, ha, nb, hb);
     // merge the 16 key columns of each row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -230,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
-    __shared__ __attribute__((aligned(16))) uint8_t qt[2][Tile<DT>::kBytes];
-    __shared__ float lt_s[2][16];
+    __shared__ __attribute__((aligned(16))) uint8_t qt[4][Tile<DT>::kBytes];
+    __shared__ float lt_s[4][16];
     const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, false);  // the first keys have the most rows
     const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
@@ -254,33 +299,46 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
         });
         lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
     };
-    // as in the row pass: two register sets and two LDS buffers, two tiles ahead
-    auto step = [&](int t0, int bi, u32x4 (&nv)[Tile<DT>::kPerThread], float& nl) {
-        tile_store<DT>(qt[bi], nv);
-        if (threadIdx.x < 16) lt_s[bi][threadIdx.x] = nl;
-        __syncthreads();
-        if (t0 + 32 < L) fetch(t0 + 32, nv, nl);
-        if (kr != nullptr && t0 + 15 >= s0) {  // some row of the tile sees this wave's keys
-            Frag<DT> qf;
-            frag_from_tile<DT>(qf, qt[bi], r, j);
-            const int t = t0 + r;
-            const float lt = lt_s[bi][r];
-            const attn::f32x4 c = dot_tile<DT>(kf, qf);  // C[key 4j+i][row r]
+    auto upd = [&](const attn::f32x4& c, int t, float lt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = s0 + 4 * j + i;
-                if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int s = s0 + 4 * j + i;
+            if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
+        }
+    };
+    // as in the row pass: two query tiles per barrier, four LDS buffers
+    auto step2 = [&](int t0, int bi, u32x4 (&va)[Tile<DT>::kPerThread], float& la, u32x4 (&vb)[Tile<DT>::kPerThread],
+                     float& lb, bool hb) {
+        tile_store<DT>(qt[bi], va);
+        if (threadIdx.x < 16) lt_s[bi][threadIdx.x] = la;
+        if (hb) {
+            tile_store<DT>(qt[bi + 1], vb);
+            if (threadIdx.x < 16) lt_s[bi + 1][threadIdx.x] = lb;
+        }
+        __syncthreads();
+        if (t0 + 32 < L) fetch(t0 + 32, va, la);
+        if (t0 + 48 < L) fetch(t0 + 48, vb, lb);
+        const bool c0 = kr != nullptr && t0 + 15 >= s0, c1 = hb && kr != nullptr && t0 + 31 >= s0;
+        if (c0 && c1) {
+            Frag<DT> q0, q1;
+            frag_from_tile<DT>(q0, qt[bi], r, j);
+            frag_from_tile<DT>(q1, qt[bi + 1], r, j);
+            attn::f32x4 r0, r1;
+            dot_tile2<DT>(kf, q0, q1, r0, r1);
+            upd(r0, t0 + r, lt_s[bi][r]);
+            upd(r1, t0 + 16 + r, lt_s[bi + 1][r]);
+        } else if (c0 || c1) {
+            const int bx = c0 ? bi : bi + 1;
+            Frag<DT> qf;
+            frag_from_tile<DT>(qf, qt[bx], r, j);
+            upd(dot_tile<DT>(kf, qf), (c0 ? t0 : t0 + 16) + r, lt_s[bx][r]);
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
     float la = 0.f, lb = 0.f;
     fetch(sw, na, la);
     if (sw + 16 < L) fetch(sw + 16, nb, lb);
-    for (int t0 = sw; t0 < L; t0 += 32) {
-        step(t0, 0, na, la);
-        if (t0 + 16 < L) step(t0 + 16, 1, nb, lb);
-    }
+    for (int t0 = sw, pb = 0; t0 < L; t0 += 32, pb ^= 2) step2(t0, pb, na, la, nb, lb, t0 + 16 < L);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float tot = group_sum<16>(acc[i]);
