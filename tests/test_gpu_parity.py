@@ -935,6 +935,63 @@ def test_graph_replay_matches_eager(qs):
         assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))
 
 
+def test_graph_replay_probe_path(qs):
+    """Page 1's path captured in a HIP graph: a metadata refresh, the prefill importance, the
+    probe selection and fp32 attention with one selection row per query head. No workspace is
+    passed, so every call takes the binding's cached workspace of the capture stream. Three
+    replays, with the same eager calls (on another stream's workspaces) between them, give
+    bitwise the eager results."""
+    say("graph replay, probe path")
+    wl = W.random_case(62, 2, 16, 8, 32, [32 * 60 + 5, 32 * 33], k=12, dtype=torch.float32, with_v=True)
+    pq = W.prefill_queries(wl, 62).to(DEV)
+    wl = wl.to(DEV)
+    B, H, N, BS = wl.B, wl.H, wl.N, wl.BS
+    mx = torch.zeros((wl.num_meta_blocks, BS, N, wl.D), dtype=torch.float32, device=DEV)
+    mn = torch.zeros_like(mx)
+    last = torch.tensor([cdiv(int(x), BS) - 1 for x in wl.seq_lens.cpu().tolist()], dtype=torch.int32, device=DEV)
+    imp = torch.empty((B, pq.shape[1]), dtype=torch.float32, device=DEV)
+    psel = torch.empty((B, H, wl.k), dtype=torch.int32, device=DEV)
+    pns = torch.empty((B, H), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, H, wl.D), dtype=torch.float32, device=DEV)
+
+    def step():
+        qs.qs_update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, last, 1, wl.meta_tables, mx, mn)
+        qs.qs_prefill_importance(pq, wl.k_cache, wl.block_tables, wl.seq_lens, importance=imp)
+        qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, wl.k, importance=imp, n_probe=8,
+                           flags=qs.QS_RECENCY, selected=psel, n_selected=pns)
+        qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, psel, pns,
+                                 sel_heads=H, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (mx, mn, imp, psel, pns, out)]
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            step()
+    torch.cuda.current_stream().wait_stream(cs)
+    for rep in range(3):
+        for t in (mx, mn, imp, out):
+            t.fill_(5.0)
+        psel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (mx, mn, imp, psel, pns, out)
+        for name, a, b in zip(("maxblocks", "minblocks", "importance", "selected", "n_selected", "out"), got, want):
+            if name in ("maxblocks", "minblocks"):  # only the refreshed rows are defined after the fill
+                rows = [(int(wl.meta_tables[bb, int(last[bb]) // BS]), int(last[bb]) % BS) for bb in range(B)]
+                for m, r in rows:
+                    assert torch.equal(a[m, r].view(torch.int32), b[m, r].view(torch.int32)), (rep, name)
+            else:
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, name)
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), want[5].view(torch.int32))
+
+
 # ------------------------------------------------------------------------------------------
 # page-3 call shapes (top_kv_block_amd.quest_ops)
 # ------------------------------------------------------------------------------------------
