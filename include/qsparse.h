@@ -282,7 +282,9 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                                 int32_t* selected, int32_t* n_selected,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* bytes of workspace qs_prefill_importance needs (0 for invalid sizes) */
+/* bytes of workspace qs_prefill_importance needs (0 for invalid sizes): B * H * max_len
+ * floats of row normalisers plus, per chunk of the causal work, three more (a job of fewer
+ * than 8192 tiles of 64 rows x heads x requests is cut into up to 8 chunks) */
 size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_len);
 
 /*
@@ -305,7 +307,7 @@ size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_l
  *   head_importance    [B, H, importance_stride] fp32 output, or NULL (not both NULL)
  *   workspace          at least qs_prefill_importance_workspace_bytes(); 256-byte aligned
  * Dot products run on the matrix cores in fp32 accumulation from exactly widened inputs;
- * the heads are summed in head order, so results are deterministic.
+ * chunk partials and heads are summed in a fixed order, so results are deterministic.
  */
 qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
                                 qs_dtype dtype, const void* query, int32_t max_len,

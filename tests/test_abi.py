@@ -227,7 +227,11 @@ def test_prefill_importance_rejects(qs, kw, status):
 
 
 def test_prefill_importance_workspace_size(qs):
-    assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == 2 * 16 * 4096 * 4
+    # fp32 row normalisers + per chunk (row max, row sum, column sums); 64 tiles of 64 rows
+    # x 16 heads is too few items to balance, so 8 chunks; 2 x 32 x 128 tiles are enough: 1
+    assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == (1 + 3 * 8) * 16 * 4096 * 4
+    assert qs.prefill_importance_workspace_bytes(2, 32, 8192) == (1 + 3 * 1) * 2 * 32 * 8192 * 4
+    assert qs.prefill_importance_workspace_bytes(1, 1, 100) == 2816  # (1 + 3 * 2 chunks) * 100 * 4 = 2800, rounded up to 256 B
     assert qs.prefill_importance_workspace_bytes(0, 16, 4096) == 256
     assert qs.prefill_importance_workspace_bytes(1, 0, 4096) == 0
     assert _imp(qs, imp=None, himp=FAKE, wsb=qs.prefill_importance_workspace_bytes(0, 16, 4096)) == 0

@@ -1048,6 +1048,7 @@ IMP_CASES = [
     (103, 1, 16, 8, 32, [640], torch.float16, 640, 700, 0.2),
     (104, 2, 6, 3, 64, [129, 300], torch.float32, 301, 250, 0.0),   # stride shorter than a prompt
     (105, 1, 2, 1, 128, [1000], torch.bfloat16, 1000, 1000, 0.0),
+    (106, 2, 3, 1, 16, [1500, 700], torch.bfloat16, 1500, 1500, 0.0),  # 8 chunks of 192 keys, ragged
 ]
 
 
@@ -1085,6 +1086,26 @@ def test_prefill_importance_page1_prompt_sampled_heads(qs, oracle):
     assert abs(g[0].astype(np.float64).sum() - wl.H * L) <= 1e-4 * wl.H * L
     for lo in (0, 15):
         _, oh = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, wl.N, heads=(lo, lo + 1))
+        check_importance(gh[:, lo], oh[:, lo], f"head {lo}")
+
+
+def test_prefill_importance_one_chunk_sampled_heads(qs, oracle):
+    """A job large enough to balance without chunks (2 requests x 32 heads x 128 tiles of 64
+    rows): one chunk per tile. Ragged lengths (8192 and 5000 tokens), bf16; heads 0 and 31
+    against the oracle, zeros past each prompt."""
+    B, H, N, BS, lens = 2, 32, 8, 64, [8192, 5000]
+    say(f"prefill importance one chunk B={B} H={H} lens={lens}")
+    wl = W.random_case(107, B, H, N, BS, lens, k=2, dtype=torch.bfloat16, with_v=False)
+    q = W.prefill_queries(wl, 107, max_len=max(lens))
+    imp, himp = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                         with_heads=True)
+    torch.cuda.synchronize()
+    g, gh = tnp(imp), tnp(himp)
+    for b, L in enumerate(lens):
+        assert not g[b, L:].any() and not gh[b, :, L:].any()
+        assert abs(g[b, :L].astype(np.float64).sum() - H * L) <= 1e-4 * H * L
+    for lo in (0, H - 1):
+        _, oh = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, N, heads=(lo, lo + 1))
         check_importance(gh[:, lo], oh[:, lo], f"head {lo}")
 
 

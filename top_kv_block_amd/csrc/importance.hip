@@ -11,15 +11,26 @@
 // Design (CDNA4). The weights need each row's softmax normaliser before any column can
 // be summed, so there are two passes over the causal score matrix, both dense
 // contractions on the matrix cores (the scores are never stored):
-//   row pass     grid (64-row query tile, head, request): each wave takes 16 query rows
-//                and walks the 16-key tiles up to its last row, S = Q K^T on
+//   row pass     work item (64-row query tile, key chunk): each wave takes 16 query rows
+//                and walks the chunk's 16-key tiles up to its last row, S = Q K^T on
 //                v_mfma_f32_16x16x4_f32 (fp32 inputs) or v_mfma_f32_16x16x32_{bf16,f16};
 //                each lane keeps an online (max, sum) of its key column for its 4 rows and
-//                the 16 lanes of a row merge once at the end into log2-sum-exp per row;
-//   column pass  grid (64-key tile, head, request): each wave takes 16 keys and walks the
-//                16-row query tiles from its first key to the end, S^T = K Q^T, adds
-//                2^(x - lse_row) into per-lane column sums, merges the 16 lanes at the end;
-//   reduce       sums the heads in a fixed order (deterministic) and writes the outputs.
+//                the 16 lanes of a row merge once at the end into the chunk's (max, sum);
+//   merge        per row, the chunks' (max, sum) in chunk order -> log2-sum-exp (with
+//                one chunk the row pass writes it itself);
+//   column pass  work item (64-key tile, query-row chunk): each wave takes 16 keys and
+//                walks the chunk's 16-row query tiles from its first key on, S^T = K Q^T,
+//                adds 2^(x - lse_row) into per-lane column sums, merges the 16 lanes and
+//                writes the chunk's column sums;
+//   reduce       sums the chunks, then the heads, in a fixed order (deterministic).
+// Chunks: a causal tile's work grows with its distance from the diagonal. With 16-bit
+// inputs a wave's matrix work between two barriers is short, so a CU whose short tiles
+// have finished cannot keep its matrix pipe fed from the one long tile left; there every
+// tile's range is cut into chunks of R tiles (64 R keys or rows, at most 8 chunks), giving
+// several times more, bounded items, which the dispatcher hands to CUs as they free up.
+// With fp32 inputs one wave's matrix work alone keeps the pipe busy and the extra items
+// only cost their start-up, so each tile stays one item, as do jobs that already hold
+// enough tiles to balance (>= 8192); the snake order below evens the first items out.
 // Operand layout: a lane (row r = lane % 16, group j = lane / 16) holds channels
 // 32j .. 32j+31 of its row, contiguous in memory (16-byte loads). The contraction order
 // over channels is free, so both operands use that same channel order: at step ks the
@@ -45,9 +56,40 @@ struct ImpParams {
     const int32_t* sl;
     int B, H, N, BS, max_len;
     float scale2;  // softmax scale * log2(e)
+    int T, R, C;   // 64-row tiles of max_len, tiles per chunk, chunks
     float* lse;    // [B, H, max_len] workspace: log2-sum-exp2 of each row
-    float* himp;   // [B, H, max_len] workspace: per-head column sums
+    float* mpart;  // [C, B, H, max_len] workspace: each key chunk's row max (log2 units)
+    float* lpart;  // [C, B, H, max_len] workspace: each key chunk's sum of 2^(x - max)
+    float* cpart;  // [C, B, H, max_len] workspace: each row chunk's column sums
 };
+
+// chunking of a (B, H, max_len) job
+constexpr int kMaxChunks = 8;
+struct Split { int T, R, C; };
+inline Split imp_split(int B, int H, int max_len, bool chunked) {
+    constexpr int kEnoughItems = 8192;
+    Split sp;
+    sp.T = (max_len + 63) / 64;
+    if (sp.T <= 0) return Split{0, 1, 1};
+    const long items = long(sp.T) * H * B;
+    const int want = (!chunked || items >= kEnoughItems) ? 1 : min(kMaxChunks, sp.T);
+    sp.R = (sp.T + want - 1) / want;
+    sp.C = (sp.T + sp.R - 1) / sp.R;
+    return sp;
+}
+// items of the two passes per (head, request): the diagonal chunk of every tile plus the
+// full chunks (row pass: chunks c < i / R of row tile i; column pass: chunks c > j / R of
+// key tile j)
+inline long row_items(const Split& s) {
+    long n = s.T;
+    for (int c = 0; c < s.C; ++c) n += max(0, s.T - (c + 1) * s.R);
+    return n;
+}
+inline long col_items(const Split& s) {
+    long n = s.T;
+    for (int c = 1; c < s.C; ++c) n += long(c) * s.R;
+    return n;
+}
 
 // one row's channels 32j .. 32j+31 (this lane's operand slice)
 template <int DT>
@@ -122,22 +164,45 @@ __device__ __forceinline__ void dot_tile2(const Frag<DT>& a, const Frag<DT>& b0,
     r1 = d0 + d1;
 }
 
-// Work item of this workgroup in a 1-D grid of tiles x heads x requests, in decreasing
-// order of work (longest_first: tile gx-1 first, else tile 0 first). All workgroups are
-// resident at once and the dispatcher hands linear ids to the CUs round-robin, so CU c
-// holds ids c, c + kCus, c + 2 kCus, ...; a snake order over those rounds (round r
-// takes ranks r*kCus .. in forward order when r is even, backward when odd) gives every
-// CU a mix of long and short tiles instead of four equal ones.
+// Work item of this workgroup: (tile, chunk, head, request). Consecutive ranks take the
+// heads and requests of one (tile, chunk), so the items running together share their
+// other operand in L2. The full chunks (all of one size) come first, chunk by chunk, then
+// the diagonal chunks, longest tile first when there is one chunk. The first 1024 items
+// are all resident at once and the dispatcher hands ids to the CUs round-robin (CU c
+// holds ids c, c + kCus, ...), so ids map to ranks in a snake order over rounds of kCus
+// (forward in even rounds, backward in odd ones): with one chunk per tile every CU then
+// holds a mix of long and short tiles instead of four equal ones.
 constexpr int kCus = 256;
-struct WorkItem { int tile, h, b; };
-__device__ __forceinline__ WorkItem work_item(int gx, int H, int B, bool longest_first) {
-    const int T = gx * H * B;
-    const int id = blockIdx.x;
+struct WorkItem { int tile, chunk, h, b; };
+__device__ __forceinline__ int snake_rank() {
+    const int id = blockIdx.x, total = gridDim.x;
     const int rnd = id / kCus, pos = id % kCus;
-    const int cnt = min(kCus, T - rnd * kCus);  // ids in this round
-    const int rank = rnd * kCus + ((rnd & 1) ? cnt - 1 - pos : pos);
-    const int hb = rank % (H * B), k = rank / (H * B);
-    return WorkItem{longest_first ? gx - 1 - k : k, hb % H, hb / H};
+    const int cnt = min(kCus, total - rnd * kCus);  // ids in this round
+    return rnd * kCus + ((rnd & 1) ? cnt - 1 - pos : pos);
+}
+__device__ __forceinline__ WorkItem row_item(const ImpParams& p) {
+    const int HB = p.H * p.B, rank = snake_rank();
+    const int hb = rank % HB;
+    int q = rank / HB;
+    int tile = -1, chunk = 0;
+    for (int c = 0; c < p.C && tile < 0; ++c) {  // row tiles i >= (c + 1) R hold a full chunk c
+        const int n = max(0, p.T - (c + 1) * p.R);
+        if (q < n) { tile = (c + 1) * p.R + q; chunk = c; } else { q -= n; }
+    }
+    if (tile < 0) { tile = p.T - 1 - q; chunk = tile / p.R; }
+    return WorkItem{tile, chunk, hb % p.H, hb / p.H};
+}
+__device__ __forceinline__ WorkItem col_item(const ImpParams& p) {
+    const int HB = p.H * p.B, rank = snake_rank();
+    const int hb = rank % HB;
+    int q = rank / HB;
+    int tile = -1, chunk = 0;
+    for (int c = p.C - 1; c >= 1 && tile < 0; --c) {  // key tiles j < c R see a full chunk c
+        const int n = c * p.R;
+        if (q < n) { tile = q; chunk = c; } else { q -= n; }
+    }
+    if (tile < 0) { tile = q; chunk = tile / p.R; }
+    return WorkItem{tile, chunk, hb % p.H, hb / p.H};
 }
 
 // address of key s (head kh) of request b, or nullptr when its block is out of range
@@ -194,7 +259,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
     __shared__ __attribute__((aligned(16))) uint8_t kt[4][Tile<DT>::kBytes];
-    const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, true);  // the last rows see the most keys
+    const WorkItem wi = row_item(p);
     const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     const int tw = wi.tile * 64;  // the workgroup's rows tw .. tw+63
     if (tw >= L) return;                              // whole workgroup
     const int t0 = tw + 16 * w;                       // this wave's rows t0 .. t0+15
+    const int s_lo = wi.chunk * p.R * 64;             // the chunk's keys s_lo .. (<= tw since chunk <= tile / R)
     const int kh = h / (p.H / p.N);
     Frag<DT> qf;
     load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
@@ -209,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     float m[4], l[4];  // online max / sum of 2^x over this lane's key column, rows 4j + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
-    const int s_end = min(tw + 63, L - 1);  // last key any wave needs
+    const int s_end = min(min(s_lo + p.R * 64, tw + 64), L) - 1;  // last key any wave needs
     // key tile s0 (16 keys in one block): rows past L repeat the last key (masked)
     auto fetch = [&](int s0, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
         const uint8_t* kr = key_row(p, b, s0, kh, es);
@@ -258,17 +324,27 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
-    bool ha = fetch(0, na);
-    bool hb = 16 <= s_end && fetch(16, nb);
-    for (int s0 = 0, pb = 0; s0 <= s_end; s0 += 32, pb ^= 2) step2(s0, kt[pb], kt[pb + 1], na, ha, nb, hb);
-    // merge the 16 key columns of each row
+    bool ha = fetch(s_lo, na);
+    bool hb = s_lo + 16 <= s_end && fetch(s_lo + 16, nb);
+    for (int s0 = s_lo, pb = 0; s0 <= s_end; s0 += 32, pb ^= 2) step2(s0, kt[pb], kt[pb + 1], na, ha, nb, hb);
+    // merge the 16 key columns of each row into the chunk's (max, sum); every row t < L
+    // has a key of the chunk (s_lo <= tw), so the max is finite. With one chunk that is
+    // the row's log2-sum-exp already.
+    const size_t o = ((size_t(wi.chunk) * p.B + b) * p.H + h) * p.max_len;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float M = group_max<16>(m[i]);
         const float part = (m[i] == -INFINITY) ? 0.f : l[i] * exp2f(m[i] - M);
         const float S = group_sum<16>(part);
         const int t = t0 + 4 * j + i;
-        if (r == 0 && t < L) p.lse[(size_t(b) * p.H + h) * p.max_len + t] = M + log2f(S);
+        if (r == 0 && t < L) {
+            if (p.C == 1) {
+                p.lse[o + t] = M + log2f(S);
+            } else {
+                p.mpart[o + t] = M;
+                p.lpart[o + t] = S;
+            }
+        }
     }
 }
 
@@ -277,13 +353,15 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
     __shared__ __attribute__((aligned(16))) uint8_t qt[4][Tile<DT>::kBytes];
     __shared__ float lt_s[4][16];
-    const WorkItem wi = work_item((p.max_len + 63) / 64, p.H, p.B, false);  // the first keys have the most rows
+    const WorkItem wi = col_item(p);
     const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
     const int sw = wi.tile * 64;  // the workgroup's keys sw .. sw+63
-    if (sw >= L) return;
+    // the chunk's query rows t_lo .. t_hi-1 (rows before sw see none of these keys)
+    const int t_lo = max(wi.chunk * p.R * 64, sw), t_hi = min((wi.chunk + 1) * p.R * 64, L);
+    if (t_lo >= t_hi) return;                         // whole workgroup (sw >= L included)
     const int s0 = sw + 16 * w;      // this wave's keys s0 .. s0+15
     const int kh = h / (p.H / p.N);
     const bool live = s0 < L;
@@ -316,8 +394,8 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
             if (threadIdx.x < 16) lt_s[bi + 1][threadIdx.x] = lb;
         }
         __syncthreads();
-        if (t0 + 32 < L) fetch(t0 + 32, va, la);
-        if (t0 + 48 < L) fetch(t0 + 48, vb, lb);
+        if (t0 + 32 < t_hi) fetch(t0 + 32, va, la);
+        if (t0 + 48 < t_hi) fetch(t0 + 48, vb, lb);
         const bool c0 = kr != nullptr && t0 + 15 >= s0, c1 = hb && kr != nullptr && t0 + 31 >= s0;
         if (c0 && c1) {
             Frag<DT> q0, q1;
@@ -336,59 +414,106 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
     float la = 0.f, lb = 0.f;
-    fetch(sw, na, la);
-    if (sw + 16 < L) fetch(sw + 16, nb, lb);
-    for (int t0 = sw, pb = 0; t0 < L; t0 += 32, pb ^= 2) step2(t0, pb, na, la, nb, lb, t0 + 16 < L);
+    fetch(t_lo, na, la);
+    if (t_lo + 16 < t_hi) fetch(t_lo + 16, nb, lb);
+    for (int t0 = t_lo, pb = 0; t0 < t_hi; t0 += 32, pb ^= 2) step2(t0, pb, na, la, nb, lb, t0 + 16 < t_hi);
+    const size_t o = ((size_t(wi.chunk) * p.B + b) * p.H + h) * p.max_len;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float tot = group_sum<16>(acc[i]);
         const int s = s0 + 4 * j + i;
-        if (r == 0 && s < L) p.himp[(size_t(b) * p.H + h) * p.max_len + s] = tot;
+        if (r == 0 && s < L) p.cpart[o + s] = tot;
     }
 }
 
-// importance[b][s] = sum over heads (in head order) for s < L; 0 elsewhere
+// lse[t] = log2 of the sum over the key chunks of row t (chunks 0 .. (t / 64) / R, in
+// chunk order) of sum * 2^max
+__global__ __launch_bounds__(kThreads) void imp_merge_kernel(ImpParams p) {
+    const int t = blockIdx.x * kThreads + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    if (t >= L) return;
+    const size_t row = (size_t(b) * p.H + h) * p.max_len + t, cs = size_t(p.B) * p.H * p.max_len;
+    const int nc = (t / 64) / p.R + 1;  // <= C <= kMaxChunks
+    float mv[kMaxChunks], lv[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {  // all loads in flight at once
+        mv[c] = c < nc ? p.mpart[c * cs + row] : -INFINITY;
+        lv[c] = c < nc ? p.lpart[c * cs + row] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mv[c]);
+    float S = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+        if (c < nc) S += lv[c] * exp2f(mv[c] - M);
+    p.lse[row] = M + log2f(S);
+}
+
+// importance[b][s] = sum over heads of each head's column sum (its row chunks in chunk
+// order), 0 for s >= L. Workgroup = 64 keys of one request; wave w takes heads w, w + 4,
+// ... and the four partials are added in wave order (a fixed order: deterministic).
 __global__ __launch_bounds__(kThreads) void imp_reduce_kernel(ImpParams p, float* importance, int stride,
                                                               float* head_importance) {
-    const int s = blockIdx.x * kThreads + threadIdx.x, b = blockIdx.y;
-    if (s >= stride) return;
+    static_assert(kThreads == 256, "four partials, added in wave order");
+    __shared__ float part[kThreads / 64][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int s = blockIdx.x * 64 + lane, b = blockIdx.y;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    // key s has the column sums of row chunks s / (64 R) .. those holding rows below L
+    const int c_lo = (s / 64) / p.R, c_hi = (L + 64 * p.R - 1) / (64 * p.R);
+    const size_t cs = size_t(p.B) * p.H * p.max_len;
     float tot = 0.f;
-    for (int h = 0; h < p.H; ++h) {
-        const float v = s < L ? p.himp[(size_t(b) * p.H + h) * p.max_len + s] : 0.f;
-        tot += v;
-        if (head_importance) head_importance[(size_t(b) * p.H + h) * stride + s] = v;
+    if (s < stride) {
+        for (int h = w; h < p.H; h += kThreads / 64) {
+            float v = 0.f;
+            if (s < L) {
+                const float* src = p.cpart + (size_t(b) * p.H + h) * p.max_len + s;
+                float x[kMaxChunks];
+#pragma unroll
+                for (int c = 0; c < kMaxChunks; ++c) x[c] = (c >= c_lo && c < c_hi) ? src[c * cs] : 0.f;
+#pragma unroll
+                for (int c = 0; c < kMaxChunks; ++c) v += x[c];
+            }
+            tot += v;
+            if (head_importance) head_importance[(size_t(b) * p.H + h) * stride + s] = v;
+        }
     }
-    if (importance) importance[size_t(b) * stride + s] = tot;
+    part[w][lane] = tot;
+    __syncthreads();
+    if (w == 0 && s < stride && importance)
+        importance[size_t(b) * stride + s] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
 }  // namespace
 
 size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
-    size_t bytes = size_t(B) * H * max_len * sizeof(float) * 2;
+    const Split sp = imp_split(B, H, max_len, true);  // the larger of the two splits
+    size_t bytes = size_t(B) * H * max_len * sizeof(float) * (1 + 3 * size_t(sp.C));
     bytes = (bytes + 255) & ~size_t(255);
     return bytes < 256 ? 256 : bytes;
 }
 
 hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s) {
     float* ws = (float*)a.workspace;
+    const Split sp = imp_split(a.B, a.H, a.max_len, a.dtype != kF32);
+    const size_t plane = size_t(a.B) * a.H * a.max_len;
     ImpParams p{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr,
-                a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, ws,
-                ws + size_t(a.B) * a.H * a.max_len};
-    const dim3 grid(unsigned((a.max_len + 63) / 64 * a.H * a.B));  // tiles x heads x requests, see work_item
+                a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, sp.T, sp.R, sp.C,
+                ws, ws + plane, ws + plane * (1 + sp.C), ws + plane * (1 + 2 * size_t(sp.C))};
     if (a.max_len > 0) {
-        if (a.dtype == kBF16) {
-            hipLaunchKernelGGL(imp_row_kernel<kBF16>, grid, dim3(kThreads), 0, s, p);
-            hipLaunchKernelGGL(imp_col_kernel<kBF16>, grid, dim3(kThreads), 0, s, p);
-        } else if (a.dtype == kF16) {
-            hipLaunchKernelGGL(imp_row_kernel<kF16>, grid, dim3(kThreads), 0, s, p);
-            hipLaunchKernelGGL(imp_col_kernel<kF16>, grid, dim3(kThreads), 0, s, p);
-        } else {
-            hipLaunchKernelGGL(imp_row_kernel<kF32>, grid, dim3(kThreads), 0, s, p);
-            hipLaunchKernelGGL(imp_col_kernel<kF32>, grid, dim3(kThreads), 0, s, p);
-        }
+        const long hb = long(a.H) * a.B;
+        const dim3 rgrid(unsigned(row_items(sp) * hb)), cgrid(unsigned(col_items(sp) * hb));
+        const dim3 mgrid(unsigned((a.max_len + kThreads - 1) / kThreads), unsigned(a.H), unsigned(a.B));
+        if (a.dtype == kBF16) hipLaunchKernelGGL(imp_row_kernel<kBF16>, rgrid, dim3(kThreads), 0, s, p);
+        else if (a.dtype == kF16) hipLaunchKernelGGL(imp_row_kernel<kF16>, rgrid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(imp_row_kernel<kF32>, rgrid, dim3(kThreads), 0, s, p);
+        if (sp.C > 1) hipLaunchKernelGGL(imp_merge_kernel, mgrid, dim3(kThreads), 0, s, p);
+        if (a.dtype == kBF16) hipLaunchKernelGGL(imp_col_kernel<kBF16>, cgrid, dim3(kThreads), 0, s, p);
+        else if (a.dtype == kF16) hipLaunchKernelGGL(imp_col_kernel<kF16>, cgrid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(imp_col_kernel<kF32>, cgrid, dim3(kThreads), 0, s, p);
     }
-    hipLaunchKernelGGL(imp_reduce_kernel, dim3(unsigned((a.stride + kThreads - 1) / kThreads), unsigned(a.B)),
+    hipLaunchKernelGGL(imp_reduce_kernel, dim3(unsigned((a.stride + 63) / 64), unsigned(a.B)),
                        dim3(kThreads), 0, s, p, a.importance, a.stride, a.head_importance);
     return hipGetLastError();
 }
