@@ -35,6 +35,7 @@
 // 32j .. 32j+31 of its row, contiguous in memory (16-byte loads). The contraction order
 // over channels is free, so both operands use that same channel order: at step ks the
 // f32 MFMA pairs channel 32j + ks, the 16-bit one channels 32j + 8ks .. 8ks + 7.
+#include <float.h>
 #include <math.h>
 
 #include "attn_dev.h"
@@ -205,12 +206,18 @@ __device__ __forceinline__ WorkItem col_item(const ImpParams& p) {
     return WorkItem{tile, chunk, hb % p.H, hb / p.H};
 }
 
-// address of key s (head kh) of request b, or nullptr when its block is out of range
+// address of key s >= 0 (head kh) of request b, or nullptr when its block is out of range
 __device__ __forceinline__ const uint8_t* key_row(const ImpParams& p, int b, int s, int kh, int esize) {
-    const int phys = p.bt[size_t(b) * p.mkbpr + s / p.BS];
+    const unsigned blk = unsigned(s) / unsigned(p.BS), off = unsigned(s) - blk * unsigned(p.BS);
+    const int phys = p.bt[size_t(b) * p.mkbpr + blk];
     if (phys < 0 || phys >= p.num_kv_blocks) return nullptr;
-    return p.kc + ((size_t(phys) * p.BS + s % p.BS) * p.N + kh) * D * esize;
+    return p.kc + ((size_t(phys) * p.BS + off) * p.N + kh) * D * esize;
 }
+
+// 2^x on the hardware's exp2 (v_exp_f32), without the library's rescaling of results
+// below 2^-126: such a term changes none of the sums here (a row's sum is >= 1, and a
+// column sum's terms are the weights themselves)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A 16-row operand tile shared by the workgroup's four waves through LDS: the workgroup
 // loads it once (each thread 16-byte pieces of whole rows), every wave reads its
@@ -272,9 +279,11 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     Frag<DT> qf;
     load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
 
-    float m[4], l[4];  // online max / sum of 2^x over this lane's key column, rows 4j + i
+    // online max / sum of 2^x over this lane's key column, rows 4j + i. The max starts at
+    // -FLT_MAX, below every finite score, so a masked score (-inf) never meets an infinite max
+    float m[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
+    for (int i = 0; i < 4; ++i) { m[i] = -FLT_MAX; l[i] = 0.f; }
     const int s_end = min(min(s_lo + p.R * 64, tw + 64), L) - 1;  // last key any wave needs
     // key tile s0 (16 keys in one block): rows past L repeat the last key (masked)
     auto fetch = [&](int s0, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
@@ -283,20 +292,24 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         tile_fetch<DT>(v, [&](int i) { return kr + size_t(min(i, L - 1 - s0)) * p.N * D * es; });
         return true;
     };
-    // the softmax update of this lane's 4 rows with one 16-key tile's scores
-    auto upd = [&](const attn::f32x4& c, int s) {
+    // the softmax update of this lane's 4 rows with one 16-key tile's scores (key s of this
+    // lane), branch-free: a masked score enters as -inf and changes nothing. Tiles whose 16
+    // keys precede all of the wave's rows and L (all) skip the mask.
+    auto upd = [&](const attn::f32x4& c, int s, bool all) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 4 * j + i;
-            if (s <= t && s < L) {
-                // one exp2 per score: a new maximum rescales the sum, any other score adds
-                const float x = c[i] * p.scale2;
-                const float d = x - m[i];
-                const float e = exp2f(-fabsf(d));  // m = -inf: d = +inf, e = 0
-                l[i] = d > 0.f ? l[i] * e + 1.f : l[i] + e;
-                m[i] = fmaxf(m[i], x);
-            }
+            // one exp2 per score: a new maximum rescales the sum, any other score adds
+            const float x = (all || (s <= t && s < L)) ? c[i] * p.scale2 : -INFINITY;
+            const float d = x - m[i];
+            const float e = exp2_hw(-fabsf(d));
+            l[i] = d > 0.f ? fmaf(l[i], e, 1.f) : l[i] + e;
+            m[i] = fmaxf(m[i], x);
         }
+    };
+    auto upd_tile = [&](const attn::f32x4& c, int s0k) {
+        if (s0k + 15 <= t0 && s0k + 15 < L) upd(c, s0k + r, true);
+        else upd(c, s0k + r, false);
     };
     // a step takes two key tiles (32 keys): both go to LDS, one barrier, then the next two
     // are fetched into the freed register sets and the pair is multiplied; four LDS
@@ -315,12 +328,12 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
             frag_from_tile<DT>(k1, b1, r, j);
             attn::f32x4 r0, r1;
             dot_tile2<DT>(qf, k0, k1, r0, r1);
-            upd(r0, s0 + r);
-            upd(r1, s0 + 16 + r);
+            upd_tile(r0, s0);
+            upd_tile(r1, s0 + 16);
         } else if (c0 || c1) {
             Frag<DT> kf;
             frag_from_tile<DT>(kf, c0 ? b0 : b1, r, j);
-            upd(dot_tile<DT>(qf, kf), (c0 ? s0 : s0 + 16) + r);
+            upd_tile(dot_tile<DT>(qf, kf), c0 ? s0 : s0 + 16);
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float M = group_max<16>(m[i]);
-        const float part = (m[i] == -INFINITY) ? 0.f : l[i] * exp2f(m[i] - M);
+        const float part = l[i] * exp2f(m[i] - M);  // a lane without keys: l = 0
         const float S = group_sum<16>(part);
         const int t = t0 + 4 * j + i;
         if (r == 0 && t < L) {
@@ -377,12 +390,19 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
         });
         lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
     };
-    auto upd = [&](const attn::f32x4& c, int t, float lt) {
+    // this lane's weights 2^(x - lse_t) for its 4 keys and query row t; tiles whose 16
+    // rows follow all of the wave's keys and end before L (all) skip the mask
+    auto upd = [&](const attn::f32x4& c, int t, float lt, bool all) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = s0 + 4 * j + i;
-            if (t >= s && t < L) acc[i] += exp2f(c[i] * p.scale2 - lt);
+            const float wgt = exp2_hw(c[i] * p.scale2 - lt);
+            acc[i] += (all || (t >= s && t < L)) ? wgt : 0.f;
         }
+    };
+    auto upd_tile = [&](const attn::f32x4& c, int t0q, float lt) {
+        if (t0q >= s0 + 15 && t0q + 15 < L) upd(c, t0q + r, lt, true);
+        else upd(c, t0q + r, lt, false);
     };
     // as in the row pass: two query tiles per barrier, four LDS buffers
     auto step2 = [&](int t0, int bi, u32x4 (&va)[Tile<DT>::kPerThread], float& la, u32x4 (&vb)[Tile<DT>::kPerThread],
@@ -403,13 +423,13 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
             frag_from_tile<DT>(q1, qt[bi + 1], r, j);
             attn::f32x4 r0, r1;
             dot_tile2<DT>(kf, q0, q1, r0, r1);
-            upd(r0, t0 + r, lt_s[bi][r]);
-            upd(r1, t0 + 16 + r, lt_s[bi + 1][r]);
+            upd_tile(r0, t0, lt_s[bi][r]);
+            upd_tile(r1, t0 + 16, lt_s[bi + 1][r]);
         } else if (c0 || c1) {
             const int bx = c0 ? bi : bi + 1;
             Frag<DT> qf;
             frag_from_tile<DT>(qf, qt[bx], r, j);
-            upd(dot_tile<DT>(kf, qf), (c0 ? t0 : t0 + 16) + r, lt_s[bx][r]);
+            upd_tile(dot_tile<DT>(kf, qf), c0 ? t0 : t0 + 16, lt_s[bx][r]);
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
