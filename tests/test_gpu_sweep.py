@@ -5,7 +5,8 @@ size, ragged (and empty) request lengths, k, dtype and forcing flags, each held 
 rules as the hand-picked cases in test_gpu_parity.py: metadata bit-exact, block and probe
 scores within 1e-3 relative, selections equal up to near ties, attention (on the oracle's
 selection, or on random selection rows) within the dtype's tolerance, and the fused call's
-selection bit-identical to the separate selection call.
+selection bit-identical to the separate selection call. The prefill importance has a sweep
+of its own (24 draws of prompt lengths, padding, output stride, scale and dtype).
 """
 
 import numpy as np
@@ -13,8 +14,8 @@ import pytest
 import torch
 
 from tests.conftest import gpu_available
-from tests.test_gpu_parity import (DEV, attn_tol, bits, check_scores, compare_probe, compare_quest, nbs_of,
-                                   oracle_meta, random_selection, run_meta, run_select, say, tnp)
+from tests.test_gpu_parity import (DEV, attn_tol, bits, check_importance, check_scores, compare_probe, compare_quest,
+                                   nbs_of, oracle_meta, random_selection, run_meta, run_select, say, tnp)
 from top_kv_block_amd import workloads as W
 
 pytestmark = [pytest.mark.gpu,
@@ -128,3 +129,50 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
         pmask[b, :, :nb] = True
     check_scores(tnp(ps), o["probe"], pmask)
     compare_probe(tnp(psel), tnp(pns), o, nbs, k)
+
+
+IMP_DRAWS = 24
+
+
+def draw_importance(seed):
+    """One prefill-importance case: ragged (and empty) prompts of up to 1200 tokens, query
+    rows padded past the longest prompt, an output stride shorter or longer than max_len,
+    softmax scale default or drawn, dtype drawn; spans one to eight chunks of causal work."""
+    r = np.random.default_rng(9000 + seed)
+    BS = int(r.choice([16, 32, 64, 128]))
+    N = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 3, 4]))
+    B = int(r.integers(1, 4))
+    lens = []
+    for _ in range(B):
+        u = r.random()
+        lens.append(0 if u < 0.1 else int(r.integers(1, 65)) if u < 0.25 else int(r.integers(1, 1201)))
+    top = max(max(lens), 1)
+    max_len = top + int(r.choice([0, 0, int(r.integers(1, 200))]))
+    stride = max(1, int(r.choice([max_len, max_len + int(r.integers(1, 100)), int(r.integers(1, max_len + 1))])))
+    scale = 0.0 if r.random() < 0.5 else float(r.uniform(0.02, 0.3))
+    dtype = (torch.float32, torch.bfloat16, torch.float16)[int(r.integers(0, 3))]
+    return dict(B=B, H=N * G, N=N, BS=BS, lens=lens, max_len=max_len, stride=stride, scale=scale, dtype=dtype)
+
+
+@pytest.mark.parametrize("seed", range(IMP_DRAWS))
+def test_random_shapes_prefill_importance(qs, oracle, seed):
+    c = draw_importance(seed)
+    B, H, N, BS, lens, dtype = c["B"], c["H"], c["N"], c["BS"], c["lens"], c["dtype"]
+    say(f"importance sweep seed={seed} B={B} H={H} N={N} BS={BS} lens={lens} max_len={c['max_len']} "
+        f"stride={c['stride']} scale={c['scale']:.3f} dtype={dtype}")
+    wl = W.random_case(200 + seed, B, H, N, BS, lens, k=1, dtype=dtype, with_v=False)
+    q = W.prefill_queries(wl, 200 + seed, max_len=c["max_len"])
+    imp, himp = qs.qs_prefill_importance(q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV),
+                                         softmax_scale=c["scale"], importance_stride=c["stride"], with_heads=True)
+    torch.cuda.synchronize()
+    oimp, ohimp = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, N, softmax_scale=c["scale"],
+                                            stride=c["stride"])
+    check_importance(tnp(imp), oimp, "importance")
+    check_importance(tnp(himp), ohimp, "head importance")
+    g = tnp(imp)
+    for b, L in enumerate(lens):
+        n = min(L, c["stride"])
+        assert not g[b, n:].any(), "entries past the prompt must be zero"
+        if L <= c["stride"] and L > 0:  # the whole prompt is in the output: each query row's weights sum to 1
+            assert abs(g[b, :L].astype(np.float64).sum() - H * L) <= 1e-4 * H * L
