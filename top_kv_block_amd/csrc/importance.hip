@@ -235,14 +235,19 @@ struct Tile {
     static_assert(kPieces % kThreads == 0, "whole pieces per thread");
 };
 
-// this thread's pieces of a 16-row tile: row i of the tile starts at row_ptr(i)
-template <int DT, class RowPtr>
-__device__ __forceinline__ void tile_fetch(u32x4 (&v)[Tile<DT>::kPerThread], RowPtr row_ptr) {
+// this thread's pieces of a 16-row tile whose row i starts at base + i * stride for
+// i <= last (later rows repeat row last). The base is wave-uniform and the per-lane
+// offset 32-bit (stride <= 65535 * 512 bytes, rows <= 15), so each load is one
+// scalar-base global load with no 64-bit lane arithmetic.
+template <int DT>
+__device__ __forceinline__ void tile_fetch(u32x4 (&v)[Tile<DT>::kPerThread], const uint8_t* base, unsigned stride,
+                                           int last) {
     constexpr int ppr = Tile<DT>::kRowBytes / 16;  // pieces per row
 #pragma unroll
     for (int u = 0; u < Tile<DT>::kPerThread; ++u) {
         const int piece = threadIdx.x + u * kThreads;
-        v[u] = ld16(row_ptr(piece / ppr) + 16 * (piece % ppr));
+        const unsigned row = unsigned(min(piece / ppr, last));
+        v[u] = ld16(base + (row * stride + 16u * unsigned(piece % ppr)));
     }
 }
 template <int DT>
@@ -285,13 +290,18 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -FLT_MAX; l[i] = 0.f; }
     const int s_end = min(min(s_lo + p.R * 64, tw + 64), L) - 1;  // last key any wave needs
-    // key tile s0 (16 keys in one block): rows past L repeat the last key (masked)
-    auto fetch = [&](int s0, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
-        const uint8_t* kr = key_row(p, b, s0, kh, es);
-        if (kr == nullptr) return false;
-        tile_fetch<DT>(v, [&](int i) { return kr + size_t(min(i, L - 1 - s0)) * p.N * D * es; });
+    // key tile s0 (16 keys in one block, physical block ph): rows past L repeat the last
+    // key (masked). The block-table entries are read one step before their tile (bt_at),
+    // so no step waits for a lookup between its barrier and its loads.
+    const int32_t* btrow = p.bt + size_t(b) * p.mkbpr;
+    auto bt_at = [&](int s) { return btrow[unsigned(min(s, L - 1)) / unsigned(p.BS)]; };
+    auto fetch = [&](int s0, int ph, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
+        if (ph < 0 || ph >= p.num_kv_blocks) return false;
+        const uint8_t* base = p.kc + ((size_t(ph) * p.BS + unsigned(s0) % unsigned(p.BS)) * p.N + kh) * size_t(D * es);
+        tile_fetch<DT>(v, base, unsigned(p.N) * D * es, L - 1 - s0);
         return true;
     };
+    int pa = bt_at(s_lo), pb = bt_at(s_lo + 16);
     // the softmax update of this lane's 4 rows with one 16-key tile's scores (key s of this
     // lane), branch-free: a masked score enters as -inf and changes nothing. Tiles whose 16
     // keys precede all of the wave's rows and L (all) skip the mask.
@@ -320,8 +330,10 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         if (hb) tile_store<DT>(b1, vb);
         const bool c0 = ha && s0 <= t0 + 15 && t0 < L, c1 = hb && s0 + 16 <= t0 + 15 && t0 < L;
         __syncthreads();
-        ha = s0 + 32 <= s_end && fetch(s0 + 32, va);
-        hb = s0 + 48 <= s_end && fetch(s0 + 48, vb);
+        ha = s0 + 32 <= s_end && fetch(s0 + 32, pa, va);
+        hb = s0 + 48 <= s_end && fetch(s0 + 48, pb, vb);
+        pa = bt_at(s0 + 64);  // the entries of the next step's tiles
+        pb = bt_at(s0 + 80);
         if (c0 && c1) {
             Frag<DT> k0, k1;
             frag_from_tile<DT>(k0, b0, r, j);
@@ -337,8 +349,10 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         }
     };
     u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
-    bool ha = fetch(s_lo, na);
-    bool hb = s_lo + 16 <= s_end && fetch(s_lo + 16, nb);
+    bool ha = fetch(s_lo, pa, na);
+    bool hb = s_lo + 16 <= s_end && fetch(s_lo + 16, pb, nb);
+    pa = bt_at(s_lo + 32);
+    pb = bt_at(s_lo + 48);
     for (int s0 = s_lo, pb = 0; s0 <= s_end; s0 += 32, pb ^= 2) step2(s0, kt[pb], kt[pb + 1], na, ha, nb, hb);
     // merge the 16 key columns of each row into the chunk's (max, sum); every row t < L
     // has a key of the chunk (s_lo <= tw), so the max is finite. With one chunk that is
@@ -385,9 +399,8 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};  // keys 4j + i, partial over this lane's query column
     // query tile t0: 16 rows of head h (rows past L repeat the last row, masked) and their lse
     auto fetch = [&](int t0, u32x4 (&v)[Tile<DT>::kPerThread], float& lv) {
-        tile_fetch<DT>(v, [&](int i) {
-            return p.q + ((size_t(b) * p.max_len + min(t0 + i, L - 1)) * p.H + h) * D * es;
-        });
+        tile_fetch<DT>(v, p.q + ((size_t(b) * p.max_len + t0) * p.H + h) * size_t(D * es), unsigned(p.H) * D * es,
+                       L - 1 - t0);
         lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
     };
     // this lane's weights 2^(x - lse_t) for its 4 keys and query row t; tiles whose 16
