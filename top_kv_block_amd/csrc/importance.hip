@@ -326,8 +326,10 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     // buffers, so a pair's stores never meet the previous pair's reads
     auto step2 = [&](int s0, uint8_t* b0, uint8_t* b1, u32x4 (&va)[Tile<DT>::kPerThread], bool& ha,
                      u32x4 (&vb)[Tile<DT>::kPerThread], bool& hb) {
-        if (ha) tile_store<DT>(b0, va);
-        if (hb) tile_store<DT>(b1, vb);
+        // stored whether or not a tile was fetched (an unfetched buffer is never read): every
+        // step then waits for its loads here, so the MFMAs below never wait for global loads
+        tile_store<DT>(b0, va);
+        tile_store<DT>(b1, vb);
         const bool c0 = ha && s0 <= t0 + 15 && t0 < L, c1 = hb && s0 + 16 <= t0 + 15 && t0 < L;
         __syncthreads();
         ha = s0 + 32 <= s_end && fetch(s0 + 32, pa, va);
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
             upd_tile(dot_tile<DT>(qf, kf), c0 ? s0 : s0 + 16);
         }
     };
-    u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
+    u32x4 na[Tile<DT>::kPerThread] = {}, nb[Tile<DT>::kPerThread] = {};
     bool ha = fetch(s_lo, pa, na);
     bool hb = s_lo + 16 <= s_end && fetch(s_lo + 16, pb, nb);
     pa = bt_at(s_lo + 32);
@@ -421,10 +423,10 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     auto step2 = [&](int t0, int bi, u32x4 (&va)[Tile<DT>::kPerThread], float& la, u32x4 (&vb)[Tile<DT>::kPerThread],
                      float& lb, bool hb) {
         tile_store<DT>(qt[bi], va);
-        if (threadIdx.x < 16) lt_s[bi][threadIdx.x] = la;
-        if (hb) {
-            tile_store<DT>(qt[bi + 1], vb);
-            if (threadIdx.x < 16) lt_s[bi + 1][threadIdx.x] = lb;
+        tile_store<DT>(qt[bi + 1], vb);
+        if (threadIdx.x < 16) {
+            lt_s[bi][threadIdx.x] = la;
+            lt_s[bi + 1][threadIdx.x] = lb;
         }
         __syncthreads();
         if (t0 + 32 < t_hi) fetch(t0 + 32, va, la);
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
             upd_tile(dot_tile<DT>(kf, qf), c0 ? t0 : t0 + 16, lt_s[bx][r]);
         }
     };
-    u32x4 na[Tile<DT>::kPerThread], nb[Tile<DT>::kPerThread];
+    u32x4 na[Tile<DT>::kPerThread] = {}, nb[Tile<DT>::kPerThread] = {};
     float la = 0.f, lb = 0.f;
     fetch(t_lo, na, la);
     if (t_lo + 16 < t_hi) fetch(t_lo + 16, nb, lb);
