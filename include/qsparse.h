@@ -13,7 +13,9 @@
  *                            sink / local-window forcing;   (or)
  *     qs_probe_select        probe + prefill-importance + recency block selection;
  *     qs_sparse_attn_decode  exact softmax attention over the selected blocks only;
- *     qs_select_attn_decode  qs_block_select then qs_sparse_attn_decode in one call.
+ *     qs_select_attn_decode  qs_block_select then qs_sparse_attn_decode in one call;
+ *     qs_probe_attn_decode   qs_probe_select then qs_sparse_attn_decode (one selection row
+ *                            per query head) in one call.
  *
  * Sources, cited by page title and section:
  *   [P1] "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择"
@@ -281,6 +283,44 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                                 uint32_t flags, int32_t k, float softmax_scale, void* out,
                                 int32_t* selected, int32_t* n_selected,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* bytes of workspace qs_probe_attn_decode needs for these sizes (the probe keys, then the
+ * attention partials; 0 for invalid sizes) */
+size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t max_kv_blocks_per_req, int32_t k);
+
+/*
+ * qs_probe_attn_decode -- page 1's probe selection and exact attention over it, in one
+ * call. [P1] section 2 (sparse_attn_head): the selection of each query head feeds that
+ * head's attention loop directly. The result is defined as qs_probe_select (same
+ * arguments) followed by qs_sparse_attn_decode with sel_heads = H and the same k: the
+ * selection is bitwise the one qs_probe_select returns, the output matches the two calls
+ * within the attention's rounding (the pick is recomputed by each slot split of a row;
+ * it is deterministic, so every split sees the same selection).
+ *
+ *   query          [B, H, D], q_dtype QS_F32, QS_BF16 or QS_F16; out [B, H, D] in q_dtype
+ *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_F16 (the
+ *                  probe scores read K; an int8 cache takes the two calls)
+ *   block_tables   [B, max_kv_blocks_per_req] int32 (max_kv_blocks_per_req <= 4096);
+ *                  seq_lens [B] int32
+ *   importance, importance_stride, n_probe, flags   as for qs_probe_select
+ *   k              1 .. 4096 blocks per query head
+ *   softmax_scale  logit = softmax_scale * q . k; <= 0 selects 1/sqrt(D)
+ *   selected       [B, H, k] int32 output (ascending, -1 padded) and n_selected [B, H],
+ *                  or both NULL
+ *   workspace      device scratch of at least qs_probe_attn_workspace_bytes(), 256-byte
+ *                  aligned, contents ignored
+ * Attention runs on the vector ALU in fp32 for every dtype pair. An empty selection
+ * writes zeros.
+ */
+qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                               qs_dtype q_dtype, qs_dtype kv_dtype,
+                               const void* query, const void* k_cache, const void* v_cache,
+                               int32_t num_kv_blocks, const int32_t* block_tables,
+                               int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
+                               const float* importance, int32_t importance_stride,
+                               int32_t n_probe, int32_t k, uint32_t flags, float softmax_scale,
+                               void* out, int32_t* selected, int32_t* n_selected,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* bytes of workspace qs_prefill_importance needs (0 for invalid sizes): B * H * max_len
  * floats of row normalisers plus, per chunk of the causal work, three more (a job of fewer

@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_prefill_importance"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_probe_attn_decode", "qs_prefill_importance"):
         assert n in names
 
 
@@ -205,6 +205,39 @@ def test_select_attn_workspace_size(qs):
     assert qs.select_attn_workspace_bytes(1, 30, 8, 128, 1, 8, qs.QS_BF16) == 0
     assert qs.select_attn_workspace_bytes(1, 32, 8, 128, 1, 8, qs.QS_I8) == 0
     assert _fused(qs, sel=FAKE, nsel=FAKE) == 0
+
+
+def _pattn(qs, **kw):
+    a = dict(B=0, H=16, N=8, D=128, BS=32, qd=qs.QS_F32, kd=qs.QS_F32, q=FAKE, kc=FAKE, vc=FAKE, nkv=128, bt=FAKE,
+             mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32, flags=qs.QS_RECENCY, scale=0.0, out=FAKE, sel=None,
+             nsel=None, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    return qs.lib.qs_probe_attn_decode(a["B"], a["H"], a["N"], a["D"], a["BS"], a["qd"], a["kd"], a["q"], a["kc"],
+                                       a["vc"], a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["imp"], a["stride"],
+                                       a["npb"], a["k"], a["flags"], a["scale"], a["out"], a["sel"], a["nsel"],
+                                       a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kd=2), 2), (dict(qd=2), 2), (dict(k=0), 1), (dict(k=4097), 1), (dict(flags=1), 1), (dict(mkbpr=5000), 2),
+    (dict(imp=FAKE, stride=0), 1), (dict(vc=None), 1), (dict(out=None), 1), (dict(sel=FAKE), 1),
+    (dict(nsel=FAKE), 1), (dict(H=12), 1), (dict(BS=8), 2), (dict(D=96), 2), (dict(ws=None), 1),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 64)), 1), (dict(wsb=16), 1), (dict(scale=float("nan")), 1),
+    (dict(kc=ctypes.c_void_p((1 << 20) + 4)), 1),
+])
+def test_probe_attn_rejects(qs, kw, status):
+    assert _pattn(qs, **kw) == status
+    assert qs.lib.qs_last_error().decode().startswith("qs_probe_attn_decode")
+
+
+def test_probe_attn_workspace_size(qs):
+    # the probe keys (B * H * mkbpr uint32), then the attention partials: 16 rows of one
+    # query head want 2048 / 16 = 128 slot splits, capped at k = 32, each a (D + 2)-float record
+    assert qs.probe_attn_workspace_bytes(1, 16, 8, 128, 32) == 16 * 128 * 4 + 16 * 32 * 130 * 4
+    # 2048 rows: one split each, no partials
+    assert qs.probe_attn_workspace_bytes(64, 32, 8, 100, 8) == 64 * 32 * 100 * 4
+    assert qs.probe_attn_workspace_bytes(1, 12, 8, 128, 32) == 0
+    assert _pattn(qs, wsb=qs.probe_attn_workspace_bytes(0, 16, 8, 128, 32)) == 0
 
 
 def _imp(qs, **kw):

@@ -937,7 +937,8 @@ def test_graph_replay_matches_eager(qs):
 
 def test_graph_replay_probe_path(qs):
     """Page 1's path captured in a HIP graph: a metadata refresh, the prefill importance, the
-    probe selection and fp32 attention with one selection row per query head. No workspace is
+    probe selection and fp32 attention with one selection row per query head, and the fused
+    probe selection + attention call beside them. No workspace is
     passed, so every call takes the binding's cached workspace of the capture stream. Three
     replays, with the same eager calls (on another stream's workspaces) between them, give
     bitwise the eager results."""
@@ -953,6 +954,7 @@ def test_graph_replay_probe_path(qs):
     psel = torch.empty((B, H, wl.k), dtype=torch.int32, device=DEV)
     pns = torch.empty((B, H), dtype=torch.int32, device=DEV)
     out = torch.empty((B, H, wl.D), dtype=torch.float32, device=DEV)
+    fsel, fns, fout = torch.empty_like(psel), torch.empty_like(pns), torch.empty_like(out)
 
     def step():
         qs.qs_update_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, last, 1, wl.meta_tables, mx, mn)
@@ -961,10 +963,14 @@ def test_graph_replay_probe_path(qs):
                            flags=qs.QS_RECENCY, selected=psel, n_selected=pns)
         qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, psel, pns,
                                  sel_heads=H, out=out)
+        qs.qs_probe_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, wl.k, importance=imp,
+                                n_probe=8, flags=qs.QS_RECENCY, out=fout, selected=fsel, n_selected=fns)
 
     step()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (mx, mn, imp, psel, pns, out)]
+    assert torch.equal(fsel, psel) and torch.equal(fns, pns)
+    assert float((fout - out).abs().max()) <= 1e-5
+    want = [t.clone() for t in (mx, mn, imp, psel, pns, out, fsel, fns, fout)]
     g = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     cs.wait_stream(torch.cuda.current_stream())
@@ -973,14 +979,17 @@ def test_graph_replay_probe_path(qs):
             step()
     torch.cuda.current_stream().wait_stream(cs)
     for rep in range(3):
-        for t in (mx, mn, imp, out):
+        for t in (mx, mn, imp, out, fout):
             t.fill_(5.0)
         psel.fill_(-7)
+        fsel.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (mx, mn, imp, psel, pns, out)
-        for name, a, b in zip(("maxblocks", "minblocks", "importance", "selected", "n_selected", "out"), got, want):
+        got = (mx, mn, imp, psel, pns, out, fsel, fns, fout)
+        names = ("maxblocks", "minblocks", "importance", "selected", "n_selected", "out", "fused selected",
+                 "fused n_selected", "fused out")
+        for name, a, b in zip(names, got, want):
             if name in ("maxblocks", "minblocks"):  # only the refreshed rows are defined after the fill
                 rows = [(int(wl.meta_tables[bb, int(last[bb]) // BS]), int(last[bb]) % BS) for bb in range(B)]
                 for m, r in rows:
@@ -1028,6 +1037,71 @@ def test_page3_wrappers(qs, oracle, dtype):
         compare_quest(tnp(ids2), ons, osel, ons, osc, nbs_of(wl), k)
         if tsmu == 0:
             assert all(0 in set(r.tolist()) for r in tnp(ids2).reshape(-1, k))      # sink forced
+
+
+# ------------------------------------------------------------------------------------------
+# fused probe selection + attention (qs_probe_attn_decode)
+# ------------------------------------------------------------------------------------------
+
+PROBE_ATTN_CASES = [
+    # seed, B, H, N, BS, lens, k, dtype, importance, flags, n_probe
+    (401, 2, 16, 8, 32, [32 * 128, 32 * 3 + 1], 32, torch.float32, True, W.RECENCY, 8),  # page-1 shape, ragged
+    (402, 3, 8, 2, 16, [500, 0, 33], 5, torch.float32, False, W.RECENCY, 3),             # empty request, no importance
+    (403, 2, 6, 3, 64, [1000, 64], 40, torch.bfloat16, True, 0, 8),                      # k > nb
+    (404, 4, 4, 4, 128, [3000, 128 * 20 + 1, 7, 2000], 12, torch.float16, True, W.RECENCY, 64),
+    (405, 64, 32, 8, 16, [16 * 40 + 3] * 64, 4, torch.float32, True, W.RECENCY, 8),     # 2048 rows: no slot splits
+    (406, 1, 2, 1, 16, [16 * 4096], 100, torch.float32, True, W.RECENCY, 8),            # a 4096-block row
+]
+
+
+@pytest.mark.parametrize("case", PROBE_ATTN_CASES, ids=lambda c: f"seed{c[0]}")
+def test_probe_attn_matches_probe_select_and_oracle(qs, oracle, case):
+    """The fused call's selection is bitwise qs_probe_select's; its output matches the
+    oracle's attention over that selection (one row per query head)."""
+    seed, B, H, N, BS, lens, k, dtype, use_imp, flags, n_probe = case
+    say(f"probe+attn seed={seed} B={B} H={H} N={N} BS={BS} k={k} dtype={dtype} imp={use_imp} flags={flags}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=dtype, with_importance=use_imp)
+    imp = wl.importance.to(DEV) if use_imp else None
+    q, kc, vc, bt, sl = (t.to(DEV) for t in (wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens))
+    sel, ns = qs.qs_probe_select(q, kc, bt, sl, k, importance=imp, n_probe=n_probe, flags=flags)
+    fsel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+    fns = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    out = qs.qs_probe_attn_decode(q, kc, vc, bt, sl, k, importance=imp, n_probe=n_probe, flags=flags,
+                                  selected=fsel, n_selected=fns)
+    torch.cuda.synchronize()
+    assert torch.equal(fsel, sel) and torch.equal(fns, ns), "fused selection differs from qs_probe_select"
+    o = oracle.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, k, N,
+                            importance=wl.importance if use_imp else None, n_probe=n_probe, flags=flags)
+    compare_probe(tnp(fsel), tnp(fns), o, nbs_of(wl), k)
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(fsel),
+                                    tnp(fns), H)
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    assert err <= attn_tol(dtype), f"fused probe attention err {err:.3e}"
+    # without the selection outputs: the same attention, bitwise
+    out2 = qs.qs_probe_attn_decode(q, kc, vc, bt, sl, k, importance=imp, n_probe=n_probe, flags=flags)
+    assert torch.equal(out2.view(torch.int16 if dtype != torch.float32 else torch.int32),
+                       out.view(torch.int16 if dtype != torch.float32 else torch.int32))
+
+
+def test_probe_attn_page1_k_sweep(qs, oracle):
+    """Page 1's probe workload (fp32, 16 heads, 128 blocks of 32, importance, recency) for
+    k = 1 .. 32: fused selection bitwise the two calls', output within 1e-4 of the oracle."""
+    wl = W.page1_probe()
+    q, kc, vc, bt, sl, imp = (t.to(DEV) for t in (wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                                   wl.importance))
+    for k in (1, 2, 4, 8, 16, 32):
+        say(f"probe+attn, page-1 workload, k={k}")
+        sel, ns = qs.qs_probe_select(q, kc, bt, sl, k, importance=imp, n_probe=8, flags=W.RECENCY)
+        fsel = torch.empty_like(sel)
+        fns = torch.empty_like(ns)
+        out = qs.qs_probe_attn_decode(q, kc, vc, bt, sl, k, importance=imp, n_probe=8, flags=W.RECENCY,
+                                      selected=fsel, n_selected=fns)
+        torch.cuda.synchronize()
+        assert torch.equal(fsel, sel) and torch.equal(fns, ns)
+        ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(sel),
+                                        tnp(ns), wl.H)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= 1e-4, f"k={k}: err {err:.3e}"
 
 
 # ------------------------------------------------------------------------------------------

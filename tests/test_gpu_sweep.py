@@ -4,8 +4,8 @@ Every entry point of the path on 64 seeded draws of batch size, heads, group siz
 size, ragged (and empty) request lengths, k, dtype and forcing flags, each held to the same
 rules as the hand-picked cases in test_gpu_parity.py: metadata bit-exact, block and probe
 scores within 1e-3 relative, selections equal up to near ties, attention (on the oracle's
-selection, or on random selection rows) within the dtype's tolerance, and the fused call's
-selection bit-identical to the separate selection call. The prefill importance has a sweep
+selection, or on random selection rows) within the dtype's tolerance, and the fused calls'
+selections (Quest and probe) bit-identical to the separate selection calls. The prefill importance has a sweep
 of its own (24 draws of prompt lengths, padding, output stride, scale and dtype).
 """
 
@@ -129,6 +129,19 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
         pmask[b, :, :nb] = True
     check_scores(tnp(ps), o["probe"], pmask)
     compare_probe(tnp(psel), tnp(pns), o, nbs, k)
+
+    # fused probe selection + attention: the probe call's selection, bit for bit, and the
+    # oracle's attention over it (one row per query head)
+    fps = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+    fpn = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    fo = qs.qs_probe_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV), wl.block_tables.to(DEV),
+                                 wl.seq_lens.to(DEV), k, importance=wl.importance.to(DEV), n_probe=c["n_probe"],
+                                 flags=pflags, selected=fps, n_selected=fpn)
+    assert torch.equal(fps, psel) and torch.equal(fpn, pns), "fused probe selection differs from qs_probe_select"
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(psel),
+                                    tnp(pns), H)
+    err = float(np.abs(fo.float().cpu().numpy() - ref).max()) if ref.size else 0.0
+    assert err <= tol, f"fused probe attention err {err:.3e} > {tol}"
 
 
 IMP_DRAWS = 24

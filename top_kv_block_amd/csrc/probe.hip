@@ -1,74 +1,36 @@
 // probe.hip -- page 1's block selection: probe scores, prefill-importance budget,
-// probe fill and recency insurance, per query head.
+// probe fill and recency insurance, per query head; and the same selection fused with
+// exact attention over it.
 //
 // Source: "0.8MB 跑通 Qwen | 第 10-2 篇: 推理引擎的 sparse top-k 块选择" (page 1),
 // section 1 "知识点" (three signals + recency, lower-index ties, determinism) and
 // section 2 "对应代码" (probe loop, importance preselect with budget (k+1)/2, greedy fill,
-// recency replacing the lowest probe pick only).
+// recency replacing the lowest probe pick only; the selection feeds the attention loop
+// directly).
 //
-// Design (CDNA4): one workgroup per (request, query head). The probe samples are
-// independent dot products of the query with sampled key rows; a group of LPR lanes
-// (16-byte loads, the whole 128-channel row) computes one, reduces it with shuffles and
-// folds it into the block's probe score with an LDS atomic max on the score's
-// order-preserving integer image (max is order-independent, so the result is exact and
-// deterministic). Importance sums are accumulated per block by one thread in token order
-// in fp32, exactly as the page's loop does, so the importance stage is bit-exact. Each
-// greedy stage ("repeatedly take the best unused block, lower index on ties") selects
-// the same set as taking the top-r keys under (value desc, index asc); that is computed
-// with the block-wide threshold select plus one ordered pass.
+// Design (CDNA4). The probe samples are independent dot products of the query with
+// sampled key rows: a scoring grid (chunk of blocks, KV head, request) loads each sampled
+// row once for all query heads of its group; a group of LPR lanes (16-byte loads, the
+// whole 128-channel row) computes one dot, reduces it with shuffles and folds it into the
+// block's probe score with an LDS atomic max on the score's order-preserving integer
+// image (max is order-independent, so the result is exact and deterministic). The pick
+// (probe_dev.h) then runs on one workgroup per (request, query head). The fused call
+// runs the pick in every attention workgroup of the row (slot split, query head,
+// request) and attends over the selection straight from LDS with the vector-ALU
+// attention body: the pick's round trip through HBM and the attention launch's wait for
+// it disappear; the splits recompute the same deterministic pick from L2-resident probe
+// keys and the attention combine pass merges them.
 #include <math.h>
 
 #include <type_traits>
 
+#include "attn_dev.h"
+#include "probe_dev.h"
 #include "qs_device.h"
 #include "qs_internal.h"
 
 namespace qs {
 namespace {
-
-constexpr uint8_t kImp = 1, kProbe = 2;
-
-// Marks the r best candidates (value desc, index asc), r >= 1: a threshold select finds
-// the r-th best key T, then each thread takes a contiguous run of blocks and one block-wide
-// scan ranks the candidates equal to T by index. Every thread must call it.
-template <class Pred, class KeyOf>
-__device__ void mark_top(int nb, int r, Pred cand, KeyOf key_of, uint8_t* flag, uint8_t mark, uint32_t* hist,
-                         int* sh, int* wsum) {
-    const int E = (nb + kThreads - 1) / kThreads;
-    const int i0 = min(nb, int(threadIdx.x) * E), i1 = min(nb, i0 + E);
-    int nc_local = 0;
-    for (int i = i0; i < i1; ++i) nc_local += cand(i) ? 1 : 0;
-    int ncand;
-    block_excl_scan(nc_local, wsum, ncand);
-    if (r >= ncand) {
-        for (int i = i0; i < i1; ++i)
-            if (cand(i)) flag[i] = mark;
-        __syncthreads();
-        return;
-    }
-    int need_eq = 0;
-    auto kf = [&](int i, uint32_t& key) -> bool {
-        if (!cand(i)) return false;
-        key = key_of(i);
-        return true;
-    };
-    const uint32_t T = block_topk_threshold(nb, r, kf, hist, sh, need_eq);
-    int eq_local = 0;
-    for (int i = i0; i < i1; ++i) eq_local += (cand(i) && key_of(i) == T) ? 1 : 0;
-    int eq_tot;
-    int eq_seen = block_excl_scan(eq_local, wsum, eq_tot);
-    for (int i = i0; i < i1; ++i) {
-        if (!cand(i)) continue;
-        const uint32_t key = key_of(i);
-        bool pick = key > T;
-        if (key == T) {
-            pick = eq_seen < need_eq;
-            ++eq_seen;
-        }
-        if (pick) flag[i] = mark;
-    }
-    __syncthreads();
-}
 
 constexpr int kProbeChunk = 8;   // blocks per probe-scoring workgroup
 constexpr int kProbeHeads = 8;   // query heads scored per pass over the sampled rows
@@ -188,104 +150,57 @@ __global__ __launch_bounds__(kThreads) void probe_score_kernel(
     }
 }
 
-// Step 2: per (request, query head): importance sums, the two greedy stages, recency,
-// ascending output.
+// Step 2: per (request, query head): the pick (importance budget, probe fill, recency),
+// written out ascending and -1 padded.
 __global__ __launch_bounds__(kThreads) void probe_pick_kernel(
     const uint32_t* __restrict__ keys, int mkbpr, const int32_t* __restrict__ sl, const float* __restrict__ importance,
     int imp_stride, int k, uint32_t flags, int H, int BS, int32_t* __restrict__ selected,
     int32_t* __restrict__ n_selected, float* __restrict__ probe_scores) {
-    __shared__ uint32_t pkey[kProbeMaxBlocks];
-    __shared__ uint32_t ikey[kProbeMaxBlocks];
-    __shared__ uint8_t flag[kProbeMaxBlocks];
-    __shared__ uint32_t hist[512];
-    __shared__ int sh[4];
-    __shared__ int wsum[kWaves];
-    __shared__ uint32_t red_hi[kWaves], red_lo[kWaves];
-
+    __shared__ probe::PickLds s;
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
     const int L = max(sl[b], 0);
     const int nb = min((L + BS - 1) / BS, mkbpr);
-    const uint32_t* krow = keys + (size_t(b) * H + h) * mkbpr;
-    for (int i = tid; i < nb; i += kThreads) {
-        pkey[i] = krow[i];
-        flag[i] = 0;
-    }
-    // importance sums: fp32, token order, one thread per block (page 1's running sum)
-    if (importance) {
-        const float* ip = importance + size_t(b) * imp_stride;
-        for (int i = tid; i < nb; i += kThreads) {
-            const int p0 = i * BS, pe = min(min(p0 + BS, L), imp_stride);  // tokens past the row count 0
-            float s = 0.f;
-            int ps = p0;
-            for (; ps + 8 <= pe; ps += 8) {
-                float v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = ip[ps + u];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) s += v[u];
-            }
-            for (; ps < pe; ++ps) s += ip[ps];
-            ikey[i] = f2key(s);
-        }
-    }
-    __syncthreads();
-
-    // importance preselect
-    const int budget = importance ? min((k + 1) / 2, nb) : 0;
-    if (budget > 0)
-        mark_top(nb, budget, [&](int i) { return true; }, [&](int i) { return ikey[i]; }, flag, kImp, hist, sh,
-                 wsum);
-    // probe fill
-    const int r = min(k, nb) - budget;
-    if (r > 0)
-        mark_top(nb, r, [&](int i) { return flag[i] == 0; }, [&](int i) { return pkey[i]; }, flag, kProbe, hist,
-                 sh, wsum);
-    // recency insurance: the last block replaces the lowest probe pick
-    if ((flags & 4u) && nb > 0 && r > 0 && flag[nb - 1] == 0) {
-        uint64_t best = ~0ull;  // min over probe picks of (probe key, then higher index is lower)
-        for (int i = tid; i < nb; i += kThreads) {
-            if (flag[i] == kProbe) {
-                const uint64_t cc = (uint64_t(pkey[i]) << 32) | uint64_t(0xffffffffu - uint32_t(i));
-                best = cc < best ? cc : best;
-            }
-        }
-        uint32_t hi = uint32_t(best >> 32), lo = uint32_t(best);
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const uint32_t h2 = __shfl_xor(hi, o, kWave), l2 = __shfl_xor(lo, o, kWave);
-            if (h2 < hi || (h2 == hi && l2 < lo)) { hi = h2; lo = l2; }
-        }
-        if (lane_id() == 0) { red_hi[wave_id()] = hi; red_lo[wave_id()] = lo; }
-        __syncthreads();
-        if (tid == 0) {
-            for (int w = 1; w < kWaves; ++w)
-                if (red_hi[w] < hi || (red_hi[w] == hi && red_lo[w] < lo)) { hi = red_hi[w]; lo = red_lo[w]; }
-            const int victim = int(0xffffffffu - lo);
-            flag[victim] = 0;
-            flag[nb - 1] = kProbe;
-        }
-        __syncthreads();
-    }
-
-    // ascending output: contiguous runs per thread, one block-wide scan for positions
+    const int ns = probe::pick_row(keys + (size_t(b) * H + h) * mkbpr, nb, L,
+                                   importance ? importance + size_t(b) * imp_stride : nullptr, imp_stride, BS, k,
+                                   flags, s);
     int32_t* out = selected + (size_t(b) * H + h) * k;
-    const int E = (nb + kThreads - 1) / kThreads;
-    const int j0 = min(nb, tid * E), j1 = min(nb, j0 + E);
-    int pick_local = 0;
-    for (int i = j0; i < j1; ++i) pick_local += flag[i] != 0 ? 1 : 0;
-    int npick;
-    int pos = block_excl_scan(pick_local, wsum, npick);
-    for (int i = j0; i < j1; ++i) {
-        if (flag[i] != 0) {
-            if (pos < k) out[pos] = i;
-            ++pos;
-        }
-    }
-    for (int j = npick + tid; j < k; j += kThreads) out[j] = -1;
-    if (tid == 0) n_selected[size_t(b) * H + h] = min(npick, k);
+    for (int j = tid; j < k; j += kThreads) out[j] = j < ns ? s.sel[j] : -1;
+    if (tid == 0) n_selected[size_t(b) * H + h] = ns;
     if (probe_scores)
-        for (int i = tid; i < nb; i += kThreads) probe_scores[(size_t(b) * H + h) * mkbpr + i] = key2f(pkey[i]);
+        for (int i = tid; i < nb; i += kThreads) probe_scores[(size_t(b) * H + h) * mkbpr + i] = key2f(s.pkey[i]);
+}
+
+// Fused: grid (slot split, query head, request). Each workgroup picks its row into LDS,
+// split 0 publishes the selection when the caller asked for it, then the vector-ALU
+// attention body attends over the split's slots of the selection; its merge buffer
+// overlays the probe keys, dead after the pick.
+struct PickParams {
+    const uint32_t* keys;
+    int mkbpr;
+    const float* importance;
+    int imp_stride;
+    uint32_t flags;
+    int32_t* selected;
+    int32_t* n_selected;
+};
+static_assert(attn::vec_red_floats<1>() <= kProbeMaxBlocks, "the merge buffer fits the probe keys' LDS");
+
+template <int KV, int QDT>
+__global__ __launch_bounds__(kThreads) void probe_attn_vec_kernel(PickParams pp, attn::AttnParams ap) {
+    __shared__ probe::PickLds s;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int L = max(ap.sl[b], 0);
+    const int nb = min((L + ap.BS - 1) / ap.BS, pp.mkbpr);
+    const int ns = probe::pick_row(pp.keys + (size_t(b) * ap.H + h) * pp.mkbpr, nb, L,
+                                   pp.importance ? pp.importance + size_t(b) * pp.imp_stride : nullptr,
+                                   pp.imp_stride, ap.BS, ap.k, pp.flags, s);
+    if (split == 0 && pp.selected) {
+        int32_t* out = pp.selected + (size_t(b) * ap.H + h) * ap.k;
+        for (int j = threadIdx.x; j < ap.k; j += kThreads) out[j] = j < ns ? s.sel[j] : -1;
+        if (threadIdx.x == 0) pp.n_selected[size_t(b) * ap.H + h] = ns;
+    }
+    attn::vec_body<KV, QDT, 1>(ap, split, 0, h, b, s.sel, ns, reinterpret_cast<float*>(s.pkey));
 }
 
 template <int QB, int KB>
@@ -304,8 +219,8 @@ size_t probe_workspace_bytes(int B, int H, int mkbpr) {
     return bytes < 256 ? 256 : bytes;
 }
 
-hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s) {
-    uint32_t* keys = (uint32_t*)a.workspace;
+namespace {
+void launch_scores(const ProbeArgs& a, uint32_t* keys, hipStream_t s) {
     auto by_k = [&](auto q) {
         constexpr int QD = decltype(q)::value;
         if (a.kv_dtype == kBF16) launch_score<QD, kBF16>(a, keys, s);
@@ -315,9 +230,48 @@ hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s) {
     if (a.q_dtype == kBF16) by_k(std::integral_constant<int, kBF16>{});
     else if (a.q_dtype == kF16) by_k(std::integral_constant<int, kF16>{});
     else by_k(std::integral_constant<int, kF32>{});
+}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+hipError_t launch_probe_select(const ProbeArgs& a, hipStream_t s) {
+    uint32_t* keys = (uint32_t*)a.workspace;
+    launch_scores(a, keys, s);
     hipLaunchKernelGGL(probe_pick_kernel, dim3(unsigned(a.H), unsigned(a.B)), dim3(kThreads), 0, s, keys, a.mkbpr,
                        a.seq_lens, a.importance, a.imp_stride, a.k, a.flags, a.H, a.BS, a.selected, a.n_selected,
                        a.probe_scores);
+    return hipGetLastError();
+}
+
+// fused probe selection + attention: the probe keys, then the attention partials
+AttnPlan plan_probe_attn(int B, int H, int N, int mkbpr, int k) {
+    AttnPlan p = plan_sparse_attn(B, H, N, 128, H, k, kF32, kF32);  // one row per query head, vector ALU
+    p.part_off = align256(size_t(B) * H * mkbpr * sizeof(uint32_t));
+    p.bytes = p.part_off + (p.splits > 1 ? align256(size_t(B) * H * p.splits * p.hc * attn::PSTRIDE * 4) : 0);
+    if (p.bytes < 256) p.bytes = 256;
+    return p;
+}
+
+hipError_t launch_probe_attn(const ProbeArgs& a, const AttnArgs& t, const AttnPlan& pl, hipStream_t s) {
+    uint8_t* ws = (uint8_t*)a.workspace;
+    uint32_t* keys = (uint32_t*)ws;
+    launch_scores(a, keys, s);
+    PickParams pp{keys, a.mkbpr, a.importance, a.imp_stride, a.flags, a.selected, a.n_selected};
+    attn::AttnParams prm{(const uint8_t*)t.query, (const uint8_t*)t.k_cache, (const uint8_t*)t.v_cache, nullptr,
+                         nullptr, t.num_kv_blocks, t.block_tables, t.mkbpr, t.seq_lens, nullptr, nullptr, t.H, t.N,
+                         t.BS, t.H, t.k, 1, 1, pl.splits, pl.spb, t.scale * attn::kLog2e, (uint8_t*)t.out,
+                         (float*)(ws + pl.part_off)};
+    const dim3 grid(unsigned(pl.splits), unsigned(t.H), unsigned(t.B));
+    auto by_q = [&](auto kv) {
+        constexpr int KV = decltype(kv)::value;
+        if (t.q_dtype == kBF16) hipLaunchKernelGGL((probe_attn_vec_kernel<KV, kBF16>), grid, dim3(kThreads), 0, s, pp, prm);
+        else if (t.q_dtype == kF16) hipLaunchKernelGGL((probe_attn_vec_kernel<KV, kF16>), grid, dim3(kThreads), 0, s, pp, prm);
+        else hipLaunchKernelGGL((probe_attn_vec_kernel<KV, kF32>), grid, dim3(kThreads), 0, s, pp, prm);
+    };
+    if (t.kv_dtype == kBF16) by_q(std::integral_constant<int, kBF16>{});
+    else if (t.kv_dtype == kF16) by_q(std::integral_constant<int, kF16>{});
+    else by_q(std::integral_constant<int, kF32>{});
+    if (pl.splits > 1) return attn::launch_combine(prm, t.B, 1, t.q_dtype, s);
     return hipGetLastError();
 }
 

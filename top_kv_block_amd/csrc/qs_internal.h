@@ -117,6 +117,12 @@ struct AttnArgs {
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 
+// ---- fused probe selection + attention ----------------------------------------------
+// One row per query head on the vector ALU; the workspace holds the probe keys, then the
+// attention partials at part_off (bytes in total).
+AttnPlan plan_probe_attn(int B, int H, int N, int mkbpr, int k);
+hipError_t launch_probe_attn(const ProbeArgs& a, const AttnArgs& t, const AttnPlan& p, hipStream_t s);
+
 // ---- prefill importance -------------------------------------------------------------
 struct ImportanceArgs {
     int B, H, N, D, BS;

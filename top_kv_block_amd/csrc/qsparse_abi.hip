@@ -295,6 +295,58 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     return hip_status(qs::launch_select_attn(sa, aa, plan, (hipStream_t)stream), fn);
 }
 
+size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t max_kv_blocks_per_req, int32_t k) {
+    if (B < 0 || N < 1 || H < N || H % N != 0 || max_kv_blocks_per_req < 1 || k < 1) return 0;
+    return qs::plan_probe_attn(B, H, N, max_kv_blocks_per_req, k).bytes;
+}
+
+qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
+                               qs_dtype kv_dtype, const void* query, const void* k_cache, const void* v_cache,
+                               int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                               const int32_t* seq_lens, const float* importance, int32_t importance_stride,
+                               int32_t n_probe, int32_t k, uint32_t flags, float softmax_scale, void* out,
+                               int32_t* selected, int32_t* n_selected, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    const char* fn = "qs_probe_attn_decode";
+    qs_status st = check_dims(fn, B, H, N, D, block_size);
+    if (st != QS_OK) return st;
+    if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
+    if ((q_dtype != QS_F32 && q_dtype != QS_BF16 && q_dtype != QS_F16) ||
+        (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16))
+        return fail(QS_ERR_UNSUPPORTED, "%s: query and KV must be QS_F32, QS_BF16 or QS_F16", fn);
+    if (!query || !k_cache || !v_cache || !block_tables || !seq_lens || !out || !workspace)
+        return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if ((selected == nullptr) != (n_selected == nullptr))
+        return fail(QS_ERR_INVALID, "%s: selected and n_selected must be given together", fn);
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(QS_ERR_INVALID, "%s: k_cache and v_cache must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (flags & ~(uint32_t)QS_RECENCY) return fail(QS_ERR_INVALID, "%s: flags may only hold QS_RECENCY", fn);
+    if (k < 1 || k > qs::kProbeMaxBlocks)
+        return fail(QS_ERR_INVALID, "%s: k=%d must be in [1, %d]", fn, k, qs::kProbeMaxBlocks);
+    if (num_kv_blocks < 1 || max_kv_blocks_per_req < 1)
+        return fail(QS_ERR_INVALID, "%s: num_kv_blocks and max_kv_blocks_per_req must be >= 1", fn);
+    if (max_kv_blocks_per_req > qs::kProbeMaxBlocks)
+        return fail(QS_ERR_UNSUPPORTED, "%s: max_kv_blocks_per_req=%d exceeds %d", fn, max_kv_blocks_per_req,
+                    qs::kProbeMaxBlocks);
+    if (importance && importance_stride < 1)
+        return fail(QS_ERR_INVALID, "%s: importance_stride must be >= 1 when importance is given", fn);
+    if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
+    const qs::AttnPlan plan = qs::plan_probe_attn(B, H, N, max_kv_blocks_per_req, k);
+    if (workspace_bytes < plan.bytes)
+        return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
+    if (B == 0) return ok();
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
+    qs::ProbeArgs pa{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, num_kv_blocks,
+                     block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
+                     selected, n_selected, nullptr, workspace};
+    qs::AttnArgs ta{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, v_cache, nullptr, nullptr,
+                    num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, nullptr, nullptr, H, k, scale, out,
+                    workspace};
+    return hip_status(qs::launch_probe_attn(pa, ta, plan, (hipStream_t)stream), fn);
+}
+
 size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_len) {
     if (B < 0 || H < 1 || max_len < 0) return 0;
     return qs::prefill_importance_workspace_bytes(B, H, max_len);

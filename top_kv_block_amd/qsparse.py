@@ -24,8 +24,8 @@ EXPORTS = (
     "qs_build_metadata", "qs_update_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
     "qs_probe_select_workspace_bytes", "qs_probe_select",
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_select_attn_workspace_bytes",
-    "qs_select_attn_decode", "qs_prefill_importance_workspace_bytes", "qs_prefill_importance",
-    "qs_last_error", "qs_version",
+    "qs_select_attn_decode", "qs_probe_attn_workspace_bytes", "qs_probe_attn_decode",
+    "qs_prefill_importance_workspace_bytes", "qs_prefill_importance", "qs_last_error", "qs_version",
 )
 
 
@@ -60,12 +60,16 @@ def _load():
     lib.qs_select_attn_workspace_bytes.restype = sz
     lib.qs_select_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, i32, P,
                                           i32, P, P, u32, i32, ctypes.c_float, P, P, P, P, sz, P]
+    lib.qs_probe_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.qs_probe_attn_workspace_bytes.restype = sz
+    lib.qs_probe_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, i32, P, i32,
+                                         P, P, i32, i32, i32, u32, ctypes.c_float, P, P, P, P, sz, P]
     lib.qs_prefill_importance_workspace_bytes.argtypes = [i32, i32, i32]
     lib.qs_prefill_importance_workspace_bytes.restype = sz
     lib.qs_prefill_importance.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, i32, P,
                                           ctypes.c_float, P, i32, P, P, sz, P]
     for f in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_prefill_importance"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_probe_attn_decode", "qs_prefill_importance"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
@@ -316,6 +320,49 @@ def qs_sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selec
                                      _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(selected),
                                      _ptr(n_selected), int(sel_heads), int(k), float(softmax_scale), _ptr(out),
                                      _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def probe_attn_workspace_bytes(B, H, N, mkbpr, k):
+    return lib.qs_probe_attn_workspace_bytes(B, H, N, mkbpr, k)
+
+
+def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
+                         flags=QS_RECENCY, softmax_scale=0.0, out=None, selected=None, n_selected=None,
+                         workspace_buf=None):
+    """Page 1's probe selection and attention over it in one call (qs_probe_select then
+    qs_sparse_attn_decode with one selection row per query head). Returns out [B, H, D] in
+    the query dtype; selected [B, H, k] / n_selected [B, H] receive the selection if given."""
+    dev = _dev(query, k_cache, v_cache, block_tables, seq_lens, importance, out, selected, n_selected)
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    if importance is not None and importance.dtype != torch.float32:
+        raise TypeError("importance must be fp32")
+    B, H, D = query.shape
+    nkv, BS, N, D2 = k_cache.shape
+    mkbpr = block_tables.shape[1]
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    _need(D2 == D and H % N == 0, "query and KV shapes disagree")
+    _rows(block_tables, B, "block_tables")
+    _rows(seq_lens, B, "seq_lens")
+    _rows(importance, B, "importance")
+    _need((selected is None) == (n_selected is None), "selected and n_selected go together")
+    if selected is not None:
+        _i32(selected, "selected")
+        _i32(n_selected, "n_selected")
+        _need(selected.numel() >= B * H * k and n_selected.numel() >= B * H, "selected must hold [B, H, k]")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=query.dtype, device=dev)
+    _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
+    stride = 0 if importance is None else importance.shape[1]
+    nbytes = probe_attn_workspace_bytes(B, H, N, mkbpr, k)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe_attn")
+    _check(lib.qs_probe_attn_decode(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
+                                    _ptr(k_cache), _ptr(v_cache), nkv, _ptr(block_tables), mkbpr, _ptr(seq_lens),
+                                    _ptr(importance), stride, int(n_probe), int(k), int(flags),
+                                    float(softmax_scale), _ptr(out), _ptr(selected), _ptr(n_selected), _ptr(ws),
+                                    ws.numel(), _stream(dev)))
     return out
 
 
