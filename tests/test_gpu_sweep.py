@@ -9,6 +9,8 @@ selections (Quest and probe) bit-identical to the separate selection calls. The 
 of its own (24 draws of prompt lengths, padding, output stride, scale and dtype).
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,7 +23,8 @@ from top_kv_block_amd import workloads as W
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
 
-N_DRAWS = 64
+# QS_SWEEP_DRAWS / QS_SWEEP_IMP_DRAWS widen the sweep for a longer run
+N_DRAWS = int(os.environ.get("QS_SWEEP_DRAWS", "64"))
 
 
 @pytest.fixture(scope="module")
@@ -144,7 +147,7 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
     assert err <= tol, f"fused probe attention err {err:.3e} > {tol}"
 
 
-IMP_DRAWS = 24
+IMP_DRAWS = int(os.environ.get("QS_SWEEP_IMP_DRAWS", "24"))
 
 
 def draw_importance(seed):
