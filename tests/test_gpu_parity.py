@@ -1051,6 +1051,8 @@ PROBE_ATTN_CASES = [
     (404, 4, 4, 4, 128, [3000, 128 * 20 + 1, 7, 2000], 12, torch.float16, True, W.RECENCY, 64),
     (405, 64, 32, 8, 16, [16 * 40 + 3] * 64, 4, torch.float32, True, W.RECENCY, 8),     # 2048 rows: no slot splits
     (406, 1, 2, 1, 16, [16 * 4096], 100, torch.float32, True, W.RECENCY, 8),            # a 4096-block row
+    (407, 1, 2, 1, 16, [16 * 4096], 4096, torch.float32, True, W.RECENCY, 8),           # k at its maximum: all blocks
+    (408, 2, 4, 2, 16, [16 * 50, 16 * 50 - 9], 4096, torch.float32, False, W.RECENCY, 2),  # k far above nb
 ]
 
 
