@@ -935,6 +935,26 @@ def test_graph_replay_matches_eager(qs):
         assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))
 
 
+def test_workspace_cache_grows_twofold(qs):
+    """The binding's cached workspace of one (device, stream, operation) is reused while it
+    suffices and grows at least twofold when it does not, so the replaced buffers it keeps
+    allocated (a captured graph may hold their addresses) stay under twice the largest."""
+    op = "growth_check"
+    before = len(qs._retired)
+    w1 = qs.workspace(1000, DEV, op)
+    assert w1.numel() >= 1000 and qs.workspace(900, DEV, op) is w1
+    sizes = [w1.numel()]
+    for n in range(1001, 200000, 997):   # slowly growing requests
+        w = qs.workspace(n, DEV, op)
+        assert w.numel() >= n
+        if w.numel() != sizes[-1]:
+            sizes.append(w.numel())
+    assert all(b >= 2 * a for a, b in zip(sizes, sizes[1:]))
+    retired = len(qs._retired) - before
+    assert retired == len(sizes) - 1 <= 8
+    assert sum(sizes[:-1]) < sizes[-1]
+
+
 def test_graph_replay_probe_path(qs):
     """Page 1's path captured in a HIP graph: a metadata refresh, the prefill importance, the
     probe selection and fp32 attention with one selection row per query head, and the fused

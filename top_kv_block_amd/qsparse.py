@@ -147,15 +147,19 @@ def workspace(nbytes, device, op):
     """An uninitialised, 256-byte aligned workspace cached per (device, stream, operation)
     and grown on demand, so that calls of one operation on different streams never share
     scratch memory (calls on one stream are ordered). A workspace that is replaced by a
-    larger one stays allocated: a HIP graph captured with it keeps a valid address."""
+    larger one stays allocated: a HIP graph captured with it keeps a valid address. It
+    grows at least twofold each time, so what stays allocated is under twice the largest
+    workspace of each (device, stream, operation)."""
     dev = torch.device(device)
     index = dev.index if dev.index is not None else torch.cuda.current_device()
     key = (index, torch.cuda.current_stream(index).cuda_stream, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        size = max(int(nbytes), 256)
         if ws is not None:
             _retired.append(ws)
-        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+            size = max(size, 2 * ws.numel())
+        ws = torch.empty(size, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
