@@ -261,6 +261,58 @@ def test_update_metadata_serving_chain(qs, oracle):
     assert np.array_equal(bits(tnp(mx)), bits(omx)) and np.array_equal(bits(tnp(mn)), bits(omn))
 
 
+def test_decode_loop_refresh_select_attend(qs, oracle):
+    """Page 3's serving loop on a small paged batch: metadata built after the prefill; each
+    decode step appends one token per request (the pools already hold it; the length
+    grows), runs the fused Quest selection + attention with per-request tokens_since_update
+    and sink + window forcing, and every BS tokens since its last refresh a request has its
+    newest blocks refreshed (from the block that was partial then). Every step's selection
+    equals the oracle's over metadata the oracle builds for the covered tokens (up to near
+    ties), and every output the oracle's attention over the GPU's selection."""
+    BS, N, H, k = 16, 2, 8, 6
+    L0 = [16 * 20 + 5, 16 * 7, 33]
+    steps = 2 * BS + 7
+    final = [x + steps for x in L0]
+    B = len(L0)
+    say(f"decode loop BS={BS} L0={L0} steps={steps}")
+    wl = W.random_case(31, B, H, N, BS, final, k=k, dtype=torch.float32)
+    kc, vc, bt, mt = (t.to(DEV) for t in (wl.k_cache, wl.v_cache, wl.block_tables, wl.meta_tables))
+    shape = (wl.num_meta_blocks, BS, N, wl.D)
+    mx = torch.zeros(shape, device=DEV)
+    mn = torch.zeros(shape, device=DEV)
+    cur, covered = list(L0), list(L0)
+    qs.qs_build_metadata(kc, bt, torch.tensor(cur, dtype=torch.int32, device=DEV), mt, mx, mn)
+    flags = W.FORCE_SINK | W.FORCE_WINDOW
+    gen = torch.Generator().manual_seed(31)
+    for step in range(steps):
+        cur = [x + 1 for x in cur]
+        due = [c - cv >= BS for c, cv in zip(cur, covered)]
+        if any(due):
+            # requests not due get first_block = nb: nothing of theirs is written
+            fb = [cv // BS if d else cdiv(c, BS) for c, cv, d in zip(cur, covered, due)]
+            qs.qs_update_metadata(kc, bt, torch.tensor(cur, dtype=torch.int32, device=DEV),
+                                  torch.tensor(fb, dtype=torch.int32, device=DEV), 2, mt, mx, mn)
+            covered = [c if d else cv for c, cv, d in zip(cur, covered, due)]
+        tsmu = [c - cv for c, cv in zip(cur, covered)]
+        q = (torch.rand((B, H, wl.D), generator=gen) * 2 - 1).float()
+        sl = torch.tensor(cur, dtype=torch.int32)
+        ts = torch.tensor(tsmu, dtype=torch.int32)
+        sel = torch.full((B, N, k), -7, dtype=torch.int32, device=DEV)
+        ns = torch.full((B, N), -7, dtype=torch.int32, device=DEV)
+        out = qs.qs_select_attn_decode(q.to(DEV), mx, mn, mt, kc, vc, bt, sl.to(DEV), k, tokens_since_update=ts.to(DEV),
+                                       flags=flags, selected=sel, n_selected=ns)
+        torch.cuda.synchronize()
+        z = np.zeros(shape, dtype=np.float32)
+        omx, omn = oracle.build_metadata(wl.k_cache, wl.block_tables, torch.tensor(covered, dtype=torch.int32),
+                                         wl.meta_tables, wl.num_meta_blocks, maxb=z, minb=z)
+        osel, ons, osc = oracle.block_select(q, omx, omn, wl.meta_tables, sl, k, tsmu=ts, flags=flags)
+        compare_quest(tnp(sel), tnp(ns), osel, ons, osc, [cdiv(c, BS) for c in cur], k)
+        ref = oracle.sparse_attn_decode(q, wl.k_cache, wl.v_cache, wl.block_tables, sl, tnp(sel), tnp(ns), N)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= 1e-4, f"step {step}: attention err {err:.3e}"
+    assert covered != L0  # every request was refreshed at least once
+
+
 def test_update_metadata_serving_newest_blocks(qs, oracle):
     """Serving shape (B=128, N=8, BS=128, 256 blocks a request, 8 GiB K pool): refresh the
     last blocks of every request in one call; sampled requests against the oracle, and no
