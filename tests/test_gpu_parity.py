@@ -1157,6 +1157,43 @@ def test_probe_attn_matches_probe_select_and_oracle(qs, oracle, case):
                        out.view(torch.int16 if dtype != torch.float32 else torch.int32))
 
 
+def test_probe_decode_loop(qs, oracle):
+    """Page 1's decode path over growing lengths: per step one more token per request and the
+    fused probe selection + attention (prefill importance over the prompt only, so the new
+    tokens add nothing to it; recency forces the newest block), every step's selection and
+    output against the oracle."""
+    BS, N, H, k = 16, 4, 8, 7
+    prompt = [16 * 18 + 3, 16 * 10 + 15]
+    steps = BS + 9
+    final = [x + steps for x in prompt]
+    B = len(prompt)
+    say(f"probe decode loop BS={BS} prompt={prompt} steps={steps}")
+    wl = W.random_case(32, B, H, N, BS, final, k=k, dtype=torch.float32, with_importance=True)
+    imp = wl.importance[:, :max(prompt)].contiguous()     # the prefill's importance row
+    for b, L in enumerate(prompt):
+        imp[b, L:] = 0.0
+    kc, vc, bt = wl.k_cache.to(DEV), wl.v_cache.to(DEV), wl.block_tables.to(DEV)
+    gen = torch.Generator().manual_seed(32)
+    cur = list(prompt)
+    for step in range(steps):
+        cur = [x + 1 for x in cur]
+        q = torch.randn((B, H, wl.D), generator=gen)
+        sl = torch.tensor(cur, dtype=torch.int32)
+        sel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+        ns = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+        out = qs.qs_probe_attn_decode(q.to(DEV), kc, vc, bt, sl.to(DEV), k, importance=imp.to(DEV), n_probe=8,
+                                      flags=W.RECENCY, selected=sel, n_selected=ns)
+        torch.cuda.synchronize()
+        o = oracle.probe_select(q, wl.k_cache, wl.block_tables, sl, k, N, importance=imp, n_probe=8, flags=W.RECENCY)
+        nbs = [cdiv(c, BS) for c in cur]
+        compare_probe(tnp(sel), tnp(ns), o, nbs, k)
+        assert all(int(nb - 1) in set(tnp(sel)[b, h, :tnp(ns)[b, h]].tolist())
+                   for b, nb in enumerate(nbs) for h in range(H)), "recency: the newest block is picked"
+        ref = oracle.sparse_attn_decode(q, wl.k_cache, wl.v_cache, wl.block_tables, sl, tnp(sel), tnp(ns), H)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= 1e-4, f"step {step}: attention err {err:.3e}"
+
+
 def test_probe_attn_page1_k_sweep(qs, oracle):
     """Page 1's probe workload (fp32, 16 heads, 128 blocks of 32, importance, recency) for
     k = 1 .. 32: fused selection bitwise the two calls', output within 1e-4 of the oracle."""
