@@ -911,6 +911,35 @@ def test_serving_full_size_sampled(qs, oracle):
     check_large(qs, oracle, wl, [0, 77, 127], "serving")
 
 
+@pytest.mark.parametrize("which", ["long_context", "serving"])
+def test_full_size_steps_bitwise_repeatable(qs, which):
+    """Determinism at full size: the decode step of the long-context workload (split rows
+    merged by the combine pass) and of the serving workload, each run twice through the
+    fused call and twice through the two calls, gives bitwise the same selection and
+    output each time (and the two paths the same selection)."""
+    wl = W.long_context(device=DEV) if which == "long_context" else W.serving(device=DEV)
+    say(f"bitwise repeat, {wl.name}")
+    mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=wl.k_cache.dtype, device=DEV)
+    mn = torch.zeros_like(mx)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    q, ts = wl.query, wl.tsmu
+    runs = []
+    for _ in range(2):
+        sel = torch.empty((wl.B, wl.N, wl.k), dtype=torch.int32, device=DEV)
+        ns = torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)
+        out = qs.qs_select_attn_decode(q, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                       wl.seq_lens, wl.k, tokens_since_update=ts, flags=wl.flags, selected=sel,
+                                       n_selected=ns)
+        sel2, ns2 = qs.qs_block_select(q, mx, mn, wl.meta_tables, wl.seq_lens, wl.k, tokens_since_update=ts,
+                                       flags=wl.flags)
+        out2 = qs.qs_sparse_attn_decode(q, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel2, ns2)
+        torch.cuda.synchronize()
+        runs.append((sel, ns, out.view(torch.int16), sel2, ns2, out2.view(torch.int16)))
+    for a, b in zip(runs[0], runs[1]):
+        assert torch.equal(a, b)
+    assert torch.equal(runs[0][0], runs[0][3]) and torch.equal(runs[0][1], runs[0][4])
+
+
 def test_workspace_shared_across_shapes_and_operations(qs, oracle):
     """One workspace (filled with garbage first) serves select and attention calls of
     different sizes in turn (no debug score output, so the select scores live in the
