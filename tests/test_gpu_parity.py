@@ -1016,6 +1016,44 @@ def test_graph_replay_matches_eager(qs):
         assert torch.equal(out.view(torch.int16), want[2].view(torch.int16))
 
 
+def test_two_streams_run_concurrently(qs):
+    """Two different workloads issued on two streams at once, each a few times over (Quest
+    select + attention in one call, and the probe selection + attention in one call), give
+    bitwise what each gives alone: the binding keeps a workspace per (stream, operation),
+    so concurrent calls never share scratch memory."""
+    say("two streams")
+    wa = W.random_case(71, 8, 32, 8, 64, [64 * 90 + 7] * 8, k=12, dtype=torch.bfloat16,
+                       flags=W.FORCE_SINK | W.FORCE_WINDOW, tsmu=[9] * 8).to(DEV)
+    wb = W.random_case(72, 4, 16, 8, 32, [32 * 120 + 3] * 4, k=16, dtype=torch.float32,
+                       with_importance=True).to(DEV)
+    mx, mn = run_meta(qs, wa, sentinel=0.0)
+
+    def call_a():
+        return qs.qs_select_attn_decode(wa.query, mx, mn, wa.meta_tables, wa.k_cache, wa.v_cache, wa.block_tables,
+                                        wa.seq_lens, wa.k, tokens_since_update=wa.tsmu, flags=wa.flags)
+
+    def call_b():
+        return qs.qs_probe_attn_decode(wb.query, wb.k_cache, wb.v_cache, wb.block_tables, wb.seq_lens, wb.k,
+                                       importance=wb.importance, n_probe=8, flags=qs.QS_RECENCY)
+
+    want_a, want_b = call_a().clone(), call_b().clone()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    outs_a, outs_b = [], []
+    for _ in range(4):
+        with torch.cuda.stream(sa):
+            outs_a.append(call_a())
+        with torch.cuda.stream(sb):
+            outs_b.append(call_b())
+    torch.cuda.synchronize()
+    for o in outs_a:
+        assert torch.equal(o.view(torch.int16), want_a.view(torch.int16))
+    for o in outs_b:
+        assert torch.equal(o.view(torch.int32), want_b.view(torch.int32))
+
+
 def test_workspace_cache_grows_twofold(qs):
     """The binding's cached workspace of one (device, stream, operation) is reused while it
     suffices and grows at least twofold when it does not, so the replaced buffers it keeps
