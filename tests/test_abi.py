@@ -260,11 +260,12 @@ def test_prefill_importance_rejects(qs, kw, status):
 
 
 def test_prefill_importance_workspace_size(qs):
-    # fp32 row normalisers + per chunk (row max, row sum, column sums); 64 tiles of 64 rows
-    # x 16 heads is too few items to balance, so 8 chunks; 2 x 32 x 128 tiles are enough: 1
+    # fp32 row normalisers + per chunk (row max, row sum, column sums), for the larger of the
+    # two splits (fp32: one chunk; 16-bit: tiles of 128 rows, chunked below 8192 x 64 rows x
+    # heads x requests): 4096 rows x 16 heads -> 8 chunks; 2 x 32 heads x 8192 rows -> 1
     assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == (1 + 3 * 8) * 16 * 4096 * 4
     assert qs.prefill_importance_workspace_bytes(2, 32, 8192) == (1 + 3 * 1) * 2 * 32 * 8192 * 4
-    assert qs.prefill_importance_workspace_bytes(1, 1, 100) == 2816  # (1 + 3 * 2 chunks) * 100 * 4 = 2800, rounded up to 256 B
+    assert qs.prefill_importance_workspace_bytes(1, 1, 100) == 1792  # (1 + 3 * 1 chunk) * 100 * 4 = 1600, rounded up to 256 B
     assert qs.prefill_importance_workspace_bytes(0, 16, 4096) == 256
     assert qs.prefill_importance_workspace_bytes(1, 0, 4096) == 0
     assert _imp(qs, imp=None, himp=FAKE, wsb=qs.prefill_importance_workspace_bytes(0, 16, 4096)) == 0

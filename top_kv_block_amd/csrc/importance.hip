@@ -11,26 +11,33 @@
 // Design (CDNA4). The weights need each row's softmax normaliser before any column can
 // be summed, so there are two passes over the causal score matrix, both dense
 // contractions on the matrix cores (the scores are never stored):
-//   row pass     work item (64-row query tile, key chunk): each wave takes 16 query rows
-//                and walks the chunk's 16-key tiles up to its last row, S = Q K^T on
-//                v_mfma_f32_16x16x4_f32 (fp32 inputs) or v_mfma_f32_16x16x32_{bf16,f16};
-//                each lane keeps an online (max, sum) of its key column for its 4 rows and
-//                the 16 lanes of a row merge once at the end into the chunk's (max, sum);
+//   row pass     work item (query tile, key chunk): each wave takes 16 query rows per
+//                row tile it holds and walks the chunk's 16-key tiles up to its last row,
+//                S = Q K^T on v_mfma_f32_16x16x4_f32 (fp32 inputs) or
+//                v_mfma_f32_16x16x32_{bf16,f16}; each lane keeps an online (max, sum) of
+//                its key column for its 4 rows of each row tile, and the 16 lanes of a row
+//                merge once at the end into the chunk's (max, sum);
 //   merge        per row, the chunks' (max, sum) in chunk order -> log2-sum-exp (with
 //                one chunk the row pass writes it itself);
-//   column pass  work item (64-key tile, query-row chunk): each wave takes 16 keys and
-//                walks the chunk's 16-row query tiles from its first key on, S^T = K Q^T,
-//                adds 2^(x - lse_row) into per-lane column sums, merges the 16 lanes and
-//                writes the chunk's column sums;
+//   column pass  work item (key tile, query-row chunk): each wave takes 16 keys per key
+//                tile it holds and walks the chunk's 16-row query tiles from its first key
+//                on, S^T = K Q^T, adds 2^(x - lse_row) into per-lane column sums, merges
+//                the 16 lanes and writes the chunk's column sums;
 //   reduce       sums the chunks, then the heads, in a fixed order (deterministic).
+// A wave holds one 16-row tile with fp32 inputs and two with 16-bit ones (wave_tiles), so
+// a workgroup's tile is 64 or 128 query rows (keys). With 16-bit inputs a wave's matrix
+// work per fetched tile is short and the per-step work around it (the tile's fetch, LDS
+// store, barrier and fragment reads) dominates; two tiles per wave feed each fetched tile
+// and each fragment read to twice the MFMAs.
 // Chunks: a causal tile's work grows with its distance from the diagonal. With 16-bit
 // inputs a wave's matrix work between two barriers is short, so a CU whose short tiles
 // have finished cannot keep its matrix pipe fed from the one long tile left; there every
-// tile's range is cut into chunks of R tiles (64 R keys or rows, at most 8 chunks), giving
-// several times more, bounded items, which the dispatcher hands to CUs as they free up.
-// With fp32 inputs one wave's matrix work alone keeps the pipe busy and the extra items
-// only cost their start-up, so each tile stays one item, as do jobs that already hold
-// enough tiles to balance (>= 8192); the snake order below evens the first items out.
+// tile's range is cut into chunks of R tiles (at most 8 chunks), giving several times
+// more, bounded items, which the dispatcher hands to CUs as they free up. With fp32
+// inputs one wave's matrix work alone keeps the pipe busy and the extra items only cost
+// their start-up, so each tile stays one item, as do jobs that already hold enough work
+// to balance (>= 8192 x 64 rows x heads x requests); the snake order below evens the
+// first items out.
 // Operand layout: a lane (row r = lane % 16, group j = lane / 16) holds channels
 // 32j .. 32j+31 of its row, contiguous in memory (16-byte loads). The contraction order
 // over channels is free, so both operands use that same channel order: at step ks the
@@ -48,6 +55,16 @@ namespace {
 constexpr int D = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 16-row tiles per wave: two with 16-bit inputs, whose matrix work per tile is short, so
+// that each operand fragment read from LDS and each tile fetched into LDS feed twice the
+// MFMAs; one with fp32 inputs, where 64 more registers of query would cost occupancy. A
+// workgroup of four waves then covers wave_tiles * 64 query rows (row pass) or keys
+// (column pass).
+template <int DT>
+constexpr int wave_tiles() { return DT == kF32 ? 1 : 2; }
+template <int DT>
+constexpr int tile_rows() { return 64 * wave_tiles<DT>(); }
+
 struct ImpParams {
     const uint8_t* q;   // [B, max_len, H, D]
     const uint8_t* kc;  // [num_kv_blocks, BS, N, D]
@@ -57,23 +74,24 @@ struct ImpParams {
     const int32_t* sl;
     int B, H, N, BS, max_len;
     float scale2;  // softmax scale * log2(e)
-    int T, R, C;   // 64-row tiles of max_len, tiles per chunk, chunks
+    int TR;        // rows (keys) of a workgroup's tile: 64 or 128
+    int T, R, C;   // tiles of max_len, tiles per chunk, chunks
     float* lse;    // [B, H, max_len] workspace: log2-sum-exp2 of each row
     float* mpart;  // [C, B, H, max_len] workspace: each key chunk's row max (log2 units)
     float* lpart;  // [C, B, H, max_len] workspace: each key chunk's sum of 2^(x - max)
     float* cpart;  // [C, B, H, max_len] workspace: each row chunk's column sums
 };
 
-// chunking of a (B, H, max_len) job
+// chunking of a (B, H, max_len) job with tiles of TR rows
 constexpr int kMaxChunks = 8;
 struct Split { int T, R, C; };
-inline Split imp_split(int B, int H, int max_len, bool chunked) {
-    constexpr int kEnoughItems = 8192;
+inline Split imp_split(int B, int H, int max_len, bool chunked, int TR) {
+    constexpr long kEnoughRows = 8192L * 64;  // rows x heads x requests that balance unaided
     Split sp;
-    sp.T = (max_len + 63) / 64;
+    sp.T = (max_len + TR - 1) / TR;
     if (sp.T <= 0) return Split{0, 1, 1};
-    const long items = long(sp.T) * H * B;
-    const int want = (!chunked || items >= kEnoughItems) ? 1 : min(kMaxChunks, sp.T);
+    const long rows = long(sp.T) * TR * H * B;
+    const int want = (!chunked || rows >= kEnoughRows) ? 1 : min(kMaxChunks, sp.T);
     sp.R = (sp.T + want - 1) / want;
     sp.C = (sp.T + sp.R - 1) / sp.R;
     return sp;
@@ -159,6 +177,39 @@ __device__ __forceinline__ void dot_tile2(const Frag<DT>& a, const Frag<DT>& b0,
             d0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i]), attn::as_op8<DT>(b1.v[i]), d0);
             c1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i + 1]), attn::as_op8<DT>(b0.v[i + 1]), c1);
             d1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a.v[i + 1]), attn::as_op8<DT>(b1.v[i + 1]), d1);
+        }
+    }
+    r0 = c0 + c1;
+    r1 = d0 + d1;
+}
+
+// two tiles sharing the operand b (two row tiles against one key tile in the row pass, two
+// key tiles against one query tile in the column pass): four independent chains
+template <int DT>
+__device__ __forceinline__ void dot_tile2a(const Frag<DT>& a0, const Frag<DT>& a1, const Frag<DT>& b,
+                                           attn::f32x4& r0, attn::f32x4& r1) {
+    attn::f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, d0 = c0, d1 = c0;
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t aw[4] = {a0.v[i].x, a0.v[i].y, a0.v[i].z, a0.v[i].w};
+            const uint32_t ew[4] = {a1.v[i].x, a1.v[i].y, a1.v[i].z, a1.v[i].w};
+            const uint32_t bw[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e]), __uint_as_float(bw[e]), c0, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ew[e]), __uint_as_float(bw[e]), d0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(aw[e + 1]), __uint_as_float(bw[e + 1]), c1, 0, 0, 0);
+                d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ew[e + 1]), __uint_as_float(bw[e + 1]), d1, 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            c0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a0.v[i]), attn::as_op8<DT>(b.v[i]), c0);
+            d0 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a1.v[i]), attn::as_op8<DT>(b.v[i]), d0);
+            c1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a0.v[i + 1]), attn::as_op8<DT>(b.v[i + 1]), c1);
+            d1 = attn::mfma16x16x32<DT>(attn::as_op8<DT>(a1.v[i + 1]), attn::as_op8<DT>(b.v[i + 1]), d1);
         }
     }
     r0 = c0 + c1;
@@ -270,26 +321,32 @@ __device__ __forceinline__ void frag_from_tile(Frag<DT>& f, const uint8_t* buf, 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
+    constexpr int RW = wave_tiles<DT>(), TR = tile_rows<DT>();
     __shared__ __attribute__((aligned(16))) uint8_t kt[4][Tile<DT>::kBytes];
     const WorkItem wi = row_item(p);
     const int b = wi.b, h = wi.h;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int tw = wi.tile * 64;  // the workgroup's rows tw .. tw+63
+    const int tw = wi.tile * TR;  // the workgroup's rows tw .. tw + TR - 1
     if (tw >= L) return;                              // whole workgroup
-    const int t0 = tw + 16 * w;                       // this wave's rows t0 .. t0+15
-    const int s_lo = wi.chunk * p.R * 64;             // the chunk's keys s_lo .. (<= tw since chunk <= tile / R)
+    const int t0 = tw + 16 * RW * w;                  // this wave's rows t0 .. t0 + 16 RW - 1
+    const int s_lo = wi.chunk * p.R * TR;             // the chunk's keys s_lo .. (<= tw since chunk <= tile / R)
     const int kh = h / (p.H / p.N);
-    Frag<DT> qf;
-    load_frag<DT>(qf, p.q + ((size_t(b) * p.max_len + min(t0 + r, L - 1)) * p.H + h) * D * es, j);
-
-    // online max / sum of 2^x over this lane's key column, rows 4j + i. The max starts at
-    // -FLT_MAX, below every finite score, so a masked score (-inf) never meets an infinite max
-    float m[4], l[4];
+    Frag<DT> qf[RW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { m[i] = -FLT_MAX; l[i] = 0.f; }
-    const int s_end = min(min(s_lo + p.R * 64, tw + 64), L) - 1;  // last key any wave needs
+    for (int rr = 0; rr < RW; ++rr)
+        load_frag<DT>(qf[rr], p.q + ((size_t(b) * p.max_len + min(t0 + 16 * rr + r, L - 1)) * p.H + h) * D * es, j);
+
+    // online max / sum of 2^x over this lane's key column, rows t0 + 16 rr + 4j + i. The max
+    // starts at -FLT_MAX, below every finite score, so a masked score (-inf) never meets an
+    // infinite max
+    float m[RW][4], l[RW][4];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { m[rr][i] = -FLT_MAX; l[rr][i] = 0.f; }
+    const int s_end = min(min(s_lo + p.R * TR, tw + TR), L) - 1;  // last key any wave needs
     // key tile s0 (16 keys in one block, physical block ph): rows past L repeat the last
     // key (masked). The block-table entries are read one step before their tile (bt_at),
     // so no step waits for a lookup between its barrier and its loads.
@@ -302,24 +359,24 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         return true;
     };
     int pa = bt_at(s_lo), pb = bt_at(s_lo + 16);
-    // the softmax update of this lane's 4 rows with one 16-key tile's scores (key s of this
-    // lane), branch-free: a masked score enters as -inf and changes nothing. Tiles whose 16
-    // keys precede all of the wave's rows and L (all) skip the mask.
-    auto upd = [&](const attn::f32x4& c, int s, bool all) {
+    // the softmax update of row tile rr (this lane's 4 rows) with one 16-key tile's scores
+    // (key s of this lane), branch-free: a masked score enters as -inf and changes nothing.
+    // Tiles whose 16 keys precede all of the tile's rows and L (all) skip the mask.
+    auto upd = [&](const attn::f32x4& c, int rr, int s, bool all) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 4 * j + i;
+            const int t = t0 + 16 * rr + 4 * j + i;
             // one exp2 per score: a new maximum rescales the sum, any other score adds
             const float x = (all || (s <= t && s < L)) ? c[i] * p.scale2 : -INFINITY;
-            const float d = x - m[i];
+            const float d = x - m[rr][i];
             const float e = exp2_hw(-fabsf(d));
-            l[i] = d > 0.f ? fmaf(l[i], e, 1.f) : l[i] + e;
-            m[i] = fmaxf(m[i], x);
+            l[rr][i] = d > 0.f ? fmaf(l[rr][i], e, 1.f) : l[rr][i] + e;
+            m[rr][i] = fmaxf(m[rr][i], x);
         }
     };
-    auto upd_tile = [&](const attn::f32x4& c, int s0k) {
-        if (s0k + 15 <= t0 && s0k + 15 < L) upd(c, s0k + r, true);
-        else upd(c, s0k + r, false);
+    auto upd_tile = [&](const attn::f32x4& c, int rr, int s0k) {
+        if (s0k + 15 <= t0 + 16 * rr && s0k + 15 < L) upd(c, rr, s0k + r, true);
+        else upd(c, rr, s0k + r, false);
     };
     // a step takes two key tiles (32 keys): both go to LDS, one barrier, then the next two
     // are fetched into the freed register sets and the pair is multiplied; four LDS
@@ -330,24 +387,55 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
         // step then waits for its loads here, so the MFMAs below never wait for global loads
         tile_store<DT>(b0, va);
         tile_store<DT>(b1, vb);
-        const bool c0 = ha && s0 <= t0 + 15 && t0 < L, c1 = hb && s0 + 16 <= t0 + 15 && t0 < L;
+        // key tile kk of the pair is needed by row tile rr if it was fetched, its first key
+        // is at or before the tile's last row, and the tile has rows before L
+        auto need = [&](int kk, int rr) {
+            const int tr = t0 + 16 * rr;
+            return (kk == 0 ? ha : hb) && s0 + 16 * kk <= tr + 15 && tr < L;
+        };
+        bool nd[2][RW];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) nd[kk][rr] = need(kk, rr);
         __syncthreads();
         ha = s0 + 32 <= s_end && fetch(s0 + 32, pa, va);
         hb = s0 + 48 <= s_end && fetch(s0 + 48, pb, vb);
         pa = bt_at(s0 + 64);  // the entries of the next step's tiles
         pb = bt_at(s0 + 80);
-        if (c0 && c1) {
-            Frag<DT> k0, k1;
-            frag_from_tile<DT>(k0, b0, r, j);
-            frag_from_tile<DT>(k1, b1, r, j);
-            attn::f32x4 r0, r1;
-            dot_tile2<DT>(qf, k0, k1, r0, r1);
-            upd_tile(r0, s0);
-            upd_tile(r1, s0 + 16);
-        } else if (c0 || c1) {
-            Frag<DT> kf;
-            frag_from_tile<DT>(kf, c0 ? b0 : b1, r, j);
-            upd_tile(dot_tile<DT>(qf, kf), c0 ? s0 : s0 + 16);
+        if constexpr (RW == 1) {
+            if (nd[0][0] && nd[1][0]) {
+                Frag<DT> k0, k1;
+                frag_from_tile<DT>(k0, b0, r, j);
+                frag_from_tile<DT>(k1, b1, r, j);
+                attn::f32x4 r0, r1;
+                dot_tile2<DT>(qf[0], k0, k1, r0, r1);
+                upd_tile(r0, 0, s0);
+                upd_tile(r1, 0, s0 + 16);
+            } else if (nd[0][0] || nd[1][0]) {
+                Frag<DT> kf;
+                frag_from_tile<DT>(kf, nd[0][0] ? b0 : b1, r, j);
+                upd_tile(dot_tile<DT>(qf[0], kf), 0, nd[0][0] ? s0 : s0 + 16);
+            }
+        } else {
+            // each key fragment read from LDS feeds both row tiles
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (!nd[kk][0] && !nd[kk][1]) continue;
+                Frag<DT> kf;
+                frag_from_tile<DT>(kf, kk == 0 ? b0 : b1, r, j);
+                const int sk = s0 + 16 * kk;
+                if (nd[kk][0] && nd[kk][1]) {
+                    attn::f32x4 r0, r1;
+                    dot_tile2a<DT>(qf[0], qf[1], kf, r0, r1);
+                    upd_tile(r0, 0, sk);
+                    upd_tile(r1, 1, sk);
+                } else if (nd[kk][0]) {  // constant tile indices keep m, l and qf in registers
+                    upd_tile(dot_tile<DT>(qf[0], kf), 0, sk);
+                } else {
+                    upd_tile(dot_tile<DT>(qf[1], kf), 1, sk);
+                }
+            }
         }
     };
     u32x4 na[Tile<DT>::kPerThread] = {}, nb[Tile<DT>::kPerThread] = {};
@@ -355,23 +443,26 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     bool hb = s_lo + 16 <= s_end && fetch(s_lo + 16, pb, nb);
     pa = bt_at(s_lo + 32);
     pb = bt_at(s_lo + 48);
-    for (int s0 = s_lo, pb = 0; s0 <= s_end; s0 += 32, pb ^= 2) step2(s0, kt[pb], kt[pb + 1], na, ha, nb, hb);
+    for (int s0 = s_lo, buf = 0; s0 <= s_end; s0 += 32, buf ^= 2) step2(s0, kt[buf], kt[buf + 1], na, ha, nb, hb);
     // merge the 16 key columns of each row into the chunk's (max, sum); every row t < L
     // has a key of the chunk (s_lo <= tw), so the max is finite. With one chunk that is
     // the row's log2-sum-exp already.
     const size_t o = ((size_t(wi.chunk) * p.B + b) * p.H + h) * p.max_len;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float M = group_max<16>(m[i]);
-        const float part = l[i] * exp2f(m[i] - M);  // a lane without keys: l = 0
-        const float S = group_sum<16>(part);
-        const int t = t0 + 4 * j + i;
-        if (r == 0 && t < L) {
-            if (p.C == 1) {
-                p.lse[o + t] = M + log2f(S);
-            } else {
-                p.mpart[o + t] = M;
-                p.lpart[o + t] = S;
+    for (int rr = 0; rr < RW; ++rr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float M = group_max<16>(m[rr][i]);
+            const float part = l[rr][i] * exp2f(m[rr][i] - M);  // a lane without keys: l = 0
+            const float S = group_sum<16>(part);
+            const int t = t0 + 16 * rr + 4 * j + i;
+            if (r == 0 && t < L) {
+                if (p.C == 1) {
+                    p.lse[o + t] = M + log2f(S);
+                } else {
+                    p.mpart[o + t] = M;
+                    p.lpart[o + t] = S;
+                }
             }
         }
     }
@@ -380,6 +471,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
+    constexpr int RW = wave_tiles<DT>(), TR = tile_rows<DT>();
     __shared__ __attribute__((aligned(16))) uint8_t qt[4][Tile<DT>::kBytes];
     __shared__ float lt_s[4][16];
     const WorkItem wi = col_item(p);
@@ -387,37 +479,45 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, j = lane >> 4;
-    const int sw = wi.tile * 64;  // the workgroup's keys sw .. sw+63
+    const int sw = wi.tile * TR;  // the workgroup's keys sw .. sw + TR - 1
     // the chunk's query rows t_lo .. t_hi-1 (rows before sw see none of these keys)
-    const int t_lo = max(wi.chunk * p.R * 64, sw), t_hi = min((wi.chunk + 1) * p.R * 64, L);
+    const int t_lo = max(wi.chunk * p.R * TR, sw), t_hi = min((wi.chunk + 1) * p.R * TR, L);
     if (t_lo >= t_hi) return;                         // whole workgroup (sw >= L included)
-    const int s0 = sw + 16 * w;      // this wave's keys s0 .. s0+15
+    const int s0 = sw + 16 * RW * w;  // this wave's keys s0 .. s0 + 16 RW - 1
     const int kh = h / (p.H / p.N);
-    const bool live = s0 < L;
-    const uint8_t* kr = live ? key_row(p, b, s0, kh, es) : nullptr;
-    Frag<DT> kf;
-    if (kr != nullptr) load_frag<DT>(kf, kr + size_t(min(r, L - 1 - s0)) * p.N * D * es, j);
+    const uint8_t* kr[RW];
+    Frag<DT> kf[RW];
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk) {
+        const int sk = s0 + 16 * kk;
+        kr[kk] = sk < L ? key_row(p, b, sk, kh, es) : nullptr;
+        if (kr[kk] != nullptr) load_frag<DT>(kf[kk], kr[kk] + size_t(min(r, L - 1 - sk)) * p.N * D * es, j);
+    }
     const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // keys 4j + i, partial over this lane's query column
+    float acc[RW][4];  // keys s0 + 16 kk + 4j + i, partial over this lane's query column
+#pragma unroll
+    for (int kk = 0; kk < RW; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kk][i] = 0.f;
     // query tile t0: 16 rows of head h (rows past L repeat the last row, masked) and their lse
     auto fetch = [&](int t0, u32x4 (&v)[Tile<DT>::kPerThread], float& lv) {
         tile_fetch<DT>(v, p.q + ((size_t(b) * p.max_len + t0) * p.H + h) * size_t(D * es), unsigned(p.H) * D * es,
                        L - 1 - t0);
         lv = (threadIdx.x < 16 && t0 + int(threadIdx.x) < L) ? lse[t0 + threadIdx.x] : 0.f;
     };
-    // this lane's weights 2^(x - lse_t) for its 4 keys and query row t; tiles whose 16
-    // rows follow all of the wave's keys and end before L (all) skip the mask
-    auto upd = [&](const attn::f32x4& c, int t, float lt, bool all) {
+    // key tile kk's weights 2^(x - lse_t) for this lane's 4 keys and query row t; tiles whose
+    // 16 rows follow all of the key tile's keys and end before L (all) skip the mask
+    auto upd = [&](const attn::f32x4& c, int kk, int t, float lt, bool all) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int s = s0 + 4 * j + i;
+            const int s = s0 + 16 * kk + 4 * j + i;
             const float wgt = exp2_hw(c[i] * p.scale2 - lt);
-            acc[i] += (all || (t >= s && t < L)) ? wgt : 0.f;
+            acc[kk][i] += (all || (t >= s && t < L)) ? wgt : 0.f;
         }
     };
-    auto upd_tile = [&](const attn::f32x4& c, int t0q, float lt) {
-        if (t0q >= s0 + 15 && t0q + 15 < L) upd(c, t0q + r, lt, true);
-        else upd(c, t0q + r, lt, false);
+    auto upd_tile = [&](const attn::f32x4& c, int kk, int t0q, float lt) {
+        if (t0q >= s0 + 16 * kk + 15 && t0q + 15 < L) upd(c, kk, t0q + r, lt, true);
+        else upd(c, kk, t0q + r, lt, false);
     };
     // as in the row pass: two query tiles per barrier, four LDS buffers
     auto step2 = [&](int t0, int bi, u32x4 (&va)[Tile<DT>::kPerThread], float& la, u32x4 (&vb)[Tile<DT>::kPerThread],
@@ -431,33 +531,65 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
         __syncthreads();
         if (t0 + 32 < t_hi) fetch(t0 + 32, va, la);
         if (t0 + 48 < t_hi) fetch(t0 + 48, vb, lb);
-        const bool c0 = kr != nullptr && t0 + 15 >= s0, c1 = hb && kr != nullptr && t0 + 31 >= s0;
-        if (c0 && c1) {
-            Frag<DT> q0, q1;
-            frag_from_tile<DT>(q0, qt[bi], r, j);
-            frag_from_tile<DT>(q1, qt[bi + 1], r, j);
-            attn::f32x4 r0, r1;
-            dot_tile2<DT>(kf, q0, q1, r0, r1);
-            upd_tile(r0, t0, lt_s[bi][r]);
-            upd_tile(r1, t0 + 16, lt_s[bi + 1][r]);
-        } else if (c0 || c1) {
-            const int bx = c0 ? bi : bi + 1;
-            Frag<DT> qf;
-            frag_from_tile<DT>(qf, qt[bx], r, j);
-            upd_tile(dot_tile<DT>(kf, qf), c0 ? t0 : t0 + 16, lt_s[bx][r]);
+        // query tile qq of the pair is needed by key tile kk if it was stored, the key tile
+        // has its fragment, and the query tile holds a row at or after the key tile's first key
+        bool nd[2][RW];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int kk = 0; kk < RW; ++kk)
+                nd[qq][kk] = (qq == 0 || hb) && kr[kk] != nullptr && t0 + 16 * qq + 15 >= s0 + 16 * kk;
+        if constexpr (RW == 1) {
+            if (nd[0][0] && nd[1][0]) {
+                Frag<DT> q0, q1;
+                frag_from_tile<DT>(q0, qt[bi], r, j);
+                frag_from_tile<DT>(q1, qt[bi + 1], r, j);
+                attn::f32x4 r0, r1;
+                dot_tile2<DT>(kf[0], q0, q1, r0, r1);
+                upd_tile(r0, 0, t0, lt_s[bi][r]);
+                upd_tile(r1, 0, t0 + 16, lt_s[bi + 1][r]);
+            } else if (nd[0][0] || nd[1][0]) {
+                const int bx = nd[0][0] ? bi : bi + 1;
+                Frag<DT> qf;
+                frag_from_tile<DT>(qf, qt[bx], r, j);
+                upd_tile(dot_tile<DT>(kf[0], qf), 0, nd[0][0] ? t0 : t0 + 16, lt_s[bx][r]);
+            }
+        } else {
+            // each query fragment read from LDS feeds both key tiles
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                if (!nd[qq][0] && !nd[qq][1]) continue;
+                Frag<DT> qf;
+                frag_from_tile<DT>(qf, qt[bi + qq], r, j);
+                const float lt = lt_s[bi + qq][r];
+                const int tq = t0 + 16 * qq;
+                if (nd[qq][0] && nd[qq][1]) {
+                    attn::f32x4 r0, r1;
+                    dot_tile2a<DT>(kf[0], kf[1], qf, r0, r1);
+                    upd_tile(r0, 0, tq, lt);
+                    upd_tile(r1, 1, tq, lt);
+                } else if (nd[qq][0]) {  // constant tile indices keep acc and kf in registers
+                    upd_tile(dot_tile<DT>(kf[0], qf), 0, tq, lt);
+                } else {
+                    upd_tile(dot_tile<DT>(kf[1], qf), 1, tq, lt);
+                }
+            }
         }
     };
     u32x4 na[Tile<DT>::kPerThread] = {}, nb[Tile<DT>::kPerThread] = {};
     float la = 0.f, lb = 0.f;
     fetch(t_lo, na, la);
     if (t_lo + 16 < t_hi) fetch(t_lo + 16, nb, lb);
-    for (int t0 = t_lo, pb = 0; t0 < t_hi; t0 += 32, pb ^= 2) step2(t0, pb, na, la, nb, lb, t0 + 16 < t_hi);
+    for (int t0 = t_lo, buf = 0; t0 < t_hi; t0 += 32, buf ^= 2) step2(t0, buf, na, la, nb, lb, t0 + 16 < t_hi);
     const size_t o = ((size_t(wi.chunk) * p.B + b) * p.H + h) * p.max_len;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float tot = group_sum<16>(acc[i]);
-        const int s = s0 + 4 * j + i;
-        if (r == 0 && s < L) p.cpart[o + s] = tot;
+    for (int kk = 0; kk < RW; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float tot = group_sum<16>(acc[kk][i]);
+            const int s = s0 + 16 * kk + 4 * j + i;
+            if (r == 0 && s < L) p.cpart[o + s] = tot;
+        }
     }
 }
 
@@ -468,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void imp_merge_kernel(ImpParams p) {
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
     if (t >= L) return;
     const size_t row = (size_t(b) * p.H + h) * p.max_len + t, cs = size_t(p.B) * p.H * p.max_len;
-    const int nc = (t / 64) / p.R + 1;  // <= C <= kMaxChunks
+    const int nc = (t / p.TR) / p.R + 1;  // <= C <= kMaxChunks
     float mv[kMaxChunks], lv[kMaxChunks];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {  // all loads in flight at once
@@ -495,8 +627,8 @@ __global__ __launch_bounds__(kThreads) void imp_reduce_kernel(ImpParams p, float
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int s = blockIdx.x * 64 + lane, b = blockIdx.y;
     const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
-    // key s has the column sums of row chunks s / (64 R) .. those holding rows below L
-    const int c_lo = (s / 64) / p.R, c_hi = (L + 64 * p.R - 1) / (64 * p.R);
+    // key s has the column sums of row chunks s / (TR R) .. those holding rows below L
+    const int c_lo = (s / p.TR) / p.R, c_hi = (L + p.TR * p.R - 1) / (p.TR * p.R);
     const size_t cs = size_t(p.B) * p.H * p.max_len;
     float tot = 0.f;
     if (s < stride) {
@@ -523,18 +655,21 @@ __global__ __launch_bounds__(kThreads) void imp_reduce_kernel(ImpParams p, float
 }  // namespace
 
 size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
-    const Split sp = imp_split(B, H, max_len, true);  // the larger of the two splits
-    size_t bytes = size_t(B) * H * max_len * sizeof(float) * (1 + 3 * size_t(sp.C));
+    // the larger of the two splits: fp32 (64-row tiles, one chunk) and 16-bit (128-row tiles)
+    const int C = max(imp_split(B, H, max_len, false, tile_rows<kF32>()).C,
+                      imp_split(B, H, max_len, true, tile_rows<kBF16>()).C);
+    size_t bytes = size_t(B) * H * max_len * sizeof(float) * (1 + 3 * size_t(C));
     bytes = (bytes + 255) & ~size_t(255);
     return bytes < 256 ? 256 : bytes;
 }
 
 hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s) {
     float* ws = (float*)a.workspace;
-    const Split sp = imp_split(a.B, a.H, a.max_len, a.dtype != kF32);
+    const int TR = a.dtype == kF32 ? tile_rows<kF32>() : tile_rows<kBF16>();
+    const Split sp = imp_split(a.B, a.H, a.max_len, a.dtype != kF32, TR);
     const size_t plane = size_t(a.B) * a.H * a.max_len;
     ImpParams p{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr,
-                a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, sp.T, sp.R, sp.C,
+                a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, TR, sp.T, sp.R, sp.C,
                 ws, ws + plane, ws + plane * (1 + sp.C), ws + plane * (1 + 2 * size_t(sp.C))};
     if (a.max_len > 0) {
         const long hb = long(a.H) * a.B;
