@@ -42,6 +42,27 @@
  *   - Device-resident data (seq_lens, tables, selections) is read by the kernels. Table
  *     entries out of range are never dereferenced: the block they name is skipped.
  *     Negative seq_lens count as 0.
+ *   - Checked build (libqsparse_checked.so, same kernels and signatures; qs_checked_build()
+ *     returns 1): before its own kernels, every call checks on its stream the device-resident
+ *     entries it will use, waits for that check, and returns QS_ERR_INVALID, with a message
+ *     naming the first bad entry (lowest request first), if any is out of range:
+ *       qs_build_metadata, qs_update_metadata: ceil(L / BS) <= max_kv_blocks_per_req,
+ *         its metadata blocks <= max_meta_blocks_per_req, and the block_tables and
+ *         metadata_block_tables entries of every block the call reduces (all blocks, or
+ *         the refreshed range) in [0, num_kv_blocks) and [0, num_meta_blocks);
+ *       qs_block_select: ceil(L / BS) <= max_meta_blocks_per_req * BS and the
+ *         metadata_block_tables entry of every block of the request (forced ones too);
+ *       qs_probe_select, qs_probe_attn_decode: ceil(L / BS) <= max_kv_blocks_per_req and
+ *         every block's block_tables entry;
+ *       qs_sparse_attn_decode: the block_tables entry of every selected entry it attends
+ *         (slots below the clamped n_selected that name a block < min(nb, width));
+ *       qs_select_attn_decode: the qs_block_select rules and the block_tables entry of
+ *         every block < min(nb, max_kv_blocks_per_req);
+ *       qs_prefill_importance: L <= max_len, ceil(L / BS) <= max_kv_blocks_per_req and
+ *         every block's block_tables entry.
+ *     The check allocates and frees one 8-byte device word and synchronises the stream, so
+ *     the checked build is for debugging; a call under stream capture returns
+ *     QS_ERR_UNSUPPORTED.
  *   - Determinism: identical inputs give bit-identical outputs ([P1] section 1: same
  *     query and same KV must select the same blocks; ties go to the lower index).
  *   - Workspaces: calls that take `workspace` use it as scratch for scores and partial
@@ -363,6 +384,9 @@ const char* qs_last_error(void);
 
 /* library version string */
 const char* qs_version(void);
+
+/* 1 in the checked build (libqsparse_checked.so), 0 in libqsparse.so */
+int32_t qs_checked_build(void);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,7 @@
 """C-ABI tests that need no GPU: the library loads, exports every function the header
-declares, and rejects invalid arguments on the host before any HIP call.
+declares, and rejects invalid arguments on the host before any HIP call. Every test runs
+against both builds (libqsparse.so and libqsparse_checked.so): the checked build's device
+check comes after the host checks, so it rejects the same calls the same way.
 
 Every invalid call below also passes B = 0 where B is not under test: B = 0 returns
 before any launch, so a check that wrongly passed would still enqueue nothing.
@@ -16,15 +18,19 @@ from tests.conftest import ROOT
 HEADER = os.path.join(ROOT, "include", "qsparse.h")
 
 
-@pytest.fixture(scope="module")
-def qs():
+@pytest.fixture(scope="module", params=["plain", "checked"])
+def qs(request):
     from top_kv_block_amd import qsparse
-    return qsparse
+    if request.param == "plain":
+        yield qsparse
+    else:
+        with qsparse.checked_calls():
+            yield qsparse
 
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:qs_status|size_t|const char\s*\*)\s*(qs_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:qs_status|size_t|int32_t|const char\s*\*)\s*(qs_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_operations():
@@ -40,6 +46,9 @@ def test_library_exports_every_declared_symbol(qs):
     for n in names:
         assert hasattr(qs.lib, n), n
     assert qs.lib.qs_version().decode().startswith("qsparse")
+    checked = qs.lib._name.endswith("libqsparse_checked.so")
+    assert qs.lib.qs_checked_build() == (1 if checked else 0)
+    assert ("checked" in qs.lib.qs_version().decode()) == checked
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: every call below fails validation

@@ -2,11 +2,14 @@
 //
 // Every check that the host can make happens before the first HIP call, so invalid
 // calls return QS_ERR_INVALID / QS_ERR_UNSUPPORTED without touching the device.
+// Compiled with QS_CHECKED (libqsparse_checked.so), every call also checks the
+// device-resident tables it will use, synchronously, before its own kernels run.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "../../include/qsparse.h"
+#include "qs_check.h"
 #include "qs_internal.h"
 
 namespace {
@@ -47,13 +50,80 @@ qs_status check_dims(const char* fn, int32_t B, int32_t H, int32_t N, int32_t D,
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+#ifdef QS_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+// The checked build's device-input check: runs the check kernel on the call's stream, waits
+// for it and turns its report into QS_ERR_INVALID with a message naming the first bad entry.
+qs_status device_check(const char* fn, qs::CheckArgs c, hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(QS_ERR_UNSUPPORTED, "%s: the checked build waits for its check and cannot be captured", fn);
+    unsigned long long* d = nullptr;
+    e = hipMalloc(reinterpret_cast<void**>(&d), sizeof *d);
+    if (e != hipSuccess) return hip_status(e, fn);
+    unsigned long long h = ~0ull;
+    e = hipMemcpyAsync(d, &h, sizeof h, hipMemcpyHostToDevice, s);
+    c.out = d;
+    if (e == hipSuccess) e = qs::launch_check(c, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&h, d, sizeof h, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    const hipError_t ef = hipFree(d);
+    if (e == hipSuccess) e = ef;
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (h == ~0ull) return QS_OK;
+    const int b = int(h >> 43), rule = int((h >> 40) & 7u);
+    const long long pos = (long long)(h & ((1ull << 40) - 1));
+    const int32_t* src = rule == qs::kBadBlockTable ? c.bt + (size_t)b * c.mkbpr + pos
+                         : rule == qs::kBadMetaTable ? c.mt + (size_t)b * c.mmbpr + pos
+                                                     : c.seq_lens + b;
+    int32_t v = 0;
+    e = hipMemcpyAsync(&v, src, sizeof v, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, fn);
+    switch (rule) {
+        case qs::kLenPastMaxLen:
+            return fail(QS_ERR_INVALID, "%s: seq_lens[%d] = %d exceeds max_len = %d", fn, b, v, c.max_len);
+        case qs::kLenPastBlockTable:
+            return fail(QS_ERR_INVALID, "%s: seq_lens[%d] = %d needs more than max_kv_blocks_per_req = %d blocks",
+                        fn, b, v, c.mkbpr);
+        case qs::kLenPastMetaTable:
+            return fail(QS_ERR_INVALID,
+                        "%s: seq_lens[%d] = %d needs more than max_meta_blocks_per_req = %d metadata blocks", fn, b,
+                        v, c.mmbpr);
+        case qs::kBadBlockTable:
+            return fail(QS_ERR_INVALID, "%s: block_tables[%d][%lld] = %d is outside [0, num_kv_blocks = %d)", fn, b,
+                        pos, v, c.nkv);
+        default:
+            return fail(QS_ERR_INVALID,
+                        "%s: metadata_block_tables[%d][%lld] = %d is outside [0, num_meta_blocks = %d)", fn, b, pos,
+                        v, c.nmeta);
+    }
+}
+
+qs::CheckArgs check_args(int B, int BS, uint32_t rules, const int32_t* seq_lens) {
+    qs::CheckArgs c{};
+    c.B = B;
+    c.BS = BS;
+    c.rules = rules;
+    c.seq_lens = seq_lens;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* qs_last_error(void) { return g_err; }
 
-const char* qs_version(void) { return "qsparse 0.1 (gfx950)"; }
+const char* qs_version(void) { return kChecked ? "qsparse 0.1 (gfx950, checked)" : "qsparse 0.1 (gfx950)"; }
+
+int32_t qs_checked_build(void) { return kChecked ? 1 : 0; }
 
 qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size, qs_dtype kv_dtype,
                             const void* k_cache, int32_t num_kv_blocks, const int32_t* block_tables,
@@ -74,6 +144,13 @@ qs_status qs_build_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size,
     if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinBt | qs::kRuleNbWithinMt | qs::kRuleBtUsed |
+                                                        qs::kRuleMtUsed, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        c.mt = metadata_block_tables, c.mmbpr = max_meta_blocks_per_req, c.nmeta = num_meta_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     qs::MetaArgs a{B, N, D, block_size, kv_dtype != QS_F32, k_cache, num_kv_blocks, block_tables,
                    max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
                    maxblocks, minblocks, num_meta_blocks};
@@ -102,6 +179,14 @@ qs_status qs_update_metadata(int32_t B, int32_t N, int32_t D, int32_t block_size
     if ((long long)max_meta_blocks_per_req * block_size > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: max_meta_blocks_per_req * block_size overflows", fn);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinBt | qs::kRuleNbWithinMt | qs::kRuleBtUsed |
+                                                        qs::kRuleMtUsed, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        c.mt = metadata_block_tables, c.mmbpr = max_meta_blocks_per_req, c.nmeta = num_meta_blocks;
+        c.first_block = first_block, c.max_new = max_new_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     qs::MetaArgs a{B, N, D, block_size, kv_dtype != QS_F32, k_cache, num_kv_blocks, block_tables,
                    max_kv_blocks_per_req, seq_lens, metadata_block_tables, max_meta_blocks_per_req,
                    maxblocks, minblocks, num_meta_blocks};
@@ -142,6 +227,11 @@ qs_status qs_block_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     if (workspace_bytes < plan.bytes)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinMt | qs::kRuleMtUsed, seq_lens);
+        c.mt = metadata_block_tables, c.mmbpr = max_meta_blocks_per_req, c.nmeta = num_meta_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     qs::SelectArgs a{B, H, N, D, block_size, int(dtype), query, maxblocks, minblocks, num_meta_blocks,
                      metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
                      selected, n_selected, block_scores, workspace};
@@ -184,6 +274,11 @@ qs_status qs_probe_select(int32_t B, int32_t H, int32_t N, int32_t D, int32_t bl
     if (workspace_bytes < need)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinBt | qs::kRuleBtUsed, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     qs::ProbeArgs a{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, num_kv_blocks,
                     block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
                     selected, n_selected, probe_scores, workspace};
@@ -233,6 +328,12 @@ qs_status qs_sparse_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if ((long long)plan.splits * plan.hchunks > 0x7fffffffLL) return fail(QS_ERR_INVALID, "%s: grid too large", fn);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleBtSelected, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        c.sel = selected, c.nsel = n_selected, c.rows = sel_heads, c.k = k;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::AttnArgs a{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, v_cache, k_scale, v_scale,
                    num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, selected, n_selected, sel_heads, k,
@@ -285,6 +386,12 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
     if ((long long)plan.attn.splits * plan.attn.hchunks > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: grid too large", fn);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinMt | qs::kRuleMtUsed | qs::kRuleBtUsed, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        c.mt = metadata_block_tables, c.mmbpr = max_meta_blocks_per_req, c.nmeta = num_meta_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::SelectArgs sa{B, H, N, D, block_size, int(dtype), query, maxblocks, minblocks, num_meta_blocks,
                       metadata_block_tables, max_meta_blocks_per_req, seq_lens, tokens_since_update, flags, k,
@@ -337,6 +444,11 @@ qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32
     if (workspace_bytes < plan.bytes)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinBt | qs::kRuleBtUsed, seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::ProbeArgs pa{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, num_kv_blocks,
                      block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
@@ -382,6 +494,12 @@ qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int3
     if (workspace_bytes < need)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if (B == 0) return ok();
+    if (kChecked) {
+        qs::CheckArgs c = check_args(B, block_size, qs::kRuleLenWithinMax | qs::kRuleNbWithinBt | qs::kRuleBtUsed,
+                                     seq_lens);
+        c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks, c.max_len = max_len;
+        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+    }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::ImportanceArgs a{B, H, N, D, block_size, int(dtype), query, max_len, k_cache, num_kv_blocks, block_tables,
                          max_kv_blocks_per_req, seq_lens, scale, importance, importance_stride, head_importance,

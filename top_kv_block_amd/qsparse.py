@@ -4,16 +4,23 @@ Argument marshalling only: shape/dtype/device checks on torch tensors, output an
 workspace allocation, and the call on torch's current HIP stream. Every step of the
 computation runs in the library's HIP kernels; there is no fallback. Importing this
 module fails loudly if the library has not been built (python -m top_kv_block_amd.build).
+
+QSPARSE_CHECKED=1 in the environment loads the checked build instead, whose calls first
+check the device-resident tables they will use (and wait for that check);
+`checked_calls()` switches to it for a block of code.
 """
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsparse.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqsparse.so")
+_LIB_CHECKED_PATH = os.path.join(_HERE, "libqsparse_checked.so")
 
 QS_OK, QS_ERR_INVALID, QS_ERR_UNSUPPORTED, QS_ERR_HIP = 0, 1, 2, 3
 QS_F32, QS_BF16, QS_I8, QS_F16 = 0, 1, 2, 3
@@ -26,6 +33,7 @@ EXPORTS = (
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_select_attn_workspace_bytes",
     "qs_select_attn_decode", "qs_probe_attn_workspace_bytes", "qs_probe_attn_decode",
     "qs_prefill_importance_workspace_bytes", "qs_prefill_importance", "qs_last_error", "qs_version",
+    "qs_checked_build",
 )
 
 
@@ -35,11 +43,11 @@ class QsError(RuntimeError):
         self.status = status
 
 
-def _load():
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m top_kv_block_amd.build` "
+def _load(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m top_kv_block_amd.build` "
                           "(the HIP path has no fallback)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
     lib.qs_build_metadata.argtypes = [i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, P, i32, P, P, i32, P]
     lib.qs_update_metadata.argtypes = [i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, P, i32, P, i32, P, P,
@@ -73,10 +81,31 @@ def _load():
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
+    lib.qs_checked_build.restype = ctypes.c_int32
     return lib
 
 
-lib = _load()
+lib = _load(_LIB_CHECKED_PATH if os.environ.get("QSPARSE_CHECKED", "0") not in ("", "0") else _LIB_PATH)
+_checked_lib = None
+
+
+def load_checked():
+    """The checked build (loaded on first use)."""
+    global _checked_lib
+    if _checked_lib is None:
+        _checked_lib = _load(_LIB_CHECKED_PATH)
+    return _checked_lib
+
+
+@contextlib.contextmanager
+def checked_calls():
+    """Routes this module's calls through the checked build inside the block (not thread-safe)."""
+    global lib
+    saved, lib = lib, load_checked()
+    try:
+        yield lib
+    finally:
+        lib = saved
 
 
 def _check(status):
