@@ -56,8 +56,9 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attn_mfma_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMfmaLdsBytes];  // 40 KiB
-    const int split = blockIdx.x % p.splits, hcix = blockIdx.x / p.splits;
-    const int s = blockIdx.y, b = blockIdx.z;
+    const uint3 w = xcd_block_index(p.splits > 1);
+    const int split = int(w.x) % p.splits, hcix = int(w.x) / p.splits;
+    const int s = int(w.y), b = int(w.z);
     const int row = b * p.sel_heads + s;
     mfma_body<DT>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
 }

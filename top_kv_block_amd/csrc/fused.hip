@@ -111,8 +111,9 @@ template <int DT, bool PRESCORED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void select_attn_mfma_kernel(sel::SelParams sp, attn::AttnParams ap) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[attn::kMfmaLdsBytes];
-    const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
-    const int n = blockIdx.y, b = blockIdx.z;
+    const uint3 w = xcd_block_index(ap.splits > 1);
+    const int split = int(w.x) % ap.splits, hcix = int(w.x) / ap.splits;
+    const int n = int(w.y), b = int(w.z);
     const int ns = select_phase<DT, PRESCORED>(sp, b, n, lds, split == 0 && hcix == 0);
     attn::mfma_body<DT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
 }

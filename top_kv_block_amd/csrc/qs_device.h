@@ -289,4 +289,23 @@ __device__ uint32_t block_topk_threshold(int n, int R, KeyFn kf, uint32_t* hist,
     need_eq = sh[1];
     return uint32_t(sh[0]);
 }
+// Workgroup placement on the 8 XCDs. The dispatcher deals workgroups to the XCDs
+// round-robin by linear id, so the slot splits of one row (consecutive in x) land on
+// different XCDs, and each XCD re-reads the row's shared inputs (staged scores, metadata,
+// table row) into its own L2. With `grouped` and a grid size that is a multiple of 8, the
+// workgroup with linear id l instead takes work item (l mod 8)·(total/8) + l/8, so each
+// XCD takes one contiguous eighth of the work items in (x, y, z) order: whole rows with
+// all their splits. A bijection on the work items, so every item still runs exactly once.
+// Rows of one workgroup share nothing, and there the round-robin placement streams
+// faster (measured on the serving workload: 221 against 230 us), so callers group only
+// split rows. Returns the item's (x, y, z).
+constexpr int kXcds = 8;
+__device__ __forceinline__ uint3 xcd_block_index(bool grouped) {
+    const uint64_t nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+    if (!grouped || total % kXcds) return make_uint3(blockIdx.x, blockIdx.y, blockIdx.z);
+    const uint64_t lin = blockIdx.x + nx * (blockIdx.y + ny * uint64_t(blockIdx.z));
+    const uint64_t w = (lin % kXcds) * (total / kXcds) + lin / kXcds;
+    return make_uint3(unsigned(w % nx), unsigned((w / nx) % ny), unsigned(w / (nx * ny)));
+}
+
 }  // namespace qs
