@@ -16,8 +16,8 @@ import pytest
 import torch
 
 from tests.conftest import gpu_available
-from tests.test_gpu_parity import (DEV, attn_tol, bits, check_importance, check_scores, compare_probe, compare_quest,
-                                   nbs_of, oracle_meta, random_selection, run_meta, run_select, say, tnp)
+from tests.test_gpu_parity import (DEV, bits, check_attn, check_importance, check_scores, compare_probe,
+                                   compare_quest, nbs_of, oracle_meta, random_selection, run_meta, run_select, say, tnp)
 from top_kv_block_amd import workloads as W
 
 pytestmark = [pytest.mark.gpu,
@@ -89,13 +89,12 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
     compare_quest(tnp(sel), tnp(ns), osel, ons, osc, nbs, k)
 
     # attention on the oracle's selection (one row per KV head)
-    tol = attn_tol(dtype)
     osel_t, ons_t = torch.from_numpy(osel), torch.from_numpy(ons)
     out = qs.qs_sparse_attn_decode(wl.query.to(DEV), wl.k_cache.to(DEV), wl.v_cache.to(DEV),
                                    wl.block_tables.to(DEV), wl.seq_lens.to(DEV), osel_t.to(DEV), ons_t.to(DEV))
     ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, osel, ons, N)
-    err = float(np.abs(out.float().cpu().numpy() - ref).max()) if ref.size else 0.0
-    assert err <= tol, f"attention (Quest rows) err {err:.3e} > {tol}"
+    args = (wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens)
+    check_attn(out, ref, *args, osel, ons, N, "attention (Quest rows)")
 
     # attention on random per-query-head rows, with out-of-range entries
     rsel, rns = random_selection(seed, B, H, k, nbs)
@@ -103,8 +102,7 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
                                    wl.block_tables.to(DEV), wl.seq_lens.to(DEV), rsel.to(DEV), rns.to(DEV),
                                    sel_heads=H)
     ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, rsel, rns, H)
-    err = float(np.abs(out.float().cpu().numpy() - ref).max()) if ref.size else 0.0
-    assert err <= tol, f"attention (random rows) err {err:.3e} > {tol}"
+    check_attn(out, ref, *args, rsel, rns, H, "attention (random rows)")
 
     # fused selection + attention: the same selection as the selection call, bit for bit
     fsel = torch.full((B, N, k), -7, dtype=torch.int32, device=DEV)
@@ -116,8 +114,7 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
     assert torch.equal(fsel, sel) and torch.equal(fns, ns), "fused selection differs from qs_block_select"
     gsel, gns = tnp(fsel), tnp(fns)
     ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, gsel, gns, N)
-    err = float(np.abs(fout.float().cpu().numpy() - ref).max()) if ref.size else 0.0
-    assert err <= tol, f"fused attention err {err:.3e} > {tol}"
+    check_attn(fout, ref, *args, gsel, gns, N, "fused attention")
 
     # probe selection (importance on, recency when the flags' low bit is set)
     pflags = W.RECENCY if flags & 1 else 0
@@ -143,8 +140,7 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
     assert torch.equal(fps, psel) and torch.equal(fpn, pns), "fused probe selection differs from qs_probe_select"
     ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, tnp(psel),
                                     tnp(pns), H)
-    err = float(np.abs(fo.float().cpu().numpy() - ref).max()) if ref.size else 0.0
-    assert err <= tol, f"fused probe attention err {err:.3e} > {tol}"
+    check_attn(fo, ref, *args, tnp(psel), tnp(pns), H, "fused probe attention")
 
 
 IMP_DRAWS = int(os.environ.get("QS_SWEEP_IMP_DRAWS", "24"))

@@ -310,6 +310,13 @@ def serving(device="cpu", seed: int = 4, B: int = 128, nb: int = 256,
                     sel_heads=N, extra={"query_sets": qs})
 
 
+def extra_queries(wl: Workload, seed: int) -> torch.Tensor:
+    """An independent query set ~ N(0,1) for ``wl``'s requests, [B, H, D] in the query dtype,
+    drawn on the workload's device (a later decode step's queries on the same KV pools)."""
+    device = wl.query.device
+    return _normal((wl.B, wl.H, wl.D), _gen(seed, device), device).to(wl.query.dtype)
+
+
 # ----------------------------------------------------------------------------------------
 # small randomised cases for parity sweeps
 # ----------------------------------------------------------------------------------------
