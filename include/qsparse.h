@@ -305,6 +305,32 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                                 int32_t* selected, int32_t* n_selected,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * qs_select_attn_decode_static -- qs_select_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and results.
+ * Its scratch is a static device array of the library (QS_STATIC_SCRATCH_BYTES of
+ * workspace plus 256 bytes), one per GPU, held from the device's first call until the
+ * process ends; the call allocates and frees nothing (the checked build's verdict word is
+ * in that array too). Sizes whose workspace (qs_select_attn_workspace_bytes()) exceeds
+ * QS_STATIC_SCRATCH_BYTES return QS_ERR_INVALID before any HIP call. The array belongs
+ * to the current device, which must be the stream's. Every call on one GPU shares it and
+ * it keeps the last call's contents (no kernel needs it cleared): calls that may overlap
+ * on one GPU (other streams, other threads, concurrent graph replays) race and must be
+ * ordered by the caller. The device's first call looks up the array's address; make it
+ * before a graph capture.
+ */
+#define QS_STATIC_SCRATCH_BYTES (32u << 20)
+qs_status qs_select_attn_decode_static(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                                       qs_dtype dtype, const void* query,
+                                       const void* maxblocks, const void* minblocks, int32_t num_meta_blocks,
+                                       const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                                       const void* k_cache, const void* v_cache, int32_t num_kv_blocks,
+                                       const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                       const int32_t* seq_lens, const int32_t* tokens_since_update,
+                                       uint32_t flags, int32_t k, float softmax_scale, void* out,
+                                       int32_t* selected, int32_t* n_selected, void* stream);
+
 /* bytes of workspace qs_probe_attn_decode needs for these sizes (the probe keys, then the
  * attention partials; 0 for invalid sizes) */
 size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t max_kv_blocks_per_req, int32_t k);

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/qsparse.h"
 #include "qs_check.h"
 #include "qs_internal.h"
@@ -58,14 +60,15 @@ constexpr bool kChecked = false;
 
 // The checked build's device-input check: runs the check kernel on the call's stream, waits
 // for it and turns its report into QS_ERR_INVALID with a message naming the first bad entry.
-qs_status device_check(const char* fn, qs::CheckArgs c, hipStream_t s) {
+// `word` is device memory for the check's verdict; NULL allocates (and frees) one word.
+qs_status device_check(const char* fn, qs::CheckArgs c, hipStream_t s, unsigned long long* word = nullptr) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(s, &cs);
     if (e != hipSuccess) return hip_status(e, fn);
     if (cs != hipStreamCaptureStatusNone)
         return fail(QS_ERR_UNSUPPORTED, "%s: the checked build waits for its check and cannot be captured", fn);
-    unsigned long long* d = nullptr;
-    e = hipMalloc(reinterpret_cast<void**>(&d), sizeof *d);
+    unsigned long long* d = word;
+    if (!d) e = hipMalloc(reinterpret_cast<void**>(&d), sizeof *d);
     if (e != hipSuccess) return hip_status(e, fn);
     unsigned long long h = ~0ull;
     e = hipMemcpyAsync(d, &h, sizeof h, hipMemcpyHostToDevice, s);
@@ -73,7 +76,7 @@ qs_status device_check(const char* fn, qs::CheckArgs c, hipStream_t s) {
     if (e == hipSuccess) e = qs::launch_check(c, s);
     if (e == hipSuccess) e = hipMemcpyAsync(&h, d, sizeof h, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    const hipError_t ef = hipFree(d);
+    const hipError_t ef = word ? hipSuccess : hipFree(d);
     if (e == hipSuccess) e = ef;
     if (e != hipSuccess) return hip_status(e, fn);
     if (h == ~0ull) return QS_OK;
@@ -104,6 +107,35 @@ qs_status device_check(const char* fn, qs::CheckArgs c, hipStream_t s) {
                         "%s: metadata_block_tables[%d][%lld] = %d is outside [0, num_meta_blocks = %d)", fn, b, pos,
                         v, c.nmeta);
     }
+}
+
+// Scratch of qs_select_attn_decode_static: a static device array (each GPU the library runs
+// on holds its own copy until the process ends), QS_STATIC_SCRATCH_BYTES of workspace and
+// 256 bytes for the checked build's verdict word. Host code never uses the array's name
+// as an address: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchTotal = QS_STATIC_SCRATCH_BYTES + 256;
+__device__ __align__(256) uint8_t scratch[kScratchTotal];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the device's first call).
+qs_status static_scratch(const char* fn, uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(QS_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (!p) return fail(QS_ERR_HIP, "%s: no device address for the static scratch", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+    return QS_OK;
 }
 
 qs::CheckArgs check_args(int B, int BS, uint32_t rules, const int32_t* seq_lens) {
@@ -349,21 +381,27 @@ size_t qs_select_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t b
     return qs::plan_select_attn(B, H, N, block_size, max_meta_blocks_per_req, k, int(dtype)).bytes;
 }
 
-qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
-                                const void* query, const void* maxblocks, const void* minblocks,
-                                int32_t num_meta_blocks, const int32_t* metadata_block_tables,
-                                int32_t max_meta_blocks_per_req, const void* k_cache, const void* v_cache,
-                                int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
-                                const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags,
-                                int32_t k, float softmax_scale, void* out, int32_t* selected, int32_t* n_selected,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "qs_select_attn_decode";
+}  // extern "C"
+
+namespace {
+
+// qs_select_attn_decode with its workspace given (`word`: the checked build's verdict word,
+// NULL to allocate one). With static_ws the workspace is the static scratch: it is checked
+// against QS_STATIC_SCRATCH_BYTES instead of workspace_bytes and named so in messages.
+qs_status select_attn_impl(const char* fn, bool static_ws, int32_t B, int32_t H, int32_t N, int32_t D,
+                           int32_t block_size, qs_dtype dtype, const void* query, const void* maxblocks,
+                           const void* minblocks, int32_t num_meta_blocks, const int32_t* metadata_block_tables,
+                           int32_t max_meta_blocks_per_req, const void* k_cache, const void* v_cache,
+                           int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                           const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags, int32_t k,
+                           float softmax_scale, void* out, int32_t* selected, int32_t* n_selected, void* workspace,
+                           size_t workspace_bytes, void* stream, unsigned long long* word) {
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
     if (dtype != QS_F32 && dtype != QS_BF16 && dtype != QS_F16)
         return fail(QS_ERR_UNSUPPORTED, "%s: dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!query || !maxblocks || !minblocks || !metadata_block_tables || !k_cache || !v_cache || !block_tables ||
-        !seq_lens || !out || !workspace)
+        !seq_lens || !out || (!workspace && !static_ws))
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
     if ((selected == nullptr) != (n_selected == nullptr))
         return fail(QS_ERR_INVALID, "%s: selected and n_selected must both be given or both be NULL", fn);
@@ -381,16 +419,25 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
         return fail(QS_ERR_UNSUPPORTED, "%s: more than 2^24 blocks per request", fn);
     if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
     const qs::FusedPlan plan = qs::plan_select_attn(B, H, N, block_size, max_meta_blocks_per_req, k, int(dtype));
-    if (workspace_bytes < plan.bytes)
+    if (static_ws && plan.bytes > QS_STATIC_SCRATCH_BYTES)
+        return fail(QS_ERR_INVALID, "%s: these sizes need %zu bytes of scratch, the static scratch holds %zu", fn,
+                    plan.bytes, (size_t)QS_STATIC_SCRATCH_BYTES);
+    if (!static_ws && workspace_bytes < plan.bytes)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, plan.bytes);
     if ((long long)plan.attn.splits * plan.attn.hchunks > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: grid too large", fn);
     if (B == 0) return ok();
+    if (static_ws) {
+        uint8_t* base = nullptr;
+        if ((st = static_scratch(fn, &base)) != QS_OK) return st;
+        workspace = base;
+        word = reinterpret_cast<unsigned long long*>(base + QS_STATIC_SCRATCH_BYTES);
+    }
     if (kChecked) {
         qs::CheckArgs c = check_args(B, block_size, qs::kRuleNbWithinMt | qs::kRuleMtUsed | qs::kRuleBtUsed, seq_lens);
         c.bt = block_tables, c.mkbpr = max_kv_blocks_per_req, c.nkv = num_kv_blocks;
         c.mt = metadata_block_tables, c.mmbpr = max_meta_blocks_per_req, c.nmeta = num_meta_blocks;
-        if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
+        if ((st = device_check(fn, c, (hipStream_t)stream, word)) != QS_OK) return st;
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::SelectArgs sa{B, H, N, D, block_size, int(dtype), query, maxblocks, minblocks, num_meta_blocks,
@@ -400,6 +447,41 @@ qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int3
                     num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, selected, n_selected, N, k,
                     scale, out, workspace};
     return hip_status(qs::launch_select_attn(sa, aa, plan, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+qs_status qs_select_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype dtype,
+                                const void* query, const void* maxblocks, const void* minblocks,
+                                int32_t num_meta_blocks, const int32_t* metadata_block_tables,
+                                int32_t max_meta_blocks_per_req, const void* k_cache, const void* v_cache,
+                                int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags,
+                                int32_t k, float softmax_scale, void* out, int32_t* selected, int32_t* n_selected,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return select_attn_impl("qs_select_attn_decode", false, B, H, N, D, block_size, dtype, query, maxblocks,
+                            minblocks, num_meta_blocks, metadata_block_tables, max_meta_blocks_per_req, k_cache,
+                            v_cache, num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens,
+                            tokens_since_update, flags, k, softmax_scale, out, selected, n_selected, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+qs_status qs_select_attn_decode_static(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
+                                       qs_dtype dtype, const void* query, const void* maxblocks,
+                                       const void* minblocks, int32_t num_meta_blocks,
+                                       const int32_t* metadata_block_tables, int32_t max_meta_blocks_per_req,
+                                       const void* k_cache, const void* v_cache, int32_t num_kv_blocks,
+                                       const int32_t* block_tables, int32_t max_kv_blocks_per_req,
+                                       const int32_t* seq_lens, const int32_t* tokens_since_update, uint32_t flags,
+                                       int32_t k, float softmax_scale, void* out, int32_t* selected,
+                                       int32_t* n_selected, void* stream) {
+    return select_attn_impl("qs_select_attn_decode_static", true, B, H, N, D, block_size, dtype, query, maxblocks,
+                            minblocks, num_meta_blocks, metadata_block_tables, max_meta_blocks_per_req, k_cache,
+                            v_cache, num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens,
+                            tokens_since_update, flags, k, softmax_scale, out, selected, n_selected, nullptr, 0,
+                            stream, nullptr);
 }
 
 size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t max_kv_blocks_per_req, int32_t k) {

@@ -31,7 +31,7 @@ EXPORTS = (
     "qs_build_metadata", "qs_update_metadata", "qs_block_select_workspace_bytes", "qs_block_select",
     "qs_probe_select_workspace_bytes", "qs_probe_select",
     "qs_sparse_attn_workspace_bytes", "qs_sparse_attn_decode", "qs_select_attn_workspace_bytes",
-    "qs_select_attn_decode", "qs_probe_attn_workspace_bytes", "qs_probe_attn_decode",
+    "qs_select_attn_decode", "qs_select_attn_decode_static", "qs_probe_attn_workspace_bytes", "qs_probe_attn_decode",
     "qs_prefill_importance_workspace_bytes", "qs_prefill_importance", "qs_last_error", "qs_version",
     "qs_checked_build",
 )
@@ -68,6 +68,8 @@ def _load(path):
     lib.qs_select_attn_workspace_bytes.restype = sz
     lib.qs_select_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P, i32, P,
                                           i32, P, P, u32, i32, ctypes.c_float, P, P, P, P, sz, P]
+    lib.qs_select_attn_decode_static.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32, P, i32, P, P,
+                                                 i32, P, i32, P, P, u32, i32, ctypes.c_float, P, P, P, P]
     lib.qs_probe_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.qs_probe_attn_workspace_bytes.restype = sz
     lib.qs_probe_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, i32, P, i32,
@@ -77,7 +79,8 @@ def _load(path):
     lib.qs_prefill_importance.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, i32, P,
                                           ctypes.c_float, P, i32, P, P, sz, P]
     for f in ("qs_build_metadata", "qs_update_metadata", "qs_block_select", "qs_probe_select",
-              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_probe_attn_decode", "qs_prefill_importance"):
+              "qs_sparse_attn_decode", "qs_select_attn_decode", "qs_select_attn_decode_static", "qs_probe_attn_decode",
+              "qs_prefill_importance"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qs_last_error.restype = ctypes.c_char_p
     lib.qs_version.restype = ctypes.c_char_p
@@ -403,12 +406,8 @@ def select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype):
     return lib.qs_select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype)
 
 
-def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
-                          seq_lens, k, tokens_since_update=None, flags=0, softmax_scale=0.0, out=None,
-                          selected=None, n_selected=None, workspace_buf=None):
-    """Quest selection and attention over the selected blocks in one call (qs_block_select
-    then qs_sparse_attn_decode with one selection row per KV head). Returns out [B, H, D];
-    pass selected [B, N, k] / n_selected [B, N] to receive the selection too."""
+def _select_attn_args(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                      seq_lens, k, tokens_since_update, out, selected, n_selected):
     dev = _dev(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables, seq_lens,
                tokens_since_update, out, selected, n_selected)
     for n, t in (("metadata_block_tables", metadata_block_tables), ("block_tables", block_tables),
@@ -417,8 +416,6 @@ def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_
         _i32(t, n)
     B, H, D = query.shape
     nmeta, BS, N, D2 = maxblocks.shape
-    nkv = k_cache.shape[0]
-    mmbpr = metadata_block_tables.shape[1]
     _need(D2 == D and H % N == 0, "query and metadata shapes disagree")
     _need(maxblocks.shape == minblocks.shape and maxblocks.dtype == minblocks.dtype == query.dtype,
           "maxblocks/minblocks must match each other and the query dtype")
@@ -433,14 +430,53 @@ def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_
     if out is None:
         out = torch.empty((B, H, D), dtype=query.dtype, device=dev)
     _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
+    return dev, out
+
+
+def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                          seq_lens, k, tokens_since_update=None, flags=0, softmax_scale=0.0, out=None,
+                          selected=None, n_selected=None, workspace_buf=None):
+    """Quest selection and attention over the selected blocks in one call (qs_block_select
+    then qs_sparse_attn_decode with one selection row per KV head). Returns out [B, H, D];
+    pass selected [B, N, k] / n_selected [B, N] to receive the selection too."""
+    dev, out = _select_attn_args(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                                 seq_lens, k, tokens_since_update, out, selected, n_selected)
+    B, H, D = query.shape
+    nmeta, BS, N, _ = maxblocks.shape
+    mmbpr = metadata_block_tables.shape[1]
     dt = _dtype_code(query)
     nbytes = select_attn_workspace_bytes(B, H, N, BS, mmbpr, k, dt)
     ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select_attn")
     _check(lib.qs_select_attn_decode(B, H, N, D, BS, dt, _ptr(query), _ptr(maxblocks), _ptr(minblocks), nmeta,
-                                     _ptr(metadata_block_tables), mmbpr, _ptr(k_cache), _ptr(v_cache), nkv,
-                                     _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                                     _ptr(metadata_block_tables), mmbpr, _ptr(k_cache), _ptr(v_cache),
+                                     k_cache.shape[0], _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
                                      _ptr(tokens_since_update), int(flags), int(k), float(softmax_scale), _ptr(out),
                                      _ptr(selected), _ptr(n_selected), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+QS_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def qs_select_attn_decode_static(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                                 seq_lens, k, out, tokens_since_update=None, flags=0, softmax_scale=0.0,
+                                 selected=None, n_selected=None):
+    """qs_select_attn_decode on the library's static device scratch: no workspace, and the
+    call allocates nothing (``out``, and the selection outputs if wanted, are the caller's).
+    Calls on one GPU share the scratch, so overlapping calls race."""
+    _need(out is not None, "out must be given (the call allocates nothing)")
+    dev, out = _select_attn_args(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
+                                 seq_lens, k, tokens_since_update, out, selected, n_selected)
+    B, H, D = query.shape
+    nmeta, BS, N, _ = maxblocks.shape
+    with torch.cuda.device(dev):
+        _check(lib.qs_select_attn_decode_static(B, H, N, D, BS, _dtype_code(query), _ptr(query), _ptr(maxblocks),
+                                                _ptr(minblocks), nmeta, _ptr(metadata_block_tables),
+                                                metadata_block_tables.shape[1], _ptr(k_cache), _ptr(v_cache),
+                                                k_cache.shape[0], _ptr(block_tables), block_tables.shape[1],
+                                                _ptr(seq_lens), _ptr(tokens_since_update), int(flags), int(k),
+                                                float(softmax_scale), _ptr(out), _ptr(selected), _ptr(n_selected),
+                                                _stream(dev)))
     return out
 
 
