@@ -351,27 +351,51 @@ int qso_block_select(int B, int H, int N, int D, int BS, int dtype,
 /* O3: page 1's probe + importance + recency selection                                   */
 /* ------------------------------------------------------------------------------------ */
 /*
- * [P1] section 1 "知识点" and section 2 "对应代码" (sparse_attn_head), per query head h
- * with its KV head kh = h / G:
- *   probe loop: n_probe < 1 is raised to 1; for each block, p0 = block*bs, p_end =
- *     min(p0+bs, seq_len), step = (p_end-p0)/n_probe (integer division, at least 1);
- *     the block's probe score is the max over ps = p0, p0+step, ... < p_end of the
- *     (unscaled) dot q_h . K[ps][kh], starting from -1e30; with importance given, the
- *     block's importance sum adds importance[ps] over all its tokens (a float sum);
- *   importance preselect: budget (k+1)/2; repeatedly take the unused block with the
- *     largest importance sum, the lower index winning ties, until the budget or the
- *     blocks run out;
- *   top-k fill: the same greedy on probe scores until k picks or no block is left;
- *   recency insurance: if the last block is not picked, it replaces the lowest-scoring
- *     probe-chosen block; importance picks are never replaced.
- * readings: with no probe-chosen block recency does nothing; among equal lowest probe
- *   scores the later greedy pick (higher index) is replaced; importance is indexed
- *   importance[b * imp_stride + token] and tokens at or past imp_stride add nothing;
- *   output ascending, -1 padded.
+ * [P1] section 1 "知识点" (the two signals and the insurance) and section 2 "对应代码"
+ * (sparse_attn_head), stated as sets and rankings. Per query head h (KV head kh = h / G):
+ *
+ *   probe offsets of block i, with nt = min(BS, L - i*BS) valid tokens: the stride is
+ *     floor(nt / n_probe), at least 1, and the offsets are 0, stride, 2*stride, ... below
+ *     nt (so a short last block can take more than n_probe offsets; n_probe < 1 counts
+ *     as 1). The probe score is the largest unscaled dot q_h . K[i*BS + offset][kh] over
+ *     that (never empty) set;
+ *   importance sum of block i: the prefill importance of its tokens added in token order
+ *     in float (a running fp32 sum, which the path reproduces bit for bit);
+ *   ranking: blocks ordered by value, higher first, the lower index first among equal
+ *     values (section 1: ties go to the lower index);
+ *   importance picks (only with importance): the first ceil(k / 2) = (k + 1) / 2 blocks
+ *     of the ranking by importance sum (fewer if the request has fewer blocks);
+ *   probe picks: the first k - (importance picks) blocks, among those not yet picked, of
+ *     the ranking by probe score;
+ *   recency (QS_RECENCY): if the last block nb-1 is not picked and there is a probe pick,
+ *     the probe pick that ranks last (lowest probe score; of equal ones the higher index)
+ *     gives its place to nb-1; importance picks are never given up.
+ *
+ * readings: no threshold in the importance stage (page 1 elides a line there), so blocks
+ *   of zero importance can fill the budget; importance is read as importance[b * stride +
+ *   token] and tokens at or past the stride add nothing; output ascending, -1 padded.
  * Outputs besides the selection (all optional): probe [B, H, mkbpr] (double),
  *   imp_sum [B, mkbpr] (float), n_imp [B, H], kind [B, H, mkbpr] (int8: 0 not picked,
- *   1 importance pick, 2 probe pick, 3 added by recency, 4 probe pick evicted by recency).
+ *   1 importance pick, 2 probe pick, 3 added by recency, 4 probe pick given up for it).
  */
+
+/* the probe score of one block: the largest dot over its probe offsets */
+static double probe_score(const void* query, int q_dtype, size_t q_off, const void* k_cache, int kv_dtype,
+                          size_t first_token_off, size_t token_pitch, int32_t nt, int n_probe, int D) {
+    const int32_t stride = (nt / n_probe) > 1 ? (nt / n_probe) : 1;
+    double top = 0.0;
+    int have = 0;
+    for (int32_t off = 0; off < nt; off += stride) {
+        double dot = 0.0;
+        const size_t kb = first_token_off + (size_t)off * token_pitch;
+        for (int d = 0; d < D; ++d)
+            dot += (double)elem_f(query, q_dtype, q_off + d) * (double)elem_f(k_cache, kv_dtype, kb + d);
+        if (!have || dot > top) top = dot;
+        have = 1;
+    }
+    return top;
+}
+
 int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dtype,
                      const void* query, const void* k_cache, int num_kv_blocks,
                      const int32_t* block_tables, int mkbpr,
@@ -384,13 +408,14 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
         return QSO_BAD;
     if (N <= 0 || H % N != 0 || k < 1) return QSO_BAD;
     const int G = H / N;
-    const size_t row = (size_t)N * D;
+    const size_t pitch = (size_t)N * D;                 /* elements between tokens of one KV head */
     const int cap = mkbpr > 0 ? mkbpr : 1;
+    const int np = n_probe < 1 ? 1 : n_probe;
     double* probe = (double*)malloc(sizeof(double) * (size_t)cap);
     float* imp = (float*)malloc(sizeof(float) * (size_t)cap);
-    char* used = (char*)malloc((size_t)cap);
-    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(cap > k ? cap : k));
-    if (n_probe < 1) n_probe = 1;
+    scored_t* rank = (scored_t*)malloc(sizeof(scored_t) * (size_t)cap);
+    int8_t* role = (int8_t*)malloc((size_t)cap);        /* this head's kind of each block */
+    int32_t* picks = (int32_t*)malloc(sizeof(int32_t) * (size_t)cap);
     int rc = QSO_OK;
     for (int b = 0; b < B && rc == QSO_OK; ++b) {
         const int32_t L = seq_lens[b];
@@ -401,91 +426,62 @@ int qso_probe_select(int B, int H, int N, int D, int BS, int q_dtype, int kv_dty
             if (phys < 0 || phys >= num_kv_blocks) { rc = QSO_BAD; break; }
         }
         if (rc != QSO_OK) break;
-        /* importance sums are per request (every head reads the same record) */
+        /* per-request importance sums (every head of the request reads the same ones) */
         for (int32_t i = 0; i < nb; ++i) {
-            const int32_t p0 = i * BS;
-            int32_t pe = p0 + BS;
-            if (pe > L) pe = L;
-            float s = 0.0f;
-            if (importance)
-                for (int32_t ps = p0; ps < pe && ps < imp_stride; ++ps) s += importance[(size_t)b * imp_stride + ps];
-            imp[i] = s;
-            if (imp_out) imp_out[(size_t)b * mkbpr + i] = s;
+            const int32_t nt = (L - i * BS) < BS ? (L - i * BS) : BS;
+            float sum = 0.0f;
+            for (int32_t t = i * BS; importance && t < i * BS + nt && t < imp_stride; ++t)
+                sum += importance[(size_t)b * imp_stride + t];
+            imp[i] = sum;
+            if (imp_out) imp_out[(size_t)b * mkbpr + i] = sum;
         }
         for (int h = 0; h < H; ++h) {
             const int kh = h / G;
-            /* probe loop */
             for (int32_t i = 0; i < nb; ++i) {
-                const int32_t p0 = i * BS;
-                int32_t pe = p0 + BS;
-                if (pe > L) pe = L;
-                int32_t step = (pe - p0) / n_probe;
-                if (step < 1) step = 1;
-                double best = -1e30;
-                for (int32_t ps = p0; ps < pe; ps += step) {
-                    const int32_t phys = block_tables[(size_t)b * mkbpr + ps / BS];
-                    const size_t kb = ((size_t)phys * BS + (size_t)(ps % BS)) * row + (size_t)kh * D;
-                    const size_t qb = ((size_t)b * H + h) * D;
-                    double dot = 0.0;
-                    for (int d = 0; d < D; ++d)
-                        dot += (double)elem_f(query, q_dtype, qb + d) * (double)elem_f(k_cache, kv_dtype, kb + d);
-                    if (dot > best) best = dot;
-                }
-                probe[i] = best;
-                if (probe_out) probe_out[((size_t)b * H + h) * mkbpr + i] = best;
+                const int32_t nt = (L - i * BS) < BS ? (L - i * BS) : BS;
+                const size_t first = (size_t)block_tables[(size_t)b * mkbpr + i] * BS * pitch + (size_t)kh * D;
+                probe[i] = probe_score(query, q_dtype, ((size_t)b * H + h) * D, k_cache, kv_dtype, first, pitch, nt,
+                                       np, D);
+                if (probe_out) probe_out[((size_t)b * H + h) * mkbpr + i] = probe[i];
             }
-            /* importance preselect */
-            memset(used, 0, (size_t)cap);
-            int n_sel = 0;
+            for (int32_t i = 0; i < cap; ++i) role[i] = 0;
+            int n_imp = 0, n_pick = 0;
+            /* importance picks: a prefix of the importance ranking */
             if (importance) {
+                for (int32_t i = 0; i < nb; ++i) { rank[i].v = (double)imp[i]; rank[i].i = i; }
+                qsort(rank, (size_t)nb, sizeof(scored_t), cmp_desc_then_index);
                 const int budget = (k + 1) / 2;
-                while (n_sel < budget && n_sel < nb) {
-                    int32_t best = -1;
-                    for (int32_t j = 0; j < nb; ++j) {
-                        if (used[j]) continue;
-                        if (best < 0 || imp[j] > imp[best] || (imp[j] == imp[best] && j < best)) best = j;
-                    }
-                    sel[n_sel++] = best;
-                    used[best] = 1;
-                }
+                for (int32_t r = 0; r < nb && n_imp < budget; ++r) { role[rank[r].i] = 1; picks[n_pick++] = rank[r].i; ++n_imp; }
             }
-            const int n_imp = n_sel;
-            /* top-k fill by probe score */
-            while (n_sel < k && n_sel < nb) {
-                int32_t best = -1;
-                for (int32_t j = 0; j < nb; ++j) {
-                    if (used[j]) continue;
-                    if (best < 0 || probe[j] > probe[best] || (probe[j] == probe[best] && j < best)) best = j;
-                }
-                sel[n_sel++] = best;
-                used[best] = 1;
+            /* probe picks: a prefix of the probe ranking of the remaining blocks */
+            int nr = 0;
+            for (int32_t i = 0; i < nb; ++i)
+                if (!role[i]) { rank[nr].v = probe[i]; rank[nr].i = i; ++nr; }
+            qsort(rank, (size_t)nr, sizeof(scored_t), cmp_desc_then_index);
+            int n_probe_picks = 0;
+            for (int r = 0; r < nr && n_pick < k; ++r) { role[rank[r].i] = 2; picks[n_pick++] = rank[r].i; ++n_probe_picks; }
+            /* recency: the last-ranked probe pick gives its place to the last block */
+            if ((flags & QSO_RECENCY) && nb > 0 && role[nb - 1] == 0 && n_probe_picks > 0) {
+                const int32_t victim = rank[n_probe_picks - 1].i;
+                role[victim] = 4;
+                role[nb - 1] = 3;
+                for (int j = 0; j < n_pick; ++j)
+                    if (picks[j] == victim) picks[j] = nb - 1;
             }
-            int8_t* kind = kind_out ? kind_out + ((size_t)b * H + h) * mkbpr : NULL;
-            if (kind) {
-                for (int32_t i = 0; i < mkbpr; ++i) kind[i] = 0;
-                for (int s = 0; s < n_sel; ++s) kind[sel[s]] = (int8_t)(s < n_imp ? 1 : 2);
+            if (kind_out) {
+                int8_t* kind = kind_out + ((size_t)b * H + h) * mkbpr;
+                for (int32_t i = 0; i < mkbpr; ++i) kind[i] = i < cap ? role[i] : 0;
             }
-            /* recency insurance */
-            if ((flags & QSO_RECENCY) && nb > 0 && !used[nb - 1] && n_sel > n_imp) {
-                int victim = n_imp;
-                for (int s = n_imp + 1; s < n_sel; ++s) {
-                    const int32_t a = sel[s], c = sel[victim];
-                    if (probe[a] < probe[c] || (probe[a] == probe[c] && a > c)) victim = s;
-                }
-                used[sel[victim]] = 0;
-                if (kind) { kind[sel[victim]] = 4; kind[nb - 1] = 3; }
-                sel[victim] = nb - 1;
-                used[nb - 1] = 1;
-            }
-            write_sorted(selected + ((size_t)b * H + h) * (size_t)k, k, sel, n_sel);
-            n_selected[(size_t)b * H + h] = n_sel;
+            write_sorted(selected + ((size_t)b * H + h) * (size_t)k, k, picks, n_pick);
+            n_selected[(size_t)b * H + h] = n_pick;
             if (n_imp_out) n_imp_out[(size_t)b * H + h] = n_imp;
         }
     }
     free(probe);
     free(imp);
-    free(used);
-    free(sel);
+    free(rank);
+    free(role);
+    free(picks);
     return rc;
 }
 
