@@ -1134,6 +1134,51 @@ def test_two_streams_run_concurrently(qs):
         assert torch.equal(o.view(torch.int32), want_b.view(torch.int32))
 
 
+def test_graphs_of_one_operation_replay_concurrently(qs):
+    """Two graphs of the same operation captured on torch's default capture stream, with no
+    workspace passed (each captured call gets scratch of its own from its graph's pool),
+    replayed at the same time on two streams, several times over: each replay gives bitwise
+    its own eager result."""
+    say("two graphs of one operation replayed concurrently")
+    was = []
+    for seed in (63, 64):
+        wl = W.random_case(seed, 4, 32, 8, 64, [64 * 150 + 3, 64 * 90, 64 * 200 + 17, 64 * 40], k=12,
+                           dtype=torch.bfloat16, flags=W.FORCE_SINK | W.FORCE_WINDOW, tsmu=[3, 0, 5, 1]).to(DEV)
+        mx, mn = run_meta(qs, wl, sentinel=0.0)
+        out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.bfloat16, device=DEV)
+        was.append((wl, mx, mn, out))
+
+    def call(i):
+        wl, mx, mn, out = was[i]
+        qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                 wl.seq_lens, wl.k, tokens_since_update=wl.tsmu, flags=wl.flags, out=out)
+
+    want = []
+    for i in range(2):
+        call(i)
+        torch.cuda.synchronize()
+        want.append(was[i][3].clone())
+    graphs = []
+    for i in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(4):
+        for i in range(2):
+            was[i][3].fill_(5.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            graphs[0].replay()
+        with torch.cuda.stream(sb):
+            graphs[1].replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(was[i][3].view(torch.int16), want[i].view(torch.int16)), (rep, i)
+
+
 def test_workspace_cache_grows_twofold(qs):
     """The binding's cached workspace of one (device, stream, operation) is reused while it
     suffices and grows at least twofold when it does not, so the replaced buffers it keeps
@@ -1157,10 +1202,10 @@ def test_workspace_cache_grows_twofold(qs):
 def test_graph_replay_probe_path(qs):
     """Page 1's path captured in a HIP graph: a metadata refresh, the prefill importance, the
     probe selection and fp32 attention with one selection row per query head, and the fused
-    probe selection + attention call beside them. No workspace is
-    passed, so every call takes the binding's cached workspace of the capture stream. Three
-    replays, with the same eager calls (on another stream's workspaces) between them, give
-    bitwise the eager results."""
+    probe selection + attention call beside them. No workspace is passed, so every captured
+    call takes a workspace of its own from the graph's memory pool. Three replays, with the
+    same eager calls (on the binding's cached workspaces) between them, give bitwise the
+    eager results."""
     say("graph replay, probe path")
     wl = W.random_case(62, 2, 16, 8, 32, [32 * 60 + 5, 32 * 33], k=12, dtype=torch.float32, with_v=True)
     pq = W.prefill_queries(wl, 62).to(DEV)

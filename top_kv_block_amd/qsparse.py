@@ -181,9 +181,16 @@ def workspace(nbytes, device, op):
     scratch memory (calls on one stream are ordered). A workspace that is replaced by a
     larger one stays allocated: a HIP graph captured with it keeps a valid address. It
     grows at least twofold each time, so what stays allocated is under twice the largest
-    workspace of each (device, stream, operation)."""
+    workspace of each (device, stream, operation).
+
+    Under stream capture every call gets a workspace of its own instead, allocated from the
+    graph's private memory pool, which the graph keeps until it is destroyed: graphs
+    captured on one stream (torch captures on a shared side stream by default) then never
+    share scratch memory, so they may be replayed concurrently on different streams."""
     dev = torch.device(device)
     index = dev.index if dev.index is not None else torch.cuda.current_device()
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
     key = (index, torch.cuda.current_stream(index).cuda_stream, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
