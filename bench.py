@@ -142,6 +142,98 @@ def run_cpu_baseline(wl, qsets, tsmu_tab, n_req, min_seconds):
                       f"scaled by {wl.B}/{len(reqs)}; single-threaded C oracle (fp64)"}
 
 
+def host_info():
+    """The host the CPU baseline runs on: CPU model, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def _oracle_ms(fn, min_seconds):
+    """Average ms of fn() over repeated calls totalling at least min_seconds (one warm call)."""
+    fn()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            return el * 1e3 / n
+
+
+def cpu_baseline_rows(W, dev, min_seconds=0.5):
+    """The oracle, single-threaded, on each of the other configurations (ms per step of the
+    whole configuration; samples scaled as stated). Metadata the oracle's selection reads is
+    built by the oracle beforehand and not counted, except where the build is the row."""
+    from oracle import oracle as O
+    rows = {}
+    # the tiny fp32 workload, whole: Quest select + attention
+    wl = W.tiny_needle()
+    mx, mn = O.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, wl.num_meta_blocks)
+
+    def tiny():
+        sel, ns, _ = O.block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k)
+        O.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns, wl.N)
+    rows[wl.name] = {"ms_per_step": round(_oracle_ms(tiny, min_seconds), 3), "sample": "whole workload"}
+
+    # page-3-shaped select (bf16): 4 of its 20 requests (same shapes, drawn on the host), scaled by 5
+    wl = W.page3_select(device="cpu", B=4)
+    t_build = _oracle_ms(lambda: O.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables,
+                                                  wl.num_meta_blocks), min_seconds)
+    mx, mn = O.build_metadata(wl.k_cache, wl.block_tables, wl.seq_lens, wl.meta_tables, wl.num_meta_blocks)
+    t_sel = _oracle_ms(lambda: O.block_select(wl.query, mx, mn, wl.meta_tables, wl.seq_lens, wl.k), min_seconds)
+    rows["page3_select_b20_l16384_bf16"] = {"select_ms": round(t_sel * 5, 3), "metadata_build_ms": round(t_build * 5, 3),
+                                            "sample": "4 of 20 requests, scaled by 5"}
+
+    # page-1 probe selection + fp32 / int8 attention, k = 1 .. 32, whole workload
+    wl = W.page1_probe()
+    sweep = {}
+    for kk in (1, 2, 4, 8, 16, 32):
+        o = O.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, kk, wl.N, importance=wl.importance,
+                           n_probe=8, flags=O.RECENCY)
+
+        def step(int8, kk=kk):
+            r = O.probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, kk, wl.N,
+                               importance=wl.importance, n_probe=8, flags=O.RECENCY)
+            if int8:
+                O.sparse_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, r["selected"],
+                                     r["n_selected"], wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale)
+            else:
+                O.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, r["selected"],
+                                     r["n_selected"], wl.H)
+        sweep[f"k{kk}"] = {"step_fp32_ms": round(_oracle_ms(lambda: step(False), min_seconds / 2), 3),
+                           "step_int8_ms": round(_oracle_ms(lambda: step(True), min_seconds / 2), 3),
+                           "selected_per_head": int(o["n_selected"][0, 0])}
+    rows["page1_probe_b1_h16_l4096_k_sweep"] = {"by_k": sweep, "sample": "whole workload"}
+
+    # long-context decode: 2 of its 8 requests (gathered from the GPU-drawn pools), scaled by 4
+    wl = W.long_context(device=dev)
+    g = gather_requests(wl, [0, 1])
+    q = wl.query.cpu()[[0, 1]]
+    ts = wl.tsmu.cpu()[[0, 1]]
+    del wl
+    torch.cuda.empty_cache()
+    mx, mn = O.build_metadata(g["kc"], g["bt"], g["msl"], g["mt"], g["nmeta"])
+
+    def lc():
+        sel, ns, _ = O.block_select(q, mx, mn, g["mt"], g["sl"], 64, tsmu=ts, flags=3)
+        O.sparse_attn_decode(q, g["kc"], g["vc"], g["bt"], g["sl"], sel, ns, 8)
+    rows["long_context_b8_l8k_128k_bf16"] = {"ms_per_step": round(_oracle_ms(lc, min_seconds) * 4, 3),
+                                             "sample": f"requests 0 and 1 (lengths {g['sl'].tolist()}), scaled by 4"}
+    return rows
+
+
 def _timed(fn, reps, stream):
     """Average ms of fn() over reps back-to-back calls on the stream (after one warm call)."""
     fn()
@@ -153,6 +245,30 @@ def _timed(fn, reps, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def _graph_us(fn, reps, stream):
+    """Average us of fn() replayed from one captured HIP graph of ``reps`` calls (the GPU
+    time of the call without the host's launch and marshalling cost)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for _ in range(reps):
+                fn()
+    stream.wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (3 * reps)
 
 
 def other_workloads(qs, W, dev, stream, reps=50):
@@ -179,9 +295,13 @@ def other_workloads(qs, W, dev, stream, reps=50):
     out1 = torch.empty_like(wl.query)
     t_fused = _timed(lambda: qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
                                                       wl.block_tables, wl.seq_lens, wl.k, out=out1), reps, stream)
+    g_fused = _graph_us(lambda: qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
+                                                         wl.block_tables, wl.seq_lens, wl.k, out=out1), reps, stream)
     res[wl.name] = {"select_us": round(t_sel * 1e3, 2), "attention_us": round(t_att * 1e3, 2),
-                                "step_us": round((t_sel + t_att) * 1e3, 2),
-                                "fused_step_us": round(t_fused * 1e3, 2), "note": "latency-bound (0.33 MB a step)"}
+                    "step_us": round((t_sel + t_att) * 1e3, 2),
+                    "fused_step_us": round(t_fused * 1e3, 2), "fused_step_graph_us": round(g_fused, 2),
+                    "note": "latency-bound (0.33 MB a step); *_graph_us: the call replayed from a HIP graph "
+                            "(GPU time without host launch cost)"}
     del wl, mx, mn
 
     # page-3-shaped Quest select, bf16 and fp16 (the page's metadata example is
@@ -207,41 +327,49 @@ def other_workloads(qs, W, dev, stream, reps=50):
                         "metadata_build_gbps": gbps(build_bytes, t_build)}
         del wl, mx, mn
 
-    # page-1 probe selection + fp32 / int8 attention at k = 32
+    # page-1 probe selection + fp32 / int8 attention, k = 1 .. 32
     wl = W.page1_probe().to(dev)
-    psel, pns = qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
-                                   importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY)
-    t_probe = _timed(lambda: qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32,
-                                                importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY,
-                                                selected=psel, n_selected=pns), reps, stream)
-    t_f32 = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
-                                                    psel, pns, sel_heads=wl.H), reps, stream)
-    t_i8 = _timed(lambda: qs.qs_sparse_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, psel,
-                                                   pns, sel_heads=wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale),
-                  reps, stream)
-    pout = torch.empty_like(wl.query)
+    sweep = {}
+    for kk in (1, 2, 4, 8, 16, 32):
+        psel, pns = qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, kk,
+                                       importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY)
+        pout = torch.empty_like(wl.query)
 
-    def two_calls():
-        qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, 32, importance=wl.importance,
-                           n_probe=8, flags=qs.QS_RECENCY, selected=psel, n_selected=pns)
-        qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, psel, pns,
-                                 sel_heads=wl.H, out=pout)
-    t_two = _timed(two_calls, reps, stream)
-    t_fused = _timed(lambda: qs.qs_probe_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
-                                                     32, importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY,
-                                                     out=pout), reps, stream)
+        def probe():
+            qs.qs_probe_select(wl.query, wl.k_cache, wl.block_tables, wl.seq_lens, kk, importance=wl.importance,
+                               n_probe=8, flags=qs.QS_RECENCY, selected=psel, n_selected=pns)
+
+        def att(int8):
+            if int8:
+                qs.qs_sparse_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, psel, pns,
+                                         sel_heads=wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale, out=pout)
+            else:
+                qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, psel, pns,
+                                         sel_heads=wl.H, out=pout)
+
+        def fused(int8):
+            if int8:
+                qs.qs_probe_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, kk,
+                                        importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY, out=pout,
+                                        probe_k=wl.k_cache, k_scale=wl.k_scale, v_scale=wl.v_scale)
+            else:
+                qs.qs_probe_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, kk,
+                                        importance=wl.importance, n_probe=8, flags=qs.QS_RECENCY, out=pout)
+
+        row = {"probe_select_us": round(_timed(probe, reps, stream) * 1e3, 2)}
+        for int8, tag in ((False, "fp32"), (True, "int8")):
+            row[f"attention_{tag}_us"] = round(_timed(lambda: att(int8), reps, stream) * 1e3, 2)
+            row[f"step_{tag}_us"] = round(_timed(lambda: (probe(), att(int8)), reps, stream) * 1e3, 2)
+            row[f"fused_step_{tag}_us"] = round(_timed(lambda: fused(int8), reps, stream) * 1e3, 2)
+            row[f"fused_step_{tag}_graph_us"] = round(_graph_us(lambda: fused(int8), reps, stream), 2)
+        sweep[f"k{kk}"] = row
     probe_bytes = wl.N * 128 * 8 * wl.D * 4 + 4096 * 4 + wl.H * wl.D * 4
-    res["page1_probe_b1_h16_l4096_k32"] = {"probe_select_us": round(t_probe * 1e3, 2),
-                                   "probe_select_gbps": gbps(probe_bytes, t_probe),
-                                   "attention_fp32_us": round(t_f32 * 1e3, 2),
-                                   "attention_int8_us": round(t_i8 * 1e3, 2),
-                                   "step_fp32_us": round(t_two * 1e3, 2),
-                                   "fused_step_fp32_us": round(t_fused * 1e3, 2),
-                                   "step_int8_us": round((t_probe + t_i8) * 1e3, 2),
-                                   "note": "latency-bound (a few MB a step); step_fp32_us times qs_probe_select + "
-                                           "qs_sparse_attn_decode back to back, fused_step_fp32_us one "
-                                           "qs_probe_attn_decode call, step_int8_us is the sum of the two calls' "
-                                           "times (the fused call takes float KV only)"}
+    k32 = sweep["k32"]
+    res["page1_probe_b1_h16_l4096_k_sweep"] = {
+        "by_k": sweep, "probe_select_gbps_k32": gbps(probe_bytes, k32["probe_select_us"] * 1e-3),
+        "note": "latency-bound (a few MB a step); step_*_us: qs_probe_select + qs_sparse_attn_decode back to back; "
+                "fused_step_*_us: one qs_probe_attn_decode call (int8: probe on the float K, attention on the "
+                "int8 copy); *_graph_us: replayed from a HIP graph (GPU time without host launch cost)"}
     del wl
 
     # the prefill that produces the probe workload's importance: two causal QK^T passes on the matrix
@@ -252,11 +380,16 @@ def other_workloads(qs, W, dev, stream, reps=50):
     t_imp = _timed(lambda: qs.qs_prefill_importance(pq, wl.k_cache, wl.block_tables, wl.seq_lens, importance=imp),
                    10, stream)
     L = int(wl.seq_lens.max())
-    flops = 2 * wl.H * L * (L + 1) * wl.D
+    method_flops = wl.H * L * (L + 1) * wl.D          # one causal Q K^T: H * L(L+1)/2 dots of 2D flops
+    done_flops = 2 * method_flops                     # the kernels evaluate it twice (row pass, column pass)
     res["page1_prefill_importance_b1_h16_l4096_fp32"] = {
-        "us": round(t_imp * 1e3, 2), "tflops": round(flops / (t_imp * 1e-3) / 1e12, 2),
-        "mfma_fp32_peak_tflops": 157.3, "frac": round(flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),
-        "note": "B=1, L=4096, H=16, N=8; row pass + column pass + head reduction"}
+        "us": round(t_imp * 1e3, 2), "method_gflop": round(method_flops / 1e9, 2),
+        "tflops": round(method_flops / (t_imp * 1e-3) / 1e12, 2),
+        "mfma_fp32_peak_tflops": 157.3, "frac": round(method_flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),
+        "executed_tflops": round(done_flops / (t_imp * 1e-3) / 1e12, 2),
+        "executed_frac": round(done_flops / (t_imp * 1e-3) / 1e12 / 157.3, 4),
+        "note": "B=1, L=4096, H=16, N=8; frac counts the method's own work (one causal QK^T); executed_* counts "
+                "both passes (the second recomputes QK^T instead of storing the score matrix)"}
     del wl, pq, imp
 
     # long-context paged decode, bf16 (rows split over workgroups + combine)
@@ -580,11 +713,15 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_cpu_baseline(wl, qsets, tsmu_tab, args.cpu_sample, args.cpu_seconds)
+        result["host"] = host_info()
     if not args.no_other_workloads:
         del wl, qsets, mx, mn
         torch.cuda.empty_cache()
         log("timing the other workloads")
         result["other_workloads"] = other_workloads(qs, W, dev, stream)
+        if not args.no_cpu_baseline:
+            log("cpu baseline of the other workloads")
+            result["cpu_baseline_workloads"] = cpu_baseline_rows(W, dev)
     print(json.dumps(result), flush=True)
 
 

@@ -338,15 +338,21 @@ size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t ma
 /*
  * qs_probe_attn_decode -- page 1's probe selection and exact attention over it, in one
  * call. [P1] section 2 (sparse_attn_head): the selection of each query head feeds that
- * head's attention loop directly. The result is defined as qs_probe_select (same
- * arguments) followed by qs_sparse_attn_decode with sel_heads = H and the same k: the
- * selection is bitwise the one qs_probe_select returns, the output matches the two calls
- * within the attention's rounding (the pick is recomputed by each slot split of a row;
- * it is deterministic, so every split sees the same selection).
+ * head's attention loop directly, over a float KV cache or a q8 one (int8 x int8 dot plus
+ * the scales). The result is defined as qs_probe_select (on the float K the probes read)
+ * followed by qs_sparse_attn_decode with sel_heads = H and the same k: the selection is
+ * bitwise the one qs_probe_select returns, the output matches the two calls within the
+ * attention's rounding (the pick is recomputed by each slot split of a row; it is
+ * deterministic, so every split sees the same selection).
  *
  *   query          [B, H, D], q_dtype QS_F32, QS_BF16 or QS_F16; out [B, H, D] in q_dtype
- *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16 or QS_F16 (the
- *                  probe scores read K; an int8 cache takes the two calls)
+ *   k_cache/v_cache[num_kv_blocks, BS, N, D], kv_dtype QS_F32, QS_BF16, QS_F16 or QS_I8
+ *   k_scale/v_scale[num_kv_blocks, BS, N] fp32 per-row scales: required for QS_I8, NULL
+ *                  otherwise
+ *   probe_k_cache  the float K the probe scores read, [num_kv_blocks, BS, N, D] in
+ *                  probe_k_dtype (QS_F32, QS_BF16 or QS_F16), paged like k_cache: required
+ *                  for QS_I8 (the same call as qs_probe_select on it); NULL for a float
+ *                  cache, whose k_cache the probes read (probe_k_dtype is then ignored)
  *   block_tables   [B, max_kv_blocks_per_req] int32 (max_kv_blocks_per_req <= 4096);
  *                  seq_lens [B] int32
  *   importance, importance_stride, n_probe, flags   as for qs_probe_select
@@ -356,12 +362,14 @@ size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t ma
  *                  or both NULL
  *   workspace      device scratch of at least qs_probe_attn_workspace_bytes(), 256-byte
  *                  aligned, contents ignored
- * Attention runs on the vector ALU in fp32 for every dtype pair. An empty selection
- * writes zeros.
+ * Attention runs on the vector ALU in fp32 for every dtype pair (QS_I8: the query is
+ * quantised per head as in qs_sparse_attn_decode). An empty selection writes zeros.
  */
 qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size,
                                qs_dtype q_dtype, qs_dtype kv_dtype,
                                const void* query, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const void* probe_k_cache, qs_dtype probe_k_dtype,
                                int32_t num_kv_blocks, const int32_t* block_tables,
                                int32_t max_kv_blocks_per_req, const int32_t* seq_lens,
                                const float* importance, int32_t importance_stride,

@@ -217,18 +217,23 @@ def test_select_attn_workspace_size(qs):
 
 
 def _pattn(qs, **kw):
-    a = dict(B=0, H=16, N=8, D=128, BS=32, qd=qs.QS_F32, kd=qs.QS_F32, q=FAKE, kc=FAKE, vc=FAKE, nkv=128, bt=FAKE,
-             mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32, flags=qs.QS_RECENCY, scale=0.0, out=FAKE, sel=None,
-             nsel=None, ws=WS, wsb=1 << 30)
+    a = dict(B=0, H=16, N=8, D=128, BS=32, qd=qs.QS_F32, kd=qs.QS_F32, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None,
+             pk=None, pkd=qs.QS_F32, nkv=128, bt=FAKE, mkbpr=128, sl=FAKE, imp=None, stride=0, npb=8, k=32,
+             flags=qs.QS_RECENCY, scale=0.0, out=FAKE, sel=None, nsel=None, ws=WS, wsb=1 << 30)
     a.update(kw)
     return qs.lib.qs_probe_attn_decode(a["B"], a["H"], a["N"], a["D"], a["BS"], a["qd"], a["kd"], a["q"], a["kc"],
-                                       a["vc"], a["nkv"], a["bt"], a["mkbpr"], a["sl"], a["imp"], a["stride"],
-                                       a["npb"], a["k"], a["flags"], a["scale"], a["out"], a["sel"], a["nsel"],
-                                       a["ws"], a["wsb"], None)
+                                       a["vc"], a["ks"], a["vs"], a["pk"], a["pkd"], a["nkv"], a["bt"], a["mkbpr"],
+                                       a["sl"], a["imp"], a["stride"], a["npb"], a["k"], a["flags"], a["scale"],
+                                       a["out"], a["sel"], a["nsel"], a["ws"], a["wsb"], None)
+
+
+Q8 = dict(kd=2, ks=FAKE, vs=FAKE, pk=FAKE)            # a valid int8-cache argument set
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(kd=2), 2), (dict(qd=2), 2), (dict(k=0), 1), (dict(k=4097), 1), (dict(flags=1), 1), (dict(mkbpr=5000), 2),
+    (dict(kd=2), 1), (dict(Q8, ks=None), 1), (dict(Q8, vs=None), 1), (dict(Q8, pk=None), 1),
+    (dict(Q8, pkd=2), 2), (dict(Q8, pk=ctypes.c_void_p((1 << 20) + 8)), 1), (dict(ks=FAKE), 1), (dict(pk=FAKE), 1),
+    (dict(qd=2), 2), (dict(k=0), 1), (dict(k=4097), 1), (dict(flags=1), 1), (dict(mkbpr=5000), 2),
     (dict(imp=FAKE, stride=0), 1), (dict(vc=None), 1), (dict(out=None), 1), (dict(sel=FAKE), 1),
     (dict(nsel=FAKE), 1), (dict(H=12), 1), (dict(BS=8), 2), (dict(D=96), 2), (dict(ws=None), 1),
     (dict(ws=ctypes.c_void_p((1 << 20) + 64)), 1), (dict(wsb=16), 1), (dict(scale=float("nan")), 1),
@@ -247,6 +252,7 @@ def test_probe_attn_workspace_size(qs):
     assert qs.probe_attn_workspace_bytes(64, 32, 8, 100, 8) == 64 * 32 * 100 * 4
     assert qs.probe_attn_workspace_bytes(1, 12, 8, 128, 32) == 0
     assert _pattn(qs, wsb=qs.probe_attn_workspace_bytes(0, 16, 8, 128, 32)) == 0
+    assert _pattn(qs, **Q8) == 0                     # an int8 cache with its scales and probe K is accepted
 
 
 def _imp(qs, **kw):

@@ -49,3 +49,5 @@ def test_bench_json_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == "steps/s"
     assert isinstance(cb["sample"], str) and cb["sample"]
+    host = d["host"]
+    assert host["nproc"] >= 1 and "cpu_model" in host

@@ -1349,6 +1349,52 @@ def test_probe_attn_matches_probe_select_and_oracle(qs, oracle, case):
                        out.view(torch.int16 if dtype != torch.float32 else torch.int32))
 
 
+PROBE_ATTN_I8_CASES = [
+    # seed, B, H, N, BS, lens, k, query dtype, probe K dtype, importance, flags, n_probe
+    (411, 2, 16, 8, 32, [32 * 128, 32 * 3 + 1], 32, torch.float32, torch.float32, True, W.RECENCY, 8),  # page-1 shape
+    (412, 3, 8, 2, 16, [500, 0, 33], 5, torch.float32, torch.float32, False, W.RECENCY, 3),          # empty request
+    (413, 2, 6, 3, 64, [1000, 64], 40, torch.bfloat16, torch.bfloat16, True, 0, 8),                  # k > nb, bf16
+    (414, 64, 32, 8, 16, [16 * 40 + 3] * 64, 4, torch.float32, torch.float32, True, W.RECENCY, 8),  # no slot splits
+    (415, 2, 16, 8, 32, [32 * 200 + 5, 32 * 7], 9, torch.float16, torch.float32, True, W.RECENCY, 8),  # mixed types
+]
+
+
+@pytest.mark.parametrize("case", PROBE_ATTN_I8_CASES, ids=lambda c: f"seed{c[0]}")
+def test_probe_attn_int8_matches_two_calls_and_oracle(qs, oracle, case):
+    """The fused probe call over an int8 KV cache: the probes read the float K, the attention
+    the int8 copy with its scales. The selection is bitwise qs_probe_select's on the float K;
+    the output matches qs_sparse_attn_decode over the int8 cache on that selection and the
+    oracle's int8 attention (fp32 query: within 2e-5, i.e. the int32 dots and the query
+    quantiser bit for bit in effect; 16-bit query: the output dtype's tolerance)."""
+    seed, B, H, N, BS, lens, k, qd, pkd, use_imp, flags, n_probe = case
+    say(f"probe+attn int8 seed={seed} B={B} H={H} N={N} BS={BS} k={k} q={qd} probe K={pkd}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=k, dtype=torch.float32, with_importance=use_imp, int8=True)
+    q = wl.query.to(qd)
+    pk = wl.k_cache.to(pkd)
+    imp = wl.importance.to(DEV) if use_imp else None
+    d = lambda t: t.to(DEV)
+    sel, ns = qs.qs_probe_select(d(q), d(pk), d(wl.block_tables), d(wl.seq_lens), k, importance=imp,
+                                 n_probe=n_probe, flags=flags)
+    two = qs.qs_sparse_attn_decode(d(q), d(wl.k_i8), d(wl.v_i8), d(wl.block_tables), d(wl.seq_lens), sel, ns,
+                                   sel_heads=H, k_scale=d(wl.k_scale), v_scale=d(wl.v_scale))
+    fsel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+    fns = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    out = qs.qs_probe_attn_decode(d(q), d(wl.k_i8), d(wl.v_i8), d(wl.block_tables), d(wl.seq_lens), k,
+                                  importance=imp, n_probe=n_probe, flags=flags, selected=fsel, n_selected=fns,
+                                  k_scale=d(wl.k_scale), v_scale=d(wl.v_scale), probe_k=d(pk))
+    torch.cuda.synchronize()
+    assert torch.equal(fsel, sel) and torch.equal(fns, ns), "fused selection differs from qs_probe_select"
+    o = oracle.probe_select(q, pk, wl.block_tables, wl.seq_lens, k, N,
+                            importance=wl.importance if use_imp else None, n_probe=n_probe, flags=flags)
+    compare_probe(tnp(fsel), tnp(fns), o, nbs_of(wl), k)
+    ref = oracle.sparse_attn_decode(q, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, tnp(fsel), tnp(fns), H,
+                                    k_scale=wl.k_scale, v_scale=wl.v_scale)
+    tol = 2e-5 if qd == torch.float32 else attn_tol(qd)
+    for what, got in (("fused", out), ("two calls", two)):
+        err = float(np.abs(got.float().cpu().numpy() - ref).max()) if ref.size else 0.0
+        assert err <= tol, f"{what}: int8 attention err {err:.3e} > {tol}"
+
+
 def test_probe_decode_loop(qs, oracle):
     """Page 1's decode path over growing lengths: per step one more token per request and the
     fused probe selection + attention (prefill importance over the prompt only, so the new
@@ -1388,10 +1434,25 @@ def test_probe_decode_loop(qs, oracle):
 
 def test_probe_attn_page1_k_sweep(qs, oracle):
     """Page 1's probe workload (fp32, 16 heads, 128 blocks of 32, importance, recency) for
-    k = 1 .. 32: fused selection bitwise the two calls', output within 1e-4 of the oracle."""
+    k = 1 .. 32: fused selection bitwise the two calls', output within 1e-4 of the oracle;
+    and the same over the workload's int8 copy (probes on the fp32 K), within 2e-5 of the
+    oracle's int8 attention."""
     wl = W.page1_probe()
     q, kc, vc, bt, sl, imp = (t.to(DEV) for t in (wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
                                                    wl.importance))
+    k8, v8, ks, vs = (t.to(DEV) for t in (wl.k_i8, wl.v_i8, wl.k_scale, wl.v_scale))
+    for k in (1, 2, 4, 8, 16, 32):
+        say(f"probe+attn int8, page-1 workload, k={k}")
+        sel, ns = qs.qs_probe_select(q, kc, bt, sl, k, importance=imp, n_probe=8, flags=W.RECENCY)
+        fsel, fns = torch.empty_like(sel), torch.empty_like(ns)
+        out = qs.qs_probe_attn_decode(q, k8, v8, bt, sl, k, importance=imp, n_probe=8, flags=W.RECENCY,
+                                      selected=fsel, n_selected=fns, k_scale=ks, v_scale=vs, probe_k=kc)
+        torch.cuda.synchronize()
+        assert torch.equal(fsel, sel) and torch.equal(fns, ns)
+        ref = oracle.sparse_attn_decode(wl.query, wl.k_i8, wl.v_i8, wl.block_tables, wl.seq_lens, tnp(sel), tnp(ns),
+                                        wl.H, k_scale=wl.k_scale, v_scale=wl.v_scale)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= 2e-5, f"int8 k={k}: err {err:.3e}"
     for k in (1, 2, 4, 8, 16, 32):
         say(f"probe+attn, page-1 workload, k={k}")
         sel, ns = qs.qs_probe_select(q, kc, bt, sl, k, importance=imp, n_probe=8, flags=W.RECENCY)

@@ -142,6 +142,20 @@ def test_random_shapes_all_entry_points(qs, oracle, seed):
                                     tnp(pns), H)
     check_attn(fo, ref, *args, tnp(psel), tnp(pns), H, "fused probe attention")
 
+    # the same over an int8 copy of the cache (probes on the float K), for fp32 draws
+    if dtype == torch.float32:
+        k8, ks = W.quantize_rows_int8(wl.k_cache)
+        v8, vs = W.quantize_rows_int8(wl.v_cache)
+        fo8 = qs.qs_probe_attn_decode(wl.query.to(DEV), k8.to(DEV), v8.to(DEV), wl.block_tables.to(DEV),
+                                      wl.seq_lens.to(DEV), k, importance=wl.importance.to(DEV), n_probe=c["n_probe"],
+                                      flags=pflags, selected=fps, n_selected=fpn, k_scale=ks.to(DEV),
+                                      v_scale=vs.to(DEV), probe_k=wl.k_cache.to(DEV))
+        assert torch.equal(fps, psel) and torch.equal(fpn, pns), "int8 fused probe selection differs"
+        ref = oracle.sparse_attn_decode(wl.query, k8, v8, wl.block_tables, wl.seq_lens, tnp(psel), tnp(pns), H,
+                                        k_scale=ks, v_scale=vs)
+        check_attn(fo8, ref, wl.query, k8, v8, wl.block_tables, wl.seq_lens, tnp(psel), tnp(pns), H,
+                   "int8 fused probe attention", tol=2e-5)
+
 
 IMP_DRAWS = int(os.environ.get("QS_SWEEP_IMP_DRAWS", "24"))
 

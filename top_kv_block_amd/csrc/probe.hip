@@ -173,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void probe_pick_kernel(
 
 // Fused: grid (slot split, query head, request). Each workgroup picks its row into LDS,
 // split 0 publishes the selection when the caller asked for it, then the vector-ALU
-// attention body attends over the split's slots of the selection; its merge buffer
+// attention body attends over the split's slots of the selection (a float cache, or the
+// int8 copy with its scales while the probes read the float K); its merge buffer
 // overlays the probe keys, dead after the pick.
 struct PickParams {
     const uint32_t* keys;
@@ -257,8 +258,8 @@ hipError_t launch_probe_attn(const ProbeArgs& a, const AttnArgs& t, const AttnPl
     uint32_t* keys = (uint32_t*)ws;
     launch_scores(a, keys, s);
     PickParams pp{keys, a.mkbpr, a.importance, a.imp_stride, a.flags, a.selected, a.n_selected};
-    attn::AttnParams prm{(const uint8_t*)t.query, (const uint8_t*)t.k_cache, (const uint8_t*)t.v_cache, nullptr,
-                         nullptr, t.num_kv_blocks, t.block_tables, t.mkbpr, t.seq_lens, nullptr, nullptr, t.H, t.N,
+    attn::AttnParams prm{(const uint8_t*)t.query, (const uint8_t*)t.k_cache, (const uint8_t*)t.v_cache, t.k_scale,
+                         t.v_scale, t.num_kv_blocks, t.block_tables, t.mkbpr, t.seq_lens, nullptr, nullptr, t.H, t.N,
                          t.BS, t.H, t.k, 1, 1, pl.splits, pl.spb, t.scale * attn::kLog2e, (uint8_t*)t.out,
                          (float*)(ws + pl.part_off)};
     const dim3 grid(unsigned(pl.splits), unsigned(t.H), unsigned(t.B));
@@ -270,6 +271,7 @@ hipError_t launch_probe_attn(const ProbeArgs& a, const AttnArgs& t, const AttnPl
     };
     if (t.kv_dtype == kBF16) by_q(std::integral_constant<int, kBF16>{});
     else if (t.kv_dtype == kF16) by_q(std::integral_constant<int, kF16>{});
+    else if (t.kv_dtype == kI8) by_q(std::integral_constant<int, kI8>{});
     else by_q(std::integral_constant<int, kF32>{});
     if (pl.splits > 1) return attn::launch_combine(prm, t.B, 1, t.q_dtype, s);
     return hipGetLastError();

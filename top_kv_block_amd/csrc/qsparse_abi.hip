@@ -491,6 +491,8 @@ size_t qs_probe_attn_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t ma
 
 qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32_t block_size, qs_dtype q_dtype,
                                qs_dtype kv_dtype, const void* query, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale, const void* probe_k_cache,
+                               qs_dtype probe_k_dtype,
                                int32_t num_kv_blocks, const int32_t* block_tables, int32_t max_kv_blocks_per_req,
                                const int32_t* seq_lens, const float* importance, int32_t importance_stride,
                                int32_t n_probe, int32_t k, uint32_t flags, float softmax_scale, void* out,
@@ -500,15 +502,23 @@ qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32
     qs_status st = check_dims(fn, B, H, N, D, block_size);
     if (st != QS_OK) return st;
     if (H > kMaxGrid) return fail(QS_ERR_INVALID, "%s: H=%d exceeds %d", fn, H, kMaxGrid);
+    const bool q8 = kv_dtype == QS_I8;
     if ((q_dtype != QS_F32 && q_dtype != QS_BF16 && q_dtype != QS_F16) ||
-        (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16))
-        return fail(QS_ERR_UNSUPPORTED, "%s: query and KV must be QS_F32, QS_BF16 or QS_F16", fn);
+        (kv_dtype != QS_F32 && kv_dtype != QS_BF16 && kv_dtype != QS_F16 && !q8))
+        return fail(QS_ERR_UNSUPPORTED, "%s: query must be QS_F32, QS_BF16 or QS_F16 and KV one of those or QS_I8",
+                    fn);
+    if (q8 && probe_k_dtype != QS_F32 && probe_k_dtype != QS_BF16 && probe_k_dtype != QS_F16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: probe_k_dtype must be QS_F32, QS_BF16 or QS_F16", fn);
     if (!query || !k_cache || !v_cache || !block_tables || !seq_lens || !out || !workspace)
         return fail(QS_ERR_INVALID, "%s: null pointer argument", fn);
+    if (q8 && (!k_scale || !v_scale || !probe_k_cache))
+        return fail(QS_ERR_INVALID, "%s: an int8 cache needs k_scale, v_scale and probe_k_cache", fn);
+    if (!q8 && (k_scale || v_scale || probe_k_cache))
+        return fail(QS_ERR_INVALID, "%s: k_scale, v_scale and probe_k_cache are for an int8 cache only", fn);
     if ((selected == nullptr) != (n_selected == nullptr))
         return fail(QS_ERR_INVALID, "%s: selected and n_selected must be given together", fn);
-    if (!aligned16(k_cache) || !aligned16(v_cache))
-        return fail(QS_ERR_INVALID, "%s: k_cache and v_cache must be 16-byte aligned", fn);
+    if (!aligned16(k_cache) || !aligned16(v_cache) || (q8 && !aligned16(probe_k_cache)))
+        return fail(QS_ERR_INVALID, "%s: k_cache, v_cache and probe_k_cache must be 16-byte aligned", fn);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(QS_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
     if (flags & ~(uint32_t)QS_RECENCY) return fail(QS_ERR_INVALID, "%s: flags may only hold QS_RECENCY", fn);
@@ -532,10 +542,10 @@ qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32
         if ((st = device_check(fn, c, (hipStream_t)stream)) != QS_OK) return st;
     }
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
-    qs::ProbeArgs pa{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, num_kv_blocks,
-                     block_tables, max_kv_blocks_per_req, seq_lens, importance, importance_stride, n_probe, k, flags,
-                     selected, n_selected, nullptr, workspace};
-    qs::AttnArgs ta{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, v_cache, nullptr, nullptr,
+    qs::ProbeArgs pa{B, H, N, D, block_size, int(q_dtype), int(q8 ? probe_k_dtype : kv_dtype), query,
+                     q8 ? probe_k_cache : k_cache, num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens,
+                     importance, importance_stride, n_probe, k, flags, selected, n_selected, nullptr, workspace};
+    qs::AttnArgs ta{B, H, N, D, block_size, int(q_dtype), int(kv_dtype), query, k_cache, v_cache, k_scale, v_scale,
                     num_kv_blocks, block_tables, max_kv_blocks_per_req, seq_lens, nullptr, nullptr, H, k, scale, out,
                     workspace};
     return hip_status(qs::launch_probe_attn(pa, ta, plan, (hipStream_t)stream), fn);

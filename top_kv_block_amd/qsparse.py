@@ -72,8 +72,9 @@ def _load(path):
                                                  i32, P, i32, P, P, u32, i32, ctypes.c_float, P, P, P, P]
     lib.qs_probe_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.qs_probe_attn_workspace_bytes.restype = sz
-    lib.qs_probe_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, i32, P, i32,
-                                         P, P, i32, i32, i32, u32, ctypes.c_float, P, P, P, P, sz, P]
+    lib.qs_probe_attn_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
+                                         ctypes.c_int, i32, P, i32, P, P, i32, i32, i32, u32, ctypes.c_float, P, P, P,
+                                         P, sz, P]
     lib.qs_prefill_importance_workspace_bytes.argtypes = [i32, i32, i32]
     lib.qs_prefill_importance_workspace_bytes.restype = sz
     lib.qs_prefill_importance.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32, P, i32, P,
@@ -372,11 +373,14 @@ def probe_attn_workspace_bytes(B, H, N, mkbpr, k):
 
 def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
                          flags=QS_RECENCY, softmax_scale=0.0, out=None, selected=None, n_selected=None,
-                         workspace_buf=None):
+                         workspace_buf=None, k_scale=None, v_scale=None, probe_k=None):
     """Page 1's probe selection and attention over it in one call (qs_probe_select then
     qs_sparse_attn_decode with one selection row per query head). Returns out [B, H, D] in
-    the query dtype; selected [B, H, k] / n_selected [B, H] receive the selection if given."""
-    dev = _dev(query, k_cache, v_cache, block_tables, seq_lens, importance, out, selected, n_selected)
+    the query dtype; selected [B, H, k] / n_selected [B, H] receive the selection if given.
+    An int8 cache takes its scales (k_scale, v_scale [num_kv_blocks, BS, N] fp32) and the
+    float K the probes read (probe_k, paged like k_cache)."""
+    dev = _dev(query, k_cache, v_cache, block_tables, seq_lens, importance, out, selected, n_selected, k_scale,
+               v_scale, probe_k)
     _i32(block_tables, "block_tables")
     _i32(seq_lens, "seq_lens")
     if importance is not None and importance.dtype != torch.float32:
@@ -387,6 +391,16 @@ def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, imp
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("v_cache must match k_cache")
     _need(D2 == D and H % N == 0, "query and KV shapes disagree")
+    q8 = k_cache.dtype == torch.int8
+    if q8:
+        _need(k_scale is not None and v_scale is not None and probe_k is not None,
+              "an int8 cache needs k_scale, v_scale and probe_k")
+        _need(k_scale.dtype == v_scale.dtype == torch.float32 and k_scale.shape == v_scale.shape == (nkv, BS, N),
+              "k_scale / v_scale must be fp32 [num_kv_blocks, BS, N]")
+        _need(probe_k.shape == k_cache.shape and probe_k.dtype != torch.int8, "probe_k must be a float copy of K")
+    else:
+        _need(k_scale is None and v_scale is None and probe_k is None,
+              "k_scale, v_scale and probe_k are for an int8 cache only")
     _rows(block_tables, B, "block_tables")
     _rows(seq_lens, B, "seq_lens")
     _rows(importance, B, "importance")
@@ -402,8 +416,9 @@ def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, imp
     nbytes = probe_attn_workspace_bytes(B, H, N, mkbpr, k)
     ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe_attn")
     _check(lib.qs_probe_attn_decode(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
-                                    _ptr(k_cache), _ptr(v_cache), nkv, _ptr(block_tables), mkbpr, _ptr(seq_lens),
-                                    _ptr(importance), stride, int(n_probe), int(k), int(flags),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(probe_k),
+                                    _dtype_code(probe_k) if q8 else QS_F32, nkv, _ptr(block_tables), mkbpr,
+                                    _ptr(seq_lens), _ptr(importance), stride, int(n_probe), int(k), int(flags),
                                     float(softmax_scale), _ptr(out), _ptr(selected), _ptr(n_selected), _ptr(ws),
                                     ws.numel(), _stream(dev)))
     return out
