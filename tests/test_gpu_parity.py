@@ -764,6 +764,40 @@ def test_select_attn_random(qs, oracle, case):
     assert np.array_equal(tnp(s2), gsel) and np.array_equal(tnp(n2), gns)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_select_attn_prescored_rows_with_exact_ties(qs, oracle, dtype):
+    """Long rows selected per wave after the scoring grid (rows of 300-700 blocks): many
+    blocks hold identical keys (copies of four blocks), so the k-th score is tied across
+    many blocks and the lower indices must win. The fused selection is bitwise
+    qs_block_select's and equals the oracle's exactly (ties broken by index); outputs
+    match the oracle's attention."""
+    lens = [64 * 500 + 3, 64 * 300, 64 * 700, 64 * 2 + 5]
+    say(f"select+attention, prescored rows with exact ties, {dtype}")
+    wl = W.random_case(85, 4, 32, 8, 64, lens, k=64, dtype=dtype, flags=W.FORCE_SINK | W.FORCE_WINDOW,
+                       tsmu=[7, 0, 63, 1])
+    wl.meta_seq_lens = wl.seq_lens - wl.tsmu
+    src = wl.block_tables[0, :4].long()
+    for b in range(3):
+        nb = cdiv(lens[b], 64)
+        for i in range(1, nb - 1):
+            if i % 3:                                     # two of every three blocks copy one of four
+                wl.k_cache[int(wl.block_tables[b, i])] = wl.k_cache[int(src[i % 4])]
+    mx, mn = run_meta(qs, wl, sentinel=0.0)
+    out, sel, ns = run_fused(qs, wl, mx, mn)
+    s2, n2, _ = run_select(qs, wl, mx, mn, scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, s2) and torch.equal(ns, n2)
+    omx, omn = oracle_meta(oracle, wl, sentinel=0.0)
+    osel, ons, osc = oracle.block_select(wl.query, omx, omn, wl.meta_tables, wl.seq_lens, wl.k, tsmu=wl.tsmu,
+                                         flags=wl.flags)
+    gsel, gns = tnp(sel), tnp(ns)
+    compare_quest(gsel, gns, osel, ons, osc, nbs_of(wl), wl.k)
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, gsel, gns,
+                                    wl.N)
+    check_attn(out, ref, wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, gsel, gns, wl.N,
+               "prescored rows with ties")
+
+
 def test_select_attn_tiny(qs, oracle):
     wl = W.tiny_needle()
     say("select+attention, tiny workload")
