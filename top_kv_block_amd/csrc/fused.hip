@@ -60,7 +60,7 @@ static_assert(kFusedMaxCap <= sel::kLdsScoreCap, "scores stay on chip");
 // entries are at lds + kOffSel. With PRESCORED the row's scores come from the scoring
 // grid's output (p.ws_scores) instead of being computed here. Split 0 of head chunk 0
 // also writes the selection to the caller's selected / n_selected when those are given.
-template <int DT, bool PRESCORED>
+template <int DT, bool PRESCORED, int KPL>
 __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int n, uint8_t* lds, bool publish) {
     float* scores = (float*)(lds + kOffScores);
     uint32_t* hist = (uint32_t*)(lds + kOffHist);
@@ -72,6 +72,7 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     int32_t* nsel = (int32_t*)(lds + kOffNsel);
     const int cap = p.mmbpr * p.BS;
     const sel::RowInfo r = sel::row_info(p.sl, p.tsmu, p.flags, p.k, b, p.BS, cap);
+    for (int j = threadIdx.x; j < 256; j += kThreads) hist[j] = 0u;  // ordered by the barrier below
     if constexpr (PRESCORED) {
         // the whole workspace row (cap <= kFusedMaxCap entries) into LDS, all loads of a
         // thread in flight together and issued without waiting for the row length; entries
@@ -95,9 +96,11 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
                                    0, r.nb, cap, scores, false, qstage, mt_stage);
     }
     __syncthreads();
-    sel::topk_emit(scores, r.nb, r.F, p.k, selv, nsel, hist, sh, wsum);
+    // the query stage is dead: it holds the waves' boundary lists (256 keys each)
+    const int c = sel::topk_dispatch<KPL>(scores, r.nb, cap, r.F, p.k, selv, nsel, hist,
+                                     reinterpret_cast<uint32_t*>(qstage) + (threadIdx.x / kWave) * 256, sh, wsum);
     __syncthreads();
-    const int ns = *nsel;
+    const int ns = c >= 0 ? c : *nsel;
     if (publish && p.selected) {
         int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
         for (int j = threadIdx.x; j < p.k; j += kThreads) out[j] = selv[j];
@@ -106,15 +109,16 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
     return ns;
 }
 
-// bf16 / f16: grid (splits x head chunks, KV head, request)
-template <int DT, bool PRESCORED>
+// bf16 / f16: grid (splits x head chunks, KV head, request); KPL: the top-k variant for
+// the row capacity (sel::topk_kpl)
+template <int DT, bool PRESCORED, int KPL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void select_attn_mfma_kernel(sel::SelParams sp, attn::AttnParams ap) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[attn::kMfmaLdsBytes];
     const uint3 w = xcd_block_index(ap.splits > 1);
     const int split = int(w.x) % ap.splits, hcix = int(w.x) / ap.splits;
     const int n = int(w.y), b = int(w.z);
-    const int ns = select_phase<DT, PRESCORED>(sp, b, n, lds, split == 0 && hcix == 0);
+    const int ns = select_phase<DT, PRESCORED, KPL>(sp, b, n, lds, split == 0 && hcix == 0);
     attn::mfma_body<DT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
 }
 
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void select_attn_vec_kernel(sel::SelParam
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
     const int split = blockIdx.x % ap.splits, hcix = blockIdx.x / ap.splits;
     const int n = blockIdx.y, b = blockIdx.z;
-    const int ns = select_phase<kF32, PRESCORED>(sp, b, n, lds, split == 0 && hcix == 0);
+    const int ns = select_phase<kF32, PRESCORED, 0>(sp, b, n, lds, split == 0 && hcix == 0);
     attn::vec_body<kF32, kF32, HC>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns,
                                    (float*)(lds + kOffScores));
 }
@@ -207,13 +211,20 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
                          a.BS, a.N, a.k, ap.hpr, ap.hchunks, ap.splits, ap.spb, a.scale * attn::kLog2e,
                          (uint8_t*)a.out, (float*)(ws + ap.part_off)};
     dim3 grid(unsigned(ap.splits * ap.hchunks), unsigned(a.N), unsigned(a.B));
+    const int kpl = sel::topk_kpl(s.mmbpr * s.BS);
     auto launch = [&](auto pre_c) {
         constexpr bool P = decltype(pre_c)::value;
         if (ap.mfma) {
-            if (a.q_dtype == kF16)
-                hipLaunchKernelGGL((select_attn_mfma_kernel<kF16, P>), grid, dim3(kThreads), 0, st, sp, prm);
-            else
-                hipLaunchKernelGGL((select_attn_mfma_kernel<kBF16, P>), grid, dim3(kThreads), 0, st, sp, prm);
+            auto by_kpl = [&](auto dt) {
+                constexpr int DT = decltype(dt)::value;
+                switch (kpl) {
+                    case 2: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 2>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                    case 4: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 4>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                    default: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, -1>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                }
+            };
+            if (a.q_dtype == kF16) by_kpl(std::integral_constant<int, kF16>{});
+            else by_kpl(std::integral_constant<int, kBF16>{});
         } else {
             switch (ap.hc) {
                 case 1: hipLaunchKernelGGL((select_attn_vec_kernel<1, P>), grid, dim3(kThreads), 0, st, sp, prm); break;

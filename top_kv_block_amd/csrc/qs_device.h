@@ -130,6 +130,28 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// max / min of a uint32 over the 64 lanes of a wave (every lane active), in every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, uint32_t(dpp_i<kDppXor1>(int(v))));
+    v = max(v, uint32_t(dpp_i<kDppXor2>(int(v))));
+    v = max(v, uint32_t(dpp_i<kDppHalfMirror>(int(v))));
+    v = max(v, uint32_t(dpp_i<kDppMirror>(int(v))));
+    uint32_t r = 0u;
+#pragma unroll
+    for (int row = 0; row < kWave; row += 16) r = max(r, uint32_t(__builtin_amdgcn_readlane(int(v), row)));
+    return r;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, uint32_t(dpp_i<kDppXor1>(int(v))));
+    v = min(v, uint32_t(dpp_i<kDppXor2>(int(v))));
+    v = min(v, uint32_t(dpp_i<kDppHalfMirror>(int(v))));
+    v = min(v, uint32_t(dpp_i<kDppMirror>(int(v))));
+    uint32_t r = 0xffffffffu;
+#pragma unroll
+    for (int row = 0; row < kWave; row += 16) r = min(r, uint32_t(__builtin_amdgcn_readlane(int(v), row)));
+    return r;
+}
+
 // Exclusive prefix sum of a per-thread count over the workgroup in thread order; `total`
 // receives the sum. wsum: kWaves ints of LDS. Two barriers.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {

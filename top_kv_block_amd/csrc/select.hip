@@ -18,10 +18,13 @@
 //              workspace, then a second kernel selects per row -- used for few, long rows.
 // The top-k is exact. On an order-preserving integer image of the scores, one 256-bin
 // histogram over the row's key range finds the bin holding the k-th best key, and the
-// keys of that bin alone are ranked to give the k-th best value T (an 8-bit radix
+// keys of that bin alone are searched to give the k-th best value T (an 8-bit radix
 // select takes over when the bin is crowded); then one ordered pass keeps every block
 // above T and the lowest-index blocks equal to T ("higher score first, lower index on
-// ties"). Output is written in ascending block order.
+// ties"). Output is written in ascending block order. Rows of up to 256 blocks run it
+// with one workgroup barrier (the histogram), every wave finishing the selection on its
+// own from keys held in registers (sel::topk_waves); longer rows use the workgroup form
+// (sel::topk_emit), cheaper there when many waves of a CU select at once.
 #include <math.h>
 
 #include <type_traits>
@@ -57,13 +60,17 @@ __global__ __launch_bounds__(kThreads) void select_row_kernel(SelParams p) {
     int32_t* out = p.selected + (size_t(b) * p.N + n) * p.k;
     int32_t* n_out = p.n_selected + size_t(b) * p.N + n;
     if (cap <= kLdsScoreCap) {  // scores on chip (LDS accesses resolved at compile time)
+        for (int j = threadIdx.x; j < 256; j += kThreads) hist[j] = 0u;  // ordered by score_range's barrier
         score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
                                   0, r.nb, cap, lds_scores, false, qstage, mt_stage);
         __syncthreads();
         if (p.dbg_scores)
             for (int i = threadIdx.x; i < r.nb; i += kThreads)
                 gscores[i] = r.F.has(i) ? __builtin_nanf("") : lds_scores[i];
-        topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
+        // the query stage is dead: it holds the waves' boundary lists (256 keys each)
+        const int ns = topk_dispatch(lds_scores, r.nb, cap, r.F, p.k, out, n_out, hist,
+                                     reinterpret_cast<uint32_t*>(qstage) + wave_id() * 256, sh, wsum);
+        if (ns >= 0 && threadIdx.x == 0) *n_out = ns;
     } else {
         score_range<DT, MT_LDS>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
                                   0, r.nb, cap, gscores, p.dbg_scores != nullptr, qstage, mt_stage);
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelParams p) {
             }
         }
         __syncthreads();
-        topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
+        topk_emit(lds_scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);  // split mode: rows beyond 256 blocks
     } else {
         topk_emit(scores, r.nb, r.F, p.k, out, n_out, hist, sh, wsum);
     }

@@ -270,6 +270,185 @@ __device__ __forceinline__ void topk_emit(const float* scores, int nb, const For
     if (tid == 0) *n_out = min(npick, k);
 }
 
+// Lanes of this wave below the calling lane whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
+
+// The same selection as topk_emit, for rows of at most 64 * KPL blocks whose scores are
+// in LDS, with a single workgroup barrier. Every wave computes the whole selection on its
+// own and writes it, ascending and -1 padded to k, to its `out` (a wave passing null
+// writes nothing); every wave returns the count. Lane l holds the keys of blocks l,
+// l + 64, ... in registers (forced blocks and blocks past the row hold 0; keys of scores
+// are never 0). Steps: the wave finds the candidates' key range [kmin, kmax]; the
+// workgroup histograms the keys into 256 bins of that range (wave w adds rounds
+// w, w + 4, ..., so every key once), the barrier; each wave finds the bin holding the
+// R-th largest key, gathers that bin's m keys (m <= 256, else the workgroup radix
+// select) into its own list in LDS (wlist, 256 entries per wave), and finds the R-th
+// largest key T by a binary search over the bin's low bits, each step counting the
+// list's keys >= a trial value with ballots; finally, 64 blocks a round in ascending
+// order, it takes forced blocks and keys above T, and keys equal to T while the quota
+// lasts (lower blocks first), ballots giving each pick its output position.
+// `hist` (512 uint32 of LDS) must be zeroed, and the scores written, before a barrier
+// that precedes the call. Every thread of the workgroup must call it.
+template <int KPL>
+__device__ __forceinline__ int topk_waves(const float* scores, int nb, const Forced& F, int k, int32_t* out,
+                                          uint32_t* hist, uint32_t* wlist, int* sh) {
+    const int lane = lane_id(), wv = wave_id();
+    const int R = max(0, min(k, nb) - F.count);  // fill picks
+    const int nc = nb - F.count;                   // fill candidates
+    uint32_t key[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int i = kWave * j + lane;
+        key[j] = (i < nb && !F.has(i)) ? f2key(scores[i]) : 0u;
+    }
+    uint32_t T = 0xffffffffu;  // taken for sure: keys above T
+    int need_eq = 0;           // and this many keys equal to T
+    if (R > 0 && R < nc) {
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (key[j]) { kmin = min(kmin, key[j]); kmax = max(kmax, key[j]); }
+        kmin = wave_min_u32(kmin);
+        kmax = wave_max_u32(kmax);
+        int shift = 0;
+        if (kmin != kmax) {
+            shift = max(0, (32 - __clz(kmax - kmin)) - 8);  // (key - kmin) >> shift is in [0, 255]
+#pragma unroll
+            for (int j = 0; j < KPL; ++j)
+                if (j % kWaves == wv && key[j]) atomicAdd(&hist[(key[j] - kmin) >> shift], 1u);
+        }
+        __syncthreads();
+        if (kmin == kmax) {  // every candidate has the same key
+            T = kmin;
+            need_eq = R;
+        } else {
+            // the bin holding the R-th largest key: lane l owns bins 255-4l .. 252-4l
+            uint32_t c[4], s4 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; s4 += c[j]; }
+            const uint32_t incl = wave_incl_scan(s4);
+            uint32_t run = incl - s4;
+            int bin = -1, above = 0;
+            if (run < uint32_t(R) && uint32_t(R) <= incl) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (bin < 0 && run + c[j] >= uint32_t(R)) { bin = 255 - 4 * lane - j; above = int(run); }
+                    run += c[j];
+                }
+            }
+            const uint64_t owner = __ballot(bin >= 0);
+            const int src = __ffsll((unsigned long long)owner) - 1;
+            const uint32_t bs = uint32_t(__builtin_amdgcn_readlane(bin, src));
+            const int need = R - __builtin_amdgcn_readlane(above, src);  // 1 <= need <= the bin's count
+            const int m = int(hist[bs]);
+            if (m > 256) {
+                // crowded boundary bin: the workgroup radix select (m is the same in every
+                // wave, so every wave gets here; the barrier lets all finish reading hist)
+                __syncthreads();
+                auto kf = [&](int i, uint32_t& kk) -> bool {
+                    if (F.has(i)) return false;
+                    kk = f2key(scores[i]);
+                    return true;
+                };
+                T = block_radix_select(nb, R, kf, hist, sh, need_eq);
+            } else {
+                // the bin's keys into this wave's list (their order does not matter)
+                int base = 0;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    const bool in = key[j] && ((key[j] - kmin) >> shift) == bs;
+                    const uint64_t mk = __ballot(in);
+                    if (in) wlist[base + lanes_below(mk)] = key[j];
+                    base += __popcll(mk);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                uint32_t lk[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) lk[q] = lane + kWave * q < m ? wlist[lane + kWave * q] : 0u;
+                // the largest offset o in the bin with at least `need` of its keys >= lo + o
+                const uint32_t lo = kmin + (bs << shift);
+                const int nq = (m + kWave - 1) / kWave;
+                uint32_t o = 0;
+                for (int bit = shift - 1; bit >= 0; --bit) {
+                    const uint32_t cand = lo + (o | (1u << bit));
+                    int cnt = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (q < nq) cnt += __popcll(__ballot(lk[q] >= cand));
+                    if (cnt >= need) o |= 1u << bit;
+                }
+                T = lo + o;
+                int gt = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (q < nq) gt += __popcll(__ballot(lk[q] > T));
+                need_eq = need - gt;
+            }
+        }
+    }
+    // the picks in ascending block order, 64 blocks a round
+    const bool all_fill = R > 0 && R >= nc;
+    int base = 0, eq_base = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int i = kWave * j + lane;
+        bool sure = false, eqv = false;
+        if (i < nb) {
+            if (F.has(i) || all_fill) {
+                sure = true;
+            } else if (R > 0) {
+                sure = key[j] > T;
+                eqv = key[j] == T;
+            }
+        }
+        const uint64_t em = __ballot(eqv);
+        const bool take = sure || (eqv && eq_base + lanes_below(em) < need_eq);
+        const uint64_t tm = __ballot(take);
+        const int pos = base + lanes_below(tm);
+        if (out && take && pos < k) out[pos] = i;
+        base += __popcll(tm);
+        eq_base += __popcll(em);
+    }
+    if (out)
+        for (int j = base + lane; j < k; j += kWave) out[j] = -1;
+    return min(base, k);
+}
+
+// The selection of a row whose scores are in LDS: topk_waves for a capacity of at most
+// 1024 blocks (KPL from the capacity; wave 0 writes `out`, every wave returns the count),
+// else the workgroup top-k topk_emit, which writes `out` and *n_out itself (every thread
+// takes part) and makes this return -1: the caller then reads the count from *n_out after
+// a barrier. `hist` must be zeroed before a barrier that precedes the call.
+// KPL > 0 fixes the variant at compile time (the caller guarantees cap <= 64 * KPL);
+// KPL = -1 always takes the workgroup top-k; KPL = 0 picks from the capacity at run time.
+template <int KPL = 0>
+__device__ __forceinline__ int topk_dispatch(const float* scores, int nb, int cap, const Forced& F, int k,
+                                             int32_t* out, int32_t* n_out, uint32_t* hist, uint32_t* wlist,
+                                             int* sh, int* wsum) {
+    int32_t* w0 = wave_id() == 0 ? out : nullptr;
+    if constexpr (KPL > 0) {
+        return topk_waves<KPL>(scores, nb, F, k, w0, hist, wlist, sh);
+    } else if constexpr (KPL < 0) {
+        topk_emit(scores, nb, F, k, out, n_out, hist, sh, wsum);
+        return -1;
+    } else {
+        if (cap <= 128) return topk_waves<2>(scores, nb, F, k, w0, hist, wlist, sh);
+        if (cap <= 256) return topk_waves<4>(scores, nb, F, k, w0, hist, wlist, sh);
+        topk_emit(scores, nb, F, k, out, n_out, hist, sh, wsum);
+        return -1;
+    }
+}
+
+// keys per lane of topk_waves for a row capacity; -1: the workgroup top-k, taken beyond
+// 256 blocks: with 16 keys per lane (1024-block rows) and 16 waves per CU selecting at
+// once, the per-wave top-k measured slower than the workgroup one (long-context fused
+// step 64 -> 67 us), while rows of up to 256 blocks gain from it
+inline int topk_kpl(int cap) { return cap <= 128 ? 2 : cap <= 256 ? 4 : -1; }
+
 struct SelParams {
     const uint8_t* query;
     const uint8_t* maxb;
