@@ -283,14 +283,18 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // are never 0). Steps: the wave finds the candidates' key range [kmin, kmax]; the
 // workgroup histograms the keys into 256 bins of that range (wave w adds rounds
 // w, w + 4, ..., so every key once), the barrier; each wave finds the bin holding the
-// R-th largest key, gathers that bin's m keys (m <= 256, else the workgroup radix
-// select) into its own list in LDS (wlist, 256 entries per wave), and finds the R-th
-// largest key T by a binary search over the bin's low bits, each step counting the
-// list's keys >= a trial value with ballots; finally, 64 blocks a round in ascending
+// R-th largest key and the R-th largest key T inside it: a bin of at most kRankBin keys
+// is ranked in registers (each of its keys broadcast once and compared with the others);
+// a larger one (m <= 256, else the workgroup radix select) is gathered into the wave's
+// own list in LDS (wlist, 256 entries per wave) and T found by a binary search over the
+// bin's low bits, each step counting the list's keys >= a trial value with ballots;
+// finally, 64 blocks a round in ascending
 // order, it takes forced blocks and keys above T, and keys equal to T while the quota
 // lasts (lower blocks first), ballots giving each pick its output position.
 // `hist` (512 uint32 of LDS) must be zeroed, and the scores written, before a barrier
 // that precedes the call. Every thread of the workgroup must call it.
+constexpr int kRankBin = 16;  // boundary bins up to this many keys are ranked in registers
+
 template <int KPL>
 __device__ __forceinline__ int topk_waves(const float* scores, int nb, const Forced& F, int k, int32_t* out,
                                           uint32_t* hist, uint32_t* wlist, int* sh) {
@@ -343,7 +347,45 @@ __device__ __forceinline__ int topk_waves(const float* scores, int nb, const For
             const uint32_t bs = uint32_t(__builtin_amdgcn_readlane(bin, src));
             const int need = R - __builtin_amdgcn_readlane(above, src);  // 1 <= need <= the bin's count
             const int m = int(hist[bs]);
-            if (m > 256) {
+            if (m <= kRankBin) {
+                // few keys in the bin: rank them against each other straight from the
+                // registers, one broadcast per key of the bin (no LDS round trip). gt / ge:
+                // how many keys of the bin are above / at least this lane's key j.
+                bool in[KPL];
+                uint32_t gt[KPL], ge[KPL];
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    in[j] = key[j] && ((key[j] - kmin) >> shift) == bs;
+                    gt[j] = ge[j] = 0u;
+                }
+#pragma unroll
+                for (int j2 = 0; j2 < KPL; ++j2) {
+                    uint64_t mk = __ballot(in[j2]);
+                    while (mk) {
+                        const int src = __ffsll((unsigned long long)mk) - 1;
+                        mk &= mk - 1;
+                        const uint32_t v = uint32_t(__builtin_amdgcn_readlane(int(key[j2]), src));
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) {
+                            gt[j] += v > key[j];
+                            ge[j] += v >= key[j];
+                        }
+                    }
+                }
+                // the need-th largest key of the bin: the key with gt < need <= ge (every lane
+                // holding it agrees on gt)
+                int found = 0;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    const uint64_t hm = __ballot(in[j] && gt[j] < uint32_t(need) && uint32_t(need) <= ge[j]);
+                    if (!found && hm) {
+                        const int src = __ffsll((unsigned long long)hm) - 1;
+                        T = uint32_t(__builtin_amdgcn_readlane(int(key[j]), src));
+                        need_eq = need - __builtin_amdgcn_readlane(int(gt[j]), src);
+                        found = 1;
+                    }
+                }
+            } else if (m > 256) {
                 // crowded boundary bin: the workgroup radix select (m is the same in every
                 // wave, so every wave gets here; the barrier lets all finish reading hist)
                 __syncthreads();
