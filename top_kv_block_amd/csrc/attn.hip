@@ -51,8 +51,9 @@ constexpr int kTargetWorkgroupsMfma = 1024;
 constexpr int kTargetWorkgroupsVec = 2048;
 constexpr int kNoSplitRows = 1024;   // rows at which each row gets one workgroup
 
-// the attention kernels: one workgroup per (slot split x head chunk, selection row, request)
-template <int DT>
+// the attention kernels: one workgroup per (slot split x head chunk, selection row, request);
+// NT: K/V through non-temporal loads
+template <int DT, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attn_mfma_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMfmaLdsBytes];  // 40 KiB
@@ -60,7 +61,7 @@ void attn_mfma_kernel(AttnParams p) {
     const int split = int(w.x) % p.splits, hcix = int(w.x) / p.splits;
     const int s = int(w.y), b = int(w.z);
     const int row = b * p.sel_heads + s;
-    mfma_body<DT>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
+    mfma_body<DT, NT>(p, split, hcix, s, b, p.sel + size_t(row) * p.k, p.nsel[row], lds, false);
 }
 
 template <int KV, int QDT, int HC>
@@ -168,8 +169,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, const AttnPlan& pl, hipStream_t
                    (uint8_t*)a.out, (float*)((uint8_t*)a.workspace + pl.part_off)};
     dim3 grid(unsigned(pl.splits * pl.hchunks), unsigned(a.sel_heads), unsigned(a.B));
     if (pl.mfma) {
-        if (a.q_dtype == kF16) hipLaunchKernelGGL(attn_mfma_kernel<kF16>, grid, dim3(kThreads), 0, s, prm);
-        else hipLaunchKernelGGL(attn_mfma_kernel<kBF16>, grid, dim3(kThreads), 0, s, prm);
+        // K/V bytes the call streams (upper bound: k full blocks per selection row)
+        const size_t kv = size_t(a.B) * a.sel_heads * size_t(a.k) * a.BS * 2 * D * 2;
+        auto go = [&](auto ntc) {
+            constexpr bool NT = decltype(ntc)::value;
+            if (a.q_dtype == kF16) hipLaunchKernelGGL((attn_mfma_kernel<kF16, NT>), grid, dim3(kThreads), 0, s, prm);
+            else hipLaunchKernelGGL((attn_mfma_kernel<kBF16, NT>), grid, dim3(kThreads), 0, s, prm);
+        };
+        if (kv > kNtStreamBytes) go(std::true_type{});
+        else go(std::false_type{});
     } else {
         auto by_q = [&](auto kv) {
             constexpr int KV = decltype(kv)::value;

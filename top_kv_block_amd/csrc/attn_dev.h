@@ -14,6 +14,11 @@ namespace qs {
 namespace attn {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// A call that streams more than this many bytes (K/V plus block metadata) reads them with
+// non-temporal loads. Measured on MI355X: a 1.21 GB serving step 218 -> 197 us with them;
+// a 286 MB long-context step 52.5 -> 55.3 us (part of it stays in the 256 MB last-level
+// cache from one step to the next, and non-temporal loads give that up).
+constexpr size_t kNtStreamBytes = size_t(512) << 20;
 constexpr int D = 128;
 constexpr int PSTRIDE = D + 2;       // partial record: acc[D], max, sum
 
@@ -120,8 +125,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32(op8<DT> a, op8<DT> b, f32x4 c) {
 // Matrix-core attention of one workgroup: selection row s of request b (entries srow,
 // count ns_raw, in global memory or LDS), head chunk hcix, slot range `split`. lds: the
 // kMfmaLdsBytes work area. With sync_after_table the workgroup synchronises once every
-// wave has read its slot table, so the selection may live inside the work area.
-template <int DT>
+// wave has read its slot table, so the selection may live inside the work area. NT: K/V
+// rows are read with non-temporal loads (see kNtStreamBytes).
+template <int DT, bool NT = false>
 __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hcix, int s, int b,
                                           const int32_t* srow, int ns_raw, uint8_t* lds, bool sync_after_table) {
     const int h0 = s * p.hpr + hcix * 16;
@@ -192,7 +198,7 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
         for (int u = 0; u < 8; ++u) {
             const int t = tb + 8 * j + u;
             const int tl = t < nt ? t : 0;
-            kn[u] = ld16(kb + size_t(tl) * tstride + 8 * c16);
+            kn[u] = NT ? ld16_nt(kb + size_t(tl) * tstride + 8 * c16) : ld16(kb + size_t(tl) * tstride + 8 * c16);
         }
         // V: lane (c16, j) loads tokens tb + 8j + u, channels 8*c16 .. +7
         u32x4 vr[8];
@@ -200,7 +206,7 @@ __device__ __forceinline__ void mfma_body(const AttnParams& p, int split, int hc
         for (int u = 0; u < 8; ++u) {
             const int t = tb + 8 * j + u;
             const int tl = t < nt ? t : 0;
-            vr[u] = ld16(vb + size_t(tl) * tstride + 8 * c16);
+            vr[u] = NT ? ld16_nt(vb + size_t(tl) * tstride + 8 * c16) : ld16(vb + size_t(tl) * tstride + 8 * c16);
         }
 
         constexpr int KP = 272;  // K tile pitch: a 256-B token row + 16 B

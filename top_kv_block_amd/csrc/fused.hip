@@ -60,7 +60,7 @@ static_assert(kFusedMaxCap <= sel::kLdsScoreCap, "scores stay on chip");
 // entries are at lds + kOffSel. With PRESCORED the row's scores come from the scoring
 // grid's output (p.ws_scores) instead of being computed here. Split 0 of head chunk 0
 // also writes the selection to the caller's selected / n_selected when those are given.
-template <int DT, bool PRESCORED, int KPL>
+template <int DT, bool PRESCORED, int KPL, bool NT = false>
 __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int n, uint8_t* lds, bool publish) {
     float* scores = (float*)(lds + kOffScores);
     uint32_t* hist = (uint32_t*)(lds + kOffHist);
@@ -92,7 +92,7 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
             }
         }
     } else {
-        sel::score_range<DT, true>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
+        sel::score_range<DT, true, NT>(p.query, p.maxb, p.minb, p.num_meta, p.mt, p.mmbpr, p.H, p.N, p.BS, b, n, r.F,
                                    0, r.nb, cap, scores, false, qstage, mt_stage);
     }
     __syncthreads();
@@ -110,16 +110,16 @@ __device__ __forceinline__ int select_phase(const sel::SelParams& p, int b, int 
 }
 
 // bf16 / f16: grid (splits x head chunks, KV head, request); KPL: the top-k variant for
-// the row capacity (sel::topk_kpl)
-template <int DT, bool PRESCORED, int KPL>
+// the row capacity (sel::topk_kpl); NT: metadata and K/V through non-temporal loads
+template <int DT, bool PRESCORED, int KPL, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void select_attn_mfma_kernel(sel::SelParams sp, attn::AttnParams ap) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[attn::kMfmaLdsBytes];
     const uint3 w = xcd_block_index(ap.splits > 1);
     const int split = int(w.x) % ap.splits, hcix = int(w.x) / ap.splits;
     const int n = int(w.y), b = int(w.z);
-    const int ns = select_phase<DT, PRESCORED, KPL>(sp, b, n, lds, split == 0 && hcix == 0);
-    attn::mfma_body<DT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
+    const int ns = select_phase<DT, PRESCORED, KPL, NT>(sp, b, n, lds, split == 0 && hcix == 0);
+    attn::mfma_body<DT, NT>(ap, split, hcix, n, b, (const int32_t*)(lds + kOffSel), ns, lds, true);
 }
 
 // f32: the vector-ALU attention; its merge buffer overlays the dead scoring scratch
@@ -215,13 +215,24 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
     auto launch = [&](auto pre_c) {
         constexpr bool P = decltype(pre_c)::value;
         if (ap.mfma) {
+            // the call's streamed bytes (upper bounds: every row at capacity): metadata rows
+            // (max and min) when scored here, K/V rows of the k selected blocks
+            const size_t esz = 2, rows_kv = size_t(a.B) * a.N;
+            const size_t meta = P ? 0 : rows_kv * size_t(s.mmbpr) * s.BS * 2 * 128 * esz;
+            const size_t kv = rows_kv * size_t(a.k) * a.BS * 2 * 128 * esz;
+            const bool nt = meta + kv > attn::kNtStreamBytes;
             auto by_kpl = [&](auto dt) {
                 constexpr int DT = decltype(dt)::value;
-                switch (kpl) {
-                    case 2: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 2>), grid, dim3(kThreads), 0, st, sp, prm); break;
-                    case 4: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 4>), grid, dim3(kThreads), 0, st, sp, prm); break;
-                    default: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, -1>), grid, dim3(kThreads), 0, st, sp, prm); break;
-                }
+                auto go = [&](auto ntc) {
+                    constexpr bool NT = decltype(ntc)::value;
+                    switch (kpl) {
+                        case 2: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 2, NT>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                        case 4: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, 4, NT>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                        default: hipLaunchKernelGGL((select_attn_mfma_kernel<DT, P, -1, NT>), grid, dim3(kThreads), 0, st, sp, prm); break;
+                    }
+                };
+                if (nt) go(std::true_type{});
+                else go(std::false_type{});
             };
             if (a.q_dtype == kF16) by_kpl(std::integral_constant<int, kF16>{});
             else by_kpl(std::integral_constant<int, kBF16>{});

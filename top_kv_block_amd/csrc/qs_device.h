@@ -15,6 +15,14 @@ struct __attribute__((aligned(16))) u32x4 { uint32_t x, y, z, w; };
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
+// 16-byte load marked non-temporal (global_load_dwordx4 ... nt): for data a step streams
+// once (K/V rows, block metadata). A plain read kernel over 1 GiB measured 7.0 TB/s with
+// it against 6.2 TB/s without on MI355X.
+typedef uint32_t u32nt4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    const u32nt4 v = __builtin_nontemporal_load(reinterpret_cast<const u32nt4*>(p));
+    return u32x4{v.x, v.y, v.z, v.w};
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // f32 -> bf16 (the upper half of a binary32), round to nearest even

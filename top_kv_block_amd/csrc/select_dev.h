@@ -68,8 +68,9 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* sl, const int32_t* ts
 // row length instead of after them; i_end may be <= i0 (nothing scored). qstage: kThreads
 // 16-byte LDS slots used to stage the group's query rows; mt_stage: kMtStageCap ints of LDS
 // for the metadata-table entries of [i0, i_lim) (MT_LDS: the caller guarantees they fit).
+// NT: the metadata rows are read with non-temporal loads (attn::kNtStreamBytes).
 // Contains a barrier: every thread of the workgroup must call it.
-template <int DT, bool MT_LDS>
+template <int DT, bool MT_LDS, bool NT = false>
 __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, const uint8_t* __restrict__ maxb,
                                             const uint8_t* __restrict__ minb, int num_meta,
                                             const int32_t* __restrict__ mt, int mmbpr, int H, int N, int BS, int b,
@@ -110,8 +111,8 @@ __device__ __forceinline__ void score_range(const uint8_t* __restrict__ query, c
             // rows that are not scored read the first row (always valid) and are masked
             const size_t off = ok[u] ? (size_t(mrow[u]) * BS + (i % BS)) * row_bytes + size_t(n) * D * esize + lr * 16
                                      : size_t(lr) * 16;
-            vmx[u] = ld16(maxb + off);
-            vmn[u] = ld16(minb + off);
+            vmx[u] = NT ? ld16_nt(maxb + off) : ld16(maxb + off);
+            vmn[u] = NT ? ld16_nt(minb + off) : ld16(minb + off);
         }
     };
 
