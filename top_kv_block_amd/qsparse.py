@@ -118,7 +118,7 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()  # the argtypes convert it to void*
 
 
 def _dtype_code(t):
@@ -168,15 +168,40 @@ def _rows(t, B, name, width=None):
         _need(t.dim() == 2 and t.shape[1] == width, f"{name} must have {width} columns")
 
 
+# torch's current stream as a raw handle: the private accessor returns the pointer
+# without building a Stream object (a few microseconds a call); the public API otherwise
+_raw_stream_of = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+if _raw_stream_of is None:
+    def _raw_stream_of(index):
+        return torch.cuda.current_stream(index).cuda_stream
+
+
+def _index(dev):
+    dev = torch.device(dev)
+    return dev.index if dev.index is not None else torch.cuda.current_device()
+
+
 def _stream(dev):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    return _raw_stream_of(_index(dev))
+
+
+_ws_sizes = {}
+
+
+def _ws_bytes(fn, *args):
+    """A workspace-size query of the loaded library, remembered per argument tuple."""
+    key = (id(lib), fn, args)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = _ws_sizes[key] = getattr(lib, fn)(*args)
+    return n
 
 
 _workspaces = {}
 _retired = []
 
 
-def workspace(nbytes, device, op):
+def workspace(nbytes, device, op, stream=None):
     """An uninitialised, 256-byte aligned workspace cached per (device, stream, operation)
     and grown on demand, so that calls of one operation on different streams never share
     scratch memory (calls on one stream are ordered). A workspace that is replaced by a
@@ -187,12 +212,13 @@ def workspace(nbytes, device, op):
     Under stream capture every call gets a workspace of its own instead, allocated from the
     graph's private memory pool, which the graph keeps until it is destroyed: graphs
     captured on one stream (torch captures on a shared side stream by default) then never
-    share scratch memory, so they may be replayed concurrently on different streams."""
+    share scratch memory, so they may be replayed concurrently on different streams.
+    ``stream``: the raw handle of the current stream, when the caller has it already."""
     dev = torch.device(device)
     index = dev.index if dev.index is not None else torch.cuda.current_device()
     if torch.cuda.is_current_stream_capturing():
         return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
-    key = (index, torch.cuda.current_stream(index).cuda_stream, op)
+    key = (index, _raw_stream_of(index) if stream is None else stream, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         size = max(int(nbytes), 256)
@@ -249,7 +275,7 @@ def qs_update_metadata(k_cache, block_tables, seq_lens, first_block, max_new_blo
 
 
 def block_select_workspace_bytes(B, N, block_size, mmbpr):
-    return lib.qs_block_select_workspace_bytes(B, N, block_size, mmbpr)
+    return _ws_bytes("qs_block_select_workspace_bytes", B, N, block_size, mmbpr)
 
 
 def qs_block_select(query, maxblocks, minblocks, metadata_block_tables, seq_lens, k,
@@ -279,16 +305,17 @@ def qs_block_select(query, maxblocks, minblocks, metadata_block_tables, seq_lens
                                      block_scores.numel() < B * N * mmbpr * BS):
         raise ValueError("block_scores must be fp32 [B, N, MMBPR*BS]")
     nbytes = block_select_workspace_bytes(B, N, BS, mmbpr)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select", st)
     _check(lib.qs_block_select(B, H, N, D, BS, _dtype_code(query), _ptr(query), _ptr(maxblocks),
                                _ptr(minblocks), nmeta, _ptr(metadata_block_tables), mmbpr, _ptr(seq_lens),
                                _ptr(tokens_since_update), int(flags), int(k), _ptr(selected), _ptr(n_selected),
-                               _ptr(block_scores), _ptr(ws), ws.numel(), _stream(dev)))
+                               _ptr(block_scores), _ptr(ws), ws.numel(), st))
     return selected, n_selected
 
 
 def probe_select_workspace_bytes(B, H, mkbpr):
-    return lib.qs_probe_select_workspace_bytes(B, H, mkbpr)
+    return _ws_bytes("qs_probe_select_workspace_bytes", B, H, mkbpr)
 
 
 def qs_probe_select(query, k_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
@@ -317,16 +344,17 @@ def qs_probe_select(query, k_cache, block_tables, seq_lens, k, importance=None, 
           "probe_scores must be fp32 [B, H, MKBPR]")
     stride = 0 if importance is None else importance.shape[1]
     nbytes = probe_select_workspace_bytes(B, H, mkbpr)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe", st)
     _check(lib.qs_probe_select(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
                                _ptr(k_cache), nkv, _ptr(block_tables), mkbpr, _ptr(seq_lens), _ptr(importance),
                                stride, int(n_probe), int(k), int(flags), _ptr(selected), _ptr(n_selected),
-                               _ptr(probe_scores), _ptr(ws), ws.numel(), _stream(dev)))
+                               _ptr(probe_scores), _ptr(ws), ws.numel(), st))
     return selected, n_selected
 
 
 def sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k):
-    return lib.qs_sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k)
+    return _ws_bytes("qs_sparse_attn_workspace_bytes", B, H, N, D, sel_heads, k)
 
 
 def qs_sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selected, n_selected,
@@ -358,17 +386,18 @@ def qs_sparse_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, selec
         out = torch.empty((B, H, D), dtype=query.dtype, device=dev)
     _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
     nbytes = sparse_attn_workspace_bytes(B, H, N, D, sel_heads, k)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "attn")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "attn", st)
     _check(lib.qs_sparse_attn_decode(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
                                      _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nkv,
                                      _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(selected),
                                      _ptr(n_selected), int(sel_heads), int(k), float(softmax_scale), _ptr(out),
-                                     _ptr(ws), ws.numel(), _stream(dev)))
+                                     _ptr(ws), ws.numel(), st))
     return out
 
 
 def probe_attn_workspace_bytes(B, H, N, mkbpr, k):
-    return lib.qs_probe_attn_workspace_bytes(B, H, N, mkbpr, k)
+    return _ws_bytes("qs_probe_attn_workspace_bytes", B, H, N, mkbpr, k)
 
 
 def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, importance=None, n_probe=8,
@@ -414,18 +443,19 @@ def qs_probe_attn_decode(query, k_cache, v_cache, block_tables, seq_lens, k, imp
     _need(out.dtype == query.dtype and out.numel() >= B * H * D, "out must be [B, H, D] in the query dtype")
     stride = 0 if importance is None else importance.shape[1]
     nbytes = probe_attn_workspace_bytes(B, H, N, mkbpr, k)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe_attn")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "probe_attn", st)
     _check(lib.qs_probe_attn_decode(B, H, N, D, BS, _dtype_code(query), _dtype_code(k_cache), _ptr(query),
                                     _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(probe_k),
                                     _dtype_code(probe_k) if q8 else QS_F32, nkv, _ptr(block_tables), mkbpr,
                                     _ptr(seq_lens), _ptr(importance), stride, int(n_probe), int(k), int(flags),
                                     float(softmax_scale), _ptr(out), _ptr(selected), _ptr(n_selected), _ptr(ws),
-                                    ws.numel(), _stream(dev)))
+                                    ws.numel(), st))
     return out
 
 
 def select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype):
-    return lib.qs_select_attn_workspace_bytes(B, H, N, block_size, mmbpr, k, dtype)
+    return _ws_bytes("qs_select_attn_workspace_bytes", B, H, N, block_size, mmbpr, k, dtype)
 
 
 def _select_attn_args(query, maxblocks, minblocks, metadata_block_tables, k_cache, v_cache, block_tables,
@@ -468,12 +498,13 @@ def qs_select_attn_decode(query, maxblocks, minblocks, metadata_block_tables, k_
     mmbpr = metadata_block_tables.shape[1]
     dt = _dtype_code(query)
     nbytes = select_attn_workspace_bytes(B, H, N, BS, mmbpr, k, dt)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select_attn")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "select_attn", st)
     _check(lib.qs_select_attn_decode(B, H, N, D, BS, dt, _ptr(query), _ptr(maxblocks), _ptr(minblocks), nmeta,
                                      _ptr(metadata_block_tables), mmbpr, _ptr(k_cache), _ptr(v_cache),
                                      k_cache.shape[0], _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
                                      _ptr(tokens_since_update), int(flags), int(k), float(softmax_scale), _ptr(out),
-                                     _ptr(selected), _ptr(n_selected), _ptr(ws), ws.numel(), _stream(dev)))
+                                     _ptr(selected), _ptr(n_selected), _ptr(ws), ws.numel(), st))
     return out
 
 
@@ -503,7 +534,7 @@ def qs_select_attn_decode_static(query, maxblocks, minblocks, metadata_block_tab
 
 
 def prefill_importance_workspace_bytes(B, H, max_len):
-    return lib.qs_prefill_importance_workspace_bytes(B, H, max_len)
+    return _ws_bytes("qs_prefill_importance_workspace_bytes", B, H, max_len)
 
 
 def qs_prefill_importance(query, k_cache, block_tables, seq_lens, softmax_scale=0.0, importance=None,
@@ -529,9 +560,10 @@ def qs_prefill_importance(query, k_cache, block_tables, seq_lens, softmax_scale=
         _need(head_importance.dtype == torch.float32 and head_importance.numel() >= B * H * stride,
               "head_importance must be fp32 [B, H, stride]")
     nbytes = prefill_importance_workspace_bytes(B, H, max_len)
-    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "importance")
+    st = _stream(dev)
+    ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "importance", st)
     _check(lib.qs_prefill_importance(B, H, N, D, BS, _dtype_code(query), _ptr(query), max_len, _ptr(k_cache), nkv,
                                      _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), float(softmax_scale),
                                      _ptr(importance), int(stride), _ptr(head_importance), _ptr(ws), ws.numel(),
-                                     _stream(dev)))
+                                     st))
     return (importance, head_importance) if head_importance is not None else importance
