@@ -462,7 +462,7 @@ __device__ __forceinline__ int topk_waves(const float* scores, int nb, const For
 }
 
 // The selection of a row whose scores are in LDS: topk_waves for a capacity of at most
-// 1024 blocks (KPL from the capacity; wave 0 writes `out`, every wave returns the count),
+// 256 blocks (KPL from the capacity; wave 0 writes `out`, every wave returns the count),
 // else the workgroup top-k topk_emit, which writes `out` and *n_out itself (every thread
 // takes part) and makes this return -1: the caller then reads the count from *n_out after
 // a barrier. `hist` must be zeroed before a barrier that precedes the call.
