@@ -234,17 +234,21 @@ def cpu_baseline_rows(W, dev, min_seconds=0.5):
     return rows
 
 
-def _timed(fn, reps, stream):
-    """Average ms of fn() over reps back-to-back calls on the stream (after one warm call)."""
+def _timed(fn, reps, stream, rounds=3):
+    """Average ms of fn() over reps back-to-back calls on the stream (after one warm call);
+    the median of `rounds` such rounds."""
     fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    ts = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps)
+    return sorted(ts)[len(ts) // 2]
 
 
 def _graph_us(fn, reps, stream):
