@@ -13,7 +13,8 @@ the bound
   kernel's unit of work) left out;
 
 while the contract's absolute 2e-2 alone accepts some of the long-context drops (a block
-there carries ~1/64 of the weight), which is why the GPU parity tests apply both. A planted needle that carries almost all of a row's weight
+there carries ~1/64 of the weight), which is why the GPU parity tests apply both. The
+same holds in fp16 on serving-shaped rows whose weights are mostly fp16 subnormals. A planted needle that carries almost all of a row's weight
 (as in the long-context workload, where the needle logit sits ~20 nats above the rest)
 makes every other block invisible in the output to any comparison; there the needle's
 own block is what a drop test can see, and it is rejected.
@@ -33,6 +34,10 @@ def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
 
 
+def _f16(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float16).double().numpy()
+
+
 def _selection(seed, nb, rows, k):
     """Each row: k distinct blocks incl. block 0 and the last block, ascending."""
     rng = np.random.default_rng(seed)
@@ -43,11 +48,12 @@ def _selection(seed, nb, rows, k):
     return sel, np.full((1, rows), k, np.int32)
 
 
-def _emulate(wl, sel, ns, drop=None):
+def _emulate(wl, sel, ns, drop=None, rnd=_bf16):
     """The matrix-core kernel's roundings on the host: logits in float64, each weight
-    rounded to bf16 relative to the row maximum, denominator over the rounded weights,
-    output rounded to bf16. ``drop`` = (slot, chunk): that 32-token chunk of that selection
-    entry is left out of every row."""
+    rounded to the operand type (``rnd``: bf16, or fp16 with its subnormals) relative to
+    the row maximum, denominator over the rounded weights, output rounded to the same
+    type. ``drop`` = (slot, chunk): that 32-token chunk of that selection entry is left
+    out of every row."""
     q = wl.query.double().numpy()
     B, H, D = q.shape
     N, BS = wl.N, wl.BS
@@ -67,8 +73,8 @@ def _emulate(wl, sel, ns, drop=None):
                 Vs.append(vc[ph, keep, kh].double().numpy())
             K, V = np.concatenate(Ks), np.concatenate(Vs)
             lg = (q[b, s * hpr:(s + 1) * hpr] @ K.T) / math.sqrt(D)
-            p = _bf16(np.exp(lg - lg.max(axis=1, keepdims=True)))
-            out[b, s * hpr:(s + 1) * hpr] = _bf16((p @ V) / p.sum(axis=1, keepdims=True))
+            p = rnd(np.exp(lg - lg.max(axis=1, keepdims=True)))
+            out[b, s * hpr:(s + 1) * hpr] = rnd((p @ V) / p.sum(axis=1, keepdims=True))
     return out
 
 
@@ -164,3 +170,38 @@ def test_needle_row_rejects_the_needle_block(oracle):
     out = _bf16(oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, s2,
                                           ns - 1, N))
     assert _rows_rejected(out, ref, tol, H // N).all(), f"needle block (entry {j}) drop passes"
+
+
+def test_fp16_bound_with_subnormal_weights(oracle):
+    """fp16 rows shaped like the serving workload, with the query scaled by 6 so that the
+    logits spread over ~6 nats per standard deviation and most unnormalised weights fall
+    below fp16's smallest normal (2^-14): the bound (with its fp16-subnormal term) accepts
+    the oracle's output rounded to fp16 and the kernel-rounding emulation in fp16, and
+    rejects, in every selection row, the output with any one selected block left out."""
+    H, N, L, k = 64, 8, 32768, 16
+    wl = W.random_case(104, 1, H, N, 128, [L], k=k, dtype=torch.float16)
+    wl.query = (wl.query.double() * 6.0).to(torch.float16)
+    nb = -(-L // 128)
+    sel, ns = _selection(104, nb, N, k)
+    ref = oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns, N)
+    tol = attn16_bound(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns, N, ref,
+                       torch.float16)
+    # the regime this test is for: most weights of a row are fp16 subnormals or zero
+    q = wl.query.double().numpy()[0, :H // N]
+    ents = row_tokens(wl.block_tables[0].numpy(), L, sel[0, 0], 128)
+    Kr = np.concatenate([wl.k_cache[ph, :nt, 0].double().numpy() for ph, _, nt in ents])
+    lg = (q @ Kr.T) / math.sqrt(128)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    assert float(np.mean(p < 2.0 ** -14)) > 0.5
+    for what, got in (("oracle rounded to fp16", _f16(ref)), ("fp16 kernel-rounding emulation",
+                                                              _emulate(wl, sel, ns, rnd=_f16))):
+        ratio = float(np.max(np.abs(got - ref) / tol))
+        print(f"fp16 rows: {what}: max err/bound {ratio:.3f}")
+        assert ratio <= 1.0, f"{what} exceeds the fp16 bound ({ratio:.3f})"
+    for j in range(k):
+        s2 = np.full_like(sel, -1)
+        s2[..., :k - 1] = np.delete(sel, j, axis=-1)
+        out = _f16(oracle.sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                             s2, ns - 1, N))
+        rej = _rows_rejected(out, ref, tol, H // N)
+        assert rej.all(), f"fp16: dropping entry {j} passes the bound in rows {np.flatnonzero(~rej).tolist()}"
