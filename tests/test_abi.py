@@ -306,3 +306,17 @@ def test_page3_wrappers_exist_and_refuse_cpu_tensors(qs):
     t = torch.zeros((1, 1), dtype=torch.int32)
     with pytest.raises(ValueError):
         Q.quest_block_select_paged(q, m, m, t, torch.ones(1, dtype=torch.int32), 4)
+
+
+def test_workspace_size_queries_follow_the_loaded_library(qs):
+    """The binding remembers workspace-size answers per loaded library: under both builds
+    (and after switching between them) every query equals a direct call of the library."""
+    cases = [("select_attn_workspace_bytes", "qs_select_attn_workspace_bytes", (8, 32, 8, 128, 8, 64, qs.QS_BF16)),
+             ("block_select_workspace_bytes", "qs_block_select_workspace_bytes", (20, 8, 128, 1)),
+             ("probe_select_workspace_bytes", "qs_probe_select_workspace_bytes", (1, 16, 128)),
+             ("sparse_attn_workspace_bytes", "qs_sparse_attn_workspace_bytes", (1, 16, 8, 128, 16, 32)),
+             ("probe_attn_workspace_bytes", "qs_probe_attn_workspace_bytes", (1, 16, 8, 128, 32)),
+             ("prefill_importance_workspace_bytes", "qs_prefill_importance_workspace_bytes", (1, 16, 4096))]
+    for _ in range(2):  # the second pass answers from the remembered values
+        for wrapper, fn, args in cases:
+            assert getattr(qs, wrapper)(*args) == getattr(qs.lib, fn)(*args), wrapper
