@@ -14,6 +14,8 @@
 // of the floats (IEEE total order, -0 < +0), so the result is bit-exact whatever the
 // hardware's float max does with signed zeros. Workgroups past a request's last block
 // but inside its last metadata block write the +0.0 tail rows.
+#include <type_traits>
+
 #include "qs_device.h"
 #include "qs_internal.h"
 
@@ -76,7 +78,9 @@ __device__ __forceinline__ u32x4 unord(u32x4 v) {
     return u32x4{E::ord(v.x), E::ord(v.y), E::ord(v.z), E::ord(v.w)};
 }
 
-template <bool BF16>
+// NT: the K rows are read with non-temporal loads (a build over more bytes than the
+// last-level cache holds streams them once)
+template <bool BF16, bool NT>
 __global__ __launch_bounds__(kThreads) void meta_kernel(
     const uint8_t* __restrict__ kc, int num_kv_blocks,
     const int32_t* __restrict__ bt, int mkbpr,
@@ -132,11 +136,11 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
             for (; t + 7 * R < nt; t += 8 * R) {
                 u32x4 v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = ld16(p + size_t(t + u * R) * row_bytes);
+                for (int u = 0; u < 8; ++u) v[u] = NT ? ld16_nt(p + size_t(t + u * R) * row_bytes) : ld16(p + size_t(t + u * R) * row_bytes);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) fold<BF16>(hi, lo, v[u]);
             }
-            for (; t < nt; t += R) fold<BF16>(hi, lo, ld16(p + size_t(t) * row_bytes));
+            for (; t < nt; t += R) fold<BF16>(hi, lo, NT ? ld16_nt(p + size_t(t) * row_bytes) : ld16(p + size_t(t) * row_bytes));
         }
         red_hi[tid] = hi;
         red_lo[tid] = lo;
@@ -162,30 +166,41 @@ __global__ __launch_bounds__(kThreads) void meta_kernel(
             for (; t + 7 < nt; t += 8) {
                 u32x4 v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = ld16(p + size_t(t + u) * row_bytes);
+                for (int u = 0; u < 8; ++u) v[u] = NT ? ld16_nt(p + size_t(t + u) * row_bytes) : ld16(p + size_t(t + u) * row_bytes);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) fold<BF16>(hi, lo, v[u]);
             }
-            for (; t < nt; ++t) fold<BF16>(hi, lo, ld16(p + size_t(t) * row_bytes));
+            for (; t < nt; ++t) fold<BF16>(hi, lo, NT ? ld16_nt(p + size_t(t) * row_bytes) : ld16(p + size_t(t) * row_bytes));
             st16(omax + size_t(col) * 16, unord<BF16>(hi));
             st16(omin + size_t(col) * 16, unord<BF16>(lo));
         }
     }
 }
 
+// Above this many bytes of K a build reads them with non-temporal loads: measured on the
+// serving workload's 8.6 GB rebuild, and for the same reason as the attention's K/V (a plain
+// read kernel over 1 GiB streamed 7.0 TB/s with them against 6.2 TB/s without).
+constexpr size_t kMetaNtBytes = size_t(512) << 20;
+
 void launch_meta(const MetaArgs& a, dim3 grid, const int32_t* first, hipStream_t s) {
     const int esize = a.bf16 ? 2 : 4;
     const int row_vecs = a.N * a.D * esize / 16;
-    if (a.bf16)
-        hipLaunchKernelGGL(meta_kernel<true>, grid, dim3(kThreads), 0, s,
-                           (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens,
-                           a.meta_tables, a.mmbpr, (uint8_t*)a.maxb, (uint8_t*)a.minb, a.num_meta, a.BS,
-                           row_vecs, first);
-    else
-        hipLaunchKernelGGL(meta_kernel<false>, grid, dim3(kThreads), 0, s,
-                           (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens,
-                           a.meta_tables, a.mmbpr, (uint8_t*)a.maxb, (uint8_t*)a.minb, a.num_meta, a.BS,
-                           row_vecs, first);
+    // K bytes the grid can read (upper bound: every block of the grid full)
+    const size_t bytes = size_t(grid.x) * grid.y * a.BS * size_t(row_vecs) * 16;
+    auto go = [&](auto bf, auto nt) {
+        constexpr bool BF = decltype(bf)::value, NT = decltype(nt)::value;
+        hipLaunchKernelGGL((meta_kernel<BF, NT>), grid, dim3(kThreads), 0, s, (const uint8_t*)a.k_cache,
+                           a.num_kv_blocks, a.block_tables, a.mkbpr, a.seq_lens, a.meta_tables, a.mmbpr,
+                           (uint8_t*)a.maxb, (uint8_t*)a.minb, a.num_meta, a.BS, row_vecs, first);
+    };
+    const bool nt = bytes > kMetaNtBytes;
+    if (a.bf16) {
+        if (nt) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
+    } else {
+        if (nt) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
+    }
 }
 
 }  // namespace
