@@ -217,9 +217,9 @@ hipError_t launch_select_attn(const SelectArgs& s, const AttnArgs& a, const Fuse
         if (ap.mfma) {
             // the call's streamed bytes (upper bounds: every row at capacity): metadata rows
             // (max and min) when scored here, K/V rows of the k selected blocks
-            const size_t esz = 2, rows_kv = size_t(a.B) * a.N;
-            const size_t meta = P ? 0 : rows_kv * size_t(s.mmbpr) * s.BS * 2 * 128 * esz;
-            const size_t kv = rows_kv * size_t(a.k) * a.BS * 2 * 128 * esz;
+            const size_t esz = 2, rows_kv = size_t(a.B) * a.N;  // 16-bit query, metadata and K/V here
+            const size_t meta = P ? 0 : rows_kv * size_t(s.mmbpr) * s.BS * 2 * a.D * esz;
+            const size_t kv = rows_kv * size_t(a.k) * a.BS * 2 * a.D * esz;
             const bool nt = meta + kv > attn::kNtStreamBytes;
             auto by_kpl = [&](auto dt) {
                 constexpr int DT = decltype(dt)::value;
