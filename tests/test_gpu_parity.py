@@ -1025,6 +1025,52 @@ def test_serving_full_size_every_request(qs, oracle):
                                       ("query set 1, tsmu drawn", qsets[1].contiguous(), ts1)], chunk=16)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_nontemporal_paths_bitwise_equal_plain_loads(qs, dtype):
+    """Calls that stream more than 512 MB read with non-temporal loads, smaller ones with
+    plain loads; only the cache policy differs, so the results must be bitwise equal. 256
+    requests of 8 blocks (8 KV heads of 8 query heads, k = 4, sink + window forcing): the
+    metadata build (an 8.6 GB grid bound), the fused selection + attention (671 MB) and
+    the attention alone (537 MB) over all requests, against the same requests in batches
+    small enough for plain loads (8 requests per build, 128 per step). Every call has at
+    least 1024 rows, so both launch one workgroup per row and merge nothing."""
+    B, H, N, BS, L, k = 256, 64, 8, 128, 1024, 4
+    ts_list = [int(x) for x in torch.randint(0, 2 * BS, (B,), generator=torch.Generator().manual_seed(9))]
+    wl = W.random_case(61, B, H, N, BS, [L] * B, k=k, dtype=dtype, tsmu=ts_list,
+                       flags=W.FORCE_SINK | W.FORCE_WINDOW, spare_blocks=0, meta_spare=0).to(DEV)
+    say(f"non-temporal vs plain loads, {B} requests, {dtype}")
+    shape = (wl.num_meta_blocks, BS, N, wl.D)
+    mx, mn = torch.zeros(shape, dtype=dtype, device=DEV), torch.zeros(shape, dtype=dtype, device=DEV)
+    qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
+    mx2, mn2 = torch.zeros_like(mx), torch.zeros_like(mn)
+    for b0 in range(0, B, 8):
+        r = slice(b0, b0 + 8)
+        qs.qs_build_metadata(wl.k_cache, wl.block_tables[r], wl.meta_seq_lens[r], wl.meta_tables[r], mx2, mn2)
+    torch.cuda.synchronize()
+    assert torch.equal(mx.view(torch.int16), mx2.view(torch.int16))
+    assert torch.equal(mn.view(torch.int16), mn2.view(torch.int16))
+    sel = torch.empty((B, N, k), dtype=torch.int32, device=DEV)
+    ns = torch.empty((B, N), dtype=torch.int32, device=DEV)
+    out = qs.qs_select_attn_decode(wl.query, mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache, wl.block_tables,
+                                   wl.seq_lens, k, tokens_since_update=wl.tsmu, flags=wl.flags, selected=sel,
+                                   n_selected=ns)
+    att = qs.qs_sparse_attn_decode(wl.query, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens, sel, ns)
+    out2, att2 = torch.empty_like(out), torch.empty_like(out)
+    sel2, ns2 = torch.empty_like(sel), torch.empty_like(ns)
+    for b0 in range(0, B, 128):
+        r = slice(b0, b0 + 128)
+        qs.qs_select_attn_decode(wl.query[r], mx, mn, wl.meta_tables[r], wl.k_cache, wl.v_cache,
+                                 wl.block_tables[r], wl.seq_lens[r], k, tokens_since_update=wl.tsmu[r],
+                                 flags=wl.flags, out=out2[r], selected=sel2[r], n_selected=ns2[r])
+        qs.qs_sparse_attn_decode(wl.query[r], wl.k_cache, wl.v_cache, wl.block_tables[r], wl.seq_lens[r],
+                                 sel2[r], ns2[r], out=att2[r])
+    torch.cuda.synchronize()
+    assert int(ns.min()) == k and torch.equal(sel, sel2) and torch.equal(ns, ns2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(att.view(torch.int16), att2.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), att.view(torch.int16))
+
+
 @pytest.mark.parametrize("which", ["long_context", "serving"])
 def test_full_size_steps_bitwise_repeatable(qs, which):
     """Determinism at full size: the decode step of the long-context workload (split rows
