@@ -377,9 +377,14 @@ qs_status qs_probe_attn_decode(int32_t B, int32_t H, int32_t N, int32_t D, int32
                                void* out, int32_t* selected, int32_t* n_selected,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* bytes of workspace qs_prefill_importance needs (0 for invalid sizes): B * H * max_len
+/* bytes of workspace qs_prefill_importance can use (0 for invalid sizes): B * H * max_len
  * floats of row normalisers plus, per chunk of the causal work, three more (a job of fewer
- * than 8192 tiles of 64 rows x heads x requests is cut into up to 8 chunks) */
+ * than 8192 tiles of 64 rows x heads x requests is cut into up to 8 chunks) -- the minimum
+ * the call accepts -- then, when the causal score matrices of all heads and requests take
+ * at most 2 GiB in fp32 (B * H * T (T + 1) / 2 blocks of 16 x 16, T = ceil(max_len / 16)),
+ * room for them: an fp32 call given that much stores its scores in the first pass and reads
+ * them back in the second instead of computing them again (same results up to the order of
+ * the fp32 column sums) */
 size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_len);
 
 /*
@@ -400,7 +405,9 @@ size_t qs_prefill_importance_workspace_bytes(int32_t B, int32_t H, int32_t max_l
  *   softmax_scale      c; <= 0 selects 1/sqrt(D)
  *   importance         [B, importance_stride] fp32 output, or NULL
  *   head_importance    [B, H, importance_stride] fp32 output, or NULL (not both NULL)
- *   workspace          at least qs_prefill_importance_workspace_bytes(); 256-byte aligned
+ *   workspace          256-byte aligned; the minimum of qs_prefill_importance_workspace_bytes()
+ *                      (its size without the stored scores) is accepted, the full size lets
+ *                      fp32 inputs skip the recomputation
  * Dot products run on the matrix cores in fp32 accumulation from exactly widened inputs;
  * chunk partials and heads are summed in a fixed order, so results are deterministic.
  */

@@ -275,15 +275,27 @@ def test_prefill_importance_rejects(qs, kw, status):
 
 
 def test_prefill_importance_workspace_size(qs):
-    # fp32 row normalisers + per chunk (row max, row sum, column sums), for the larger of the
-    # two splits (fp32: one chunk; 16-bit: tiles of 128 rows, chunked below 8192 x 64 rows x
-    # heads x requests): 4096 rows x 16 heads -> 8 chunks; 2 x 32 heads x 8192 rows -> 1
-    assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == (1 + 3 * 8) * 16 * 4096 * 4
+    # the minimum: fp32 row normalisers + per chunk (row max, row sum, column sums), for the
+    # larger of the two splits (fp32: one chunk; 16-bit: tiles of 128 rows, chunked below
+    # 8192 x 64 rows x heads x requests): 4096 rows x 16 heads -> 8 chunks; 2 x 32 heads x
+    # 8192 rows -> 1; then the fp32 path's stored scores, T (T + 1) / 2 blocks of 16 x 16
+    # floats per (request, head) with T = ceil(max_len / 16), when they take at most 2 GiB
+    def blocks(max_len):
+        t = -(-max_len // 16)
+        return t * (t + 1) // 2
+    base = (1 + 3 * 8) * 16 * 4096 * 4
+    assert qs.prefill_importance_workspace_bytes(1, 16, 4096) == base + 16 * blocks(4096) * 1024
+    # 2 x 32 heads x 8192 rows: 8.6 GB of scores, over the cap: the minimum only
     assert qs.prefill_importance_workspace_bytes(2, 32, 8192) == (1 + 3 * 1) * 2 * 32 * 8192 * 4
-    assert qs.prefill_importance_workspace_bytes(1, 1, 100) == 1792  # (1 + 3 * 1 chunk) * 100 * 4 = 1600, rounded up to 256 B
+    # (1 + 3 * 1 chunk) * 100 * 4 = 1600, rounded up to 256 B, then 7 * 8 / 2 blocks
+    assert qs.prefill_importance_workspace_bytes(1, 1, 100) == 1792 + blocks(100) * 1024
     assert qs.prefill_importance_workspace_bytes(0, 16, 4096) == 256
     assert qs.prefill_importance_workspace_bytes(1, 0, 4096) == 0
     assert _imp(qs, imp=None, himp=FAKE, wsb=qs.prefill_importance_workspace_bytes(0, 16, 4096)) == 0
+    # what a call requires is the minimum (without the scores, which it then recomputes):
+    # one byte less is refused before anything is launched, naming the minimum
+    assert _imp(qs, B=1, imp=None, himp=FAKE, wsb=base - 1) == 1
+    assert qs.lib.qs_last_error().decode().endswith(f"{base - 1} bytes, {base} needed")
 
 
 def test_binding_refuses_cpu_tensors(qs):

@@ -1591,6 +1591,30 @@ def test_prefill_importance_random(qs, oracle, case):
     assert torch.equal(imp, imp2)
 
 
+@pytest.mark.parametrize("case", [(111, 2, 4, 2, 16, [1000, 517], 1000), (112, 1, 3, 3, 64, [63], 64),
+                                  (113, 3, 2, 1, 32, [0, 300, 1], 301)], ids=lambda c: f"seed{c[0]}")
+def test_prefill_importance_fp32_stored_and_recomputed_scores(qs, oracle, case):
+    """fp32 inputs with the full workspace (the first pass stores its causal score tiles and
+    the second streams them back) and with the minimum one (the second pass recomputes the
+    scores): both against the oracle, ragged prompts and an empty one included."""
+    seed, B, H, N, BS, lens, max_len = case
+    say(f"prefill importance stored/recomputed seed={seed} B={B} H={H} lens={lens}")
+    wl = W.random_case(seed, B, H, N, BS, lens, k=2, dtype=torch.float32, with_v=False)
+    q = W.prefill_queries(wl, seed, max_len=max_len)
+    t16 = (max_len + 15) // 16
+    full = qs.prefill_importance_workspace_bytes(B, H, max_len)
+    score = B * H * t16 * (t16 + 1) // 2 * 1024
+    assert full > score > 0
+    args = (q.to(DEV), wl.k_cache.to(DEV), wl.block_tables.to(DEV), wl.seq_lens.to(DEV))
+    oimp, ohimp = oracle.prefill_importance(q, wl.k_cache, wl.block_tables, wl.seq_lens, N)
+    for nb in (full, full - score):
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        imp, himp = qs.qs_prefill_importance(*args, with_heads=True, workspace_buf=ws)
+        torch.cuda.synchronize()
+        check_importance(tnp(imp), oimp, f"importance ({nb} workspace bytes)")
+        check_importance(tnp(himp), ohimp, f"head importance ({nb} workspace bytes)")
+
+
 def test_prefill_importance_page1_prompt_sampled_heads(qs, oracle):
     """The page-1 probe workload's prefill (4096 tokens, 16 heads, fp32): every head on the GPU, heads 0 and 15
     against the oracle, and the row-mass identity (the importance sums to H * L)."""

@@ -9,8 +9,11 @@
 // prefill_importance[s] = sum over heads of imp_head[h][s].
 //
 // Design (CDNA4). The weights need each row's softmax normaliser before any column can
-// be summed, so there are two passes over the causal score matrix, both dense
-// contractions on the matrix cores (the scores are never stored):
+// be summed, so there are two passes over the causal score matrix. The row pass is a
+// dense contraction on the matrix cores; the column pass either repeats it (16-bit
+// inputs, or fp32 scores too large to keep) or, for fp32 inputs when the lower triangle
+// of 16x16 score tiles fits the workspace (at most 2 GiB), streams the scores that the
+// row pass stored:
 //   row pass     work item (query tile, key chunk): each wave takes 16 query rows per
 //                row tile it holds and walks the chunk's 16-key tiles up to its last row,
 //                S = Q K^T on v_mfma_f32_16x16x4_f32 (fp32 inputs) or
@@ -23,6 +26,16 @@
 //                tile it holds and walks the chunk's 16-row query tiles from its first key
 //                on, S^T = K Q^T, adds 2^(x - lse_row) into per-lane column sums, merges
 //                the 16 lanes and writes the chunk's column sums;
+//   stored scores (fp32) the row pass also writes each causal 16x16 tile of its scaled
+//                scores (masked entries as -inf, non-temporal stores: nothing reads them
+//                before they leave the cache); the column pass is then one workgroup per
+//                (key tile, head, request) whose four waves take every fourth row tile,
+//                eight in flight per wave, add 2^(x - lse_row) per key and merge in a fixed
+//                order. A fp32 tile costs 32 MFMA steps of 4 channels (about 1000 cycles
+//                of one SIMD); a SIMD's share of the HBM rate (about 3.3 bytes a cycle)
+//                streams the tile's 1 KB in about 300, so reading the scores back is
+//                cheaper than the contraction it replaces, even before the K tile's fetch
+//                and LDS staging that the contraction needs as well;
 //   reduce       sums the chunks, then the heads, in a fixed order (deterministic).
 // A wave holds one 16-row tile with fp32 inputs and two with 16-bit ones (wave_tiles), so
 // a workgroup's tile is 64 or 128 query rows (keys). With 16-bit inputs a wave's matrix
@@ -80,7 +93,18 @@ struct ImpParams {
     float* mpart;  // [C, B, H, max_len] workspace: each key chunk's row max (log2 units)
     float* lpart;  // [C, B, H, max_len] workspace: each key chunk's sum of 2^(x - max)
     float* cpart;  // [C, B, H, max_len] workspace: each row chunk's column sums
+    float* S;      // fp32 stored-score path: the scores x (log2 units, masked -inf) of each
+                   // (b, h) in 16 x 16 blocks, key-tile-major lower triangle; null: recompute
+    int T16;       // 16-row tiles of max_len
+    size_t sblocks;  // blocks per (b, h): T16 (T16 + 1) / 2
 };
+
+// block (key tile kt, row tile rt >= kt) of one (b, h) in the stored-score layout: key tile
+// kt's blocks are consecutive, rows kt .. T16 - 1; inside a block, key column c's 16 rows
+// are contiguous (element (c, i) at c * 16 + i)
+__device__ __forceinline__ size_t sblock(int T16, int kt, int rt) {
+    return size_t(kt) * T16 - size_t(kt) * (kt - 1) / 2 + size_t(rt - kt);
+}
 
 // chunking of a (B, H, max_len) job with tiles of TR rows
 constexpr int kMaxChunks = 8;
@@ -318,7 +342,8 @@ __device__ __forceinline__ void frag_from_tile(Frag<DT>& f, const uint8_t* buf, 
     for (int i = 0; i < Frag<DT>::kVecs; ++i) f.v[i] = ld16(q + 16 * i);
 }
 
-template <int DT>
+// STORE (fp32 stored-score path): every score x of the pass is also written to p.S
+template <int DT, bool STORE = false>
 __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     constexpr int es = elem_bytes(DT);
     constexpr int RW = wave_tiles<DT>(), TR = tile_rows<DT>();
@@ -350,7 +375,11 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     // key tile s0 (16 keys in one block, physical block ph): rows past L repeat the last
     // key (masked). The block-table entries are read one step before their tile (bt_at),
     // so no step waits for a lookup between its barrier and its loads.
-    const int32_t* btrow = p.bt + size_t(b) * p.mkbpr;
+    // read through the constant address space: nothing writes the block table while the
+    // kernel runs, and with the score stores in the loop the compiler can no longer prove it
+    // by itself; scalar lookups then keep the step's K loads in flight past them
+    typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+    const const_i32p btrow = (const_i32p)(p.bt + size_t(b) * p.mkbpr);
     auto bt_at = [&](int s) { return btrow[unsigned(min(s, L - 1)) / unsigned(p.BS)]; };
     auto fetch = [&](int s0, int ph, u32x4 (&v)[Tile<DT>::kPerThread]) -> bool {
         if (ph < 0 || ph >= p.num_kv_blocks) return false;
@@ -362,21 +391,46 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     // the softmax update of row tile rr (this lane's 4 rows) with one 16-key tile's scores
     // (key s of this lane), branch-free: a masked score enters as -inf and changes nothing.
     // Tiles whose 16 keys precede all of the tile's rows and L (all) skip the mask.
-    auto upd = [&](const attn::f32x4& c, int rr, int s, bool all) {
+    float pv[2][4];            // STORE: a step's scores, written early in the next step
+    int pblk[2] = {-1, -1};    // their blocks in the stored layout (-1: nothing pending)
+    float* const sbh = STORE ? p.S + (size_t(b) * p.H + h) * p.sblocks * 256 + r * 16 + 4 * j : nullptr;
+    auto flush = [&]() {
+        if constexpr (STORE) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                if (pblk[sl] < 0) continue;
+                typedef float f4nt __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f4nt{pv[sl][0], pv[sl][1], pv[sl][2], pv[sl][3]},
+                                            reinterpret_cast<f4nt*>(sbh + size_t(pblk[sl]) * 256));
+                pblk[sl] = -1;
+            }
+        }
+    };
+    auto upd = [&](const attn::f32x4& c, int rr, int s, bool all, int s0k, int sl) {
+        float xs[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * rr + 4 * j + i;
+            xs[i] = (all || (s <= t && s < L)) ? c[i] * p.scale2 : -INFINITY;
+        }
+        if constexpr (STORE) {  // this lane's key column r, rows 4j .. 4j + 3 of the block
+            pblk[sl] = int(sblock(p.T16, s0k >> 4, (t0 + 16 * rr) >> 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[sl][i] = xs[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             // one exp2 per score: a new maximum rescales the sum, any other score adds
-            const float x = (all || (s <= t && s < L)) ? c[i] * p.scale2 : -INFINITY;
+            const float x = xs[i];
             const float d = x - m[rr][i];
             const float e = exp2_hw(-fabsf(d));
             l[rr][i] = d > 0.f ? fmaf(l[rr][i], e, 1.f) : l[rr][i] + e;
             m[rr][i] = fmaxf(m[rr][i], x);
         }
     };
-    auto upd_tile = [&](const attn::f32x4& c, int rr, int s0k) {
-        if (s0k + 15 <= t0 + 16 * rr && s0k + 15 < L) upd(c, rr, s0k + r, true);
-        else upd(c, rr, s0k + r, false);
+    auto upd_tile = [&](const attn::f32x4& c, int rr, int s0k, int sl) {
+        if (s0k + 15 <= t0 + 16 * rr && s0k + 15 < L) upd(c, rr, s0k + r, true, s0k, sl);
+        else upd(c, rr, s0k + r, false, s0k, sl);
     };
     // a step takes two key tiles (32 keys): both go to LDS, one barrier, then the next two
     // are fetched into the freed register sets and the pair is multiplied; four LDS
@@ -399,6 +453,9 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr) nd[kk][rr] = need(kk, rr);
         __syncthreads();
+        // the previous step's scores: issued before this step's loads, so the wait for those
+        // loads at the next step's start never waits on a store issued after them
+        flush();
         ha = s0 + 32 <= s_end && fetch(s0 + 32, pa, va);
         hb = s0 + 48 <= s_end && fetch(s0 + 48, pb, vb);
         pa = bt_at(s0 + 64);  // the entries of the next step's tiles
@@ -410,12 +467,14 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
                 frag_from_tile<DT>(k1, b1, r, j);
                 attn::f32x4 r0, r1;
                 dot_tile2<DT>(qf[0], k0, k1, r0, r1);
-                upd_tile(r0, 0, s0);
-                upd_tile(r1, 0, s0 + 16);
+                upd_tile(r0, 0, s0, 0);
+                upd_tile(r1, 0, s0 + 16, 1);
             } else if (nd[0][0] || nd[1][0]) {
                 Frag<DT> kf;
                 frag_from_tile<DT>(kf, nd[0][0] ? b0 : b1, r, j);
-                upd_tile(dot_tile<DT>(qf[0], kf), 0, nd[0][0] ? s0 : s0 + 16);
+                const attn::f32x4 c = dot_tile<DT>(qf[0], kf);
+                if (nd[0][0]) upd_tile(c, 0, s0, 0);
+                else upd_tile(c, 0, s0 + 16, 1);
             }
         } else {
             // each key fragment read from LDS feeds both row tiles
@@ -428,12 +487,12 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
                 if (nd[kk][0] && nd[kk][1]) {
                     attn::f32x4 r0, r1;
                     dot_tile2a<DT>(qf[0], qf[1], kf, r0, r1);
-                    upd_tile(r0, 0, sk);
-                    upd_tile(r1, 1, sk);
+                    upd_tile(r0, 0, sk, 0);
+                    upd_tile(r1, 1, sk, 0);
                 } else if (nd[kk][0]) {  // constant tile indices keep m, l and qf in registers
-                    upd_tile(dot_tile<DT>(qf[0], kf), 0, sk);
+                    upd_tile(dot_tile<DT>(qf[0], kf), 0, sk, 0);
                 } else {
-                    upd_tile(dot_tile<DT>(qf[1], kf), 1, sk);
+                    upd_tile(dot_tile<DT>(qf[1], kf), 1, sk, 0);
                 }
             }
         }
@@ -444,6 +503,7 @@ __global__ __launch_bounds__(kThreads) void imp_row_kernel(ImpParams p) {
     pa = bt_at(s_lo + 32);
     pb = bt_at(s_lo + 48);
     for (int s0 = s_lo, buf = 0; s0 <= s_end; s0 += 32, buf ^= 2) step2(s0, kt[buf], kt[buf + 1], na, ha, nb, hb);
+    flush();
     // merge the 16 key columns of each row into the chunk's (max, sum); every row t < L
     // has a key of the chunk (s_lo <= tw), so the max is finite. With one chunk that is
     // the row's log2-sum-exp already.
@@ -593,6 +653,66 @@ __global__ __launch_bounds__(kThreads) void imp_col_kernel(ImpParams p) {
     }
 }
 
+// Column sums from the stored scores (fp32 path): work item (16-key tile kt, head, request),
+// longest items (first key tiles) first through the snake order. Wave w takes the tile's
+// row blocks w, w + 4, ...; a lane takes key column c = lane / 4 and rows 4q .. 4q + 3 of
+// each block (q = lane % 4): one non-temporal 16-byte load of scores (read once), the
+// block's 16 row normalisers loaded by lanes 0..15 and handed out by lane shuffles, adding
+// 2^(x - lse_t) for rows t < L (masked scores are -inf and add 0). The four lanes of a key,
+// then the four waves, are added in a fixed order: deterministic.
+__global__ __launch_bounds__(kThreads) void imp_colS_kernel(ImpParams p) {
+    constexpr int U = 8;  // blocks in flight per wave
+    __shared__ float part[kThreads / 64][16];
+    const int HB = p.H * p.B, rank = snake_rank();
+    const int hb = rank % HB, kt = rank / HB;
+    const int h = hb % p.H, b = hb / p.H;
+    const int L = min(max(p.sl[b], 0), min(p.max_len, p.mkbpr * p.BS));
+    const int s0 = kt * 16;
+    if (s0 >= L) return;  // whole workgroup: keys past the prompt get no column sums
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = lane >> 2, q = lane & 3;
+    const int nrt = (L - 1) / 16 - kt + 1;  // row tiles kt .. (L - 1) / 16
+    const float* sb = p.S + ((size_t(b) * p.H + h) * p.sblocks + sblock(p.T16, kt, kt)) * 256 + c * 16 + 4 * q;
+    const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
+    float acc = 0.f;
+    for (int it0 = w; it0 < nrt; it0 += 4 * U) {
+        u32x4 x[U];
+        float l16[U];  // lane l < 16: the normaliser of row l of the block
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = it0 + 4 * u;
+            const bool in = it < nrt;
+            x[u] = ld16_nt(sb + size_t(in ? it : 0) * 256);
+            l16[u] = lse[min((kt + (in ? it : 0)) * 16 + (lane & 15), L - 1)];
+        }
+        float lt[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lt[u][i] = __shfl(l16[u], 4 * q + i, kWave);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = it0 + 4 * u;
+            const float xv[4] = {__uint_as_float(x[u].x), __uint_as_float(x[u].y), __uint_as_float(x[u].z),
+                                 __uint_as_float(x[u].w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = (kt + it) * 16 + 4 * q + i;
+                acc += (it < nrt && t < L) ? exp2_hw(xv[i] - lt[u][i]) : 0.f;
+            }
+        }
+    }
+    acc += __shfl_xor(acc, 1, kWave);
+    acc += __shfl_xor(acc, 2, kWave);
+    if (q == 0) part[w][c] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int s = s0 + int(threadIdx.x);
+        const float tot = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+        if (s < L) p.cpart[(size_t(b) * p.H + h) * p.max_len + s] = tot;
+    }
+}
+
 // lse[t] = log2 of the sum over the key chunks of row t (chunks 0 .. (t / 64) / R, in
 // chunk order) of sum * 2^max
 __global__ __launch_bounds__(kThreads) void imp_merge_kernel(ImpParams p) {
@@ -654,7 +774,18 @@ __global__ __launch_bounds__(kThreads) void imp_reduce_kernel(ImpParams p, float
 
 }  // namespace
 
-size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
+namespace {
+// the stored-score region of the fp32 path: 16 x 16 fp32 blocks of the causal lower
+// triangle per (b, h), used when all of them fit in kScoreCap
+constexpr size_t kScoreCap = size_t(2) << 30;
+size_t score_bytes(int B, int H, int max_len) {
+    const size_t t16 = (size_t(max(max_len, 0)) + 15) / 16;
+    const size_t bytes = t16 * (t16 + 1) / 2 * 1024 * size_t(B) * size_t(H);
+    return bytes <= kScoreCap ? bytes : 0;
+}
+}  // namespace
+
+size_t prefill_importance_min_workspace_bytes(int B, int H, int max_len) {
     // the larger of the two splits: fp32 (64-row tiles, one chunk) and 16-bit (128-row tiles)
     const int C = max(imp_split(B, H, max_len, false, tile_rows<kF32>()).C,
                       imp_split(B, H, max_len, true, tile_rows<kBF16>()).C);
@@ -663,24 +794,39 @@ size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
     return bytes < 256 ? 256 : bytes;
 }
 
+size_t prefill_importance_workspace_bytes(int B, int H, int max_len) {
+    return prefill_importance_min_workspace_bytes(B, H, max_len) + score_bytes(B, H, max_len);
+}
+
 hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s) {
     float* ws = (float*)a.workspace;
     const int TR = a.dtype == kF32 ? tile_rows<kF32>() : tile_rows<kBF16>();
     const Split sp = imp_split(a.B, a.H, a.max_len, a.dtype != kF32, TR);
     const size_t plane = size_t(a.B) * a.H * a.max_len;
+    const size_t min_bytes = prefill_importance_min_workspace_bytes(a.B, a.H, a.max_len);
+    const size_t sbytes = score_bytes(a.B, a.H, a.max_len);
+    // fp32 with room for the scores: store them in the row pass and read them back in the
+    // column pass instead of recomputing Q K^T (the 16-bit passes recompute faster than the
+    // scores stream)
+    const bool stored = a.dtype == kF32 && sbytes > 0 && a.workspace_bytes >= min_bytes + sbytes;
+    const int T16 = (a.max_len + 15) / 16;
     ImpParams p{(const uint8_t*)a.query, (const uint8_t*)a.k_cache, a.num_kv_blocks, a.block_tables, a.mkbpr,
                 a.seq_lens, a.B, a.H, a.N, a.BS, a.max_len, a.scale * kLog2e, TR, sp.T, sp.R, sp.C,
-                ws, ws + plane, ws + plane * (1 + sp.C), ws + plane * (1 + 2 * size_t(sp.C))};
+                ws, ws + plane, ws + plane * (1 + sp.C), ws + plane * (1 + 2 * size_t(sp.C)),
+                stored ? (float*)((uint8_t*)a.workspace + min_bytes) : nullptr, T16,
+                size_t(T16) * (T16 + 1) / 2};
     if (a.max_len > 0) {
         const long hb = long(a.H) * a.B;
         const dim3 rgrid(unsigned(row_items(sp) * hb)), cgrid(unsigned(col_items(sp) * hb));
         const dim3 mgrid(unsigned((a.max_len + kThreads - 1) / kThreads), unsigned(a.H), unsigned(a.B));
         if (a.dtype == kBF16) hipLaunchKernelGGL(imp_row_kernel<kBF16>, rgrid, dim3(kThreads), 0, s, p);
         else if (a.dtype == kF16) hipLaunchKernelGGL(imp_row_kernel<kF16>, rgrid, dim3(kThreads), 0, s, p);
+        else if (stored) hipLaunchKernelGGL((imp_row_kernel<kF32, true>), rgrid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL(imp_row_kernel<kF32>, rgrid, dim3(kThreads), 0, s, p);
         if (sp.C > 1) hipLaunchKernelGGL(imp_merge_kernel, mgrid, dim3(kThreads), 0, s, p);
         if (a.dtype == kBF16) hipLaunchKernelGGL(imp_col_kernel<kBF16>, cgrid, dim3(kThreads), 0, s, p);
         else if (a.dtype == kF16) hipLaunchKernelGGL(imp_col_kernel<kF16>, cgrid, dim3(kThreads), 0, s, p);
+        else if (stored) hipLaunchKernelGGL(imp_colS_kernel, dim3(unsigned(long(T16) * hb)), dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL(imp_col_kernel<kF32>, cgrid, dim3(kThreads), 0, s, p);
     }
     hipLaunchKernelGGL(imp_reduce_kernel, dim3(unsigned((a.stride + 63) / 64), unsigned(a.B)),

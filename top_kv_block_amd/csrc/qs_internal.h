@@ -139,7 +139,10 @@ struct ImportanceArgs {
     int stride;
     float* head_importance;  // [B, H, stride] or null
     void* workspace;
+    size_t workspace_bytes;  // at least the minimum; the full size lets fp32 store its scores
 };
+// the two-pass workspace, and the full one (plus the fp32 path's stored scores when they fit)
+size_t prefill_importance_min_workspace_bytes(int B, int H, int max_len);
 size_t prefill_importance_workspace_bytes(int B, int H, int max_len);
 hipError_t launch_prefill_importance(const ImportanceArgs& a, hipStream_t s);
 

@@ -582,7 +582,7 @@ qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int3
     if (!(softmax_scale == softmax_scale)) return fail(QS_ERR_INVALID, "%s: softmax_scale is NaN", fn);
     if ((long long)((max_len + 63) / 64) * H * B > 0x7fffffffLL)
         return fail(QS_ERR_INVALID, "%s: max_len * H * B too large for one grid", fn);
-    const size_t need = qs::prefill_importance_workspace_bytes(B, H, max_len);
+    const size_t need = qs::prefill_importance_min_workspace_bytes(B, H, max_len);
     if (workspace_bytes < need)
         return fail(QS_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if (B == 0) return ok();
@@ -595,7 +595,7 @@ qs_status qs_prefill_importance(int32_t B, int32_t H, int32_t N, int32_t D, int3
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(float(D));
     qs::ImportanceArgs a{B, H, N, D, block_size, int(dtype), query, max_len, k_cache, num_kv_blocks, block_tables,
                          max_kv_blocks_per_req, seq_lens, scale, importance, importance_stride, head_importance,
-                         workspace};
+                         workspace, workspace_bytes};
     return hip_status(qs::launch_prefill_importance(a, (hipStream_t)stream), fn);
 }
 
