@@ -1615,6 +1615,39 @@ def test_prefill_importance_fp32_stored_and_recomputed_scores(qs, oracle, case):
         check_importance(tnp(himp), ohimp, f"head importance ({nb} workspace bytes)")
 
 
+def test_prefill_importance_fp32_skipped_blocks(qs):
+    """Table entries out of range (the plain build skips their blocks): the skipped keys get
+    importance 0 and every other value stays finite, identically placed on the stored-score
+    and recompute paths, which agree (the oracle refuses such input, so the two paths are
+    compared with each other)."""
+    B, H, N, BS, lens = 2, 4, 2, 16, [200, 131]
+    say(f"prefill importance skipped blocks B={B} H={H} lens={lens}")
+    wl = W.random_case(114, B, H, N, BS, lens, k=2, dtype=torch.float32, with_v=False)
+    q = W.prefill_queries(wl, 114, max_len=200)
+    bt = wl.block_tables.clone()
+    nkv = wl.k_cache.shape[0]
+    bt[0, 3] = -1    # keys 48 .. 63 of request 0
+    bt[1, 0] = nkv   # keys 0 .. 15 of request 1 (row 0's only key)
+    bt[1, 8] = -5    # keys 128 .. 130 of request 1 (its last, partial block)
+    args = (q.to(DEV), wl.k_cache.to(DEV), bt.to(DEV), wl.seq_lens.to(DEV))
+    t16 = (200 + 15) // 16
+    full = qs.prefill_importance_workspace_bytes(B, H, 200)
+    outs = []
+    for nb in (full, full - B * H * t16 * (t16 + 1) // 2 * 1024):
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        ws.fill_(0x7f)  # leftover bytes read as a large finite value
+        imp, himp = qs.qs_prefill_importance(*args, with_heads=True, workspace_buf=ws)
+        torch.cuda.synchronize()
+        outs.append((tnp(imp).astype(np.float64), tnp(himp).astype(np.float64)))
+    for imp, himp in outs:
+        assert np.isfinite(imp).all() and np.isfinite(himp).all()
+        assert not imp[0, 48:64].any() and not imp[1, 0:16].any() and not imp[1, 128:131].any()
+        assert imp[0, :48].all() and imp[0, 64:200].all() and imp[1, 16:128].all()
+    for a, b in zip(outs[0], outs[1]):
+        err = np.abs(a - b)
+        assert (err <= 2e-4 * np.abs(b) + 1e-6).all(), f"stored vs recomputed: worst {err.max():.3e}"
+
+
 def test_prefill_importance_page1_prompt_sampled_heads(qs, oracle):
     """The page-1 probe workload's prefill (4096 tokens, 16 heads, fp32): every head on the GPU, heads 0 and 15
     against the oracle, and the row-mass identity (the importance sums to H * L)."""

@@ -671,7 +671,11 @@ __global__ __launch_bounds__(kThreads) void imp_colS_kernel(ImpParams p) {
     if (s0 >= L) return;  // whole workgroup: keys past the prompt get no column sums
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = lane >> 2, q = lane & 3;
-    const int nrt = (L - 1) / 16 - kt + 1;  // row tiles kt .. (L - 1) / 16
+    // a key tile in a block whose table entry is out of range was skipped by the row pass
+    // (never stored): its keys get no column sums, as in the recomputing column pass
+    const int ph = p.bt[size_t(b) * p.mkbpr + unsigned(s0) / unsigned(p.BS)];
+    const bool skipped = ph < 0 || ph >= p.num_kv_blocks;
+    const int nrt = skipped ? 0 : (L - 1) / 16 - kt + 1;  // row tiles kt .. (L - 1) / 16
     const float* sb = p.S + ((size_t(b) * p.H + h) * p.sblocks + sblock(p.T16, kt, kt)) * 256 + c * 16 + 4 * q;
     const float* lse = p.lse + (size_t(b) * p.H + h) * p.max_len;
     float acc = 0.f;
