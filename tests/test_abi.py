@@ -296,6 +296,16 @@ def test_prefill_importance_workspace_size(qs):
     # one byte less is refused before anything is launched, naming the minimum
     assert _imp(qs, B=1, imp=None, himp=FAKE, wsb=base - 1) == 1
     assert qs.lib.qs_last_error().decode().endswith(f"{base - 1} bytes, {base} needed")
+    # the binding asks for the full size for fp32 inputs and the minimum for 16-bit ones
+    # (which never store their scores)
+    assert qs.prefill_importance_call_workspace_bytes(1, 16, 4096, True) == base + 16 * blocks(4096) * 1024
+    assert qs.prefill_importance_call_workspace_bytes(1, 16, 4096, False) == base
+    assert qs.prefill_importance_call_workspace_bytes(1, 1, 100, False) == 1792
+    big = (1 + 3 * 1) * 2 * 32 * 8192 * 4
+    assert qs.prefill_importance_call_workspace_bytes(2, 32, 8192, False) == big
+    assert qs.prefill_importance_call_workspace_bytes(2, 32, 8192, True) == big
+    assert qs.prefill_importance_call_workspace_bytes(0, 16, 4096, False) == 256
+    assert qs.prefill_importance_call_workspace_bytes(1, 0, 4096, False) == 0
 
 
 def test_binding_refuses_cpu_tensors(qs):

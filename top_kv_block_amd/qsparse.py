@@ -537,6 +537,19 @@ def prefill_importance_workspace_bytes(B, H, max_len):
     return _ws_bytes("qs_prefill_importance_workspace_bytes", B, H, max_len)
 
 
+def prefill_importance_call_workspace_bytes(B, H, max_len, fp32):
+    """What one call needs: the full size for fp32 inputs, whose first pass can store the
+    scores, else the minimum -- the full size less the stored-score region, which the size
+    query adds when B * H * T (T + 1) / 2 tiles of 1 KiB (T = ceil(max_len / 16)) take at
+    most 2 GiB."""
+    full = prefill_importance_workspace_bytes(B, H, max_len)
+    if fp32 or full == 0:
+        return full
+    t = (max(max_len, 0) + 15) // 16
+    scores = B * H * (t * (t + 1) // 2) * 1024
+    return full - scores if scores <= (2 << 30) else full
+
+
 def qs_prefill_importance(query, k_cache, block_tables, seq_lens, softmax_scale=0.0, importance=None,
                           importance_stride=None, head_importance=None, with_heads=False, workspace_buf=None):
     """Page 1's prefill importance from the prefill queries [B, max_len, H, D] and the paged
@@ -559,7 +572,7 @@ def qs_prefill_importance(query, k_cache, block_tables, seq_lens, softmax_scale=
     if head_importance is not None:
         _need(head_importance.dtype == torch.float32 and head_importance.numel() >= B * H * stride,
               "head_importance must be fp32 [B, H, stride]")
-    nbytes = prefill_importance_workspace_bytes(B, H, max_len)
+    nbytes = prefill_importance_call_workspace_bytes(B, H, max_len, query.dtype == torch.float32)
     st = _stream(dev)
     ws = workspace_buf if workspace_buf is not None else workspace(nbytes, dev, "importance", st)
     _check(lib.qs_prefill_importance(B, H, N, D, BS, _dtype_code(query), _ptr(query), max_len, _ptr(k_cache), nkv,
