@@ -725,6 +725,8 @@ FUSED_CASES = [
     (78, 2, 32, 8, 128, [128 * 150 + 3, 128 * 20], 8, torch.float16, 3, [2, 0]),  # f16, one kernel, splits
     (80, 3, 8, 2, 16, [16 * 3 + 1, 1, 0], 9, torch.float32, 3, [0, 0, 0]),       # k > nb, 1 token, empty
     (81, 3, 16, 8, 64, [64 * 300 + 1, 64 * 2, 0], 64, torch.bfloat16, 3, [0, 0, 0]),  # prescored, k > nb, empty
+    (82, 1, 8, 2, 16, [16 * 4096], 64, torch.bfloat16, 3, [3]),   # at the LDS capacity: 4096 blocks, 256 table entries
+    (83, 1, 8, 2, 16, [16 * 4097 + 5], 64, torch.bfloat16, 3, [0]),  # one block past it: two kernels
 ]
 
 
