@@ -334,7 +334,10 @@ __device__ __forceinline__ void vec_body(const AttnParams& p, int split, int hci
     constexpr int LPR = D * ke / 16;    // lanes per K/V row
     constexpr int EPL = 16 / ke;        // channels per lane
     constexpr int NG = kThreads / LPR;  // independent lane groups per workgroup
-    constexpr int U = 2;                // tokens in flight per group
+    // tokens in flight per lane group: a step covers 32 tokens with fp32 rows (8 groups of
+    // 32 lanes), so a 32-token block is one round trip of loads; 16-bit and int8 rows have
+    // 16 and 32 groups, and two tokens each already cover a block
+    constexpr int U = KV == kF32 ? 4 : 2;
 
     float* red_m = red;                       // [kWaves][HC]
     float* red_l = red + kWaves * HC;         // [kWaves][HC]
