@@ -284,8 +284,7 @@ def other_workloads(qs, W, dev, stream, reps=50):
         return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
     def meta_buf(wl):
-        mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=wl.k_cache.dtype, device=dev)
-        return mx, torch.zeros_like(mx)
+        return qs.alloc_metadata_pools(wl.num_meta_blocks, wl.BS, wl.N, wl.D, dtype=wl.k_cache.dtype, device=dev)
 
     # the tiny fp32 workload: Quest select + attention
     wl = W.tiny_needle().to(dev)
@@ -477,8 +476,9 @@ def main():
         tsmu_tab = (torch.arange(128, dtype=torch.int32, device=dev)[:, None] % 128).repeat(1, B).contiguous()
     else:
         tsmu_tab = wl.tsmu[None].contiguous()
-    mx = torch.zeros((wl.num_meta_blocks, BS, N, D), dtype=wl.k_cache.dtype, device=dev)
-    mn = torch.zeros_like(mx)
+    # metadata pools placed as the library recommends (min 256 B past a 1 KiB multiple from
+    # max); the workload's K and V pools are placed the same way (workloads.paired_pools)
+    mx, mn = qs.alloc_metadata_pools(wl.num_meta_blocks, BS, N, D, dtype=wl.k_cache.dtype, device=dev)
     sel = torch.empty((B, N, k), dtype=torch.int32, device=dev)
     ns = torch.empty((B, N), dtype=torch.int32, device=dev)
     out = torch.empty((B, H, D), dtype=wl.query.dtype, device=dev)
@@ -489,14 +489,20 @@ def main():
     def rebuild():
         qs.qs_build_metadata(wl.k_cache, wl.block_tables, wl.meta_seq_lens, wl.meta_tables, mx, mn)
 
-    def select(s):
-        qs.qs_block_select(qsets[s % qsets.shape[0]], mx, mn, wl.meta_tables, wl.seq_lens, k,
-                           tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]], flags=wl.flags, selected=sel,
-                           n_selected=ns, workspace_buf=ws_sel)
+    def select_on(m):
+        def select(s):
+            qs.qs_block_select(qsets[s % qsets.shape[0]], mx, m, wl.meta_tables, wl.seq_lens, k,
+                               tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]], flags=wl.flags, selected=sel,
+                               n_selected=ns, workspace_buf=ws_sel)
+        return select
 
-    def attend(s):
-        qs.qs_sparse_attn_decode(qsets[s % qsets.shape[0]], wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
-                                 sel, ns, sel_heads=N, out=out, workspace_buf=ws_att)
+    def attend_on(v):
+        def attend(s):
+            qs.qs_sparse_attn_decode(qsets[s % qsets.shape[0]], wl.k_cache, v, wl.block_tables, wl.seq_lens,
+                                     sel, ns, sel_heads=N, out=out, workspace_buf=ws_att)
+        return attend
+
+    select, attend = select_on(mn), attend_on(wl.v_cache)
 
     log("metadata build")
     rebuild()
@@ -549,16 +555,25 @@ def main():
     ws_fused = torch.zeros(qs.select_attn_workspace_bytes(B, H, N, BS, wl.mmbpr, k, qs.QS_BF16), dtype=torch.uint8,
                            device=dev)
 
-    def fused(s):
-        # the fused entry point: selection kept on chip and attention in one launch when the
-        # rows allow it (the serving shape does); the selection is still written out
-        qs.qs_select_attn_decode(qsets[s % qsets.shape[0]], mx, mn, wl.meta_tables, wl.k_cache, wl.v_cache,
-                                 wl.block_tables, wl.seq_lens, k, tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]],
-                                 flags=wl.flags, out=out, selected=sel, n_selected=ns, workspace_buf=ws_fused)
+    def fused_on(v, m):
+        def fused(s):
+            # the fused entry point: selection kept on chip and attention in one launch when
+            # the rows allow it (the serving shape does); the selection is still written out
+            qs.qs_select_attn_decode(qsets[s % qsets.shape[0]], mx, m, wl.meta_tables, wl.k_cache, v,
+                                     wl.block_tables, wl.seq_lens, k,
+                                     tokens_since_update=tsmu_tab[s % tsmu_tab.shape[0]], flags=wl.flags, out=out,
+                                     selected=sel, n_selected=ns, workspace_buf=ws_fused)
+        return fused
 
-    def separate(s):
-        select(s)
-        attend(s)
+    def separate_on(v, m):
+        sel_f, att_f = select_on(m), attend_on(v)
+
+        def separate(s):
+            sel_f(s)
+            att_f(s)
+        return separate
+
+    fused, separate = fused_on(wl.v_cache, mn), separate_on(wl.v_cache, mn)
 
     path = args.path or ("fused" if args.workload == "serving" else "separate")
     step = fused if path == "fused" else separate
@@ -652,6 +667,36 @@ def main():
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / (reps * gs)
 
+    # (4) pool placement: the same steps with the V and min pools copied to addresses that
+    # agree with K's and max's modulo 1 KiB, as separately allocated pools (or the two halves
+    # of one [2, ...] pool) usually do; the step above uses the placement the library
+    # recommends (qs.alloc_kv_pools, qs.alloc_metadata_pools)
+    def same_phase_copy(t, ref):
+        nbytes = t.numel() * t.element_size()
+        buf = torch.empty(nbytes + 1024, dtype=torch.uint8, device=dev)
+        o = (ref.data_ptr() - buf.data_ptr()) % 1024
+        c = buf[o:o + nbytes].view(t.dtype).view(t.shape)
+        c.copy_(t)
+        return c
+
+    log("timing the step with the V and min pools at K's and max's address phase")
+    v_al, mn_al = same_phase_copy(wl.v_cache, wl.k_cache), same_phase_copy(mn, mx)
+    step_al = fused_on(v_al, mn_al) if path == "fused" else separate_on(v_al, mn_al)
+    for s in range(args.warmup):
+        step_al(s)
+    aligned_ms = time_steps(step_al) / K
+    placement = {
+        "used": "V pool 256 B past a 1 KiB multiple from the K pool, min pool likewise from max "
+                "(the layout of qs.alloc_kv_pools / qs.alloc_metadata_pools); value is measured on it",
+        "v_minus_k_mod_1KiB": (wl.v_cache.data_ptr() - wl.k_cache.data_ptr()) % 1024,
+        "min_minus_max_mod_1KiB": (mn.data_ptr() - mx.data_ptr()) % 1024,
+        "same_phase_pools": {"steps_per_s": round(1000.0 / aligned_ms, 3), "ms_per_step": round(aligned_ms, 5),
+                             "v_minus_k_mod_1KiB": (v_al.data_ptr() - wl.k_cache.data_ptr()) % 1024,
+                             "min_minus_max_mod_1KiB": (mn_al.data_ptr() - mx.data_ptr()) % 1024},
+    }
+    del v_al, mn_al, step_al
+    torch.cuda.empty_cache()
+
     # replay the selections of the timed steps to count their algorithmic bytes
     log("counting algorithmic bytes of the timed steps")
     sel_bytes = att_bytes = 0
@@ -715,6 +760,7 @@ def main():
         "metadata_refresh_gbps": round(refresh_bytes / (refresh_us * 1e-6) / 1e9, 1),
         "steps_per_s_with_refresh_every_128": round(128.0 / (128 * ms_per_step + refresh_us * 1e-3) * 1000.0, 3),
         "flushed": flushed,
+        "pool_placement": placement,
         "roofline": {"kernel": dom_kernel, "bound": "hbm",
                      "achieved": round(dom_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),

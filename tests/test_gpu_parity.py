@@ -741,6 +741,42 @@ def run_fused(qs, wl, mx, mn, want_sel=True):
     return out, sel, ns
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_pool_placement_does_not_change_results(qs, dtype):
+    """K / V and max / min pools from the placement helpers (second pool 256 B past a 1 KiB
+    multiple) against separately allocated ones: metadata, selection, fused and separate
+    attention all bitwise equal."""
+    say(f"pool placement dtype={dtype}")
+    wl = W.random_case(115, 3, 16, 4, 64, [64 * 150 + 7, 64 * 9, 1], k=12, dtype=dtype, flags=3, tsmu=[3, 0, 0])
+    q, bt, sl, mt = (t.to(DEV) for t in (wl.query, wl.block_tables, wl.seq_lens, wl.meta_tables))
+    ts = wl.tsmu.to(DEV)
+    kc, vc = wl.k_cache.to(DEV), wl.v_cache.to(DEV)
+    kp, vp = qs.alloc_kv_pools(kc.shape[0], wl.BS, wl.N, wl.D, dtype=dtype, device=DEV)
+    kp.copy_(kc)
+    vp.copy_(vc)
+    assert (vp.data_ptr() - kp.data_ptr()) % 1024 == 256
+    outs = []
+    for (k_, v_), paired in (((kc, vc), False), ((kp, vp), True)):
+        if paired:
+            mx, mn = qs.alloc_metadata_pools(wl.num_meta_blocks, wl.BS, wl.N, wl.D, dtype=dtype, device=DEV)
+            assert (mn.data_ptr() - mx.data_ptr()) % 1024 == 256
+        else:
+            mx = torch.zeros((wl.num_meta_blocks, wl.BS, wl.N, wl.D), dtype=dtype, device=DEV)
+            mn = torch.zeros_like(mx)
+        qs.qs_build_metadata(k_, bt, sl, mt, mx, mn)
+        sel, ns = qs.qs_block_select(q, mx, mn, mt, sl, wl.k, tokens_since_update=ts, flags=wl.flags)
+        att = qs.qs_sparse_attn_decode(q, k_, v_, bt, sl, sel, ns)
+        fused = qs.qs_select_attn_decode(q, mx, mn, mt, k_, v_, bt, sl, wl.k, tokens_since_update=ts, flags=wl.flags)
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (mx, mn, sel, ns, att, fused)])
+    ib = torch.int32 if dtype == torch.float32 else torch.int16
+    for a, b in zip(*outs):
+        if a.is_floating_point():
+            assert torch.equal(a.view(ib), b.view(ib))
+        else:
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"seed{c[0]}")
 def test_select_attn_random(qs, oracle, case):
     seed, B, H, N, BS, lens, k, dtype, flags, tsmu = case

@@ -533,6 +533,36 @@ def qs_select_attn_decode_static(query, maxblocks, minblocks, metadata_block_tab
     return out
 
 
+# ---- pool placement ---------------------------------------------------------------------
+# The kernels read a head's K and V rows together (and a block's max and min rows) at the
+# same offset inside their pools; when the two bases also agree modulo 1 KiB, each pair
+# falls in one 256-byte address class, which the chip's memory serves more slowly. These
+# helpers place the second pool of a pair 256 bytes past a 1 KiB multiple from the first.
+
+def alloc_paired_pools(shape, dtype, device=None, zero=False):
+    """Two contiguous tensors of `shape` (views of one allocation, uninitialised unless
+    `zero`), the second starting 256 bytes past a 1 KiB multiple from the first."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    off = (nbytes + 1023) // 1024 * 1024 + 256
+    buf = (torch.zeros if zero else torch.empty)(off + nbytes, dtype=torch.uint8, device=device)
+    return buf[:nbytes].view(dtype).view(shape), buf[off:off + nbytes].view(dtype).view(shape)
+
+
+def alloc_kv_pools(num_kv_blocks, block_size, N, D=128, dtype=torch.bfloat16, device=None):
+    """k_cache, v_cache [num_kv_blocks, block_size, N, D], uninitialised, placed as the
+    header's placement note recommends."""
+    return alloc_paired_pools((num_kv_blocks, block_size, N, D), dtype, device)
+
+
+def alloc_metadata_pools(num_meta_blocks, block_size, N, D=128, dtype=torch.bfloat16, device=None):
+    """maxblocks, minblocks [num_meta_blocks, block_size, N, D], zeroed (the +0.0 rows of
+    absent blocks), placed as the header's placement note recommends."""
+    return alloc_paired_pools((num_meta_blocks, block_size, N, D), dtype, device, zero=True)
+
+
 def prefill_importance_workspace_bytes(B, H, max_len):
     return _ws_bytes("qs_prefill_importance_workspace_bytes", B, H, max_len)
 

@@ -105,9 +105,26 @@ def _normal(shape, g, device):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
 
 
-def _fill_blocks(n_blocks, BS, N, D, g, device, dist, dtype, chunk_blocks=1024):
-    """A KV pool drawn block-chunk by block-chunk (keeps the fp32 temporary small)."""
-    out = torch.empty((n_blocks, BS, N, D), dtype=dtype, device=device)
+def paired_pools(shape, dtype, device):
+    """Two uninitialised contiguous tensors of `shape` in one allocation, the second starting
+    256 bytes past a 1 KiB multiple from the first: the placement the library documents for
+    a K / V pool pair (a head's K and V rows then fall in different 256-byte address
+    classes). The large paged workloads are laid out this way, as a caller following the
+    library's placement note would allocate them."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    off = (nbytes + 1023) // 1024 * 1024 + 256
+    buf = torch.empty(off + nbytes, dtype=torch.uint8, device=device)
+    return buf[:nbytes].view(dtype).view(shape), buf[off:off + nbytes].view(dtype).view(shape)
+
+
+def _fill_blocks(n_blocks, BS, N, D, g, device, dist, dtype, chunk_blocks=1024, out=None):
+    """A KV pool drawn block-chunk by block-chunk (keeps the fp32 temporary small), into
+    `out` when given."""
+    if out is None:
+        out = torch.empty((n_blocks, BS, N, D), dtype=dtype, device=device)
     for s in range(0, n_blocks, chunk_blocks):
         e = min(n_blocks, s + chunk_blocks)
         shape = (e - s, BS, N, D)
@@ -256,8 +273,9 @@ def long_context(device="cpu", seed: int = 2, B: int = 8, min_len: int = 8192,
     nbs = [_cdiv(L, BS) for L in sl_h]
     mkbpr = _cdiv(max_len, BS)
     bt, n_kv = _paged_tables(nbs, g, device, capacity=mkbpr)
-    kc = _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16)
-    vc = _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16)
+    kc, vc = paired_pools((n_kv, BS, N, D), torch.bfloat16, device)
+    _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16, out=kc)
+    _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16, out=vc)
     q = _normal((B, H, D), g, device).to(torch.bfloat16)
     mnbs = [_cdiv(nb, BS) for nb in nbs]
     mmbpr = _cdiv(mkbpr, BS)
@@ -297,8 +315,9 @@ def serving(device="cpu", seed: int = 4, B: int = 128, nb: int = 256,
     g = _gen(seed, device)
     n_kv = B * nb
     bt = torch.randperm(n_kv, generator=g, device=device).to(torch.int32).reshape(B, nb)
-    kc = _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16)
-    vc = _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16)
+    kc, vc = paired_pools((n_kv, BS, N, D), torch.bfloat16, device)
+    _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16, out=kc)
+    _fill_blocks(n_kv, BS, N, D, g, device, "normal", torch.bfloat16, out=vc)
     qs = _normal((n_query_sets, B, H, D), g, device).to(torch.bfloat16)
     mmbpr = _cdiv(nb, BS)
     n_meta = B * mmbpr
