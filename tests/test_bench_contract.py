@@ -51,3 +51,8 @@ def test_bench_json_line():
     assert isinstance(cb["sample"], str) and cb["sample"]
     host = d["host"]
     assert host["nproc"] >= 1 and "cpu_model" in host
+    # the pool placement the value was measured on, and the same step with same-phase pools
+    pp = d["pool_placement"]
+    assert pp["v_minus_k_mod_1KiB"] == 256 and pp["min_minus_max_mod_1KiB"] == 256
+    sp = pp["same_phase_pools"]
+    assert sp["v_minus_k_mod_1KiB"] == 0 and sp["min_minus_max_mod_1KiB"] == 0 and sp["steps_per_s"] > 0
