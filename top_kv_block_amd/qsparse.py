@@ -541,7 +541,10 @@ def qs_select_attn_decode_static(query, maxblocks, minblocks, metadata_block_tab
 
 def alloc_paired_pools(shape, dtype, device=None, zero=False):
     """Two contiguous tensors of `shape` (views of one allocation, uninitialised unless
-    `zero`), the second starting 256 bytes past a 1 KiB multiple from the first."""
+    `zero`), the second starting 256 bytes past a 1 KiB multiple from the first; on the
+    current GPU unless `device` is given."""
+    if device is None:
+        device = torch.device("cuda", torch.cuda.current_device())
     n = 1
     for d in shape:
         n *= int(d)
